@@ -1,0 +1,206 @@
+"""Python binding of libw4, the MI355X W4A16 decode library.
+
+Argument marshalling only: every function here takes torch device tensors,
+passes their device pointers and the current HIP stream to the C entry point of
+the same name in ``libw4.so`` (declared in ``include/w4.h``), and raises on a
+non-zero status.  Nothing is computed in Python and there is no fallback: if
+``libw4.so`` is missing or fails to load, the import fails.
+
+Tensor conventions:
+  codes  int32 (or uint32) tensor [N, K/8]: packed words (nibble j of word w is
+         column 8w+j);
+  steps  bfloat16 tensor (or int16/uint16 holding bf16 bits) [N, K/32];
+  activations float16 or bfloat16 tensors (their dtype selects W4_F16/W4_BF16);
+  outputs float32 (products) or bfloat16 (row gather).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # must load before libw4 so that both share torch's HIP runtime
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libw4.so")
+
+W4_OK = 0
+W4_ERR_INVALID_ARG = -1
+W4_ERR_ALIGNMENT = -2
+W4_ERR_DTYPE = -3
+W4_ERR_UNSUPPORTED = -4
+W4_ERR_NODEV = -5
+W4_ERR_HIP = -6
+W4_F16 = 0
+W4_BF16 = 1
+W4_MAX_K = 16384
+W4_MAX_M = 16
+W4_MAX_TOPK = 32
+W4_CHAIN_SYNC_BYTES = 4096
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with bit_weight_only_02_amd/build.py "
+                      "(or __graft_entry__.build()) first")
+
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_I64 = ctypes.c_int64
+
+lib = ctypes.CDLL(LIB_PATH)
+
+_SIGNATURES = {
+    "w4_gemv": [_P, _P, _I32, _I32, _P, _I32, _P, _P],
+    "w4_gemm_smallM": [_P, _P, _I32, _I32, _P, _I32, _I32, _I64, _P, _I64, _P],
+    "w4_moe_gemv_ids": [_P, _P, _I64, _I64, _I32, _I32, _P, _I32, _I32, _I64, _P, _I32, _I32,
+                        _P, _I32, _I32, _P, _P, _P, _P, _P],
+    "w4_embed_gather": [_P, _P, _I32, _I32, _P, _I32, _P, _P, _P],
+    "w4_rms_renorm": [_P, _I32, _P, _I32, _P],
+    "w4_gemv_chain": [_P, _P, _P, _P, _I32, _P, _P, _P, _P],
+    "w4_probe_stream": [_P, _I64, _P, _P],
+}
+for _name, _args in _SIGNATURES.items():
+    _fn = getattr(lib, _name)
+    _fn.argtypes = _args
+    _fn.restype = ctypes.c_int
+lib.w4_strerror.argtypes = [ctypes.c_int]
+lib.w4_strerror.restype = ctypes.c_char_p
+lib.w4_last_error_detail.argtypes = []
+lib.w4_last_error_detail.restype = ctypes.c_char_p
+
+
+class W4Error(RuntimeError):
+    def __init__(self, status: int, fn: str):
+        self.status = status
+        detail = lib.w4_last_error_detail().decode()
+        super().__init__(f"{fn}: {lib.w4_strerror(status).decode()} ({status}) {detail}")
+
+
+def _check(status: int, fn: str) -> None:
+    if status != W4_OK:
+        raise W4Error(status, fn)
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream=None) -> int:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _act_dtype(t: torch.Tensor) -> int:
+    if t.dtype == torch.float16:
+        return W4_F16
+    if t.dtype == torch.bfloat16:
+        return W4_BF16
+    raise TypeError(f"activations must be float16 or bfloat16, got {t.dtype}")
+
+
+def _matrix(codes: torch.Tensor, steps: torch.Tensor):
+    if codes.dim() != 2 or steps.dim() != 2:
+        raise ValueError("codes and steps must be 2-D [N, K/8] and [N, K/32]")
+    if codes.element_size() != 4 or steps.element_size() != 2:
+        raise TypeError("codes must hold 32-bit words and steps 16-bit bf16 bits")
+    if not (codes.is_contiguous() and steps.is_contiguous()):
+        raise ValueError("codes and steps must be contiguous")
+    N, K = codes.shape[0], codes.shape[1] * 8
+    if tuple(steps.shape) != (N, K // 32):
+        raise ValueError(f"steps shape {tuple(steps.shape)} does not match codes [N={N}, K={K}]")
+    return N, K
+
+
+def w4_gemv(codes, steps, x, y=None, stream=None):
+    """y[n] = sum_k (code(n,k) - 8) * step(n,k/32) * x[k]; returns y (fp32 [N])."""
+    N, K = _matrix(codes, steps)
+    if x.numel() != K or not x.is_contiguous():
+        raise ValueError("x must be contiguous with K elements")
+    if y is None:
+        y = torch.empty(N, dtype=torch.float32, device=codes.device)
+    _check(lib.w4_gemv(_ptr(codes), _ptr(steps), N, K, _ptr(x), _act_dtype(x), _ptr(y),
+                       _stream(stream)), "w4_gemv")
+    return y
+
+
+def w4_gemm_smallM(codes, steps, X, Y=None, stream=None):
+    """Y[m, n] for the M rows of X ([M, ldx] with row stride >= K); Y fp32 [M, N]."""
+    N, K = _matrix(codes, steps)
+    if X.dim() != 2 or X.stride(1) != 1 or X.shape[1] < K:
+        raise ValueError("X must be [M, >=K] with unit column stride")
+    M = X.shape[0]
+    if Y is None:
+        Y = torch.empty((M, N), dtype=torch.float32, device=codes.device)
+    if Y.dim() != 2 or Y.stride(1) != 1 or Y.shape[0] != M or Y.shape[1] < N:
+        raise ValueError("Y must be [M, >=N] with unit column stride")
+    _check(lib.w4_gemm_smallM(_ptr(codes), _ptr(steps), N, K, _ptr(X), _act_dtype(X), M,
+                              X.stride(0), _ptr(Y), Y.stride(0), _stream(stream)),
+           "w4_gemm_smallM")
+    return Y
+
+
+def w4_moe_gemv_ids(codes_base, steps_base, expert_stride_codes, expert_stride_steps, N, K,
+                    X, ids, x_per_pair=False, slot_of=None, n_experts=None, n_slots=0,
+                    row_scale=None, route_w=None, Y=None, dev_err=None, stream=None):
+    """Expert-indexed product (see w4.h).  ``ids`` int32 [T, topk] of real ids;
+    strides in uint32 words / uint16 elements; ``slot_of`` int32 [n_experts]
+    selects pool addressing."""
+    T, topk = ids.shape
+    if n_experts is None:
+        raise ValueError("n_experts is required")
+    if X.dim() != 2 or X.stride(1) != 1:
+        raise ValueError("X must be 2-D with unit column stride")
+    rows = T * topk if route_w is None else T
+    if Y is None:
+        Y = torch.empty((rows, N), dtype=torch.float32, device=X.device)
+    _check(lib.w4_moe_gemv_ids(_ptr(codes_base), _ptr(steps_base), expert_stride_codes,
+                               expert_stride_steps, N, K, _ptr(X), _act_dtype(X),
+                               1 if x_per_pair else 0, X.stride(0), _ptr(ids), T, topk,
+                               _ptr(slot_of), n_experts, n_slots, _ptr(row_scale),
+                               _ptr(route_w), _ptr(Y), _ptr(dev_err), _stream(stream)),
+           "w4_moe_gemv_ids")
+    return Y
+
+
+def w4_embed_gather(codes, steps, ids, out=None, dev_err=None, stream=None):
+    """bf16 rows (code - 8) * step of the table rows ``ids``; returns [n, K] bf16."""
+    V, K = _matrix(codes, steps)
+    n = ids.numel()
+    if out is None:
+        out = torch.empty((n, K), dtype=torch.bfloat16, device=codes.device)
+    _check(lib.w4_embed_gather(_ptr(codes), _ptr(steps), V, K, _ptr(ids), n, _ptr(out),
+                               _ptr(dev_err), _stream(stream)), "w4_embed_gather")
+    return out
+
+
+def w4_rms_renorm(v, K, out=None, out_dtype=torch.float16, stream=None):
+    """Leading K entries of fp32 ``v`` divided by their RMS, rounded to out_dtype."""
+    if out is None:
+        out = torch.empty(K, dtype=out_dtype, device=v.device)
+    _check(lib.w4_rms_renorm(_ptr(v), K, _ptr(out), _act_dtype(out), _stream(stream)),
+           "w4_rms_renorm")
+    return out
+
+
+def w4_gemv_chain(mats, x0, ys, sync, stream=None):
+    """Chained products (see w4.h): ``mats`` is a list of (codes, steps)."""
+    n = len(mats)
+    Ns, Ks = [], []
+    for c, s in mats:
+        N, K = _matrix(c, s)
+        Ns.append(N)
+        Ks.append(K)
+    arr_p = ctypes.c_void_p * n
+    arr_i = ctypes.c_int32 * n
+    codes = arr_p(*[c.data_ptr() for c, _ in mats])
+    steps = arr_p(*[s.data_ptr() for _, s in mats])
+    yp = arr_p(*[y.data_ptr() for y in ys])
+    _check(lib.w4_gemv_chain(codes, steps, arr_i(*Ns), arr_i(*Ks), n, _ptr(x0), yp, _ptr(sync),
+                             _stream(stream)), "w4_gemv_chain")
+    return ys
+
+
+def w4_probe_stream(buf, out, stream=None):
+    """Streaming read of ``buf`` (bytes multiple of 16); word sum added into out."""
+    _check(lib.w4_probe_stream(_ptr(buf), buf.numel() * buf.element_size(), _ptr(out),
+                               _stream(stream)), "w4_probe_stream")
+    return out

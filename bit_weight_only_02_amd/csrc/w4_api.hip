@@ -1,0 +1,146 @@
+// C ABI of libw4: argument checks on the host, then launches on the caller's
+// stream.  Declarations and the contract of every entry point are in w4.h.
+//
+// A failed call never reports success over untouched outputs (the ardana.ai
+// page "Fixing Gemma 4's oversized KV cache", section "A failed decode must not
+// look uncertain"): argument errors return before anything is enqueued, launch
+// errors are read back with hipGetLastError and returned as W4_ERR_HIP.
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+
+#include "w4.h"
+#include "w4_internal.h"
+
+namespace {
+
+thread_local char g_detail[256] = "";
+
+int fail(int status, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int status, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_detail, sizeof(g_detail), fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Test hook: W4_FORCE_LAUNCH_ERROR=1 makes every entry point return W4_ERR_HIP
+// after validation without enqueuing anything, so that tests can check that
+// outputs stay untouched on a failed call.
+bool forced_launch_error() {
+    const char *e = getenv("W4_FORCE_LAUNCH_ERROR");
+    return e && e[0] == '1';
+}
+
+int device_ready() {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(W4_ERR_NODEV, "hipGetDevice: %s", hipGetErrorString(e));
+    return W4_OK;
+}
+
+int launched(hipError_t e, const char *what) {
+    if (e != hipSuccess) return fail(W4_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+    g_detail[0] = 0;
+    return W4_OK;
+}
+
+int check_matrix(const uint32_t *codes, const uint16_t *steps, int32_t N, int32_t K) {
+    if (N < 0 || K < 0) return fail(W4_ERR_INVALID_ARG, "negative size N=%d K=%d", N, K);
+    if (K % 32) return fail(W4_ERR_INVALID_ARG, "K=%d is not a multiple of 32", K);
+    if (K > W4_MAX_K) return fail(W4_ERR_UNSUPPORTED, "K=%d exceeds %d", K, W4_MAX_K);
+    if (N > 0 && K > 0 && (!codes || !steps)) return fail(W4_ERR_INVALID_ARG, "null codes/steps");
+    if (codes && !aligned(codes, 16)) return fail(W4_ERR_ALIGNMENT, "codes not 16-byte aligned");
+    if (steps && !aligned(steps, 2)) return fail(W4_ERR_ALIGNMENT, "steps not 2-byte aligned");
+    return W4_OK;
+}
+
+int check_dtype(int32_t dt) {
+    if (dt != W4_F16 && dt != W4_BF16) return fail(W4_ERR_DTYPE, "unknown dtype %d", dt);
+    return W4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int w4_gemv(const uint32_t *codes, const uint16_t *steps, int32_t N, int32_t K,
+            const void *x, int32_t xdt, float *y, void *stream) {
+    int st;
+    if ((st = check_matrix(codes, steps, N, K))) return st;
+    if ((st = check_dtype(xdt))) return st;
+    if (N > 0 && (!y || (K > 0 && !x))) return fail(W4_ERR_INVALID_ARG, "null x/y");
+    if (x && !aligned(x, 2)) return fail(W4_ERR_ALIGNMENT, "x not 2-byte aligned");
+    if (y && !aligned(y, 4)) return fail(W4_ERR_ALIGNMENT, "y not 4-byte aligned");
+    if (N == 0) return W4_OK;
+    if ((st = device_ready())) return st;
+    if (forced_launch_error()) return fail(W4_ERR_HIP, "forced launch error (test hook)");
+    return launched(w4::launch_gemv(codes, steps, N, K, static_cast<const uint16_t *>(x), xdt, y,
+                                    static_cast<hipStream_t>(stream)),
+                    "w4_gemv");
+}
+
+int w4_embed_gather(const uint32_t *codes, const uint16_t *steps, int32_t V, int32_t K,
+                    const int32_t *ids, int32_t n, uint16_t *out_bf16, int32_t *dev_err,
+                    void *stream) {
+    int st;
+    if ((st = check_matrix(codes, steps, V, K))) return st;
+    if (n < 0) return fail(W4_ERR_INVALID_ARG, "negative n");
+    if (n > 0 && (!ids || !out_bf16)) return fail(W4_ERR_INVALID_ARG, "null ids/out");
+    if (n > 0 && K > 0 && (!codes || !steps)) return fail(W4_ERR_INVALID_ARG, "null codes/steps");
+    if (ids && !aligned(ids, 4)) return fail(W4_ERR_ALIGNMENT, "ids not 4-byte aligned");
+    if (out_bf16 && !aligned(out_bf16, 16)) return fail(W4_ERR_ALIGNMENT, "out not 16-byte aligned");
+    if (dev_err && !aligned(dev_err, 4)) return fail(W4_ERR_ALIGNMENT, "dev_err not aligned");
+    if (n == 0 || K == 0) return W4_OK;
+    if ((st = device_ready())) return st;
+    if (forced_launch_error()) return fail(W4_ERR_HIP, "forced launch error (test hook)");
+    return launched(w4::launch_gather(codes, steps, V, K, ids, n, out_bf16, dev_err,
+                                      static_cast<hipStream_t>(stream)),
+                    "w4_embed_gather");
+}
+
+int w4_rms_renorm(const float *v, int32_t K, void *out, int32_t out_dt, void *stream) {
+    int st;
+    if ((st = check_dtype(out_dt))) return st;
+    if (K < 0) return fail(W4_ERR_INVALID_ARG, "negative K");
+    if (K > 0 && (!v || !out)) return fail(W4_ERR_INVALID_ARG, "null v/out");
+    if (v && !aligned(v, 4)) return fail(W4_ERR_ALIGNMENT, "v not 4-byte aligned");
+    if (out && !aligned(out, 2)) return fail(W4_ERR_ALIGNMENT, "out not 2-byte aligned");
+    if (K == 0) return W4_OK;
+    if ((st = device_ready())) return st;
+    if (forced_launch_error()) return fail(W4_ERR_HIP, "forced launch error (test hook)");
+    return launched(w4::launch_rms_renorm(v, K, out, out_dt, static_cast<hipStream_t>(stream)),
+                    "w4_rms_renorm");
+}
+
+int w4_probe_stream(const void *buf, int64_t bytes, uint32_t *out, void *stream) {
+    int st;
+    if (bytes < 0 || bytes % 16) return fail(W4_ERR_INVALID_ARG, "bytes must be a multiple of 16");
+    if (!out || (bytes > 0 && !buf)) return fail(W4_ERR_INVALID_ARG, "null buf/out");
+    if ((buf && !aligned(buf, 16)) || !aligned(out, 4)) return fail(W4_ERR_ALIGNMENT, "misaligned");
+    if ((st = device_ready())) return st;
+    if (forced_launch_error()) return fail(W4_ERR_HIP, "forced launch error (test hook)");
+    return launched(w4::launch_probe_stream(buf, bytes, out, static_cast<hipStream_t>(stream)),
+                    "w4_probe_stream");
+}
+
+const char *w4_strerror(int status) {
+    switch (status) {
+        case W4_OK: return "ok";
+        case W4_ERR_INVALID_ARG: return "invalid argument";
+        case W4_ERR_ALIGNMENT: return "misaligned pointer";
+        case W4_ERR_DTYPE: return "unknown activation dtype";
+        case W4_ERR_UNSUPPORTED: return "unsupported size";
+        case W4_ERR_NODEV: return "no HIP device";
+        case W4_ERR_HIP: return "HIP launch or runtime error";
+    }
+    return "unknown status";
+}
+
+const char *w4_last_error_detail(void) { return g_detail; }
+
+}  // extern "C"

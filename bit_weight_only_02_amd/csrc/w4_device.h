@@ -1,0 +1,169 @@
+// Device helpers shared by the W4A16 kernels (gfx950 / CDNA4, wave64).
+//
+// Packed format: codes uint32[N][K/8] (nibble j of word w = column 8w+j), bf16
+// steps [N][K/32]; weight = (code - 8) * step.  One 16-byte load (uint4) of a
+// row is exactly one group of 32 codes, and it pairs with one bf16 step.
+//
+// Exact operands.  The dev.to page "Gemma 4 on a 4 GB GPU in Plain PyTorch"
+// (section "Step 3 - Multiply Straight From the Packed Weights") turns a code
+// into a float by OR-ing it into the bits of 2^23 and subtracting 2^23 + 8.
+// Here the same idea runs two lanes at a time in fp16: OR-ing a nibble into
+// the mantissa of 1024.0h gives 1024 + c exactly, and one packed subtract of
+// 1032 gives c - 8 exactly.  A nibble sitting four bits higher gives 1024 + 16c,
+// and one packed FMA (x 1/16, - 72) gives c - 8 exactly.  The packed pairs then
+// feed v_dot2_f32_f16, which multiplies fp16 pairs and accumulates in fp32.
+//
+// Activations are staged as fp16 scaled by a power of two 2^s chosen from the
+// vector's largest exponent (so that every staged value is a normal fp16 equal
+// to x * 2^s exactly).  Then every product (c - 8) * x * 2^s is exact in fp32,
+// and the result is scaled back by 2^-s at the end (also exact).  A vector whose
+// values cannot all be staged exactly (a dynamic range above 2^28, or inf/NaN)
+// takes a plain fp32 path instead, with the same exact products.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace w4 {
+
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ h2 as_h2(uint32_t u) { return __builtin_bit_cast(h2, u); }
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits) {
+    return __uint_as_float(bits << 16);
+}
+
+__device__ __forceinline__ float f16_to_f32(uint32_t bits) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
+}
+
+__device__ __forceinline__ float act_to_f32(uint32_t bits, int dt) {
+    return dt == 0 ? f16_to_f32(bits) : bf16_to_f32(bits);
+}
+
+// Unbiased exponent of a finite nonzero fp32 value that is normal in fp32
+// (every fp16 value and every normal bf16 value); -127 for fp32 subnormals.
+__device__ __forceinline__ int f32_exponent(float v) {
+    return (int)((__float_as_uint(v) >> 23) & 0xFFu) - 127;
+}
+
+// Eight codes of one packed word -> four exact fp16 pairs (c - 8), ordered
+// (c0,c4), (c1,c5), (c2,c6), (c3,c7).
+__device__ __forceinline__ void unpack_word(uint32_t w, h2 &p0, h2 &p1, h2 &p2, h2 &p3) {
+    const h2 kSub = {(_Float16)-1032.0f, (_Float16)-1032.0f};
+    const h2 kInv16 = {(_Float16)0.0625f, (_Float16)0.0625f};
+    const h2 kSub72 = {(_Float16)-72.0f, (_Float16)-72.0f};
+    const uint32_t u = w >> 8;
+    p0 = as_h2((w & 0x000F000Fu) | 0x64006400u) + kSub;
+    p1 = as_h2((w & 0x00F000F0u) | 0x64006400u) * kInv16 + kSub72;
+    p2 = as_h2((u & 0x000F000Fu) | 0x64006400u) + kSub;
+    p3 = as_h2((u & 0x00F000F0u) | 0x64006400u) * kInv16 + kSub72;
+}
+
+__device__ __forceinline__ float dot2(h2 a, h2 b, float c) {
+    return __builtin_amdgcn_fdot2(a, b, c, false);
+}
+
+// Sum over one group of 32 codes: q holds the 4 packed words, xr the 16 staged
+// activation pairs of the group in the order unpack_word produces.
+__device__ __forceinline__ float group_dot(uint4 q, const h2 *xr) {
+    h2 a0, a1, a2, a3;
+    float s0 = 0.0f, s1 = 0.0f;
+    unpack_word(q.x, a0, a1, a2, a3);
+    s0 = dot2(a0, xr[0], s0); s1 = dot2(a1, xr[1], s1);
+    s0 = dot2(a2, xr[2], s0); s1 = dot2(a3, xr[3], s1);
+    unpack_word(q.y, a0, a1, a2, a3);
+    s0 = dot2(a0, xr[4], s0); s1 = dot2(a1, xr[5], s1);
+    s0 = dot2(a2, xr[6], s0); s1 = dot2(a3, xr[7], s1);
+    unpack_word(q.z, a0, a1, a2, a3);
+    s0 = dot2(a0, xr[8], s0); s1 = dot2(a1, xr[9], s1);
+    s0 = dot2(a2, xr[10], s0); s1 = dot2(a3, xr[11], s1);
+    unpack_word(q.w, a0, a1, a2, a3);
+    s0 = dot2(a0, xr[12], s0); s1 = dot2(a1, xr[13], s1);
+    s0 = dot2(a2, xr[14], s0); s1 = dot2(a3, xr[15], s1);
+    return s0 + s1;
+}
+
+// Exact fp32 group sum for the fallback path: activations read as fp32 from a
+// pointer to the group's 32 raw values.
+__device__ __forceinline__ float group_dot_f32(uint4 q, const uint16_t *xg, int dt) {
+    float s = 0.0f;
+    const uint32_t ws[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int c = (int)((ws[w] >> (4 * j)) & 0xFu) - 8;
+            s = __builtin_fmaf((float)c, act_to_f32(xg[w * 8 + j], dt), s);
+        }
+    }
+    return s;
+}
+
+// Position (in halves) of column i inside the staged pair layout: group g,
+// word w = (i % 32) / 8, lane j = i % 8 -> pair (j % 4) of the word, half j / 4.
+__device__ __forceinline__ int staged_index(int i) {
+    const int g = i >> 5, w = (i >> 3) & 3, j = i & 7;
+    return ((((g << 2) + w) << 2) + (j & 3)) * 2 + (j >> 2);
+}
+
+__device__ __forceinline__ int wave_max_i32(int v) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v = max(v, __shfl_xor(v, off, kWave));
+    return v;
+}
+
+__device__ __forceinline__ int wave_or_i32(int v) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v |= __shfl_xor(v, off, kWave);
+    return v;
+}
+
+struct Staging {
+    int scale;     // s: staged value = x * 2^s
+    int fallback;  // 1: the vector cannot be staged exactly; use the fp32 path
+};
+
+// Stage activations x[0..K) into `xs` (K halves, pair layout) as x * 2^s.
+// Every thread of the workgroup must call this (it contains barriers).
+// `red` is 2 * (blockDim/64) ints of shared scratch.
+__device__ __forceinline__ Staging stage_activations(const uint16_t *__restrict__ x, int K,
+                                                     int dt, _Float16 *xs, int *red) {
+    const int tid = threadIdx.x, nt = blockDim.x;
+    const int wave = tid >> 6, nwaves = nt >> 6;
+    int emax = -100000, bad = 0;
+    for (int i = tid; i < K; i += nt) {
+        const float v = act_to_f32(x[i], dt);
+        if (!__builtin_isfinite(v)) bad = 1;
+        else if (v != 0.0f) emax = max(emax, f32_exponent(v));
+    }
+    emax = wave_max_i32(emax);
+    bad = wave_or_i32(bad);
+    if ((tid & 63) == 0) { red[wave] = emax; red[nwaves + wave] = bad; }
+    __syncthreads();
+    emax = red[0]; bad = red[nwaves];
+    for (int w = 1; w < nwaves; ++w) { emax = max(emax, red[w]); bad |= red[nwaves + w]; }
+    const int s = (emax == -100000) ? 0 : 14 - emax;
+    int lost = 0;
+    if (!bad) {
+        for (int i = tid; i < K; i += nt) {
+            const float v = act_to_f32(x[i], dt);
+            if (v != 0.0f && f32_exponent(v) < emax - 28) lost = 1;
+            xs[staged_index(i)] = (_Float16)__builtin_ldexpf(v, s);
+        }
+    }
+    lost = wave_or_i32(lost);
+    __syncthreads();  // everyone has read red[] before it is rewritten
+    if ((tid & 63) == 0) red[wave] = lost;
+    __syncthreads();
+    for (int w = 0; w < nwaves; ++w) lost |= red[w];
+    Staging st;
+    st.scale = s;
+    st.fallback = bad | lost;
+    return st;
+}
+
+}  // namespace w4

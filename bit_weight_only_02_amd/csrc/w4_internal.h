@@ -1,0 +1,32 @@
+// Internal launchers of libw4 (host side).  Every launcher enqueues on `stream`
+// and returns hipGetLastError() of its launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace w4 {
+
+struct GemvTile {
+    int L;       // lanes per row slot
+    int NG;      // groups per lane
+    int R;       // rows per slot in flight
+    int waves;   // waves per workgroup
+    int blocks;  // workgroups
+};
+
+GemvTile gemv_tile(int N, int K);
+
+hipError_t launch_gemv(const uint32_t *codes, const uint16_t *steps, int N, int K,
+                       const uint16_t *x, int dt, float *y, hipStream_t stream);
+
+hipError_t launch_gather(const uint32_t *codes, const uint16_t *steps, int V, int K,
+                         const int32_t *ids, int n, uint16_t *out, int32_t *dev_err,
+                         hipStream_t stream);
+
+hipError_t launch_rms_renorm(const float *v, int K, void *out, int out_dt, hipStream_t stream);
+
+hipError_t launch_probe_stream(const void *buf, int64_t bytes, uint32_t *out,
+                               hipStream_t stream);
+
+}  // namespace w4

@@ -1,0 +1,67 @@
+// Small kernels around the products: the renormalisation between chained
+// products, and a plain streaming-read probe.
+#include "w4_device.h"
+#include "w4_internal.h"
+
+namespace w4 {
+
+// Leading K entries u of v -> u / sqrt(mean(u^2)), rounded to nearest-even in
+// fp16 (out_dt 0) or bf16 (out_dt 1).  One workgroup of 1024 threads; the sum
+// of squares is accumulated in fp64 in a fixed order.
+__global__ __launch_bounds__(1024) void rms_renorm_kernel(const float *__restrict__ v, int K,
+                                                          uint16_t *__restrict__ out, int out_dt) {
+    __shared__ double part[16];
+    const int tid = threadIdx.x;
+    double ss = 0.0;
+    for (int k = tid; k < K; k += blockDim.x) ss += (double)v[k] * (double)v[k];
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off, kWave);
+    if ((tid & 63) == 0) part[tid >> 6] = ss;
+    __syncthreads();
+    double tot = 0.0;
+    for (int w = 0; w < (int)(blockDim.x >> 6); ++w) tot += part[w];
+    const double r = sqrt(tot / (double)K);
+    for (int k = tid; k < K; k += blockDim.x) {
+        const float q = r > 0.0 ? (float)((double)v[k] / r) : 0.0f;
+        out[k] = out_dt == 0 ? __builtin_bit_cast(uint16_t, (_Float16)q)
+                             : __builtin_bit_cast(uint16_t, (__bf16)q);
+    }
+}
+
+hipError_t launch_rms_renorm(const float *v, int K, void *out, int out_dt, hipStream_t stream) {
+    hipLaunchKernelGGL(rms_renorm_kernel, dim3(1), dim3(1024), 0, stream, v, K,
+                       static_cast<uint16_t *>(out), out_dt);
+    return hipGetLastError();
+}
+
+// Streaming read: sum of all 32-bit words (mod 2^32) into *out.  Integer adds
+// only, so the result is order independent.
+__global__ __launch_bounds__(256) void probe_stream_kernel(const uint4 *__restrict__ buf,
+                                                           int64_t n16, uint32_t *__restrict__ out) {
+    uint32_t s = 0;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    for (; i + 3 * stride < n16; i += 4 * stride) {
+        const uint4 a = buf[i], b = buf[i + stride], c = buf[i + 2 * stride], d = buf[i + 3 * stride];
+        s += a.x + a.y + a.z + a.w + b.x + b.y + b.z + b.w + c.x + c.y + c.z + c.w + d.x + d.y + d.z + d.w;
+    }
+    for (; i < n16; i += stride) {
+        const uint4 a = buf[i];
+        s += a.x + a.y + a.z + a.w;
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off, kWave);
+    if ((threadIdx.x & 63) == 0) atomicAdd(out, s);
+}
+
+hipError_t launch_probe_stream(const void *buf, int64_t bytes, uint32_t *out, hipStream_t stream) {
+    const int64_t n16 = bytes / 16;
+    int64_t blocks = (n16 + 256 * 4 - 1) / (256 * 4);
+    if (blocks > 4096) blocks = 4096;
+    if (blocks < 1) blocks = 1;
+    hipLaunchKernelGGL(probe_stream_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       static_cast<const uint4 *>(buf), n16, out);
+    return hipGetLastError();
+}
+
+}  // namespace w4

@@ -1,0 +1,196 @@
+/*
+ * w4.h -- C ABI of the MI355X (gfx950) W4A16 decode library (libw4.so).
+ *
+ * The operation throughout is the decode-time product of a 4-bit weight-only
+ * quantised matrix with a 16-bit activation vector, computed straight from the
+ * packed weights without ever writing a 16-bit copy of them.
+ *
+ * Sources of the operations (web pages; cited by title and section):
+ *   [P1-S1] dev.to, "Gemma 4 on a 4 GB GPU in Plain PyTorch: From Out of Memory
+ *           to Faster Than llama.cpp", section "Step 1 - Load Google's QAT
+ *           Weights Without Unpacking Them": the W4A16 format -- 4-bit codes in
+ *           groups of 32, one bf16 step per group, 16-bit activations.
+ *   [P1-S2] same page, "Step 2 - Keep the Vocabulary Tables in 4-Bit": the
+ *           vocabulary table kept as 4-bit codes; one copy serves as the input
+ *           embedding (a row lookup) and as the output layer (a GEMV).
+ *   [P1-S3] same page, "Step 3 - Multiply Straight From the Packed Weights":
+ *           a decode step multiplies one vector by every weight matrix, reading
+ *           packed words and unpacking in registers; code c stands for c - 8.
+ *   [P1-S4] same page, "Step 4 - Replay Each Decode Step as One CUDA Graph" and
+ *           the tip "Merge the Small Projections": a decode step is a long chain
+ *           of small products, run without host launches in between.
+ *   [P3]    anyesh.me, "Running a 26B MoE on an 8 GB Jetson by streaming experts
+ *           from SSD", section "Streaming without touching a single GPU kernel":
+ *           the expert matmul addresses expert id as base + id * stride; a pool
+ *           of slots is read through slot ids and must give bitwise the same
+ *           result; per-expert side tensors keep the real expert id.
+ *   [P2]    ardana.ai, "Fixing Gemma 4's oversized KV cache", section "A failed
+ *           decode must not look uncertain": a failed GPU call must never
+ *           leave an untouched output that looks like a valid result.
+ *
+ * Storage format (shared by every entry point):
+ *   codes  uint32[N][K/8], row-major; nibble j (bits 4j..4j+3) of word w of a
+ *          row is the code of column 8w+j.  Must be 16-byte aligned.
+ *   steps  bf16[N][K/32] (raw uint16 bits), row-major; step of group g of row n
+ *          at steps[n*(K/32) + g].
+ *   weight w(n,k) = (code(n,k) - 8) * step(n, k/32).
+ *   K must be a multiple of 32 and at most W4_MAX_K.
+ *   Activations are fp16 or bf16 (raw uint16 bits).  Outputs of products are
+ *   fp32; the row gather writes bf16.
+ *
+ * Conventions:
+ *   - All array pointers are DEVICE pointers owned by the caller.  Besides the
+ *     per-device staging buffer documented at w4_moe_gemv_ids, the library
+ *     allocates nothing and frees nothing.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Calls
+ *     enqueue and return; the caller synchronises.
+ *   - Return value: W4_OK (0) or a negative w4_status.  Argument errors are
+ *     detected on the host before any launch (nothing is enqueued, outputs are
+ *     untouched).  A failed launch returns W4_ERR_HIP; W4_OK is returned only
+ *     after every kernel of the call has been enqueued.
+ *   - Results do not depend on pointer values, alignment or the stream: the
+ *     kernel configuration is chosen from the shape alone, and no float atomics
+ *     are used, so every call is bitwise reproducible.
+ *   - Numerics: each product c-8 times an activation is exact; sums run in fp32.
+ *     Every product output satisfies |y - y_exact| <= 1e-3 * sum_k |w(n,k) x_k|.
+ *   - Thread safety: entry points may be called from several host threads and
+ *     streams at once.
+ */
+#ifndef W4_H
+#define W4_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    W4_OK = 0,
+    W4_ERR_INVALID_ARG = -1, /* null pointer, bad size, K % 32 != 0, ... */
+    W4_ERR_ALIGNMENT = -2,   /* a pointer is not aligned as documented */
+    W4_ERR_DTYPE = -3,       /* unknown activation dtype */
+    W4_ERR_UNSUPPORTED = -4, /* valid but beyond this build's limits */
+    W4_ERR_NODEV = -5,       /* no usable HIP device */
+    W4_ERR_HIP = -6          /* a HIP call or kernel launch failed */
+} w4_status;
+
+typedef enum { W4_F16 = 0, W4_BF16 = 1 } w4_dtype;
+
+#define W4_MAX_K 16384  /* largest supported K (input length) */
+#define W4_MAX_M 16     /* largest M of w4_gemm_smallM */
+#define W4_MAX_TOPK 32  /* largest experts per token of w4_moe_gemv_ids */
+
+/*
+ * Batch-1 product [P1-S3]:  y[n] = sum_k w(n,k) * x[k]  for n in [0, N).
+ *   codes, steps: one packed matrix [N][K] (see above).
+ *   x:   K activations of dtype xdt (W4_F16 or W4_BF16), 2-byte aligned.
+ *   y:   N floats (written, never read).
+ * N == 0 is a no-op; K == 0 writes zeros.
+ */
+int w4_gemv(const uint32_t *codes, const uint16_t *steps, int32_t N, int32_t K,
+            const void *x, int32_t xdt, float *y, void *stream);
+
+/*
+ * Small-batch product [P1-S3] with M activation rows, 1 <= M <= W4_MAX_M:
+ *   Y[m*ldy + n] = sum_k w(n,k) * X[m*ldx + k]   for m < M, n < N.
+ * Each weight is read from memory once for all M rows.  ldx >= K, ldy >= N.
+ */
+int w4_gemm_smallM(const uint32_t *codes, const uint16_t *steps, int32_t N, int32_t K,
+                   const void *X, int32_t xdt, int32_t M, int64_t ldx,
+                   float *Y, int64_t ldy, void *stream);
+
+/*
+ * Expert-indexed product [P3].  T tokens each select topk experts:
+ * ids[t*topk + j] is a REAL expert id in [0, n_experts).  The weights used for
+ * that choice are the packed matrix [N][K] at
+ *     codes_base + a * expert_stride_codes   (uint32 units, multiple of 4)
+ *     steps_base + a * expert_stride_steps   (uint16 units)
+ * with a = ids[...] (slot_of == NULL: direct addressing) or a = slot_of[id]
+ * (pool addressing; slot_of is int32[n_experts] on the device, values in
+ * [0, n_slots), -1 for "not resident").  Both addressings run the same kernels
+ * with the same reduction order, so equal bytes give bitwise equal results.
+ *
+ *   X: activation rows, ldx apart: row t (x_per_pair == 0, the same input for
+ *      all choices of a token) or row t*topk + j (x_per_pair == 1).
+ *   row_scale: optional float[n_experts][N] per-expert output scale, ALWAYS
+ *      indexed by the real id (only the weight read goes through slot_of).
+ *   route_w: optional float[T][topk].  NULL: Y is float[T*topk][N], one row per
+ *      choice.  Non-NULL: Y is float[T][N] = sum over j = 0..topk-1 (ascending)
+ *      of route_w[t][j] * (choice j's row).
+ *   A choice used by several tokens reads its expert's weights once.
+ *   dev_err: optional device int32; an id or slot out of range sets it to 1 and
+ *      fills the affected output rows with NaN (never leaves them untouched).
+ *   The combined form (route_w != NULL) stages per-choice rows in a device
+ *   buffer the library allocates once per device and reuses (grown on demand
+ *   while no graph capture is active; concurrent combined calls on one device
+ *   from different streams are serialised by the caller).
+ * Limits: T*topk <= 1024, topk <= W4_MAX_TOPK.
+ */
+int w4_moe_gemv_ids(const uint32_t *codes_base, const uint16_t *steps_base,
+                    int64_t expert_stride_codes, int64_t expert_stride_steps,
+                    int32_t N, int32_t K,
+                    const void *X, int32_t xdt, int32_t x_per_pair, int64_t ldx,
+                    const int32_t *ids, int32_t T, int32_t topk,
+                    const int32_t *slot_of, int32_t n_experts, int32_t n_slots,
+                    const float *row_scale, const float *route_w,
+                    float *Y, int32_t *dev_err, void *stream);
+
+/*
+ * Row gather from a 4-bit table [P1-S2] (the input-embedding use of the same
+ * table that w4_gemv multiplies as the output layer):
+ *   out[i*K + k] = bf16_round_nearest_even((code(ids[i], k) - 8) * step)
+ * for i < n.  The product is exact in fp32, so the result is bit-exact.
+ *   ids: int32[n] on the device; an id outside [0, V) sets *dev_err (if given)
+ *   to 1 and fills that output row with bf16 NaN.
+ */
+int w4_embed_gather(const uint32_t *codes, const uint16_t *steps, int32_t V, int32_t K,
+                    const int32_t *ids, int32_t n, uint16_t *out_bf16,
+                    int32_t *dev_err, void *stream);
+
+/*
+ * Renormalisation between chained products [P1-S4]: take the leading K entries
+ * u of the fp32 vector v, r = sqrt(mean(u^2)), and write out[k] = u[k] / r
+ * rounded to nearest-even in dtype out_dt (zeros if r == 0).  Runs on the device
+ * in one workgroup.
+ */
+int w4_rms_renorm(const float *v, int32_t K, void *out, int32_t out_dt, void *stream);
+
+/*
+ * One decode-step chain as a single launch [P1-S4]: n_mats packed matrices
+ * applied in sequence.  Matrix i has shape [Ns[i]][Ks[i]] at codes[i], steps[i]
+ * and writes float ys[i][Ns[i]].  Its input is x0 (dtype W4_F16, Ks[0] long)
+ * for i == 0, else the renormalisation above applied to the leading Ks[i]
+ * entries of ys[i-1] (Ks[i] <= Ns[i-1]), rounded to fp16.  The weights of the
+ * next matrix are fetched while the previous one finishes.
+ *   codes, steps, ys, Ns, Ks: HOST arrays of n_mats device pointers / sizes.
+ *   sync: device buffer of at least W4_CHAIN_SYNC_BYTES bytes, zeroed by the
+ *   caller before the first call and left zeroed by every call that returns
+ *   W4_OK and completes.
+ * Results equal n_mats calls of w4_gemv with w4_rms_renorm in between
+ * (bitwise for the products, given the same inputs).
+ */
+#define W4_CHAIN_SYNC_BYTES 4096
+int w4_gemv_chain(const uint32_t *const *codes, const uint16_t *const *steps,
+                  const int32_t *Ns, const int32_t *Ks, int32_t n_mats,
+                  const uint16_t *x0, float *const *ys, void *sync, void *stream);
+
+/*
+ * Plain streaming read of `bytes` bytes (a multiple of 16, buf 16-byte aligned):
+ * every 32-bit word is added into *out (device uint32, mod 2^32; the caller
+ * zeroes it).  This is the memory-read ceiling that product bandwidths are
+ * quoted against ([P1-S3] compares its kernel with a plain sum over memory).
+ */
+int w4_probe_stream(const void *buf, int64_t bytes, uint32_t *out, void *stream);
+
+/* Static description of a status code. */
+const char *w4_strerror(int status);
+
+/* Detail of the last error returned on this host thread ("" if none). */
+const char *w4_last_error_detail(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W4_H */

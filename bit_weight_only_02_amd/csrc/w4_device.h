@@ -89,16 +89,15 @@ __device__ __forceinline__ float group_dot(uint4 q, const h2 *xr) {
 
 // Exact fp32 group sum for the fallback path: activations read as fp32 from a
 // pointer to the group's 32 raw values.
-__device__ __forceinline__ float group_dot_f32(uint4 q, const uint16_t *xg, int dt) {
+// (Kept rolled: it is the rare path, and unrolling it would raise the register
+// count of the whole kernel.)
+__device__ __noinline__ float group_dot_f32(uint4 q, const uint16_t *xg, int dt) {
     float s = 0.0f;
-    const uint32_t ws[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int c = (int)((ws[w] >> (4 * j)) & 0xFu) - 8;
-            s = __builtin_fmaf((float)c, act_to_f32(xg[w * 8 + j], dt), s);
-        }
+#pragma unroll 1
+    for (int k = 0; k < 32; ++k) {
+        const uint32_t word = k < 8 ? q.x : k < 16 ? q.y : k < 24 ? q.z : q.w;
+        const int c = (int)((word >> (4 * (k & 7))) & 0xFu) - 8;
+        s = __builtin_fmaf((float)c, act_to_f32(xg[k], dt), s);
     }
     return s;
 }
@@ -127,38 +126,97 @@ struct Staging {
     int fallback;  // 1: the vector cannot be staged exactly; use the fp32 path
 };
 
-// Stage activations x[0..K) into `xs` (K halves, pair layout) as x * 2^s.
-// Every thread of the workgroup must call this (it contains barriers).
-// `red` is 2 * (blockDim/64) ints of shared scratch.
-__device__ __forceinline__ Staging stage_activations(const uint16_t *__restrict__ x, int K,
-                                                     int dt, _Float16 *xs, int *red) {
+// Staging is split in two so that a kernel can put its first weight loads in
+// flight between the two halves.  stage_issue() requests all of x straight into
+// LDS (global_load_lds_dwordx4: no registers; each wave moves 64 chunks of 16
+// bytes per instruction); the kernel then issues its first weight loads; and
+// stage_complete() waits for every outstanding load before reading the staged
+// bytes.  (Waiting for a partial count would depend on the compiler keeping
+// the weight loads after the activation loads, which it does not promise.)
+// `raw` needs stage_raw_halves(K) halves.
+__device__ __forceinline__ bool stage_vector_path(const uint16_t *x) {
+    return (reinterpret_cast<uintptr_t>(x) & 15) == 0;
+}
+
+__host__ __device__ constexpr int stage_raw_halves(int K) {
+    return ((K / 8 + 63) / 64) * 64 * 8;
+}
+
+__device__ __forceinline__ void stage_issue(const uint16_t *__restrict__ x, int K, uint16_t *raw) {
+    const int n16 = K >> 3;
+    if (!stage_vector_path(x) || n16 == 0) return;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const uint4 *x16 = reinterpret_cast<const uint4 *>(x);
+    uint4 *r16 = reinterpret_cast<uint4 *>(raw);
+    for (int c0 = wave * 64; c0 < n16; c0 += (int)blockDim.x) {
+        const int c = min(c0 + lane, n16 - 1);
+        __builtin_amdgcn_global_load_lds(
+            (const __attribute__((address_space(1))) void *)(x16 + c),
+            (__attribute__((address_space(3))) void *)(r16 + c0), 16, 0, 0);
+    }
+}
+
+// Workgroup barrier that orders LDS accesses only.  __syncthreads() also makes
+// the wave wait for every outstanding global load (its release fence covers all
+// address spaces), which would stall on weight loads that were deliberately
+// left in flight across the barrier.
+// Written as one asm statement with a memory clobber: the compiler neither
+// moves memory accesses across it nor adds waits for loads still in flight.
+// LDS written by global_load_lds must be waited for (wait_vmcnt) beforehand.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Wait until at most `pending` vector-memory loads are outstanding (gfx9
+// s_waitcnt encoding: vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt left at
+// their maxima so they are not waited for).
+template <int pending>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(pending >= 0 && pending < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((pending & 15) | ((pending >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Stage activations x[0..K) into `xs` (K halves, pair layout) as x * 2^s,
+// after stage_issue().  `red` is 2*(blockDim/64) ints.  Every thread of the
+// workgroup must call this (it has barriers).
+__device__ __forceinline__ Staging stage_complete(const uint16_t *__restrict__ x, int K, int dt,
+                                                  _Float16 *xs, uint16_t *raw, int *red) {
     const int tid = threadIdx.x, nt = blockDim.x;
     const int wave = tid >> 6, nwaves = nt >> 6;
+    // 1. raw copy global -> LDS: issued by stage_issue() on the vector path
+    if (stage_vector_path(x)) {
+        wait_vmcnt<0>();
+    } else {
+        for (int i = tid; i < K; i += nt) raw[i] = x[i];
+    }
+    lds_barrier();
+    // 2. largest exponent and non-finite values
     int emax = -100000, bad = 0;
     for (int i = tid; i < K; i += nt) {
-        const float v = act_to_f32(x[i], dt);
+        const float v = act_to_f32(raw[i], dt);
         if (!__builtin_isfinite(v)) bad = 1;
         else if (v != 0.0f) emax = max(emax, f32_exponent(v));
     }
     emax = wave_max_i32(emax);
     bad = wave_or_i32(bad);
     if ((tid & 63) == 0) { red[wave] = emax; red[nwaves + wave] = bad; }
-    __syncthreads();
+    lds_barrier();
     emax = red[0]; bad = red[nwaves];
     for (int w = 1; w < nwaves; ++w) { emax = max(emax, red[w]); bad |= red[nwaves + w]; }
     const int s = (emax == -100000) ? 0 : 14 - emax;
+    // 3. exact conversion to fp16 x 2^s in the pair layout
     int lost = 0;
     if (!bad) {
         for (int i = tid; i < K; i += nt) {
-            const float v = act_to_f32(x[i], dt);
+            const float v = act_to_f32(raw[i], dt);
             if (v != 0.0f && f32_exponent(v) < emax - 28) lost = 1;
             xs[staged_index(i)] = (_Float16)__builtin_ldexpf(v, s);
         }
     }
     lost = wave_or_i32(lost);
-    __syncthreads();  // everyone has read red[] before it is rewritten
+    lds_barrier();  // everyone has read red[] before it is rewritten
     if ((tid & 63) == 0) red[wave] = lost;
-    __syncthreads();
+    lds_barrier();
     for (int w = 0; w < nwaves; ++w) lost |= red[w];
     Staging st;
     st.scale = s;

@@ -13,6 +13,10 @@
 // the workgroup loops over rows with a grid stride, R rows per slot in flight.
 // Partial row sums are reduced across the L lanes of a slot by lane shuffles
 // in a fixed order, so results are bitwise reproducible.
+#include <cstdio>
+#include <cstdlib>
+#include <type_traits>
+
 #include "w4_device.h"
 #include "w4_internal.h"
 
@@ -25,69 +29,112 @@ __global__ __launch_bounds__(256) void gemv_kernel(const uint4 *__restrict__ cod
                                                    const uint16_t *__restrict__ x, int dt,
                                                    float *__restrict__ y) {
     constexpr int SLOTS = kWave / L;
-    extern __shared__ _Float16 xs[];
+    extern __shared__ _Float16 xs[];  // K staged halves, then K raw halves
     __shared__ int red[8];
     const int G = K >> 5;
-    const Staging st = stage_activations(x, K, dt, xs, red);
-    __syncthreads();
-
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int nwaves = blockDim.x >> 6;
     const int l = lane % L, slot = lane / L;
     const int rows_per_iter = nwaves * SLOTS * R;
+    const int gstride = gridDim.x * rows_per_iter;
 
-    h2 xr[NG][16];
-    const h2 *xs2 = reinterpret_cast<const h2 *>(xs);
-#pragma unroll
-    for (int i = 0; i < NG; ++i) {
-        const int g = l + i * L;
-#pragma unroll
-        for (int p = 0; p < 16; ++p) xr[i][p] = (g < G) ? xs2[g * 16 + p] : h2{0, 0};
+    if (G == 0) {  // empty sums
+        for (int n = blockIdx.x * blockDim.x + threadIdx.x; n < N; n += gridDim.x * blockDim.x)
+            y[n] = 0.0f;
+        return;
     }
 
-    for (int row0 = blockIdx.x * rows_per_iter; row0 < N; row0 += gridDim.x * rows_per_iter) {
-        uint4 q[R][NG];
-        uint32_t sb[R][NG];
+    // Group indices of this lane, clamped so that every load is in bounds and
+    // can be issued without a branch; lanes past the row end contribute zero.
+    int gc[NG];
+#pragma unroll
+    for (int i = 0; i < NG; ++i) gc[i] = min(l + i * L, G - 1);
+
+    auto load_rows = [&](uint4 (&q)[R][NG], uint32_t (&sv)[R][NG], int r0)
+        __attribute__((always_inline)) {
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            const int row = row0 + (r * nwaves + wave) * SLOTS + slot;
+            const int row = min(r0 + (r * nwaves + wave) * SLOTS + slot, N - 1);
+            const uint4 *cp = codes + (size_t)row * G;
+            const uint16_t *sp = steps + (size_t)row * G;
 #pragma unroll
             for (int i = 0; i < NG; ++i) {
-                const int g = l + i * L;
-                if (row < N && g < G) {
-                    q[r][i] = codes[(size_t)row * G + g];
-                    sb[r][i] = steps[(size_t)row * G + g];
-                } else {
-                    q[r][i] = make_uint4(0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u);
-                    sb[r][i] = 0;
-                }
+                q[r][i] = cp[gc[i]];
+                sv[r][i] = sp[gc[i]];
             }
         }
+    };
+
+    // The first rows' weights are requested before the activations are staged,
+    // so the staging latency overlaps the first HBM reads.
+    // (Activation loads are issued first: they come from L2 and return before
+    // the weights, and vector loads retire in order.)
+    uint16_t *raw = reinterpret_cast<uint16_t *>(xs + K);
+    stage_issue(x, K, raw);
+    int row0 = blockIdx.x * rows_per_iter;
+    uint4 qa[R][NG];
+    uint32_t sa[R][NG];
+    if (row0 < N) load_rows(qa, sa, row0);
+
+    const Staging st = stage_complete(x, K, dt, xs, raw, red);
+
+    h2 xr[NG][16];
+    auto load_xr = [&]() __attribute__((always_inline)) {
+        const h2 *xs2 = reinterpret_cast<const h2 *>(xs);
+#pragma unroll
+        for (int i = 0; i < NG; ++i) {
+            const int g = l + i * L;
+#pragma unroll
+            for (int p = 0; p < 16; ++p) xr[i][p] = (g < G) ? xs2[g * 16 + p] : h2{0, 0};
+        }
+    };
+
+    auto compute_rows = [&](const uint4 (&q)[R][NG], const uint32_t (&sv)[R][NG], int r0,
+                            auto exact_f32) __attribute__((always_inline)) {
         float acc[R];
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             acc[r] = 0.0f;
-            const int row = row0 + (r * nwaves + wave) * SLOTS + slot;
-            if (!st.fallback) {
 #pragma unroll
-                for (int i = 0; i < NG; ++i)
-                    acc[r] = __builtin_fmaf(group_dot(q[r][i], xr[i]), bf16_to_f32(sb[r][i]), acc[r]);
-            } else {
-                for (int i = 0; i < NG; ++i) {
-                    const int g = l + i * L;
-                    if (row < N && g < G)
-                        acc[r] = __builtin_fmaf(group_dot_f32(q[r][i], x + g * 32, dt),
-                                                bf16_to_f32(sb[r][i]), acc[r]);
-                }
+            for (int i = 0; i < NG; ++i) {
+                const int g = l + i * L;
+                float part;
+                if constexpr (decltype(exact_f32)::value)
+                    part = group_dot_f32(q[r][i], raw + gc[i] * 32, dt);
+                else
+                    part = group_dot(q[r][i], xr[i]);
+                acc[r] = (g < G) ? __builtin_fmaf(part, bf16_to_f32(sv[r][i]), acc[r]) : acc[r];
             }
         }
 #pragma unroll
         for (int r = 0; r < R; ++r) {
 #pragma unroll
             for (int off = L / 2; off > 0; off >>= 1) acc[r] += __shfl_xor(acc[r], off, kWave);
-            const int row = row0 + (r * nwaves + wave) * SLOTS + slot;
-            if (l == 0 && row < N) y[row] = st.fallback ? acc[r] : __builtin_ldexpf(acc[r], -st.scale);
+            const int row = r0 + (r * nwaves + wave) * SLOTS + slot;
+            if (l == 0 && row < N)
+                y[row] = decltype(exact_f32)::value ? acc[r] : __builtin_ldexpf(acc[r], -st.scale);
         }
+    };
+
+    // Each step issues all R*NG row loads of the lane back to back (clamped,
+    // so none sits behind a branch), then does the math; other waves on the
+    // CU keep the memory system busy meanwhile.  The first step's loads were
+    // issued before the staging.
+    auto row_loop = [&](auto exact_f32) __attribute__((always_inline)) {
+        if (row0 >= N) return;
+        compute_rows(qa, sa, row0, exact_f32);
+        for (row0 += gstride; row0 < N; row0 += gstride) {
+            load_rows(qa, sa, row0);
+            compute_rows(qa, sa, row0, exact_f32);
+        }
+    };
+    // The staging outcome is the same for every wave: branch on it once, in a
+    // scalar register.
+    if (__builtin_amdgcn_readfirstlane(st.fallback)) {
+        row_loop(std::true_type{});
+    } else {
+        load_xr();
+        row_loop(std::false_type{});
     }
 }
 
@@ -99,7 +146,12 @@ typedef void (*GemvFn)(const uint4 *, const uint16_t *, int, int, const uint16_t
 
 template <int L, int NG>
 GemvFn pick_r(int R) {
-    return R == 1 ? gemv_kernel<L, NG, 1> : gemv_kernel<L, NG, 2>;
+    switch (R) {
+        case 1: return gemv_kernel<L, NG, 1>;
+        case 2: return gemv_kernel<L, NG, 2>;
+        case 4: return gemv_kernel<L, NG, 4>;
+    }
+    return nullptr;
 }
 
 template <int L>
@@ -117,7 +169,6 @@ GemvFn pick_ng(int NG, int R) {
 
 GemvFn pick(int L, int NG, int R) {
     switch (L) {
-        case 4: return pick_ng<4>(NG, R);
         case 8: return pick_ng<8>(NG, R);
         case 16: return pick_ng<16>(NG, R);
         case 32: return pick_ng<32>(NG, R);
@@ -130,47 +181,49 @@ GemvFn pick(int L, int NG, int R) {
 
 GemvTile gemv_tile(int N, int K) {
     // Lanes per row L and groups per lane NG: cover the G = K/32 groups of a
-    // row with as few idle lane slots as possible, preferring NG <= 4 (fewer
-    // activation registers) and wider L for long rows.
+    // row with as few idle lane slots as possible; among equal covers prefer
+    // 16 lanes per row and three or four groups per lane, which measured best
+    // on MI355X (e.g. 262144 x 1536: L=16, NG=3 at 4.8 TB/s against 3.1 TB/s
+    // for L=64, NG=1 with a quarter of the lanes idle).
     const int G = K / 32;
-    static const int kL[] = {64, 32, 16, 8, 4};
-    static const int kNG[] = {1, 2, 3, 4, 6, 8};
-    GemvTile best{64, 8, 1, 4, 0};
+    static const int kL[] = {16, 32, 64, 8};
+    static const int kNG[] = {3, 4, 2, 6, 1, 8};
+    GemvTile best{16, 3, 2, 4, 0};
     double best_cost = 1e30;
     for (int L : kL) {
         for (int NG : kNG) {
             if (L * NG < G) continue;
-            const double idle = double(L * NG - G) / double(L * NG);
-            double cost = idle + (NG > 4 ? 0.05 * (NG - 4) : 0.0);
-            if (L < 16 && G >= 32) cost += 0.2;  // short runs per load
+            double cost = double(L * NG - G) / double(L * NG);
+            if (NG > 4) cost += 0.02 * (NG - 4);  // register pressure
             if (cost < best_cost - 1e-9) {
                 best_cost = cost;
-                best = GemvTile{L, NG, 1, 4, 0};
+                best = GemvTile{L, NG, 2, 4, 0};
             }
         }
     }
     if (G == 0) best = GemvTile{64, 1, 1, 4, 0};
-    // Rows in flight per slot and waves per workgroup: big matrices keep two
-    // rows per slot in flight with four-wave workgroups; small ones use one
-    // row and one-wave workgroups so that the rows spread over every CU.
-    const int slots = 64 / best.L;
-    const long rows_wave = (long)slots;
-    if ((long)N >= rows_wave * 2 * 4 * 1024) { best.R = 2; best.waves = 4; }
-    else if ((long)N >= rows_wave * 4 * 512) { best.R = 1; best.waves = 4; }
-    else { best.R = 1; best.waves = 1; }
-    const long rows_per_iter = rows_wave * best.R * best.waves;
-    long blocks = (N + rows_per_iter - 1) / rows_per_iter;
-    const long cap = 2048;
-    best.blocks = (int)(blocks < cap ? (blocks < 1 ? 1 : blocks) : cap);
+    // Two rows per slot in flight and four-wave workgroups; at most four
+    // workgroups per CU (1024), each looping over rows with a grid stride.
+    const long rows_per_iter = (long)(64 / best.L) * best.R * best.waves;
+    const long blocks = (N + rows_per_iter - 1) / rows_per_iter;
+    best.blocks = (int)(blocks < 1 ? 1 : (blocks > 1024 ? 1024 : blocks));
     return best;
 }
 
 hipError_t launch_gemv(const uint32_t *codes, const uint16_t *steps, int N, int K,
                        const uint16_t *x, int dt, float *y, hipStream_t stream) {
-    const GemvTile t = gemv_tile(N, K);
+    GemvTile t = gemv_tile(N, K);
+    // W4_GEMV_TILE="L,NG,R,waves,blocks" overrides the table (tile sweeps);
+    // it changes only the schedule, never what is computed.
+    if (const char *e = getenv("W4_GEMV_TILE")) {
+        GemvTile o;
+        if (sscanf(e, "%d,%d,%d,%d,%d", &o.L, &o.NG, &o.R, &o.waves, &o.blocks) == 5 &&
+            o.L * o.NG * 32 >= K && o.waves >= 1 && o.waves <= 4 && o.blocks >= 1)
+            t = o;
+    }
     GemvFn fn = pick(t.L, t.NG, t.R);
     if (!fn) return hipErrorInvalidConfiguration;
-    const size_t lds = (size_t)(K > 0 ? K : 2) * sizeof(_Float16);
+    const size_t lds = (size_t)(K + stage_raw_halves(K) + 8) * sizeof(_Float16);
     hipLaunchKernelGGL(fn, dim3(t.blocks), dim3(64 * t.waves), lds, stream,
                        reinterpret_cast<const uint4 *>(codes), steps, N, K, x, dt, y);
     return hipGetLastError();

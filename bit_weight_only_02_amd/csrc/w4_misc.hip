@@ -35,19 +35,28 @@ hipError_t launch_rms_renorm(const float *v, int K, void *out, int out_dt, hipSt
 }
 
 // Streaming read: sum of all 32-bit words (mod 2^32) into *out.  Integer adds
-// only, so the result is order independent.
+// only, so the result is order independent.  Each workgroup step covers one
+// contiguous chunk of 8 * blockDim 16-byte words; every thread has its 8 loads
+// in flight at once (indices clamped, so no load sits behind a branch).
+constexpr int kProbeUnroll = 8;
+
 __global__ __launch_bounds__(256) void probe_stream_kernel(const uint4 *__restrict__ buf,
                                                            int64_t n16, uint32_t *__restrict__ out) {
+    const int64_t chunk = (int64_t)kProbeUnroll * blockDim.x;
     uint32_t s = 0;
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    for (; i + 3 * stride < n16; i += 4 * stride) {
-        const uint4 a = buf[i], b = buf[i + stride], c = buf[i + 2 * stride], d = buf[i + 3 * stride];
-        s += a.x + a.y + a.z + a.w + b.x + b.y + b.z + b.w + c.x + c.y + c.z + c.w + d.x + d.y + d.z + d.w;
-    }
-    for (; i < n16; i += stride) {
-        const uint4 a = buf[i];
-        s += a.x + a.y + a.z + a.w;
+    for (int64_t base = (int64_t)blockIdx.x * chunk; base < n16; base += (int64_t)gridDim.x * chunk) {
+        uint4 v[kProbeUnroll];
+#pragma unroll
+        for (int u = 0; u < kProbeUnroll; ++u) {
+            const int64_t i = base + (int64_t)u * blockDim.x + threadIdx.x;
+            v[u] = buf[i < n16 ? i : n16 - 1];
+        }
+#pragma unroll
+        for (int u = 0; u < kProbeUnroll; ++u) {
+            const int64_t i = base + (int64_t)u * blockDim.x + threadIdx.x;
+            const uint32_t t = v[u].x + v[u].y + v[u].z + v[u].w;
+            s += i < n16 ? t : 0u;
+        }
     }
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off, kWave);
@@ -56,9 +65,9 @@ __global__ __launch_bounds__(256) void probe_stream_kernel(const uint4 *__restri
 
 hipError_t launch_probe_stream(const void *buf, int64_t bytes, uint32_t *out, hipStream_t stream) {
     const int64_t n16 = bytes / 16;
-    int64_t blocks = (n16 + 256 * 4 - 1) / (256 * 4);
-    if (blocks > 4096) blocks = 4096;
-    if (blocks < 1) blocks = 1;
+    if (n16 == 0) return hipSuccess;
+    int64_t blocks = (n16 + 256 * kProbeUnroll - 1) / (256 * kProbeUnroll);
+    if (blocks > 2048) blocks = 2048;
     hipLaunchKernelGGL(probe_stream_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
                        static_cast<const uint4 *>(buf), n16, out);
     return hipGetLastError();

@@ -34,6 +34,7 @@ W4_ERR_HIP = -6
 W4_F16 = 0
 W4_BF16 = 1
 W4_MAX_K = 16384
+W4_MAX_K_SMALLM = 8192
 W4_MAX_M = 16
 W4_MAX_TOPK = 32
 W4_CHAIN_SYNC_BYTES = 4096
@@ -54,7 +55,7 @@ _SIGNATURES = {
     "w4_moe_gemv_ids": [_P, _P, _I64, _I64, _I32, _I32, _P, _I32, _I32, _I64, _P, _I32, _I32,
                         _P, _I32, _I32, _P, _P, _P, _P, _P],
     "w4_embed_gather": [_P, _P, _I32, _I32, _P, _I32, _P, _P, _P],
-    "w4_rms_renorm": [_P, _I32, _P, _I32, _P],
+    "w4_rms_renorm": [_P, _I64, _I32, _I32, _P, _I64, _I32, _P],
     "w4_gemv_chain": [_P, _P, _P, _P, _I32, _P, _P, _P, _P],
     "w4_probe_stream": [_P, _I64, _P, _P],
 }
@@ -173,11 +174,17 @@ def w4_embed_gather(codes, steps, ids, out=None, dev_err=None, stream=None):
 
 
 def w4_rms_renorm(v, K, out=None, out_dtype=torch.float16, stream=None):
-    """Leading K entries of fp32 ``v`` divided by their RMS, rounded to out_dtype."""
+    """Leading K entries of each fp32 row of ``v`` ([K'] or [rows, K'] with unit
+    column stride) divided by their RMS, rounded to out_dtype; returns [K] or
+    [rows, K]."""
+    rows = 1 if v.dim() == 1 else v.shape[0]
+    ldv = v.shape[-1] if v.dim() == 1 else v.stride(0)
     if out is None:
-        out = torch.empty(K, dtype=out_dtype, device=v.device)
-    _check(lib.w4_rms_renorm(_ptr(v), K, _ptr(out), _act_dtype(out), _stream(stream)),
-           "w4_rms_renorm")
+        shape = (K,) if v.dim() == 1 else (rows, K)
+        out = torch.empty(shape, dtype=out_dtype, device=v.device)
+    ldo = K if out.dim() == 1 else out.stride(0)
+    _check(lib.w4_rms_renorm(_ptr(v), ldv, K, rows, _ptr(out), ldo, _act_dtype(out),
+                             _stream(stream)), "w4_rms_renorm")
     return out
 
 

@@ -9,6 +9,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 
 #include "w4.h"
 #include "w4_internal.h"
@@ -64,6 +65,48 @@ int check_dtype(int32_t dt) {
     return W4_OK;
 }
 
+// Per-device staging buffer of the combined expert product: allocated on first
+// use, grown (never shrunk) when a call needs more, and kept until the process
+// ends.  Growing is refused during graph capture.
+constexpr int kMaxDevices = 64;
+std::mutex g_ws_mu;
+void *g_ws_ptr[kMaxDevices] = {};
+size_t g_ws_bytes[kMaxDevices] = {};
+
+int staging_buffer(size_t bytes, hipStream_t stream, void **out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(W4_ERR_NODEV, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(W4_ERR_UNSUPPORTED, "device index %d", dev);
+    std::lock_guard<std::mutex> lock(g_ws_mu);
+    if (g_ws_bytes[dev] >= bytes) {
+        *out = g_ws_ptr[dev];
+        return W4_OK;
+    }
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    e = hipStreamIsCapturing(stream, &cs);
+    if (e != hipSuccess) return fail(W4_ERR_HIP, "hipStreamIsCapturing: %s", hipGetErrorString(e));
+    if (cs != hipStreamCaptureStatusNone)
+        return fail(W4_ERR_UNSUPPORTED, "staging buffer must grow to %zu bytes outside graph capture",
+                    bytes);
+    if (g_ws_ptr[dev]) {
+        // the old buffer may still be read by queued work
+        e = hipDeviceSynchronize();
+        if (e != hipSuccess) return fail(W4_ERR_HIP, "hipDeviceSynchronize: %s", hipGetErrorString(e));
+        e = hipFree(g_ws_ptr[dev]);
+        g_ws_ptr[dev] = nullptr;
+        g_ws_bytes[dev] = 0;
+        if (e != hipSuccess) return fail(W4_ERR_HIP, "hipFree: %s", hipGetErrorString(e));
+    }
+    void *p = nullptr;
+    e = hipMalloc(&p, bytes);
+    if (e != hipSuccess) return fail(W4_ERR_HIP, "hipMalloc(%zu): %s", bytes, hipGetErrorString(e));
+    g_ws_ptr[dev] = p;
+    g_ws_bytes[dev] = bytes;
+    *out = p;
+    return W4_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -82,6 +125,35 @@ int w4_gemv(const uint32_t *codes, const uint16_t *steps, int32_t N, int32_t K,
     return launched(w4::launch_gemv(codes, steps, N, K, static_cast<const uint16_t *>(x), xdt, y,
                                     static_cast<hipStream_t>(stream)),
                     "w4_gemv");
+}
+
+int w4_gemm_smallM(const uint32_t *codes, const uint16_t *steps, int32_t N, int32_t K,
+                   const void *X, int32_t xdt, int32_t M, int64_t ldx,
+                   float *Y, int64_t ldy, void *stream) {
+    int st;
+    if ((st = check_matrix(codes, steps, N, K))) return st;
+    if ((st = check_dtype(xdt))) return st;
+    if (M < 1 || M > W4_MAX_M) return fail(W4_ERR_INVALID_ARG, "M=%d outside 1..%d", M, W4_MAX_M);
+    if (K > W4_MAX_K_SMALLM) return fail(W4_ERR_UNSUPPORTED, "K=%d exceeds %d", K, W4_MAX_K_SMALLM);
+    if (ldx < K || ldy < N) return fail(W4_ERR_INVALID_ARG, "ldx < K or ldy < N");
+    if (N > 0 && (!Y || (K > 0 && !X))) return fail(W4_ERR_INVALID_ARG, "null X/Y");
+    if (X && !aligned(X, 2)) return fail(W4_ERR_ALIGNMENT, "X not 2-byte aligned");
+    if (Y && !aligned(Y, 4)) return fail(W4_ERR_ALIGNMENT, "Y not 4-byte aligned");
+    if (N == 0) return W4_OK;
+    if ((st = device_ready())) return st;
+    if (forced_launch_error()) return fail(W4_ERR_HIP, "forced launch error (test hook)");
+    if (K == 0) {
+        // empty sums: write zeros through the product kernel path of the GEMV
+        for (int m = 0; m < M; ++m) {
+            hipError_t e = w4::launch_gemv(codes, steps, N, 0, static_cast<const uint16_t *>(X), xdt,
+                                           Y + (int64_t)m * ldy, static_cast<hipStream_t>(stream));
+            if (e != hipSuccess) return launched(e, "w4_gemm_smallM");
+        }
+        return launched(hipSuccess, "w4_gemm_smallM");
+    }
+    return launched(w4::launch_gemm_smallm(codes, steps, N, K, static_cast<const uint16_t *>(X), ldx,
+                                           xdt, M, Y, ldy, static_cast<hipStream_t>(stream)),
+                    "w4_gemm_smallM");
 }
 
 int w4_embed_gather(const uint32_t *codes, const uint16_t *steps, int32_t V, int32_t K,
@@ -103,18 +175,67 @@ int w4_embed_gather(const uint32_t *codes, const uint16_t *steps, int32_t V, int
                     "w4_embed_gather");
 }
 
-int w4_rms_renorm(const float *v, int32_t K, void *out, int32_t out_dt, void *stream) {
+int w4_rms_renorm(const float *v, int64_t ldv, int32_t K, int32_t rows, void *out, int64_t ldo,
+                  int32_t out_dt, void *stream) {
     int st;
     if ((st = check_dtype(out_dt))) return st;
-    if (K < 0) return fail(W4_ERR_INVALID_ARG, "negative K");
-    if (K > 0 && (!v || !out)) return fail(W4_ERR_INVALID_ARG, "null v/out");
+    if (K < 0 || rows < 0) return fail(W4_ERR_INVALID_ARG, "negative K or rows");
+    if (rows > 65535) return fail(W4_ERR_UNSUPPORTED, "rows=%d exceeds 65535", rows);
+    if (rows > 1 && (ldv < K || ldo < K)) return fail(W4_ERR_INVALID_ARG, "ldv or ldo < K");
+    if (K > 0 && rows > 0 && (!v || !out)) return fail(W4_ERR_INVALID_ARG, "null v/out");
     if (v && !aligned(v, 4)) return fail(W4_ERR_ALIGNMENT, "v not 4-byte aligned");
     if (out && !aligned(out, 2)) return fail(W4_ERR_ALIGNMENT, "out not 2-byte aligned");
-    if (K == 0) return W4_OK;
+    if (K == 0 || rows == 0) return W4_OK;
     if ((st = device_ready())) return st;
     if (forced_launch_error()) return fail(W4_ERR_HIP, "forced launch error (test hook)");
-    return launched(w4::launch_rms_renorm(v, K, out, out_dt, static_cast<hipStream_t>(stream)),
+    return launched(w4::launch_rms_renorm(v, ldv, K, rows, out, ldo, out_dt,
+                                          static_cast<hipStream_t>(stream)),
                     "w4_rms_renorm");
+}
+
+int w4_moe_gemv_ids(const uint32_t *codes_base, const uint16_t *steps_base,
+                    int64_t expert_stride_codes, int64_t expert_stride_steps,
+                    int32_t N, int32_t K,
+                    const void *X, int32_t xdt, int32_t x_per_pair, int64_t ldx,
+                    const int32_t *ids, int32_t T, int32_t topk,
+                    const int32_t *slot_of, int32_t n_experts, int32_t n_slots,
+                    const float *row_scale, const float *route_w,
+                    float *Y, int32_t *dev_err, void *stream) {
+    int st;
+    if ((st = check_matrix(codes_base, steps_base, N, K))) return st;
+    if ((st = check_dtype(xdt))) return st;
+    if (K > W4_MAX_K_SMALLM) return fail(W4_ERR_UNSUPPORTED, "K=%d exceeds %d", K, W4_MAX_K_SMALLM);
+    if (T < 0 || topk < 1 || topk > W4_MAX_TOPK)
+        return fail(W4_ERR_INVALID_ARG, "T=%d topk=%d (topk must be 1..%d)", T, topk, W4_MAX_TOPK);
+    if ((int64_t)T * topk > 1024) return fail(W4_ERR_UNSUPPORTED, "T*topk exceeds 1024");
+    if (x_per_pair != 0 && x_per_pair != 1) return fail(W4_ERR_INVALID_ARG, "x_per_pair must be 0 or 1");
+    if (n_experts < 1) return fail(W4_ERR_INVALID_ARG, "n_experts must be >= 1");
+    if (slot_of && n_slots < 1) return fail(W4_ERR_INVALID_ARG, "n_slots must be >= 1 with slot_of");
+    if (expert_stride_codes < 0 || expert_stride_steps < 0 || expert_stride_codes % 4)
+        return fail(W4_ERR_ALIGNMENT, "expert_stride_codes must be a non-negative multiple of 4");
+    if (expert_stride_codes < (int64_t)N * (K / 8) || expert_stride_steps < (int64_t)N * (K / 32))
+        return fail(W4_ERR_INVALID_ARG, "expert strides smaller than one expert matrix");
+    if (ldx < K) return fail(W4_ERR_INVALID_ARG, "ldx < K");
+    if (T > 0 && N > 0 && (!ids || !Y || (K > 0 && !X))) return fail(W4_ERR_INVALID_ARG, "null ids/X/Y");
+    if (X && !aligned(X, 2)) return fail(W4_ERR_ALIGNMENT, "X not 2-byte aligned");
+    if (Y && !aligned(Y, 4)) return fail(W4_ERR_ALIGNMENT, "Y not 4-byte aligned");
+    if (ids && !aligned(ids, 4)) return fail(W4_ERR_ALIGNMENT, "ids not 4-byte aligned");
+    if (T == 0 || N == 0) return W4_OK;
+    if (K == 0) return fail(W4_ERR_UNSUPPORTED, "K == 0");
+    if ((st = device_ready())) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    float *rows = Y;
+    if (route_w) {
+        void *ws = nullptr;
+        if ((st = staging_buffer((size_t)T * topk * N * sizeof(float), s, &ws))) return st;
+        rows = static_cast<float *>(ws);
+    }
+    if (forced_launch_error()) return fail(W4_ERR_HIP, "forced launch error (test hook)");
+    hipError_t e = w4::launch_moe(codes_base, steps_base, expert_stride_codes, expert_stride_steps,
+                                  N, K, static_cast<const uint16_t *>(X), ldx, xdt, x_per_pair, ids, T,
+                                  topk, slot_of, n_experts, n_slots, row_scale, rows, dev_err, s);
+    if (e != hipSuccess || !route_w) return launched(e, "w4_moe_gemv_ids");
+    return launched(w4::launch_moe_combine(rows, route_w, T, topk, N, Y, s), "w4_moe_gemv_ids");
 }
 
 int w4_probe_stream(const void *buf, int64_t bytes, uint32_t *out, void *stream) {

@@ -116,9 +116,15 @@ __device__ __forceinline__ int wave_max_i32(int v) {
 }
 
 __device__ __forceinline__ int wave_or_i32(int v) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) v |= __shfl_xor(v, off, kWave);
-    return v;
+    return __builtin_amdgcn_ballot_w64(v != 0) != 0 ? 1 : 0;
+}
+
+// max over the four lanes l, l^16, l^32, l^48 (the 16-lane groups of a wave)
+__device__ __forceinline__ int max_across_lane_groups(int v) {
+    auto a = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    v = max((int)a[0], (int)a[1]);
+    auto b = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return max((int)b[0], (int)b[1]);
 }
 
 struct Staging {

@@ -8,10 +8,13 @@ namespace w4 {
 // Leading K entries u of v -> u / sqrt(mean(u^2)), rounded to nearest-even in
 // fp16 (out_dt 0) or bf16 (out_dt 1).  One workgroup of 1024 threads; the sum
 // of squares is accumulated in fp64 in a fixed order.
-__global__ __launch_bounds__(1024) void rms_renorm_kernel(const float *__restrict__ v, int K,
-                                                          uint16_t *__restrict__ out, int out_dt) {
+__global__ __launch_bounds__(1024) void rms_renorm_kernel(const float *__restrict__ v0, long ldv,
+                                                          int K, uint16_t *__restrict__ out0,
+                                                          long ldo, int out_dt) {
     __shared__ double part[16];
     const int tid = threadIdx.x;
+    const float *v = v0 + (long)blockIdx.x * ldv;
+    uint16_t *out = out0 + (long)blockIdx.x * ldo;
     double ss = 0.0;
     for (int k = tid; k < K; k += blockDim.x) ss += (double)v[k] * (double)v[k];
 #pragma unroll
@@ -28,9 +31,11 @@ __global__ __launch_bounds__(1024) void rms_renorm_kernel(const float *__restric
     }
 }
 
-hipError_t launch_rms_renorm(const float *v, int K, void *out, int out_dt, hipStream_t stream) {
-    hipLaunchKernelGGL(rms_renorm_kernel, dim3(1), dim3(1024), 0, stream, v, K,
-                       static_cast<uint16_t *>(out), out_dt);
+hipError_t launch_rms_renorm(const float *v, long ldv, int K, int rows, void *out, long ldo,
+                             int out_dt, hipStream_t stream) {
+    const int threads = K >= 1024 ? 1024 : (K >= 256 ? 256 : 64);
+    hipLaunchKernelGGL(rms_renorm_kernel, dim3(rows), dim3(threads), 0, stream, v, ldv, K,
+                       static_cast<uint16_t *>(out), ldo, out_dt);
     return hipGetLastError();
 }
 

@@ -1,12 +1,6 @@
 // Entry points declared in w4.h whose kernels are not built yet.
 #include "w4.h"
 extern "C" {
-int w4_gemm_smallM(const uint32_t *, const uint16_t *, int32_t, int32_t, const void *, int32_t,
-                   int32_t, int64_t, float *, int64_t, void *) { return W4_ERR_UNSUPPORTED; }
-int w4_moe_gemv_ids(const uint32_t *, const uint16_t *, int64_t, int64_t, int32_t, int32_t,
-                    const void *, int32_t, int32_t, int64_t, const int32_t *, int32_t, int32_t,
-                    const int32_t *, int32_t, int32_t, const float *, const float *, float *,
-                    int32_t *, void *) { return W4_ERR_UNSUPPORTED; }
 int w4_gemv_chain(const uint32_t *const *, const uint16_t *const *, const int32_t *,
                   const int32_t *, int32_t, const uint16_t *, float *const *, void *, void *) {
     return W4_ERR_UNSUPPORTED;

@@ -77,7 +77,8 @@ typedef enum {
 
 typedef enum { W4_F16 = 0, W4_BF16 = 1 } w4_dtype;
 
-#define W4_MAX_K 16384  /* largest supported K (input length) */
+#define W4_MAX_K 16384       /* largest K of w4_gemv and w4_embed_gather */
+#define W4_MAX_K_SMALLM 8192 /* largest K of w4_gemm_smallM and w4_moe_gemv_ids */
 #define W4_MAX_M 16     /* largest M of w4_gemm_smallM */
 #define W4_MAX_TOPK 32  /* largest experts per token of w4_moe_gemv_ids */
 
@@ -94,7 +95,8 @@ int w4_gemv(const uint32_t *codes, const uint16_t *steps, int32_t N, int32_t K,
 /*
  * Small-batch product [P1-S3] with M activation rows, 1 <= M <= W4_MAX_M:
  *   Y[m*ldy + n] = sum_k w(n,k) * X[m*ldx + k]   for m < M, n < N.
- * Each weight is read from memory once for all M rows.  ldx >= K, ldy >= N.
+ * Each weight is read from memory once for all M rows.  ldx >= K, ldy >= N,
+ * K <= W4_MAX_K_SMALLM (larger K: W4_ERR_UNSUPPORTED).
  */
 int w4_gemm_smallM(const uint32_t *codes, const uint16_t *steps, int32_t N, int32_t K,
                    const void *X, int32_t xdt, int32_t M, int64_t ldx,
@@ -125,7 +127,7 @@ int w4_gemm_smallM(const uint32_t *codes, const uint16_t *steps, int32_t N, int3
  *   buffer the library allocates once per device and reuses (grown on demand
  *   while no graph capture is active; concurrent combined calls on one device
  *   from different streams are serialised by the caller).
- * Limits: T*topk <= 1024, topk <= W4_MAX_TOPK.
+ * Limits: T*topk <= 1024, topk <= W4_MAX_TOPK, K <= W4_MAX_K_SMALLM.
  */
 int w4_moe_gemv_ids(const uint32_t *codes_base, const uint16_t *steps_base,
                     int64_t expert_stride_codes, int64_t expert_stride_steps,
@@ -149,12 +151,14 @@ int w4_embed_gather(const uint32_t *codes, const uint16_t *steps, int32_t V, int
                     int32_t *dev_err, void *stream);
 
 /*
- * Renormalisation between chained products [P1-S4]: take the leading K entries
- * u of the fp32 vector v, r = sqrt(mean(u^2)), and write out[k] = u[k] / r
- * rounded to nearest-even in dtype out_dt (zeros if r == 0).  Runs on the device
- * in one workgroup.
+ * Renormalisation between chained products [P1-S4], for `rows` vectors at
+ * once: for each row r, take the leading K entries u of the fp32 vector
+ * v + r*ldv, r_rms = sqrt(mean(u^2)), and write (out + r*ldo)[k] = u[k] / r_rms
+ * rounded to nearest-even in dtype out_dt (zeros if r_rms == 0).  The sum of
+ * squares is taken in fp64.  One workgroup per row.
  */
-int w4_rms_renorm(const float *v, int32_t K, void *out, int32_t out_dt, void *stream);
+int w4_rms_renorm(const float *v, int64_t ldv, int32_t K, int32_t rows, void *out, int64_t ldo,
+                  int32_t out_dt, void *stream);
 
 /*
  * One decode-step chain as a single launch [P1-S4]: n_mats packed matrices

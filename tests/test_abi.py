@@ -72,9 +72,33 @@ def test_gather_and_renorm_argument_errors():
     assert L.w4_embed_gather(FAKE, FAKE, 10, 64, FAKE, 4, FAKE + 2, None, None) == -2
     assert L.w4_embed_gather(FAKE, FAKE, 10, 64, None, 4, FAKE, None, None) == -1
     assert L.w4_embed_gather(FAKE, FAKE, 10, 64, FAKE, 0, FAKE, None, None) == 0    # empty
-    assert L.w4_rms_renorm(FAKE, 64, FAKE, 5, None) == -3
-    assert L.w4_rms_renorm(None, 64, FAKE, 0, None) == -1
+    assert L.w4_rms_renorm(FAKE, 64, 64, 1, FAKE, 64, 5, None) == -3
+    assert L.w4_rms_renorm(None, 64, 64, 1, FAKE, 64, 0, None) == -1
+    assert L.w4_rms_renorm(FAKE, 32, 64, 2, FAKE, 64, 0, None) == -1   # ldv < K
     assert L.w4_probe_stream(FAKE, 17, FAKE, None) == -1
+
+
+def test_moe_argument_errors():
+    import bit_weight_only_02_amd as w4
+    L = w4.lib
+    ok = dict(cb=FAKE, sb=FAKE, sc=1408 * 2816 // 8, ss=1408 * 2816 // 32, N=1408, K=2816,
+              X=FAKE, dt=1, xpp=0, ldx=2816, ids=FAKE, T=1, topk=8, slot=None, ne=128, ns=0,
+              rs=None, rw=None, Y=FAKE, err=None)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return L.w4_moe_gemv_ids(a["cb"], a["sb"], a["sc"], a["ss"], a["N"], a["K"], a["X"], a["dt"],
+                                 a["xpp"], a["ldx"], a["ids"], a["T"], a["topk"], a["slot"], a["ne"],
+                                 a["ns"], a["rs"], a["rw"], a["Y"], a["err"], None)
+    assert call(topk=0) == -1
+    assert call(topk=33) == -1
+    assert call(T=200) == -4                      # T*topk > 1024
+    assert call(sc=1408 * 2816 // 8 + 2) == -2    # stride not a multiple of 4 words
+    assert call(sc=8) == -1                       # stride smaller than one expert
+    assert call(slot=FAKE, ns=0) == -1
+    assert call(xpp=2) == -1
+    assert call(K=16384, sc=1408 * 16384 // 8, ss=1408 * 16384 // 32, ldx=16384) == -4
+    assert call(T=0) == 0
 
 
 @pytest.mark.skipif(os.path.exists("/dev/kfd"), reason="a GPU is present")

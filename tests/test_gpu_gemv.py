@@ -165,6 +165,7 @@ def test_rms_renorm_within_one_ulp(w4):
         v = (rng.normal(0, 5, size=K + 100)).astype(np.float32)
         out = w4.w4_rms_renorm(torch.from_numpy(v).cuda(), K,
                                out_dtype=torch.float16 if dt == F16 else torch.bfloat16)
+        assert out.shape == (K,)
         torch.cuda.synchronize()
         got = out.view(torch.int16).cpu().numpy().view(np.uint16).astype(np.int64)
         ref = oracle.rms_renorm(v, K, dt).astype(np.int64)

@@ -56,7 +56,7 @@ _SIGNATURES = {
                         _P, _I32, _I32, _P, _P, _P, _P, _P],
     "w4_embed_gather": [_P, _P, _I32, _I32, _P, _I32, _P, _P, _P],
     "w4_rms_renorm": [_P, _I64, _I32, _I32, _P, _I64, _I32, _P],
-    "w4_gemv_chain": [_P, _P, _P, _P, _I32, _P, _P, _P, _P],
+    "w4_gemv_chain": [_P, _I32, _P, _P, _P],
     "w4_probe_stream": [_P, _I64, _P, _P],
 }
 for _name, _args in _SIGNATURES.items():
@@ -188,22 +188,30 @@ def w4_rms_renorm(v, K, out=None, out_dtype=torch.float16, stream=None):
     return out
 
 
-def w4_gemv_chain(mats, x0, ys, sync, stream=None):
-    """Chained products (see w4.h): ``mats`` is a list of (codes, steps)."""
-    n = len(mats)
-    Ns, Ks = [], []
-    for c, s in mats:
+def w4_chain_desc(mats, ys):
+    """Device descriptor array for w4_gemv_chain: ``mats`` is a list of
+    (codes, steps) and ``ys`` the fp32 outputs.  Returns an int64 tensor of
+    records {codes, steps, y, N | K << 32} (the layout of w4_chain_mat)."""
+    rec = []
+    for (c, s), y in zip(mats, ys):
         N, K = _matrix(c, s)
-        Ns.append(N)
-        Ks.append(K)
-    arr_p = ctypes.c_void_p * n
-    arr_i = ctypes.c_int32 * n
-    codes = arr_p(*[c.data_ptr() for c, _ in mats])
-    steps = arr_p(*[s.data_ptr() for _, s in mats])
-    yp = arr_p(*[y.data_ptr() for y in ys])
-    _check(lib.w4_gemv_chain(codes, steps, arr_i(*Ns), arr_i(*Ks), n, _ptr(x0), yp, _ptr(sync),
-                             _stream(stream)), "w4_gemv_chain")
-    return ys
+        if y.numel() < N or y.dtype != torch.float32:
+            raise ValueError("each y must be fp32 with at least N elements")
+        rec.append([c.data_ptr(), s.data_ptr(), y.data_ptr(), (N & 0xFFFFFFFF) | (K << 32)])
+    return torch.tensor(rec, dtype=torch.int64).cuda()
+
+
+def w4_chain_sync(device="cuda"):
+    """A zeroed sync buffer for w4_gemv_chain."""
+    return torch.zeros(W4_CHAIN_SYNC_BYTES // 4, dtype=torch.int32, device=device)
+
+
+def w4_gemv_chain(desc, x0, sync, stream=None):
+    """Run the chain described by ``desc`` (from w4_chain_desc) on fp16 ``x0``."""
+    if x0.dtype != torch.float16:
+        raise TypeError("x0 must be float16")
+    _check(lib.w4_gemv_chain(_ptr(desc), desc.shape[0], _ptr(x0), _ptr(sync), _stream(stream)),
+           "w4_gemv_chain")
 
 
 def w4_probe_stream(buf, out, stream=None):

@@ -238,6 +238,23 @@ int w4_moe_gemv_ids(const uint32_t *codes_base, const uint16_t *steps_base,
     return launched(w4::launch_moe_combine(rows, route_w, T, topk, N, Y, s), "w4_moe_gemv_ids");
 }
 
+int w4_gemv_chain(const w4_chain_mat *desc, int32_t n_mats, const uint16_t *x0, void *sync,
+                  void *stream) {
+    int st;
+    if (n_mats < 1) return fail(W4_ERR_INVALID_ARG, "n_mats must be >= 1");
+    if (!desc || !x0 || !sync) return fail(W4_ERR_INVALID_ARG, "null desc/x0/sync");
+    if (!aligned(desc, 8) || !aligned(x0, 2) || !aligned(sync, 16))
+        return fail(W4_ERR_ALIGNMENT, "desc, x0 or sync misaligned");
+    if ((st = device_ready())) return st;
+    if (forced_launch_error()) return fail(W4_ERR_HIP, "forced launch error (test hook)");
+    // W4_CHAIN_SPIN_LIMIT bounds each barrier wait (polls); tests set it tiny to
+    // exercise the timeout path without a hang.
+    unsigned spin = 1u << 22;
+    if (const char *e = getenv("W4_CHAIN_SPIN_LIMIT")) spin = (unsigned)strtoul(e, nullptr, 10);
+    return launched(w4::launch_chain(desc, n_mats, x0, sync, spin, static_cast<hipStream_t>(stream)),
+                    "w4_gemv_chain");
+}
+
 int w4_probe_stream(const void *buf, int64_t bytes, uint32_t *out, void *stream) {
     int st;
     if (bytes < 0 || bytes % 16) return fail(W4_ERR_INVALID_ARG, "bytes must be a multiple of 16");

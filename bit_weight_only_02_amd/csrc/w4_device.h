@@ -127,6 +127,37 @@ __device__ __forceinline__ int max_across_lane_groups(int v) {
     return max((int)b[0], (int)b[1]);
 }
 
+// Sum of squares of v[0..K) in fp64 with one fixed order, shared by every
+// kernel that renormalises (so that they agree bit for bit): thread t of a
+// 256-thread workgroup adds v[t], v[t+256], ... in ascending order; the 64
+// lanes of a wave are folded by xor shuffles 32, 16, ..., 1; the four wave
+// sums are added in wave order.  `load(k)` returns v[k] as float.  Every
+// thread gets the total.  `red` is 4 doubles of shared scratch.
+template <class Load>
+__device__ __forceinline__ double sum_squares_256(int K, Load load, double *red) {
+    const int tid = threadIdx.x;
+    double ss = 0.0;
+    for (int k = tid; k < K; k += 256) {
+        const double v = (double)load(k);
+        ss += v * v;
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off, kWave);
+    if ((tid & 63) == 0) red[tid >> 6] = ss;
+    __syncthreads();
+    const double tot = ((red[0] + red[1]) + red[2]) + red[3];
+    __syncthreads();
+    return tot;
+}
+
+// u / sqrt(ss / K) rounded to nearest-even in fp16 (dt 0) or bf16 (dt 1),
+// zero when the vector is zero.
+__device__ __forceinline__ uint16_t renorm_value(float u, double ss, int K, int dt) {
+    const double r = sqrt(ss / (double)K);
+    const float q = r > 0.0 ? (float)((double)u / r) : 0.0f;
+    return dt == 0 ? __builtin_bit_cast(uint16_t, (_Float16)q) : __builtin_bit_cast(uint16_t, (__bf16)q);
+}
+
 struct Staging {
     int scale;     // s: staged value = x * 2^s
     int fallback;  // 1: the vector cannot be staged exactly; use the fp32 path
@@ -182,6 +213,9 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((pending & 15) | ((pending >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+__device__ __forceinline__ Staging stage_convert(int K, int dt, _Float16 *xs, const uint16_t *raw,
+                                                 int *red);
+
 // Stage activations x[0..K) into `xs` (K halves, pair layout) as x * 2^s,
 // after stage_issue().  `red` is 2*(blockDim/64) ints.  Every thread of the
 // workgroup must call this (it has barriers).
@@ -196,6 +230,15 @@ __device__ __forceinline__ Staging stage_complete(const uint16_t *__restrict__ x
         for (int i = tid; i < K; i += nt) raw[i] = x[i];
     }
     lds_barrier();
+    return stage_convert(K, dt, xs, raw, red);
+}
+
+// Convert raw activations (K halves of dtype dt, already in LDS) into the
+// staged pair layout: 2. largest exponent, 3. exact conversion.
+__device__ __forceinline__ Staging stage_convert(int K, int dt, _Float16 *xs, const uint16_t *raw,
+                                                 int *red) {
+    const int tid = threadIdx.x, nt = blockDim.x;
+    const int wave = tid >> 6, nwaves = nt >> 6;
     // 2. largest exponent and non-finite values
     int emax = -100000, bad = 0;
     for (int i = tid; i < K; i += nt) {

@@ -49,6 +49,10 @@ hipError_t launch_moe(const uint32_t *codes_base, const uint16_t *steps_base,
 hipError_t launch_moe_combine(const float *rows, const float *route_w, int T, int topk, int N,
                               float *Y, hipStream_t stream);
 
+size_t chain_lds_bytes();
+hipError_t launch_chain(const void *desc, int n, const uint16_t *x0, void *sync, unsigned spin_limit,
+                        hipStream_t stream);
+
 hipError_t launch_probe_stream(const void *buf, int64_t bytes, uint32_t *out,
                                hipStream_t stream);
 

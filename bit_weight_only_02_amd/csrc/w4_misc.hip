@@ -5,36 +5,22 @@
 
 namespace w4 {
 
-// Leading K entries u of v -> u / sqrt(mean(u^2)), rounded to nearest-even in
-// fp16 (out_dt 0) or bf16 (out_dt 1).  One workgroup of 1024 threads; the sum
-// of squares is accumulated in fp64 in a fixed order.
-__global__ __launch_bounds__(1024) void rms_renorm_kernel(const float *__restrict__ v0, long ldv,
-                                                          int K, uint16_t *__restrict__ out0,
-                                                          long ldo, int out_dt) {
-    __shared__ double part[16];
-    const int tid = threadIdx.x;
+// Leading K entries u of each row of v -> u / sqrt(mean(u^2)), rounded to
+// nearest-even in fp16 (out_dt 0) or bf16 (out_dt 1).  One 256-thread
+// workgroup per row, with the canonical sum-of-squares order.
+__global__ __launch_bounds__(256) void rms_renorm_kernel(const float *__restrict__ v0, long ldv,
+                                                         int K, uint16_t *__restrict__ out0,
+                                                         long ldo, int out_dt) {
+    __shared__ double red[4];
     const float *v = v0 + (long)blockIdx.x * ldv;
     uint16_t *out = out0 + (long)blockIdx.x * ldo;
-    double ss = 0.0;
-    for (int k = tid; k < K; k += blockDim.x) ss += (double)v[k] * (double)v[k];
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off, kWave);
-    if ((tid & 63) == 0) part[tid >> 6] = ss;
-    __syncthreads();
-    double tot = 0.0;
-    for (int w = 0; w < (int)(blockDim.x >> 6); ++w) tot += part[w];
-    const double r = sqrt(tot / (double)K);
-    for (int k = tid; k < K; k += blockDim.x) {
-        const float q = r > 0.0 ? (float)((double)v[k] / r) : 0.0f;
-        out[k] = out_dt == 0 ? __builtin_bit_cast(uint16_t, (_Float16)q)
-                             : __builtin_bit_cast(uint16_t, (__bf16)q);
-    }
+    const double ss = sum_squares_256(K, [&](int k) { return v[k]; }, red);
+    for (int k = threadIdx.x; k < K; k += 256) out[k] = renorm_value(v[k], ss, K, out_dt);
 }
 
 hipError_t launch_rms_renorm(const float *v, long ldv, int K, int rows, void *out, long ldo,
                              int out_dt, hipStream_t stream) {
-    const int threads = K >= 1024 ? 1024 : (K >= 256 ? 256 : 64);
-    hipLaunchKernelGGL(rms_renorm_kernel, dim3(rows), dim3(threads), 0, stream, v, ldv, K,
+    hipLaunchKernelGGL(rms_renorm_kernel, dim3(rows), dim3(256), 0, stream, v, ldv, K,
                        static_cast<uint16_t *>(out), ldo, out_dt);
     return hipGetLastError();
 }

@@ -162,22 +162,34 @@ int w4_rms_renorm(const float *v, int64_t ldv, int32_t K, int32_t rows, void *ou
 
 /*
  * One decode-step chain as a single launch [P1-S4]: n_mats packed matrices
- * applied in sequence.  Matrix i has shape [Ns[i]][Ks[i]] at codes[i], steps[i]
- * and writes float ys[i][Ns[i]].  Its input is x0 (dtype W4_F16, Ks[0] long)
- * for i == 0, else the renormalisation above applied to the leading Ks[i]
- * entries of ys[i-1] (Ks[i] <= Ns[i-1]), rounded to fp16.  The weights of the
- * next matrix are fetched while the previous one finishes.
- *   codes, steps, ys, Ns, Ks: HOST arrays of n_mats device pointers / sizes.
- *   sync: device buffer of at least W4_CHAIN_SYNC_BYTES bytes, zeroed by the
- *   caller before the first call and left zeroed by every call that returns
- *   W4_OK and completes.
- * Results equal n_mats calls of w4_gemv with w4_rms_renorm in between
- * (bitwise for the products, given the same inputs).
+ * applied in sequence.  Matrix i (a w4_chain_mat record) has shape [N][K] at
+ * codes/steps and writes fp32 y[0..N).  Its input is x0 (fp16, K of matrix 0
+ * long) for i == 0, else the leading K entries of the previous matrix's y,
+ * renormalised to RMS 1 and rounded to fp16 bit for bit as w4_rms_renorm
+ * does on that output.  Each product meets the bound of w4_gemv; its row
+ * mapping (and so the order of its fp32 sums) is chosen per matrix for the
+ * whole-chip launch and can differ from w4_gemv's.
+ *   desc: DEVICE array of n_mats records (it is read by the kernel).
+ *   sync: device buffer of W4_CHAIN_SYNC_BYTES bytes, all zero before the
+ *         first call; each call that runs to completion leaves words 0 and 1
+ *         zero again.  Word 2 is an error word written by the kernel: 1 if a
+ *         grid barrier timed out (results incomplete), 2 if a record was
+ *         invalid (N < 1, K not a multiple of 32, K > W4_MAX_K_SMALLM, K larger
+ *         than the previous N, a null or misaligned pointer; nothing computed).
+ *         The caller clears it after reading it.
+ * All workgroups of the launch are resident at once (cooperative launch);
+ * concurrent chains must use different sync buffers.
  */
 #define W4_CHAIN_SYNC_BYTES 4096
-int w4_gemv_chain(const uint32_t *const *codes, const uint16_t *const *steps,
-                  const int32_t *Ns, const int32_t *Ks, int32_t n_mats,
-                  const uint16_t *x0, float *const *ys, void *sync, void *stream);
+typedef struct {
+    const uint32_t *codes; /* device, 16-byte aligned */
+    const uint16_t *steps; /* device */
+    float *y;              /* device, N floats */
+    int32_t N;
+    int32_t K;
+} w4_chain_mat;
+int w4_gemv_chain(const w4_chain_mat *desc, int32_t n_mats, const uint16_t *x0, void *sync,
+                  void *stream);
 
 /*
  * Plain streaming read of `bytes` bytes (a multiple of 16, buf 16-byte aligned):

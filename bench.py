@@ -9,8 +9,10 @@ the Vocabulary Tables in 4-Bit").  Three copies of the table are rotated so that
 the 256 MB Infinity Cache cannot hold the working set.
 
 `value` = algorithmic HBM bytes of one step / measured step time (GB/s, 1e9 B).
-Printed as ONE JSON line, with the dominant kernel's roofline and the CPU
-oracle's time on a bounded sample of the same workload.
+Printed as ONE JSON line, with the dominant kernel's roofline, the CPU oracle's
+time on a bounded sample of the same workload, and (under "extra") the other
+workloads of this path: the single 2048 x 1536 GEMV, the 35-layer decode-step
+sweep, the small-batch products and the expert-indexed layers.
 """
 
 from __future__ import annotations
@@ -29,6 +31,8 @@ HBM_PEAK_GBPS = 8000.0  # MI355X published HBM3E bandwidth
 
 V, K, NIDS = 262144, 1536, 64
 COPIES = 3
+SWEEP_SHAPES = [(2560, 1536), (1536, 2048), (16384, 1536), (1536, 8192)]
+SWEEP_LAYERS = 35
 
 
 def gbps(nbytes: float, seconds: float) -> float:
@@ -74,23 +78,247 @@ def cpu_baseline(codes, steps, x, ids, min_seconds: float = 10.0):
                       f"{per_step:.3f} s per step"}
 
 
+class Timer:
+    """HIP events on torch's current stream (the stream every call runs on)."""
+
+    def __init__(self, torch):
+        self.torch = torch
+
+    def per_call(self, fn, n: int, warmup: int = 2) -> float:
+        """Seconds per call of fn(i) over n back-to-back calls."""
+        t = self.torch
+        for i in range(warmup):
+            fn(i)
+        t.cuda.synchronize()
+        e0, e1 = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(n):
+            fn(i)
+        e1.record()
+        t.cuda.synchronize()
+        return e0.elapsed_time(e1) / 1e3 / n
+
+    def graph_per_call(self, fn, n: int, replays: int = 5) -> float:
+        """Seconds per call when n calls are captured in one HIP graph."""
+        t = self.torch
+        fn(0)
+        t.cuda.synchronize()
+        g = t.cuda.CUDAGraph()
+        s = t.cuda.Stream()
+        with t.cuda.stream(s):
+            with t.cuda.graph(g, stream=s):
+                for i in range(n):
+                    fn(i)
+        t.cuda.synchronize()
+        g.replay()
+        t.cuda.synchronize()
+        e0, e1 = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(replays):
+            g.replay()
+        e1.record()
+        t.cuda.synchronize()
+        return e0.elapsed_time(e1) / 1e3 / replays / n
+
+
 def probe_ceiling(w4, torch, nbytes: int = 2 << 30, reps: int = 10) -> float:
     """Plain streaming-read ceiling (GB/s) of this device."""
-    buf = torch.empty(nbytes // 4, dtype=torch.int32, device="cuda")
-    buf.fill_(1)
+    buf = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
     out = torch.zeros(1, dtype=torch.int32, device="cuda")
-    for _ in range(2):
-        w4.w4_probe_stream(buf, out)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(reps):
-        w4.w4_probe_stream(buf, out)
-    e1.record()
-    torch.cuda.synchronize()
-    t = e0.elapsed_time(e1) / 1e3 / reps
+    t = Timer(torch).per_call(lambda i: w4.w4_probe_stream(buf, out), reps)
     del buf
+    torch.cuda.empty_cache()
     return gbps(nbytes, t)
+
+
+def dev_matrix(torch, np, codes, steps):
+    return (torch.from_numpy(codes.view(np.int32)).cuda(),
+            torch.from_numpy(steps.view(np.int16)).cuda().view(torch.bfloat16))
+
+
+def extra_single_gemv(w4, torch, np, synth, timer):
+    """Single W4A16 GEMV 2048 x 1536, fp16 x, seed 0: back-to-back calls over
+    300 rotated copies (534 MB, beyond the Infinity Cache), eager and in one
+    HIP graph."""
+    rng = np.random.default_rng(0)
+    N, Kc = 2048, 1536
+    codes, steps = synth.w4_matrix(rng, N, Kc)
+    x = synth.activations(rng, Kc, synth.F16)
+    c0, s0 = dev_matrix(torch, np, codes, steps)
+    copies = 300
+    cs = [c0] + [c0.clone() for _ in range(copies - 1)]
+    ss = [s0] + [s0.clone() for _ in range(copies - 1)]
+    dx = torch.from_numpy(x.view(np.int16)).cuda().view(torch.float16)
+    y = torch.empty(N, device="cuda")
+
+    def call(i):
+        w4.w4_gemv(cs[i % copies], ss[i % copies], dx, y)
+    eager = timer.per_call(call, copies)
+    graph = timer.graph_per_call(call, copies)
+    wb = w4_bytes(N, Kc)
+    out = {"us_per_call_eager": round(eager * 1e6, 3), "us_per_call_graph": round(graph * 1e6, 3),
+           "weight_GBps_graph": round(gbps(wb, graph), 1),
+           "frac_of_peak_graph": round(gbps(wb, graph) / HBM_PEAK_GBPS, 4)}
+    del cs, ss
+    torch.cuda.empty_cache()
+    return out
+
+
+def extra_sweep(w4, torch, np, synth, timer, reps: int = 20):
+    """Decode-step weight sweep: 35 layers x {2560x1536, 1536x2048, 16384x1536,
+    1536x8192}, fp16 x ~ N(0,1), outputs renormalised between matrices: one
+    persistent chain launch, and for reference the same 140 products as
+    separate launches (eager and in one HIP graph)."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(0)
+    shapes = SWEEP_SHAPES * SWEEP_LAYERS
+    mats = []
+    for N, Kc in shapes:
+        c, s = synth.w4_matrix_torch(g, N, Kc, "cuda")
+        mats.append((c[0], s[0].view(torch.bfloat16)))
+    ys = [torch.empty(N, device="cuda") for N, _ in shapes]
+    xs = [torch.empty(Kc, dtype=torch.float16, device="cuda") for _, Kc in shapes]
+    x0 = torch.from_numpy(synth.activations(np.random.default_rng(0), 1536, synth.F16).view(np.int16)
+                          ).cuda().view(torch.float16)
+    desc = w4.w4_chain_desc(mats, ys)
+    sync = w4.w4_chain_sync()
+    chain = timer.per_call(lambda i: w4.w4_gemv_chain(desc, x0, sync), reps)
+    err = int(sync[2].item())
+
+    def separate(i):
+        for j, ((c, s), y) in enumerate(zip(mats, ys)):
+            if j == 0:
+                w4.w4_gemv(c, s, x0, y)
+            else:
+                w4.w4_rms_renorm(ys[j - 1], shapes[j][1], out=xs[j])
+                w4.w4_gemv(c, s, xs[j], y)
+    eager = timer.per_call(separate, 3, warmup=1)
+    graph = timer.graph_per_call(separate, 1, replays=reps)
+    wb = sum(w4_bytes(N, Kc) for N, Kc in shapes)
+    out = {"us_per_sweep_chain": round(chain * 1e6, 2),
+           "weight_GBps_chain": round(gbps(wb, chain), 1),
+           "frac_of_peak_chain": round(gbps(wb, chain) / HBM_PEAK_GBPS, 4),
+           "us_per_sweep_separate_eager": round(eager * 1e6, 1),
+           "us_per_sweep_separate_graph": round(graph * 1e6, 1),
+           "sweep_weight_bytes": wb, "chain_error_word": err}
+    del mats, ys, xs
+    torch.cuda.empty_cache()
+    return out
+
+
+def extra_small_m(w4, torch, np, synth, timer, reps: int = 20):
+    """Small-batch products on the four sweep shapes, M in {2, 4, 8, 16} bf16
+    rows; copies rotated to exceed the Infinity Cache."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(0)
+    copies = 24  # 24 x 25.2 MB per set
+    sets = []
+    for _ in range(copies):
+        mats = []
+        for N, Kc in SWEEP_SHAPES:
+            c, s = synth.w4_matrix_torch(g, N, Kc, "cuda")
+            mats.append((c[0], s[0].view(torch.bfloat16)))
+        sets.append(mats)
+    set_bytes = sum(w4_bytes(N, Kc) for N, Kc in SWEEP_SHAPES)
+    out = {}
+    for M in (2, 4, 8, 16):
+        X = [torch.randn((M, Kc), generator=g, device="cuda").to(torch.bfloat16) for _, Kc in SWEEP_SHAPES]
+        Y = [torch.empty((M, N), device="cuda") for N, _ in SWEEP_SHAPES]
+        per_shape = {}
+        for si, (N, Kc) in enumerate(SWEEP_SHAPES):
+            t = timer.per_call(lambda i: w4.w4_gemm_smallM(*sets[i % copies][si], X[si], Y[si]), reps)
+            per_shape[f"{N}x{Kc}"] = round(t * 1e6, 2)
+
+        def one_set(i):
+            for si in range(4):
+                w4.w4_gemm_smallM(*sets[i % copies][si], X[si], Y[si])
+        tset = timer.graph_per_call(one_set, copies)
+        bytes_set = set_bytes + sum(2 * M * Kc + 4 * M * N for N, Kc in SWEEP_SHAPES)
+        out[f"M{M}"] = {"us_per_shape_eager": per_shape, "us_per_set_graph": round(tset * 1e6, 2),
+                        "GBps_set_graph": round(gbps(bytes_set, tset), 1),
+                        "frac_of_peak_set_graph": round(gbps(bytes_set, tset) / HBM_PEAK_GBPS, 4)}
+    del sets
+    torch.cuda.empty_cache()
+    return out
+
+
+def extra_moe(w4, torch, np, synth, timer, reps: int = 5):
+    """Expert layers: 30 layers x 128 experts, gate/up 1408x2816 and down
+    2816x704 (group 32, bf16 steps), top-8 of 128 per token, router weights
+    softmax of N(0,1); T = 1 and 4 tokens; direct addressing and a 32-slot pool
+    (the two must agree bit for bit)."""
+    E, topk, S, L = 128, 8, 32, 30
+    g = torch.Generator(device="cuda")
+    g.manual_seed(0)
+    layers = []
+    for _ in range(L):
+        gu_c, gu_s = synth.w4_matrix_torch(g, 1408, 2816, "cuda", count=E)
+        dn_c, dn_s = synth.w4_matrix_torch(g, 2816, 704, "cuda", count=E)
+        layers.append((gu_c.view(-1, 2816 // 8), gu_s.view(-1, 2816 // 32).view(torch.bfloat16),
+                       dn_c.view(-1, 704 // 8), dn_s.view(-1, 704 // 32).view(torch.bfloat16)))
+    per_expert = w4_bytes(1408, 2816) + w4_bytes(2816, 704)
+    out = {}
+    for T in (1, 4):
+        rng = np.random.default_rng(T)
+        picks = [synth.expert_choice(rng, T, E, topk) for _ in range(L)]
+        ids = [torch.from_numpy(p[0]).cuda() for p in picks]
+        route = [torch.from_numpy(p[1]).cuda() for p in picks]
+        x0 = torch.randn((T, 2816), generator=g, device="cuda").to(torch.bfloat16)
+        G = torch.empty((T * topk, 1408), device="cuda")
+        H = torch.empty((T * topk, 704), dtype=torch.bfloat16, device="cuda")
+        Dn = torch.empty((T, 2816), device="cuda")
+        Xn = torch.empty((T, 2816), dtype=torch.bfloat16, device="cuda")
+
+        def token(i, slot=None, pools=None):
+            x = x0
+            for li, (gc, gs, dc, ds) in enumerate(layers):
+                kw = {}
+                if pools is not None:
+                    gc, gs, dc, ds = pools[li]
+                    kw = dict(slot_of=slot[li], n_slots=S)
+                w4.w4_moe_gemv_ids(gc, gs, 1408 * 2816 // 8, 1408 * 2816 // 32, 1408, 2816, x, ids[li],
+                                   n_experts=E, Y=G, **kw)
+                w4.w4_rms_renorm(G, 704, out=H)
+                w4.w4_moe_gemv_ids(dc, ds, 2816 * 704 // 8, 2816 * 704 // 32, 2816, 704, H, ids[li],
+                                   x_per_pair=True, n_experts=E, route_w=route[li], Y=Dn, **kw)
+                w4.w4_rms_renorm(Dn, 2816, out=Xn)
+                x = Xn
+        eager = timer.per_call(token, reps, warmup=1)
+        graph = timer.graph_per_call(token, 1, replays=reps)
+        # unique expert bytes read per token step (each distinct expert once per layer)
+        distinct = sum(len(np.unique(p[0])) for p in picks)
+        nbytes = distinct * per_expert
+        # 32-slot pools holding each layer's chosen experts
+        slots, pools = [], []
+        for li, p in enumerate(picks):
+            slot_of, used = synth.slot_map(np.random.default_rng(100 + li), p[0], E, S)
+            gc, gs, dc, ds = layers[li]
+            sel = torch.from_numpy(used).cuda().long()
+            dst = torch.from_numpy(slot_of[used]).cuda().long()
+
+            def pool(t, rows):
+                pt = torch.zeros((S * rows, t.shape[1]), dtype=t.dtype, device="cuda")
+                pt.view(S, rows, -1)[dst] = t.view(E, rows, -1)[sel]
+                return pt
+            pools.append((pool(gc, 1408), pool(gs, 1408), pool(dc, 2816), pool(ds, 2816)))
+            slots.append(torch.from_numpy(slot_of).cuda())
+        token(0)
+        ref = Xn.clone()
+        token(0, slot=slots, pools=pools)
+        torch.cuda.synchronize()
+        identical = bool(torch.equal(ref.view(torch.int16), Xn.view(torch.int16)))
+        pool_graph = timer.graph_per_call(lambda i: token(i, slots, pools), 1, replays=reps)
+        out[f"T{T}"] = {"us_per_token_eager": round(eager * 1e6, 1),
+                        "us_per_token_graph": round(graph * 1e6, 1),
+                        "us_per_token_pool_graph": round(pool_graph * 1e6, 1),
+                        "expert_GBps_graph": round(gbps(nbytes, graph), 1),
+                        "frac_of_peak_graph": round(gbps(nbytes, graph) / HBM_PEAK_GBPS, 4),
+                        "expert_bytes_per_token": nbytes,
+                        "pool_bitwise_identical_to_direct": identical}
+        del pools
+    del layers
+    torch.cuda.empty_cache()
+    return out
 
 
 def main(argv=None):
@@ -99,6 +327,7 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-extra", action="store_true", help="only the vocabulary-head step")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
@@ -112,48 +341,36 @@ def main(argv=None):
     import synth
 
     torch.cuda.set_device(0)
+    timer = Timer(torch)
     rng = np.random.default_rng(0)
     codes, steps = synth.w4_matrix(rng, V, K)
     x = synth.activations(rng, K, synth.BF16)
     ids = synth.token_ids(rng, NIDS, V)
 
-    dcodes = [torch.from_numpy(codes.view(np.int32)).cuda()]
-    dsteps = [torch.from_numpy(steps.view(np.int16)).cuda().view(torch.bfloat16)]
-    for _ in range(COPIES - 1):
-        dcodes.append(dcodes[0].clone())
-        dsteps.append(dsteps[0].clone())
+    c0, s0 = dev_matrix(torch, np, codes, steps)
+    dcodes = [c0] + [c0.clone() for _ in range(COPIES - 1)]
+    dsteps = [s0] + [s0.clone() for _ in range(COPIES - 1)]
     dx = torch.from_numpy(x.view(np.int16)).cuda().view(torch.bfloat16)
     dids = torch.from_numpy(ids).cuda()
     y = torch.empty(V, dtype=torch.float32, device="cuda")
-    g = torch.empty((NIDS, K), dtype=torch.bfloat16, device="cuda")
+    gout = torch.empty((NIDS, K), dtype=torch.bfloat16, device="cuda")
 
-    def step(i, ev=None):
+    def step(i):
         c = i % COPIES
-        if ev is not None:
-            ev[0].record()
         w4.w4_gemv(dcodes[c], dsteps[c], dx, y)
-        if ev is not None:
-            ev[1].record()
-        w4.w4_embed_gather(dcodes[c], dsteps[c], dids, g)
+        w4.w4_embed_gather(dcodes[c], dsteps[c], dids, gout)
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
-    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     t0 = time.perf_counter()
-    t_start.record()
-    for i in range(args.steps):
-        step(i, evs[i])
-    t_end.record()
-    torch.cuda.synchronize()
+    step_s = timer.per_call(step, args.steps, warmup=0)
     wall = time.perf_counter() - t0
-    step_s = t_start.elapsed_time(t_end) / 1e3 / args.steps
-    gemv_s = sum(a.elapsed_time(b) for a, b in evs) / 1e3 / args.steps
-
+    # dominant kernel: the GEMV alone, back to back on the same stream
+    gemv_s = timer.per_call(lambda i: w4.w4_gemv(dcodes[i % COPIES], dsteps[i % COPIES], dx, y),
+                            args.steps, warmup=0)
+    gather_s = timer.per_call(lambda i: w4.w4_embed_gather(dcodes[i % COPIES], dsteps[i % COPIES],
+                                                            dids, gout), args.steps, warmup=0)
     ceiling = probe_ceiling(w4, torch)
     achieved = gbps(gemv_bytes(V, K), gemv_s)
     result = {
@@ -167,21 +384,30 @@ def main(argv=None):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16/bf16 products, fp32 accumulate",
+        "dtype": "f16 (exact operands), fp32 accumulate",
         "data": "synthetic (seeded; codes uniform 0..15, steps bf16(|N(0,0.02)|+1e-4), x ~ N(0,1))",
         "config": {"workload": "vocabulary-head W4A16 GEMV 262144x1536 (bf16 x, batch 1) + "
                                "4-bit row gather of 64 ids from the same table",
                    "table_copies_rotated": COPIES, "step_bytes": STEP_BYTES},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": None, "kernel": "w4::gemv_kernel",
+                     "traffic": None, "kernel": "w4::gemv_kernel<16, 3, 2>",
                      "bytes_per_launch": gemv_bytes(V, K),
                      "avg_launch_us": round(gemv_s * 1e6, 3)},
         "extra": {"gemv_weight_GBps": round(gbps(w4_bytes(V, K), gemv_s), 2),
+                  "gather_us": round(gather_s * 1e6, 3),
                   "probe_read_ceiling_GBps": round(ceiling, 1),
                   "gemv_frac_of_probe": round(achieved / ceiling, 4),
-                  "timed_wall_s": round(wall, 3)},
+                  "timed_wall_s": round(wall, 4)},
     }
+    del dcodes, dsteps
+    torch.cuda.empty_cache()
+    if not args.no_extra:
+        ex = result["extra"]
+        ex["single_gemv_2048x1536_f16"] = extra_single_gemv(w4, torch, np, synth, timer)
+        ex["decode_sweep_35_layers"] = extra_sweep(w4, torch, np, synth, timer)
+        ex["small_m_sweep_shapes_bf16"] = extra_small_m(w4, torch, np, synth, timer)
+        ex["moe_30_layers_top8_of_128"] = extra_moe(w4, torch, np, synth, timer)
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(codes, steps, x, ids)
     print(json.dumps(result), flush=True)

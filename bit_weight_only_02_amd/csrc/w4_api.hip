@@ -180,6 +180,7 @@ int w4_rms_renorm(const float *v, int64_t ldv, int32_t K, int32_t rows, void *ou
     int st;
     if ((st = check_dtype(out_dt))) return st;
     if (K < 0 || rows < 0) return fail(W4_ERR_INVALID_ARG, "negative K or rows");
+    if (K % 4) return fail(W4_ERR_INVALID_ARG, "K=%d is not a multiple of 4", K);
     if (rows > 65535) return fail(W4_ERR_UNSUPPORTED, "rows=%d exceeds 65535", rows);
     if (rows > 1 && (ldv < K || ldo < K)) return fail(W4_ERR_INVALID_ARG, "ldv or ldo < K");
     if (K > 0 && rows > 0 && (!v || !out)) return fail(W4_ERR_INVALID_ARG, "null v/out");
@@ -243,7 +244,7 @@ int w4_gemv_chain(const w4_chain_mat *desc, int32_t n_mats, const uint16_t *x0, 
     int st;
     if (n_mats < 1) return fail(W4_ERR_INVALID_ARG, "n_mats must be >= 1");
     if (!desc || !x0 || !sync) return fail(W4_ERR_INVALID_ARG, "null desc/x0/sync");
-    if (!aligned(desc, 8) || !aligned(x0, 2) || !aligned(sync, 16))
+    if (!aligned(desc, 8) || !aligned(x0, 16) || !aligned(sync, 16))
         return fail(W4_ERR_ALIGNMENT, "desc, x0 or sync misaligned");
     if ((st = device_ready())) return st;
     if (forced_launch_error()) return fail(W4_ERR_HIP, "forced launch error (test hook)");

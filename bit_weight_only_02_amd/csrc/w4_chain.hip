@@ -12,16 +12,18 @@
 // Per step:
 //   1. input: x0 for the first matrix, else the leading K entries of the
 //      previous output divided by their RMS and rounded to fp16 (the same
-//      arithmetic as w4_rms_renorm, so that results are bitwise those of the
-//      separate calls), staged as exactly scaled fp16 like the GEMV;
+//      arithmetic as w4_rms_renorm, bit for bit), read with agent-coherent
+//      16-byte loads all issued at once; fp16 operands are exact as they are,
+//      so each wave only permutes them into the pair layout of the GEMV;
 //   2. the rows of this workgroup (a row mapping chosen from the shape), the
 //      results written with agent-scope stores;
-//   3. the barrier: every wave waits for its stores, then wave 0 adds to a
-//      counter and polls it (agent scope, bounded), while waves 1..3 pull this
+//   3. the barrier: every wave waits for its stores, the workgroup stores its
+//      generation into its own flag and wave 0 polls all flags (agent scope,
+//      bounded; no contended read-modify-write), while waves 1..3 pull this
 //      workgroup's share of the NEXT matrix into L2 with LDS-DMA loads into a
 //      scratch LDS area, so that the next step reads its weights from L2.
 // Outputs of every step are read back with agent-scope loads, which see the
-// stores of workgroups on other XCDs.
+// stores of workgroups on other XCDs.  One workgroup of eight waves per CU.
 #include <cstdio>
 #include <cstdlib>
 #include <type_traits>
@@ -41,11 +43,14 @@ struct ChainMat {
 };
 static_assert(sizeof(ChainMat) == sizeof(w4_chain_mat), "descriptor layout");
 
-constexpr int kChainThreads = 256;
+constexpr int kChainThreads = 512;  // eight waves; the renorm uses the first four
 constexpr int kChainMaxK = 8192;
 constexpr int kPrefetchBytes = 32768;  // LDS scratch for the L2 prefetch
-// sync words
-constexpr int kSyncArrive = 0, kSyncExit = 1, kSyncError = 2;
+// sync buffer: word 0 exit counter, word 1 epoch (barrier generations used by
+// earlier calls), word 2 error; from word 64 on, one arrival flag per
+// workgroup (the generation it last reached).
+constexpr int kSyncExit = 0, kSyncEpoch = 1, kSyncError = 2, kSyncFlags = 64;
+constexpr int kMaxChainWG = (W4_CHAIN_SYNC_BYTES / 4) - kSyncFlags;
 
 __device__ __forceinline__ float load_agent(const float *p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -87,8 +92,7 @@ __device__ __forceinline__ ChainVariant variant_shape(int v) {
 template <int L, int NG>
 __device__ __forceinline__ void chain_rows(const uint4 *__restrict__ codes,
                                            const uint16_t *__restrict__ steps, int N, int K,
-                                           const _Float16 *xs, const uint16_t *raw,
-                                           const Staging &st, float *y) {
+                                           const uint16_t *raw, float *y) {
     constexpr int SLOTS = kWave / L;
     const int G = K >> 5;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -97,14 +101,16 @@ __device__ __forceinline__ void chain_rows(const uint4 *__restrict__ codes,
     int gc[NG];
 #pragma unroll
     for (int i = 0; i < NG; ++i) gc[i] = min(l + i * L, G - 1);
+    // this wave's activations (fp16, staged as they are), LDS -> registers
     h2 xr[NG][16];
-    if (!st.fallback) {
-        const h2 *xs2 = reinterpret_cast<const h2 *>(xs);
 #pragma unroll
-        for (int i = 0; i < NG; ++i) {
-            const int g = l + i * L;
+    for (int i = 0; i < NG; ++i) {
+        const int g = l + i * L;
+        if (g < G) {
+            permute_group_f16(raw, g, xr[i]);
+        } else {
 #pragma unroll
-            for (int p = 0; p < 16; ++p) xr[i][p] = (g < G) ? xs2[g * 16 + p] : h2{0, 0};
+            for (int p = 0; p < 16; ++p) xr[i][p] = h2{0, 0};
         }
     }
     for (int row0 = blockIdx.x * rows_per_iter; row0 < N; row0 += gridDim.x * rows_per_iter) {
@@ -121,68 +127,94 @@ __device__ __forceinline__ void chain_rows(const uint4 *__restrict__ codes,
 #pragma unroll
         for (int i = 0; i < NG; ++i) {
             const int g = l + i * L;
-            const float part = st.fallback ? group_dot_f32(q[i], raw + gc[i] * 32, 0)
-                                           : group_dot(q[i], xr[i]);
-            acc = (g < G) ? __builtin_fmaf(part, bf16_to_f32(sv[i]), acc) : acc;
+            acc = (g < G) ? __builtin_fmaf(group_dot(q[i], xr[i]), bf16_to_f32(sv[i]), acc) : acc;
         }
 #pragma unroll
         for (int off = L / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, kWave);
-        if (l == 0 && row < N)
-            store_agent(y + row, st.fallback ? acc : __builtin_ldexpf(acc, -st.scale));
+        if (l == 0 && row < N) store_agent(y + row, acc);
     }
 }
 
-// Pull this workgroup's rows of the next matrix into L2 (waves 1..3 only; the
-// data land in a scratch LDS area that nobody reads).
+// Pull this workgroup's rows of the next matrix (codes, then steps) into L2
+// (waves 1.. only; the data land in a scratch LDS area that nobody reads).
 __device__ __forceinline__ void chain_prefetch(const ChainMat &m, int nwg, uint4 *scratch) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int nw = kChainThreads / 64 - 1;  // prefetching waves
     if (wave == 0) return;
     const int G = m.K >> 5;
     const ChainVariant vs = variant_shape(chain_variant(m.N, G, nwg));
     const int rows_per_iter = (kChainThreads / 64) * (kWave / vs.L);
-    const uint4 *codes = reinterpret_cast<const uint4 *>(m.codes);
     int budget = kPrefetchBytes / 16;  // 16-byte chunks this workgroup may pull
     int dst = 0;
-    for (int row0 = blockIdx.x * rows_per_iter; row0 < m.N && budget > 0; row0 += nwg * rows_per_iter) {
-        const int nrows = min(rows_per_iter, m.N - row0);
-        const long first = (long)row0 * G;
-        const int chunks = min(nrows * G, budget);
-        for (int c0 = (wave - 1) * 64; c0 < chunks; c0 += 3 * 64) {
+    auto pull = [&](const uint4 *base, long first, int chunks) __attribute__((always_inline)) {
+        for (int c0 = (wave - 1) * 64; c0 < chunks; c0 += nw * 64) {
             const int c = min(c0 + lane, chunks - 1);
             const int d = (dst + c0) % (kPrefetchBytes / 16 - 63);
             __builtin_amdgcn_global_load_lds(
-                (const __attribute__((address_space(1))) void *)(codes + first + c),
+                (const __attribute__((address_space(1))) void *)(base + first + c),
                 (__attribute__((address_space(3))) void *)(scratch + d), 16, 0, 0);
         }
-        budget -= chunks;
         dst += chunks;
+    };
+    for (int row0 = blockIdx.x * rows_per_iter; row0 < m.N && budget > 0; row0 += nwg * rows_per_iter) {
+        const int nrows = min(rows_per_iter, m.N - row0);
+        const int chunks = min(nrows * G, budget);
+        pull(reinterpret_cast<const uint4 *>(m.codes), (long)row0 * G, chunks);
+        budget -= chunks;
+        // the steps of these rows: the 16-byte chunks lying wholly inside
+        // their nrows*G bf16 values (never past the end of the step array)
+        const long s_first = ((long)row0 * G * 2 + 15) / 16;
+        const long s_end = ((long)(row0 + nrows) * G * 2) / 16;
+        const int s_chunks = (int)min((long)budget, s_end - s_first);
+        if (s_chunks > 0 && (reinterpret_cast<uintptr_t>(m.steps) & 15) == 0) {
+            pull(reinterpret_cast<const uint4 *>(m.steps), s_first, s_chunks);
+            budget -= s_chunks;
+        }
     }
 }
 
-// Grid barrier number `gen` (1-based).  Stores of every wave complete first;
-// wave 0 of each workgroup arrives and polls with a bounded spin; a timeout
-// sets the error word.  Returns false if the chain must stop.
+// Grid barrier to generation `gen`.  No read-modify-write on a shared word:
+// each workgroup stores `gen` into its own flag, then wave 0 reads every
+// workgroup's flag (agent-coherent loads, all issued at once, one or more per
+// lane) until all have reached `gen`, with a bounded number of polls; a
+// timeout sets the error word.  Meanwhile waves 1..3 pull this workgroup's
+// share of the next matrix into L2.  Returns false if the chain must stop.
 __device__ __forceinline__ bool chain_barrier(unsigned *sync, unsigned gen, unsigned spin_limit,
                                               const ChainMat *next, int nwg, uint4 *scratch) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's stores are done
     lds_barrier();
     __shared__ int stop_s;
+    unsigned *flags = sync + kSyncFlags;
+    if (threadIdx.x == 0)
+        __hip_atomic_store(flags + blockIdx.x, gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (next) chain_prefetch(*next, nwg, scratch);
-    if (threadIdx.x == 0) {
-        __hip_atomic_fetch_add(sync + kSyncArrive, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const unsigned target = gen * (unsigned)nwg;
+    if (threadIdx.x < 64) {
+        const int lane = threadIdx.x;
+        const __amdgpu_buffer_rsrc_t fr = buffer_rsrc(flags, nwg * 4);
         unsigned it = 0;
         int stop = 0;
-        while (load_agent_u(sync + kSyncArrive) < target) {
+        for (;;) {
+            // lane l checks flags l, l+64, ... (four at a time per load)
+            int behind = 0;
+            for (int f0 = lane * 4; f0 < nwg; f0 += 256) {
+                const float4 v = load_coherent_f4(fr, f0 * 4);
+                const unsigned a = __float_as_uint(v.x), b = __float_as_uint(v.y);
+                const unsigned c = __float_as_uint(v.z), d = __float_as_uint(v.w);
+                // generations only grow; compare with wrap-around arithmetic
+                behind |= (int)(a - gen) < 0 && f0 + 0 < nwg;
+                behind |= (int)(b - gen) < 0 && f0 + 1 < nwg;
+                behind |= (int)(c - gen) < 0 && f0 + 2 < nwg;
+                behind |= (int)(d - gen) < 0 && f0 + 3 < nwg;
+            }
+            if (!wave_or_i32(behind)) break;
             if (++it > spin_limit) {
-                __hip_atomic_store(sync + kSyncError, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (lane == 0)
+                    __hip_atomic_store(sync + kSyncError, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 stop = 1;
                 break;
             }
-            __builtin_amdgcn_s_sleep(1);
         }
-        if (load_agent_u(sync + kSyncError) != 0) stop = 1;
-        stop_s = stop;
+        if (lane == 0) stop_s = stop || load_agent_u(sync + kSyncError) != 0;
     }
     lds_barrier();
     return stop_s == 0;
@@ -192,11 +224,9 @@ __global__ __launch_bounds__(kChainThreads) void chain_kernel(const ChainMat *__
                                                               int n, const uint16_t *__restrict__ x0,
                                                               unsigned *sync, unsigned spin_limit) {
     extern __shared__ uint4 smem[];
-    _Float16 *xs = reinterpret_cast<_Float16 *>(smem);            // kChainMaxK halves
-    uint16_t *raw = reinterpret_cast<uint16_t *>(xs + kChainMaxK);  // kChainMaxK halves
-    uint4 *scratch = smem + (2 * kChainMaxK * 2) / 16;              // kPrefetchBytes
-    __shared__ double dred[4];
-    __shared__ int ired[8];
+    uint16_t *raw = reinterpret_cast<uint16_t *>(smem);          // kChainMaxK halves
+    uint4 *scratch = smem + (kChainMaxK * 2) / 16;                // kPrefetchBytes
+    __shared__ double dred[8];
     const int nwg = gridDim.x;
     const int tid = threadIdx.x;
 
@@ -205,60 +235,91 @@ __global__ __launch_bounds__(kChainThreads) void chain_kernel(const ChainMat *__
     for (int i = 0; i < n && ok; ++i) {
         const ChainMat m = desc[i];
         if (m.N < 1 || m.K < 32 || (m.K & 31) || m.K > kChainMaxK || !m.codes || !m.steps || !m.y ||
-            (reinterpret_cast<uintptr_t>(m.codes) & 15) || (i > 0 && m.K > desc[i - 1].N))
+            (reinterpret_cast<uintptr_t>(m.codes) & 15) || (reinterpret_cast<uintptr_t>(m.y) & 15) ||
+            (i > 0 && m.K > desc[i - 1].N))
             ok = false;
     }
+    if (nwg > kMaxChainWG) ok = false;
+    // barrier generations of this call continue from those of earlier calls
+    const unsigned epoch = load_agent_u(sync + kSyncEpoch);
     if (ok) {
         for (int i = 0; i < n; ++i) {
             const ChainMat m = desc[i];
             const int K = m.K, G = K >> 5;
-            // 1. input
+            // 1. input into LDS (raw fp16)
+            uint4 *r16 = reinterpret_cast<uint4 *>(raw);
             if (i == 0) {
-                for (int k = tid; k < K; k += kChainThreads) raw[k] = x0[k];
+                const uint4 *x16 = reinterpret_cast<const uint4 *>(x0);
+                for (int c = tid; c < (K >> 3); c += kChainThreads) r16[c] = x16[c];
             } else {
-                const float *prev = desc[i - 1].y;
-                const double ss = sum_squares_256(K, [&](int k) { return load_agent(prev + k); }, dred);
-                for (int k = tid; k < K; k += kChainThreads) raw[k] = renorm_value(load_agent(prev + k), ss, K, 0);
+                // previous output: all of this thread's chunks requested at
+                // once with agent-coherent loads, then the canonical sum
+                const __amdgpu_buffer_rsrc_t pr = buffer_rsrc(desc[i - 1].y, K * 4);
+                constexpr int J = kChainMaxK / 4 / 256;
+                float4 v[J];
+                const bool rn = tid < 256;  // the canonical 256-thread order
+#pragma unroll
+                for (int j = 0; j < J; ++j) {
+                    const int c = min((rn ? tid : 0) + 256 * j, (K >> 2) - 1);
+                    v[j] = load_coherent_f4(pr, c * 16);
+                }
+                const double ss = sum_squares_256_regs(K, v, dred, rn);
+                if (rn) {
+#pragma unroll
+                    for (int j = 0; j < J; ++j) {
+                        const int c = tid + 256 * j;
+                        if (c < (K >> 2)) {
+                            const uint32_t lo = renorm_value(v[j].x, ss, K, 0) | ((uint32_t)renorm_value(v[j].y, ss, K, 0) << 16);
+                            const uint32_t hi = renorm_value(v[j].z, ss, K, 0) | ((uint32_t)renorm_value(v[j].w, ss, K, 0) << 16);
+                            reinterpret_cast<uint2 *>(raw)[c] = make_uint2(lo, hi);
+                        }
+                    }
+                }
             }
             __syncthreads();
-            const Staging st = stage_convert(K, 0, xs, raw, ired);
             // 2. rows
             const uint4 *codes = reinterpret_cast<const uint4 *>(m.codes);
             switch (__builtin_amdgcn_readfirstlane(chain_variant(m.N, G, nwg))) {
-                case 0: chain_rows<64, 1>(codes, m.steps, m.N, K, xs, raw, st, m.y); break;
-                case 1: chain_rows<64, 2>(codes, m.steps, m.N, K, xs, raw, st, m.y); break;
-                case 2: chain_rows<64, 4>(codes, m.steps, m.N, K, xs, raw, st, m.y); break;
-                case 3: chain_rows<16, 3>(codes, m.steps, m.N, K, xs, raw, st, m.y); break;
-                case 4: chain_rows<16, 4>(codes, m.steps, m.N, K, xs, raw, st, m.y); break;
-                default: chain_rows<32, 4>(codes, m.steps, m.N, K, xs, raw, st, m.y); break;
+                case 0: chain_rows<64, 1>(codes, m.steps, m.N, K, raw, m.y); break;
+                case 1: chain_rows<64, 2>(codes, m.steps, m.N, K, raw, m.y); break;
+                case 2: chain_rows<64, 4>(codes, m.steps, m.N, K, raw, m.y); break;
+                case 3: chain_rows<16, 3>(codes, m.steps, m.N, K, raw, m.y); break;
+                case 4: chain_rows<16, 4>(codes, m.steps, m.N, K, raw, m.y); break;
+                default: chain_rows<32, 4>(codes, m.steps, m.N, K, raw, m.y); break;
             }
             // 3. barrier before the next matrix reads this output
             if (i + 1 < n) {
                 const ChainMat next = desc[i + 1];
-                if (!chain_barrier(sync, (unsigned)(i + 1), spin_limit, &next, nwg, scratch)) break;
+                if (!chain_barrier(sync, epoch + (unsigned)(i + 1), spin_limit, &next, nwg, scratch)) break;
             }
         }
     } else if (blockIdx.x == 0 && tid == 0) {
         __hip_atomic_store(sync + kSyncError, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    // Exit: the last workgroup out (every other one is past its last barrier)
-    // returns the counters to zero for the next call.
+    // Exit: the last workgroup out (every other one is past its last barrier
+    // and has read the epoch) advances the epoch past this call's generations
+    // and returns the exit counter to zero.
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     lds_barrier();
     if (tid == 0) {
         const unsigned prev = __hip_atomic_fetch_add(sync + kSyncExit, 1u, __ATOMIC_RELAXED,
                                                      __HIP_MEMORY_SCOPE_AGENT);
         if (prev == (unsigned)nwg - 1) {
-            __hip_atomic_store(sync + kSyncArrive, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(sync + kSyncEpoch, epoch + (unsigned)n, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
             __hip_atomic_store(sync + kSyncExit, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
 }
 
-size_t chain_lds_bytes() { return (size_t)2 * kChainMaxK * 2 + kPrefetchBytes; }
+size_t chain_lds_bytes() { return (size_t)kChainMaxK * 2 + kPrefetchBytes; }
 
 hipError_t launch_chain(const void *desc, int n, const uint16_t *x0, void *sync, unsigned spin_limit,
                         hipStream_t stream) {
+    // One workgroup per CU, all resident together on an otherwise idle device
+    // (the occupancy check makes sure one fits per CU).  A plain launch: if
+    // some workgroups could not start while others wait, the bounded barrier
+    // waits end with the timeout error instead of a hang.
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
@@ -268,13 +329,11 @@ hipError_t launch_chain(const void *desc, int n, const uint16_t *x0, void *sync,
     const size_t lds = chain_lds_bytes();
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, chain_kernel, kChainThreads, lds);
     if (e != hipSuccess) return e;
-    if (per_cu < 1) return hipErrorInvalidConfiguration;
-    if (per_cu > 2) per_cu = 2;
-    const ChainMat *d = static_cast<const ChainMat *>(desc);
-    unsigned *s = static_cast<unsigned *>(sync);
-    void *args[] = {&d, &n, &x0, &s, &spin_limit};
-    return hipLaunchCooperativeKernel(reinterpret_cast<const void *>(chain_kernel), dim3(cus * per_cu),
-                                      dim3(kChainThreads), args, (unsigned)lds, stream);
+    if (per_cu < 1 || cus > kMaxChainWG) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(chain_kernel, dim3(cus), dim3(kChainThreads), lds, stream,
+                       static_cast<const ChainMat *>(desc), n, x0, static_cast<unsigned *>(sync),
+                       spin_limit);
+    return hipGetLastError();
 }
 
 }  // namespace w4

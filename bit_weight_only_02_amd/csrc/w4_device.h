@@ -127,19 +127,23 @@ __device__ __forceinline__ int max_across_lane_groups(int v) {
     return max((int)b[0], (int)b[1]);
 }
 
-// Sum of squares of v[0..K) in fp64 with one fixed order, shared by every
-// kernel that renormalises (so that they agree bit for bit): thread t of a
-// 256-thread workgroup adds v[t], v[t+256], ... in ascending order; the 64
-// lanes of a wave are folded by xor shuffles 32, 16, ..., 1; the four wave
-// sums are added in wave order.  `load(k)` returns v[k] as float.  Every
-// thread gets the total.  `red` is 4 doubles of shared scratch.
-template <class Load>
-__device__ __forceinline__ double sum_squares_256(int K, Load load, double *red) {
+// Sum of squares of v[0..K) (K a multiple of 4) in fp64 with one fixed order,
+// shared by every kernel that renormalises (so that they agree bit for bit):
+// thread t of a 256-thread workgroup owns the 4-element chunks c = t, t+256,
+// ... and adds their squares in ascending (c, element) order; the 64 lanes of
+// a wave are folded by xor shuffles 32, 16, ..., 1; the four wave sums are
+// added in wave order.  load4(c) returns chunk c as a float4.  Every thread
+// gets the total.  `red` is 4 doubles of shared scratch.
+template <class Load4>
+__device__ __forceinline__ double sum_squares_256(int K, Load4 load4, double *red) {
     const int tid = threadIdx.x;
     double ss = 0.0;
-    for (int k = tid; k < K; k += 256) {
-        const double v = (double)load(k);
-        ss += v * v;
+    for (int c = tid; c < (K >> 2); c += 256) {
+        const float4 v = load4(c);
+        ss += (double)v.x * (double)v.x;
+        ss += (double)v.y * (double)v.y;
+        ss += (double)v.z * (double)v.z;
+        ss += (double)v.w * (double)v.w;
     }
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off, kWave);
@@ -150,12 +154,130 @@ __device__ __forceinline__ double sum_squares_256(int K, Load load, double *red)
     return tot;
 }
 
+// The same sum over chunks already in registers: v[j] is chunk tid + 256*j
+// (valid while tid + 256*j < K/4), up to J chunks per thread.  Threads with
+// `active` false (beyond the first 256 of a larger workgroup) add nothing and
+// only take part in the barriers; `red` holds one double per wave.
+template <int J>
+__device__ __forceinline__ double sum_squares_256_regs(int K, const float4 (&v)[J], double *red,
+                                                       bool active = true) {
+    const int tid = threadIdx.x;
+    double ss = 0.0;
+    if (active) {
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            if (tid + 256 * j < (K >> 2)) {
+                ss += (double)v[j].x * (double)v[j].x;
+                ss += (double)v[j].y * (double)v[j].y;
+                ss += (double)v[j].z * (double)v[j].z;
+                ss += (double)v[j].w * (double)v[j].w;
+            }
+        }
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off, kWave);
+    if ((tid & 63) == 0 && tid < 256) red[tid >> 6] = ss;
+    __syncthreads();
+    const double tot = ((red[0] + red[1]) + red[2]) + red[3];
+    __syncthreads();
+    return tot;
+}
+
+// Buffer resource over `bytes` bytes at p (raw buffer loads, gfx9 format word).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *p, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, bytes, 0x00020000);
+}
+
+// 16-byte load that is coherent at agent scope (cache policy SC1): it sees
+// stores made with agent scope by workgroups on any XCD.
+__device__ __forceinline__ float4 load_coherent_f4(__amdgpu_buffer_rsrc_t r, int byte_offset) {
+    return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_offset, 0, 16));
+}
+
 // u / sqrt(ss / K) rounded to nearest-even in fp16 (dt 0) or bf16 (dt 1),
 // zero when the vector is zero.
 __device__ __forceinline__ uint16_t renorm_value(float u, double ss, int K, int dt) {
     const double r = sqrt(ss / (double)K);
     const float q = r > 0.0 ? (float)((double)u / r) : 0.0f;
     return dt == 0 ? __builtin_bit_cast(uint16_t, (_Float16)q) : __builtin_bit_cast(uint16_t, (__bf16)q);
+}
+
+// ---- per-wave activation staging -------------------------------------------
+// Every wave scans the whole raw vector itself (no cross-wave reduction), then
+// each lane converts only the groups it owns, straight from LDS into its
+// registers.  The staged value is x * 2^s with s = 14 - (largest exponent):
+// every nonzero value must land in the normal fp16 range, i.e. lie within 2^28
+// of the largest; otherwise (or with inf/NaN) the wave takes the fp32 path.
+struct WaveScale {
+    int scale;  // s
+    int emax;   // largest exponent (-100000: all zero)
+    int bad;    // inf/NaN present
+};
+
+// raw: K halves in LDS, 16-byte aligned, K a multiple of 32.
+__device__ __forceinline__ WaveScale wave_scan(const uint16_t *raw, int K, int dt) {
+    const int lane = threadIdx.x & 63;
+    const uint4 *r16 = reinterpret_cast<const uint4 *>(raw);
+    int emax = -100000, bad = 0;
+    for (int c = lane; c < (K >> 3); c += 64) {
+        const uint4 v = r16[c];
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float f = act_to_f32((w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu, dt);
+            if (!__builtin_isfinite(f)) bad = 1;
+            else if (f != 0.0f) emax = max(emax, f32_exponent(f));
+        }
+    }
+    WaveScale ws;
+    ws.emax = wave_max_i32(emax);
+    ws.bad = wave_or_i32(bad);
+    ws.scale = ws.emax == -100000 ? 0 : 14 - ws.emax;
+    return ws;
+}
+
+// Group g of raw -> 16 staged pairs in unpack_word order; returns 1 if a value
+// cannot be staged exactly.
+__device__ __forceinline__ int convert_group(const uint16_t *raw, int g, int dt, const WaveScale &ws,
+                                             h2 *xr) {
+    const uint4 *r16 = reinterpret_cast<const uint4 *>(raw) + g * 4;
+    int lost = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        const uint4 v = r16[w];
+        const uint32_t b[4] = {v.x, v.y, v.z, v.w};
+        float f[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            f[e] = act_to_f32((b[e >> 1] >> (16 * (e & 1))) & 0xFFFFu, dt);
+            if (f[e] != 0.0f && f32_exponent(f[e]) < ws.emax - 28) lost = 1;
+        }
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            h2 t;
+            t[0] = (_Float16)__builtin_ldexpf(f[p], ws.scale);
+            t[1] = (_Float16)__builtin_ldexpf(f[p + 4], ws.scale);
+            xr[w * 4 + p] = t;
+        }
+    }
+    return lost;
+}
+
+// fp16 activations need no scaling: v_dot2_f32_f16 and the f16 MFMA take
+// fp16 subnormals as they are (measured on gfx950), so (c - 8) * x is exact in
+// fp32 for every fp16 x.  Staging is then only the pair permutation:
+// words (x0,x1) (x2,x3) (x4,x5) (x6,x7) -> (x0,x4) (x1,x5) (x2,x6) (x3,x7).
+__device__ __forceinline__ void permute_group_f16(const uint16_t *raw, int g, h2 *xr) {
+    const uint4 *r16 = reinterpret_cast<const uint4 *>(raw) + g * 4;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        const uint4 v = r16[w];
+        // v_perm_b32 selector: bytes 0-3 from src1, 4-7 from src0
+        xr[w * 4 + 0] = as_h2(__builtin_amdgcn_perm(v.z, v.x, 0x05040100u));
+        xr[w * 4 + 1] = as_h2(__builtin_amdgcn_perm(v.z, v.x, 0x07060302u));
+        xr[w * 4 + 2] = as_h2(__builtin_amdgcn_perm(v.w, v.y, 0x05040100u));
+        xr[w * 4 + 3] = as_h2(__builtin_amdgcn_perm(v.w, v.y, 0x07060302u));
+    }
 }
 
 struct Staging {

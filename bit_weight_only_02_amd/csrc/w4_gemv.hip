@@ -29,8 +29,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(const uint4 *__restrict__ cod
                                                    const uint16_t *__restrict__ x, int dt,
                                                    float *__restrict__ y) {
     constexpr int SLOTS = kWave / L;
-    extern __shared__ _Float16 xs[];  // K staged halves, then K raw halves
-    __shared__ int red[8];
+    extern __shared__ _Float16 xs[];  // the raw activations (stage_raw_halves(K))
     const int G = K >> 5;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int nwaves = blockDim.x >> 6;
@@ -65,29 +64,47 @@ __global__ __launch_bounds__(256) void gemv_kernel(const uint4 *__restrict__ cod
         }
     };
 
-    // The first rows' weights are requested before the activations are staged,
-    // so the staging latency overlaps the first HBM reads.
-    // (Activation loads are issued first: they come from L2 and return before
-    // the weights, and vector loads retire in order.)
-    uint16_t *raw = reinterpret_cast<uint16_t *>(xs + K);
+    // The activations go to LDS by DMA with the first rows' weights requested
+    // right behind them; one barrier later every wave stages its own lanes'
+    // activations into registers (wave_scan / convert_group) -- no further
+    // workgroup-wide step.  A wave that cannot stage exactly takes the fp32
+    // path on its own.
+    uint16_t *raw = reinterpret_cast<uint16_t *>(xs);
     stage_issue(x, K, raw);
     int row0 = blockIdx.x * rows_per_iter;
     uint4 qa[R][NG];
     uint32_t sa[R][NG];
     if (row0 < N) load_rows(qa, sa, row0);
+    if (!stage_vector_path(x))
+        for (int i = threadIdx.x; i < K; i += blockDim.x) raw[i] = x[i];
+    wait_vmcnt<0>();
+    lds_barrier();
 
-    const Staging st = stage_complete(x, K, dt, xs, raw, red);
-
+    // fp16: the values are staged as they are (scale 0, never the fp32 path);
+    // bf16: scaled into fp16 after a per-wave exponent scan.
+    WaveScale ws{0, 0, 0};
+    if (dt != 0) ws = wave_scan(raw, K, dt);
     h2 xr[NG][16];
+    int lost = ws.bad;
     auto load_xr = [&]() __attribute__((always_inline)) {
-        const h2 *xs2 = reinterpret_cast<const h2 *>(xs);
 #pragma unroll
         for (int i = 0; i < NG; ++i) {
             const int g = l + i * L;
+            if (g < G) {
+                if (dt == 0)
+                    permute_group_f16(raw, g, xr[i]);
+                else
+                    lost |= convert_group(raw, g, dt, ws, xr[i]);
+            } else {
 #pragma unroll
-            for (int p = 0; p < 16; ++p) xr[i][p] = (g < G) ? xs2[g * 16 + p] : h2{0, 0};
+                for (int p = 0; p < 16; ++p) xr[i][p] = h2{0, 0};
+            }
         }
     };
+    if (!ws.bad) load_xr();
+    Staging st;
+    st.scale = ws.scale;
+    st.fallback = wave_or_i32(lost);
 
     auto compute_rows = [&](const uint4 (&q)[R][NG], const uint32_t (&sv)[R][NG], int r0,
                             auto exact_f32) __attribute__((always_inline)) {
@@ -128,14 +145,12 @@ __global__ __launch_bounds__(256) void gemv_kernel(const uint4 *__restrict__ cod
             compute_rows(qa, sa, row0, exact_f32);
         }
     };
-    // The staging outcome is the same for every wave: branch on it once, in a
+    // The staging outcome is uniform within the wave: branch on it once, in a
     // scalar register.
-    if (__builtin_amdgcn_readfirstlane(st.fallback)) {
+    if (__builtin_amdgcn_readfirstlane(st.fallback))
         row_loop(std::true_type{});
-    } else {
-        load_xr();
+    else
         row_loop(std::false_type{});
-    }
 }
 
 // ---- tiling table ------------------------------------------------------------
@@ -197,12 +212,13 @@ GemvTile gemv_tile(int N, int K) {
             if (NG > 4) cost += 0.02 * (NG - 4);  // register pressure
             if (cost < best_cost - 1e-9) {
                 best_cost = cost;
-                best = GemvTile{L, NG, 2, 4, 0};
+                best = GemvTile{L, NG, 1, 4, 0};
             }
         }
     }
     if (G == 0) best = GemvTile{64, 1, 1, 4, 0};
-    // Two rows per slot in flight and four-wave workgroups; at most four
+    // One row per slot in flight and four-wave workgroups (fewer registers,
+    // more waves per CU measured faster than two rows per slot); at most four
     // workgroups per CU (1024), each looping over rows with a grid stride.
     const long rows_per_iter = (long)(64 / best.L) * best.R * best.waves;
     const long blocks = (N + rows_per_iter - 1) / rows_per_iter;
@@ -223,7 +239,7 @@ hipError_t launch_gemv(const uint32_t *codes, const uint16_t *steps, int N, int 
     }
     GemvFn fn = pick(t.L, t.NG, t.R);
     if (!fn) return hipErrorInvalidConfiguration;
-    const size_t lds = (size_t)(K + stage_raw_halves(K) + 8) * sizeof(_Float16);
+    const size_t lds = (size_t)(stage_raw_halves(K) + 8) * sizeof(_Float16);
     hipLaunchKernelGGL(fn, dim3(t.blocks), dim3(64 * t.waves), lds, stream,
                        reinterpret_cast<const uint4 *>(codes), steps, N, K, x, dt, y);
     return hipGetLastError();

@@ -14,7 +14,12 @@ __global__ __launch_bounds__(256) void rms_renorm_kernel(const float *__restrict
     __shared__ double red[4];
     const float *v = v0 + (long)blockIdx.x * ldv;
     uint16_t *out = out0 + (long)blockIdx.x * ldo;
-    const double ss = sum_squares_256(K, [&](int k) { return v[k]; }, red);
+    const bool vec = (reinterpret_cast<uintptr_t>(v) & 15) == 0;
+    auto load4 = [&](int c) {
+        return vec ? reinterpret_cast<const float4 *>(v)[c]
+                   : make_float4(v[4 * c], v[4 * c + 1], v[4 * c + 2], v[4 * c + 3]);
+    };
+    const double ss = sum_squares_256(K, load4, red);
     for (int k = threadIdx.x; k < K; k += 256) out[k] = renorm_value(v[k], ss, K, out_dt);
 }
 

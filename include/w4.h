@@ -152,7 +152,8 @@ int w4_embed_gather(const uint32_t *codes, const uint16_t *steps, int32_t V, int
 
 /*
  * Renormalisation between chained products [P1-S4], for `rows` vectors at
- * once: for each row r, take the leading K entries u of the fp32 vector
+ * once (K a multiple of 4): for each row r, take the leading K entries u of
+ * the fp32 vector
  * v + r*ldv, r_rms = sqrt(mean(u^2)), and write (out + r*ldo)[k] = u[k] / r_rms
  * rounded to nearest-even in dtype out_dt (zeros if r_rms == 0).  The sum of
  * squares is taken in fp64.  One workgroup per row.
@@ -164,27 +165,29 @@ int w4_rms_renorm(const float *v, int64_t ldv, int32_t K, int32_t rows, void *ou
  * One decode-step chain as a single launch [P1-S4]: n_mats packed matrices
  * applied in sequence.  Matrix i (a w4_chain_mat record) has shape [N][K] at
  * codes/steps and writes fp32 y[0..N).  Its input is x0 (fp16, K of matrix 0
- * long) for i == 0, else the leading K entries of the previous matrix's y,
+ * long, 16-byte aligned) for i == 0, else the leading K entries of the previous matrix's y,
  * renormalised to RMS 1 and rounded to fp16 bit for bit as w4_rms_renorm
  * does on that output.  Each product meets the bound of w4_gemv; its row
  * mapping (and so the order of its fp32 sums) is chosen per matrix for the
  * whole-chip launch and can differ from w4_gemv's.
  *   desc: DEVICE array of n_mats records (it is read by the kernel).
  *   sync: device buffer of W4_CHAIN_SYNC_BYTES bytes, all zero before the
- *         first call; each call that runs to completion leaves words 0 and 1
- *         zero again.  Word 2 is an error word written by the kernel: 1 if a
- *         grid barrier timed out (results incomplete), 2 if a record was
- *         invalid (N < 1, K not a multiple of 32, K > W4_MAX_K_SMALLM, K larger
- *         than the previous N, a null or misaligned pointer; nothing computed).
- *         The caller clears it after reading it.
- * All workgroups of the launch are resident at once (cooperative launch);
- * concurrent chains must use different sync buffers.
+ *         first call and then owned by the chain (it carries barrier
+ *         generations from call to call; reuse it only for chains run one
+ *         after another on one stream).  Word 2 is an error word written by
+ *         the kernel: 1 if a grid barrier timed out (results incomplete), 2 if
+ *         a record was invalid (N < 1, K not a multiple of 32, K larger than
+ *         W4_MAX_K_SMALLM or than the previous N, a null or misaligned
+ *         pointer; nothing computed).  The caller clears it after reading it.
+ * One workgroup per CU, all resident at once on an otherwise idle device; if
+ * they cannot all run together the bounded barrier waits end with error 1
+ * rather than a hang.  Concurrent chains must use different sync buffers.
  */
-#define W4_CHAIN_SYNC_BYTES 4096
+#define W4_CHAIN_SYNC_BYTES 8192
 typedef struct {
     const uint32_t *codes; /* device, 16-byte aligned */
     const uint16_t *steps; /* device */
-    float *y;              /* device, N floats */
+    float *y;              /* device, N floats, 16-byte aligned */
     int32_t N;
     int32_t K;
 } w4_chain_mat;

@@ -34,7 +34,8 @@ W4_ERR_HIP = -6
 W4_F16 = 0
 W4_BF16 = 1
 W4_MAX_K = 16384
-W4_MAX_K_SMALLM = 8192
+W4_MAX_K_SMALLM = 16384
+W4_MAX_K_CHAIN = 8192
 W4_MAX_M = 16
 W4_MAX_TOPK = 32
 W4_CHAIN_SYNC_BYTES = 8192

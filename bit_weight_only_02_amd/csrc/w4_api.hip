@@ -151,8 +151,13 @@ int w4_gemm_smallM(const uint32_t *codes, const uint16_t *steps, int32_t N, int3
         }
         return launched(hipSuccess, "w4_gemm_smallM");
     }
+    void *ws = nullptr;
+    const size_t ws_bytes = w4::gemm_smallm_workspace(N, K, M);
+    if (ws_bytes && (st = staging_buffer(ws_bytes, static_cast<hipStream_t>(stream), &ws)))
+        return st;
     return launched(w4::launch_gemm_smallm(codes, steps, N, K, static_cast<const uint16_t *>(X), ldx,
-                                           xdt, M, Y, ldy, static_cast<hipStream_t>(stream)),
+                                           xdt, M, Y, ldy, static_cast<float *>(ws),
+                                           static_cast<hipStream_t>(stream)),
                     "w4_gemm_smallM");
 }
 
@@ -225,18 +230,15 @@ int w4_moe_gemv_ids(const uint32_t *codes_base, const uint16_t *steps_base,
     if (K == 0) return fail(W4_ERR_UNSUPPORTED, "K == 0");
     if ((st = device_ready())) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    float *rows = Y;
-    if (route_w) {
-        void *ws = nullptr;
-        if ((st = staging_buffer((size_t)T * topk * N * sizeof(float), s, &ws))) return st;
-        rows = static_cast<float *>(ws);
-    }
+    void *ws = nullptr;
+    const size_t ws_bytes = w4::moe_workspace(N, K, T, topk, route_w != nullptr);
+    if (ws_bytes && (st = staging_buffer(ws_bytes, s, &ws))) return st;
     if (forced_launch_error()) return fail(W4_ERR_HIP, "forced launch error (test hook)");
-    hipError_t e = w4::launch_moe(codes_base, steps_base, expert_stride_codes, expert_stride_steps,
-                                  N, K, static_cast<const uint16_t *>(X), ldx, xdt, x_per_pair, ids, T,
-                                  topk, slot_of, n_experts, n_slots, row_scale, rows, dev_err, s);
-    if (e != hipSuccess || !route_w) return launched(e, "w4_moe_gemv_ids");
-    return launched(w4::launch_moe_combine(rows, route_w, T, topk, N, Y, s), "w4_moe_gemv_ids");
+    return launched(w4::launch_moe(codes_base, steps_base, expert_stride_codes, expert_stride_steps,
+                                   N, K, static_cast<const uint16_t *>(X), ldx, xdt, x_per_pair, ids,
+                                   T, topk, slot_of, n_experts, n_slots, row_scale, route_w, Y,
+                                   static_cast<float *>(ws), dev_err, s),
+                    "w4_moe_gemv_ids");
 }
 
 int w4_gemv_chain(const w4_chain_mat *desc, int32_t n_mats, const uint16_t *x0, void *sync,

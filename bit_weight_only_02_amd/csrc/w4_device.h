@@ -102,13 +102,6 @@ __device__ __noinline__ float group_dot_f32(uint4 q, const uint16_t *xg, int dt)
     return s;
 }
 
-// Position (in halves) of column i inside the staged pair layout: group g,
-// word w = (i % 32) / 8, lane j = i % 8 -> pair (j % 4) of the word, half j / 4.
-__device__ __forceinline__ int staged_index(int i) {
-    const int g = i >> 5, w = (i >> 3) & 3, j = i & 7;
-    return ((((g << 2) + w) << 2) + (j & 3)) * 2 + (j >> 2);
-}
-
 __device__ __forceinline__ int wave_max_i32(int v) {
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) v = max(v, __shfl_xor(v, off, kWave));
@@ -285,13 +278,12 @@ struct Staging {
     int fallback;  // 1: the vector cannot be staged exactly; use the fp32 path
 };
 
-// Staging is split in two so that a kernel can put its first weight loads in
-// flight between the two halves.  stage_issue() requests all of x straight into
-// LDS (global_load_lds_dwordx4: no registers; each wave moves 64 chunks of 16
-// bytes per instruction); the kernel then issues its first weight loads; and
-// stage_complete() waits for every outstanding load before reading the staged
-// bytes.  (Waiting for a partial count would depend on the compiler keeping
-// the weight loads after the activation loads, which it does not promise.)
+// Staging of a raw activation vector: stage_issue() requests all of x straight
+// into LDS (global_load_lds_dwordx4: no registers; each wave moves 64 chunks of
+// 16 bytes per instruction); the kernel then issues its first weight loads and
+// waits for every outstanding load (wait_vmcnt<0>) before reading the staged
+// bytes.  (Waiting for a partial count would depend on the compiler keeping the
+// weight loads after the activation loads, which it does not promise.)
 // `raw` needs stage_raw_halves(K) halves.
 __device__ __forceinline__ bool stage_vector_path(const uint16_t *x) {
     return (reinterpret_cast<uintptr_t>(x) & 15) == 0;
@@ -333,66 +325,6 @@ template <int pending>
 __device__ __forceinline__ void wait_vmcnt() {
     static_assert(pending >= 0 && pending < 64, "vmcnt range");
     __builtin_amdgcn_s_waitcnt((pending & 15) | ((pending >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-__device__ __forceinline__ Staging stage_convert(int K, int dt, _Float16 *xs, const uint16_t *raw,
-                                                 int *red);
-
-// Stage activations x[0..K) into `xs` (K halves, pair layout) as x * 2^s,
-// after stage_issue().  `red` is 2*(blockDim/64) ints.  Every thread of the
-// workgroup must call this (it has barriers).
-__device__ __forceinline__ Staging stage_complete(const uint16_t *__restrict__ x, int K, int dt,
-                                                  _Float16 *xs, uint16_t *raw, int *red) {
-    const int tid = threadIdx.x, nt = blockDim.x;
-    const int wave = tid >> 6, nwaves = nt >> 6;
-    // 1. raw copy global -> LDS: issued by stage_issue() on the vector path
-    if (stage_vector_path(x)) {
-        wait_vmcnt<0>();
-    } else {
-        for (int i = tid; i < K; i += nt) raw[i] = x[i];
-    }
-    lds_barrier();
-    return stage_convert(K, dt, xs, raw, red);
-}
-
-// Convert raw activations (K halves of dtype dt, already in LDS) into the
-// staged pair layout: 2. largest exponent, 3. exact conversion.
-__device__ __forceinline__ Staging stage_convert(int K, int dt, _Float16 *xs, const uint16_t *raw,
-                                                 int *red) {
-    const int tid = threadIdx.x, nt = blockDim.x;
-    const int wave = tid >> 6, nwaves = nt >> 6;
-    // 2. largest exponent and non-finite values
-    int emax = -100000, bad = 0;
-    for (int i = tid; i < K; i += nt) {
-        const float v = act_to_f32(raw[i], dt);
-        if (!__builtin_isfinite(v)) bad = 1;
-        else if (v != 0.0f) emax = max(emax, f32_exponent(v));
-    }
-    emax = wave_max_i32(emax);
-    bad = wave_or_i32(bad);
-    if ((tid & 63) == 0) { red[wave] = emax; red[nwaves + wave] = bad; }
-    lds_barrier();
-    emax = red[0]; bad = red[nwaves];
-    for (int w = 1; w < nwaves; ++w) { emax = max(emax, red[w]); bad |= red[nwaves + w]; }
-    const int s = (emax == -100000) ? 0 : 14 - emax;
-    // 3. exact conversion to fp16 x 2^s in the pair layout
-    int lost = 0;
-    if (!bad) {
-        for (int i = tid; i < K; i += nt) {
-            const float v = act_to_f32(raw[i], dt);
-            if (v != 0.0f && f32_exponent(v) < emax - 28) lost = 1;
-            xs[staged_index(i)] = (_Float16)__builtin_ldexpf(v, s);
-        }
-    }
-    lost = wave_or_i32(lost);
-    lds_barrier();  // everyone has read red[] before it is rewritten
-    if ((tid & 63) == 0) red[wave] = lost;
-    lds_barrier();
-    for (int w = 0; w < nwaves; ++w) lost |= red[w];
-    Staging st;
-    st.scale = s;
-    st.fallback = bad | lost;
-    return st;
 }
 
 }  // namespace w4

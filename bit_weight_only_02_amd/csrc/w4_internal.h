@@ -20,17 +20,15 @@ GemvTile gemv_tile(int N, int K);
 hipError_t launch_gemv(const uint32_t *codes, const uint16_t *steps, int N, int K,
                        const uint16_t *x, int dt, float *y, hipStream_t stream);
 
-struct GemmTile {
-    int gpw;     // groups per wave (K-slice)
-    int waves;   // waves per workgroup
-    int blocks;  // workgroups
-};
-
-GemmTile gemm_tile(int N, int K);
+// Small-M products (w4_mfma.h engine).  A workspace is needed when the plan
+// splits K (and, for the expert product, when route weights are given);
+// *_workspace() returns its size in bytes (0: none).
+size_t gemm_smallm_workspace(int N, int K, int M);
+int smallm_grid_x(int N);
 
 hipError_t launch_gemm_smallm(const uint32_t *codes, const uint16_t *steps, int N, int K,
                               const uint16_t *X, long ldx, int dt, int M, float *Y, long ldy,
-                              hipStream_t stream);
+                              float *ws, hipStream_t stream);
 
 hipError_t launch_gather(const uint32_t *codes, const uint16_t *steps, int V, int K,
                          const int32_t *ids, int n, uint16_t *out, int32_t *dev_err,
@@ -39,15 +37,14 @@ hipError_t launch_gather(const uint32_t *codes, const uint16_t *steps, int V, in
 hipError_t launch_rms_renorm(const float *v, long ldv, int K, int rows, void *out, long ldo,
                              int out_dt, hipStream_t stream);
 
+size_t moe_workspace(int N, int K, int T, int topk, bool route);
+
 hipError_t launch_moe(const uint32_t *codes_base, const uint16_t *steps_base,
                       int64_t stride_codes, int64_t stride_steps, int N, int K,
                       const uint16_t *X, long ldx, int dt, int x_per_pair,
                       const int32_t *ids, int T, int topk, const int32_t *slot_of,
-                      int n_experts, int n_slots, const float *row_scale, float *rows_out,
-                      int32_t *dev_err, hipStream_t stream);
-
-hipError_t launch_moe_combine(const float *rows, const float *route_w, int T, int topk, int N,
-                              float *Y, hipStream_t stream);
+                      int n_experts, int n_slots, const float *row_scale, const float *route_w,
+                      float *Y, float *ws, int32_t *dev_err, hipStream_t stream);
 
 size_t chain_lds_bytes();
 hipError_t launch_chain(const void *desc, int n, const uint16_t *x0, void *sync, unsigned spin_limit,

@@ -9,15 +9,18 @@
 // (scales, biases) keeps the real expert id.
 //
 // Here: T tokens x topk choices = P pairs.  Each workgroup takes one DISTINCT
-// expert (deduplicated on the device, in order of first appearance) and a
-// range of 16-row tiles, reads that expert's packed weights once, and runs the
-// MFMA small-M engine with one A row per pair that chose the expert.  Results
-// go to one output row per pair, multiplied by row_scale[e] of the real id e.
-// The weight address is the only place where slot_of enters, so direct and
-// pool addressing execute identical arithmetic and agree bit for bit.
+// expert (deduplicated on the device, in order of first appearance), one
+// K-slice and a group of 16-row tiles, reads that part of the expert's packed
+// weights once, and runs the MFMA small-M engine with one A row per pair that
+// chose the expert.  The weight address is the only place where slot_of
+// enters, so direct and pool addressing execute identical arithmetic and agree
+// bit for bit.  Per-expert side inputs (row_scale) are read with the real id.
 //
-// The route-weighted sum over a token's choices runs as a second kernel over
-// the per-pair rows, in ascending choice order.
+// With one K-slice and no route weights the engine stores each pair's row,
+// times row_scale[e], straight into Y.  Otherwise it stores unscaled per-slice
+// rows into a workspace [S][P][N], and a finishing kernel adds the slices in
+// order, applies row_scale[e] and, with route weights, sums a token's choices
+// in ascending order.
 #include <cstdio>
 #include <cstdlib>
 
@@ -29,25 +32,22 @@ namespace w4 {
 
 constexpr int kMaxPairs = 1024;
 
-template <int GPW, bool STEPS8>
-__global__ __launch_bounds__(1024) void moe_kernel(const uint4 *__restrict__ codes_base,
-                                                   const uint16_t *__restrict__ steps_base,
-                                                   int64_t stride_c4, int64_t stride_s,
-                                                   int N, int K,
-                                                   const uint16_t *__restrict__ X, long ldx, int dt,
-                                                   int x_per_pair,
-                                                   const int32_t *__restrict__ ids, int P, int topk,
-                                                   const int32_t *__restrict__ slot_of,
-                                                   int n_experts, int n_slots,
-                                                   const float *__restrict__ row_scale,
-                                                   float *__restrict__ out,
-                                                   int32_t *__restrict__ dev_err) {
+template <int R, bool STEPS8>
+__global__ __launch_bounds__(64 * kSmallMWaves) void moe_kernel(
+    const uint4 *__restrict__ codes_base, const uint16_t *__restrict__ steps_base,
+    int64_t stride_c4, int64_t stride_s, int N, int K, const uint16_t *__restrict__ X, long ldx,
+    int dt, int x_per_pair, const int32_t *__restrict__ ids, int P, int topk,
+    const int32_t *__restrict__ slot_of, int n_experts, int n_slots,
+    const float *__restrict__ row_scale, float *__restrict__ out, int direct, int Gs,
+    int32_t *__restrict__ dev_err) {
     __shared__ SmallMShared sh;
     __shared__ int ids_s[kMaxPairs];
     __shared__ unsigned char first_s[kMaxPairs];
     __shared__ int pairs_s[kMaxPairs];
     __shared__ int info_s[3];  // expert id, number of pairs, found
-    const int u = blockIdx.y;
+    const int u = blockIdx.y, slice = blockIdx.z;
+    const int G = K >> 5;
+    const int g_lo = slice * Gs, g_hi = min(G, g_lo + Gs);
 
     // ---- this workgroup's distinct expert and the pairs that chose it
     for (int p = threadIdx.x; p < P; p += blockDim.x) ids_s[p] = ids[p];
@@ -79,6 +79,10 @@ __global__ __launch_bounds__(1024) void moe_kernel(const uint4 *__restrict__ cod
     if (!info_s[2]) return;  // fewer distinct experts than this grid row
     const int e = info_s[0], npairs = info_s[1];
     const int ntiles = (N + 15) >> 4;
+    // destination of pair p, column n: Y[p][n], or this slice's workspace row
+    auto dst = [&](int p, int n) __attribute__((always_inline)) -> float & {
+        return out[((long)(direct ? 0 : slice) * P + p) * N + n];
+    };
 
     // ---- addressing: the only use of slot_of
     long a = e;
@@ -89,10 +93,12 @@ __global__ __launch_bounds__(1024) void moe_kernel(const uint4 *__restrict__ cod
     }
     if (!valid) {
         // never leave an untouched row behind: NaN rows and the error flag
-        for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x)
-            for (int o = threadIdx.x; o < 16 * npairs; o += blockDim.x) {
-                const int n = tile * 16 + (o & 15);
-                if (n < N) out[(long)pairs_s[o >> 4] * N + n] = __builtin_nanf("");
+        // (the tiles this workgroup's waves own: kSmallMWaves consecutive ones)
+        constexpr int kCols = kSmallMWaves * 16;
+        for (int t0 = blockIdx.x * kSmallMWaves; t0 < ntiles; t0 += gridDim.x * kSmallMWaves)
+            for (int o = threadIdx.x; o < kCols * npairs; o += blockDim.x) {
+                const int n = t0 * 16 + o % kCols;
+                if (n < N) dst(pairs_s[o / kCols], n) = __builtin_nanf("");
             }
         if (threadIdx.x == 0 && blockIdx.x == 0 && dev_err) *dev_err = 1;
         return;
@@ -110,28 +116,47 @@ __global__ __launch_bounds__(1024) void moe_kernel(const uint4 *__restrict__ cod
         };
         auto store = [&](int m, int n, float v) __attribute__((always_inline)) {
             const int p = pairs_s[c0 + m];
-            if (row_scale) v *= row_scale[(long)e * N + n];
-            out[(long)p * N + n] = v;
+            if (direct && row_scale) v *= row_scale[(long)e * N + n];
+            dst(p, n) = v;
         };
-        smallm_engine<GPW, STEPS8>(codes, steps, N, K, xrow, xvec, dt, M, blockIdx.x, gridDim.x,
-                                   store, sh);
+        smallm_engine<R, STEPS8>(codes, steps, N, K, g_lo, g_hi, xrow, xvec, dt, M,
+                                 blockIdx.x * kSmallMWaves, gridDim.x * kSmallMWaves, store, sh);
         lds_barrier();  // the engine's shared memory is reused by the next pass
     }
 }
 
-// Y[t][n] = sum over j = 0..topk-1, ascending, of route_w[t][j] * rows[t*topk + j][n].
-__global__ __launch_bounds__(256) void moe_combine_kernel(const float *__restrict__ rows,
-                                                          const float *__restrict__ route_w,
-                                                          int T, int topk, int N,
-                                                          float *__restrict__ Y) {
-    const long total = (long)T * N;
+// Finish: v(p, n) = sum over slices s ascending of ws[s][p][n], times
+// row_scale[e_p][n] (real id e_p; rows of an invalid id are already NaN).
+// route_w: Y[t][n] = sum over j = 0..topk-1 ascending of route_w[t][j] * v(t*topk + j, n);
+// otherwise Y[p][n] = v(p, n).
+__global__ __launch_bounds__(256) void moe_finish_kernel(const float *__restrict__ ws, int S, int P,
+                                                         int N, const int32_t *__restrict__ ids,
+                                                         int n_experts,
+                                                         const float *__restrict__ row_scale,
+                                                         const float *__restrict__ route_w, int T,
+                                                         int topk, float *__restrict__ Y) {
+    const int rows = route_w ? T : P;
+    const long total = (long)rows * N;
+    const long plane = (long)P * N;
     for (long i = (long)blockIdx.x * blockDim.x + threadIdx.x; i < total;
          i += (long)gridDim.x * blockDim.x) {
-        const int t = (int)(i / N), n = (int)(i % N);
-        float s = 0.0f;
-        for (int j = 0; j < topk; ++j)
-            s = __builtin_fmaf(route_w[t * topk + j], rows[((long)t * topk + j) * N + n], s);
-        Y[i] = s;
+        const int r = (int)(i / N), n = (int)(i % N);
+        auto pair_value = [&](int p) __attribute__((always_inline)) {
+            const long o = (long)p * N + n;
+            float v = ws[o];
+            for (int s = 1; s < S; ++s) v += ws[(long)s * plane + o];
+            const int e = ids[p];
+            if (row_scale && e >= 0 && e < n_experts) v *= row_scale[(long)e * N + n];
+            return v;
+        };
+        if (route_w) {
+            float s = 0.0f;
+            for (int j = 0; j < topk; ++j)
+                s = __builtin_fmaf(route_w[r * topk + j], pair_value(r * topk + j), s);
+            Y[i] = s;
+        } else {
+            Y[i] = pair_value(r);
+        }
     }
 }
 
@@ -139,53 +164,52 @@ namespace {
 
 typedef void (*MoeFn)(const uint4 *, const uint16_t *, int64_t, int64_t, int, int, const uint16_t *,
                       long, int, int, const int32_t *, int, int, const int32_t *, int, int,
-                      const float *, float *, int32_t *);
+                      const float *, float *, int, int, int32_t *);
 
 template <bool S8>
-MoeFn pick_moe_s(int gpw) {
-    switch (gpw) {
+MoeFn pick_moe_s(int R) {
+    switch (R) {
         case 4: return moe_kernel<4, S8>;
         case 8: return moe_kernel<8, S8>;
-        case 12: return moe_kernel<12, S8>;
         case 16: return moe_kernel<16, S8>;
+        case 24: return moe_kernel<24, S8>;
     }
     return nullptr;
 }
 
 }  // namespace
 
+size_t moe_workspace(int N, int K, int T, int topk, bool route) {
+    const SmallMPlan p = smallm_plan(K);
+    if (p.S == 1 && !route) return 0;
+    return (size_t)p.S * T * topk * N * sizeof(float);
+}
+
 hipError_t launch_moe(const uint32_t *codes_base, const uint16_t *steps_base,
                       int64_t stride_codes, int64_t stride_steps, int N, int K,
                       const uint16_t *X, long ldx, int dt, int x_per_pair,
                       const int32_t *ids, int T, int topk, const int32_t *slot_of,
-                      int n_experts, int n_slots, const float *row_scale, float *rows_out,
-                      int32_t *dev_err, hipStream_t stream) {
-    const GemmTile t = gemm_tile(N, K);
+                      int n_experts, int n_slots, const float *row_scale, const float *route_w,
+                      float *Y, float *ws, int32_t *dev_err, hipStream_t stream) {
+    const SmallMPlan p = smallm_plan(K);
     const bool steps8 = (K / 32) % 4 == 0 && (reinterpret_cast<uintptr_t>(steps_base) & 7) == 0 &&
                         (stride_steps % 4) == 0;
-    MoeFn fn = steps8 ? pick_moe_s<true>(t.gpw) : pick_moe_s<false>(t.gpw);
-    if (!fn || t.waves > 16) return hipErrorInvalidConfiguration;
+    MoeFn fn = steps8 ? pick_moe_s<true>(p.R) : pick_moe_s<false>(p.R);
+    const int direct = (p.S == 1 && !route_w) ? 1 : 0;
+    if (!fn || (!direct && !ws)) return hipErrorInvalidConfiguration;
     const int P = T * topk;
-    const int ntiles = (N + 15) / 16;
-    // tiles of one expert spread over workgroups; about 1024 workgroups in all
-    int per_expert = 1024 / (P > 0 ? P : 1);
-    if (per_expert < 16) per_expert = 16;
-    const int bx = ntiles < per_expert ? ntiles : per_expert;
-    hipLaunchKernelGGL(fn, dim3(bx, P), dim3(64 * t.waves), 0, stream,
+    hipLaunchKernelGGL(fn, dim3(smallm_grid_x(N), P, p.S), dim3(64 * kSmallMWaves), 0, stream,
                        reinterpret_cast<const uint4 *>(codes_base), steps_base, stride_codes / 4,
                        stride_steps, N, K, X, ldx, dt, x_per_pair, ids, P, topk, slot_of,
-                       n_experts, n_slots, row_scale, rows_out, dev_err);
-    return hipGetLastError();
-}
-
-hipError_t launch_moe_combine(const float *rows, const float *route_w, int T, int topk, int N,
-                              float *Y, hipStream_t stream) {
-    const long total = (long)T * N;
+                       n_experts, n_slots, row_scale, direct ? Y : ws, direct, p.Gs, dev_err);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || direct) return e;
+    const long total = (long)(route_w ? T : P) * N;
     long blocks = (total + 255) / 256;
     if (blocks > 4096) blocks = 4096;
     if (blocks < 1) blocks = 1;
-    hipLaunchKernelGGL(moe_combine_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, rows,
-                       route_w, T, topk, N, Y);
+    hipLaunchKernelGGL(moe_finish_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, ws, p.S, P,
+                       N, ids, n_experts, row_scale, route_w, T, topk, Y);
     return hipGetLastError();
 }
 

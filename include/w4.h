@@ -78,7 +78,8 @@ typedef enum {
 typedef enum { W4_F16 = 0, W4_BF16 = 1 } w4_dtype;
 
 #define W4_MAX_K 16384       /* largest K of w4_gemv and w4_embed_gather */
-#define W4_MAX_K_SMALLM 8192 /* largest K of w4_gemm_smallM and w4_moe_gemv_ids */
+#define W4_MAX_K_SMALLM 16384 /* largest K of w4_gemm_smallM and w4_moe_gemv_ids */
+#define W4_MAX_K_CHAIN 8192   /* largest K of a w4_gemv_chain record */
 #define W4_MAX_M 16     /* largest M of w4_gemm_smallM */
 #define W4_MAX_TOPK 32  /* largest experts per token of w4_moe_gemv_ids */
 
@@ -97,6 +98,10 @@ int w4_gemv(const uint32_t *codes, const uint16_t *steps, int32_t N, int32_t K,
  *   Y[m*ldy + n] = sum_k w(n,k) * X[m*ldx + k]   for m < M, n < N.
  * Each weight is read from memory once for all M rows.  ldx >= K, ldy >= N,
  * K <= W4_MAX_K_SMALLM (larger K: W4_ERR_UNSUPPORTED).
+ * For K > 3072 the product is summed over K-slices in a fixed order, through a
+ * device buffer that the library allocates once per device and reuses (grown
+ * on demand while no graph capture is active; such calls on one device from
+ * different streams must not overlap).
  */
 int w4_gemm_smallM(const uint32_t *codes, const uint16_t *steps, int32_t N, int32_t K,
                    const void *X, int32_t xdt, int32_t M, int64_t ldx,
@@ -123,10 +128,11 @@ int w4_gemm_smallM(const uint32_t *codes, const uint16_t *steps, int32_t N, int3
  *   A choice used by several tokens reads its expert's weights once.
  *   dev_err: optional device int32; an id or slot out of range sets it to 1 and
  *      fills the affected output rows with NaN (never leaves them untouched).
- *   The combined form (route_w != NULL) stages per-choice rows in a device
- *   buffer the library allocates once per device and reuses (grown on demand
- *   while no graph capture is active; concurrent combined calls on one device
- *   from different streams are serialised by the caller).
+ *   The combined form (route_w != NULL), and any K > 3072 (summed over
+ *   K-slices in a fixed order), stage per-choice rows in a device buffer the
+ *   library allocates once per device and reuses (grown on demand while no
+ *   graph capture is active; such calls on one device from different streams
+ *   must not overlap).
  * Limits: T*topk <= 1024, topk <= W4_MAX_TOPK, K <= W4_MAX_K_SMALLM.
  */
 int w4_moe_gemv_ids(const uint32_t *codes_base, const uint16_t *steps_base,
@@ -177,7 +183,7 @@ int w4_rms_renorm(const float *v, int64_t ldv, int32_t K, int32_t rows, void *ou
  *         after another on one stream).  Word 2 is an error word written by
  *         the kernel: 1 if a grid barrier timed out (results incomplete), 2 if
  *         a record was invalid (N < 1, K not a multiple of 32, K larger than
- *         W4_MAX_K_SMALLM or than the previous N, a null or misaligned
+ *         W4_MAX_K_CHAIN or than the previous N, a null or misaligned
  *         pointer; nothing computed).  The caller clears it after reading it.
  * One workgroup per CU, all resident at once on an otherwise idle device; if
  * they cannot all run together the bounded barrier waits end with error 1

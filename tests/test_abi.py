@@ -97,7 +97,7 @@ def test_moe_argument_errors():
     assert call(sc=8) == -1                       # stride smaller than one expert
     assert call(slot=FAKE, ns=0) == -1
     assert call(xpp=2) == -1
-    assert call(K=16384, sc=1408 * 16384 // 8, ss=1408 * 16384 // 32, ldx=16384) == -4
+    assert call(K=16416, sc=1408 * 16416 // 8, ss=1408 * 16416 // 32, ldx=16416) == -4
     assert call(T=0) == 0
 
 

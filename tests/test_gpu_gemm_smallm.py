@@ -41,7 +41,8 @@ def oracle_rows(codes, steps, N, K, X, dt, M):
 @pytest.mark.parametrize("dt", [F16, BF16])
 @pytest.mark.parametrize("N,K,M", [(33, 64, 1), (97, 704, 2), (257, 1536, 4), (1000, 2048, 8),
                                    (129, 8192, 16), (1536, 2816, 3), (65, 96, 16),
-                                   (4097, 1536, 16), (17, 4096, 5), (31, 8192, 7)])
+                                   (4097, 1536, 16), (17, 4096, 5), (31, 8192, 7),
+                                   (300, 3104, 9), (65, 3072, 16), (31, 16384, 2)])
 def test_gemm_shapes_vs_oracle(w4, N, K, M, dt):
     print(f"gemm N={N} K={K} M={M} dt={dt}", flush=True)
     rng = np.random.default_rng(N + K + M + dt)
@@ -126,9 +127,10 @@ def test_gemm_integer_inputs_are_bit_exact(w4):
 
 
 def test_gemm_rejects_k_beyond_limit(w4):
-    codes = torch.zeros((4, 16384 // 8), dtype=torch.int32, device="cuda")
-    steps = torch.zeros((4, 16384 // 32), dtype=torch.bfloat16, device="cuda")
-    X = torch.zeros((2, 16384), dtype=torch.float16, device="cuda")
+    K = w4.W4_MAX_K_SMALLM + 32
+    codes = torch.zeros((4, K // 8), dtype=torch.int32, device="cuda")
+    steps = torch.zeros((4, K // 32), dtype=torch.bfloat16, device="cuda")
+    X = torch.zeros((2, K), dtype=torch.float16, device="cuda")
     with pytest.raises(w4.W4Error) as e:
         w4.w4_gemm_smallM(codes, steps, X)
     assert e.value.status == w4.W4_ERR_UNSUPPORTED

@@ -74,6 +74,64 @@ def test_moe_small_vs_oracle_and_pool_identity(w4, T, topk, xpp, dt):
         assert ok, worst
 
 
+@pytest.mark.parametrize("dt", [F16, BF16])
+def test_moe_long_rows_summed_over_k_slices(w4, dt):
+    """K = 3200 (100 groups) is split into two K-slices whose partial rows are
+    added in order by the finishing pass; also with a bad id (NaN rows)."""
+    print(f"moe k-slices dt={dt}", flush=True)
+    rng = np.random.default_rng(40 + dt)
+    E, N, K, S, T, topk = 12, 70, 3200, 12, 3, 4
+    codes, steps = experts(rng, E, N, K)
+    ids, route = synth.expert_choice(rng, T, E, topk)
+    slot_of, used = synth.slot_map(rng, ids, E, S)
+    pc, ps = pool_of(codes, steps, slot_of, used, S)
+    X = synth.activations(rng, (T, K), dt)
+    scale = rng.uniform(0.5, 1.5, size=(E, N)).astype(np.float32)
+    for rw in (None, route):
+        Yd = run(w4, codes, steps, N, K, X, dt, ids, 0, scale=scale, route=rw)
+        Yp = run(w4, pc, ps, N, K, X, dt, ids, 0, slot_of=slot_of, n_slots=S, scale=scale,
+                 route=rw, n_experts=E)
+        assert Yd.tobytes() == Yp.tobytes()
+        Yo, Ao = oracle.moe(codes, steps, N * K // 8, N * K // 32, N, K, X, dt, 0, ids, topk,
+                            n_experts=E, row_scale=scale, route_w=rw)
+        ok, worst = within_bound(Yd, Yo, Ao)
+        assert ok, worst
+    bad = ids.copy()
+    bad[1, 2] = E + 3
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    Y = run(w4, codes, steps, N, K, X, dt, bad, 0, scale=scale, err=err)
+    assert err.item() == 1
+    assert np.all(np.isnan(Y[1 * topk + 2]))
+    assert not np.any(np.isnan(np.delete(Y, 1 * topk + 2, axis=0)))
+
+
+def test_moe_side_input_follows_real_ids_under_pool_addressing(w4):
+    """Only the weight read goes through slot_of: a per-expert side input read
+    at the slot id instead of the real id would change the result."""
+    rng = np.random.default_rng(41)
+    E, N, K, S, T, topk = 16, 48, 256, 16, 2, 4
+    codes, steps = experts(rng, E, N, K)
+    ids, _ = synth.expert_choice(rng, T, E, topk)
+    slot_of, used = synth.slot_map(rng, ids, E, S)
+    pc, ps = pool_of(codes, steps, slot_of, used, S)
+    X = synth.activations(rng, (T, K), BF16)
+    scale = rng.uniform(0.5, 1.5, size=(E, N)).astype(np.float32)
+    Yp = run(w4, pc, ps, N, K, X, BF16, ids, 0, slot_of=slot_of, n_slots=S, scale=scale,
+             n_experts=E)
+    sc, ss = N * K // 8, N * K // 32
+    Yo, Ao = oracle.moe(codes, steps, sc, ss, N, K, X, BF16, 0, ids, topk, n_experts=E,
+                        row_scale=scale)
+    assert within_bound(Yp, Yo, Ao)[0]
+    # the wrong reading: side input indexed by slot id
+    wrong = np.zeros_like(scale)
+    for e in used:
+        wrong[e] = scale[slot_of[e]]
+    assert np.any(slot_of[used] != used)
+    Yw, Aw = oracle.moe(codes, steps, sc, ss, N, K, X, BF16, 0, ids, topk, n_experts=E,
+                        row_scale=wrong)
+    assert not within_bound(Yp, Yw, Aw)[0]
+
+
 def test_moe_bad_id_and_missing_slot_give_nan_and_flag(w4):
     rng = np.random.default_rng(5)
     E, N, K = 8, 20, 64

@@ -7,10 +7,10 @@
 // plain multiply-and-sum.  Here the M activation rows make the product a real
 // (if thin) contraction, so it runs on MFMA (engine in w4_mfma.h).
 //
-// Grid: x = groups of kSmallMWaves 16-row tiles (one tile per wave), y = the
-// K-slice.  With one slice the engine stores Y directly; with several, each
-// slice writes its partial sums to a workspace [S][M][N] and a second kernel
-// adds them in slice order.
+// Grid: x = steps of kSmallMWaves/KW 16-row tiles, y = the K-slice.  With one
+// slice the engine stores Y directly; with several, each slice writes its
+// partial sums to a workspace [S][M][N] and a second kernel adds them in slice
+// order.
 #include <cstdio>
 #include <cstdlib>
 
@@ -26,8 +26,9 @@ template <int R, bool STEPS8>
 __global__ __launch_bounds__(64 * kSmallMWaves) void gemm_smallm_kernel(
     const uint4 *__restrict__ codes, const uint16_t *__restrict__ steps, int N, int K,
     const uint16_t *__restrict__ X, long ldx, int dt, int M, float *__restrict__ Y, long ldy,
-    float *__restrict__ ws, int Gs) {
+    float *__restrict__ ws, int Gs, int mp_log2, int KW) {
     __shared__ SmallMShared sh;
+    extern __shared__ uint4 smallm_a[];
     const int G = K >> 5;
     const int slice = blockIdx.y;
     const int g_lo = slice * Gs, g_hi = min(G, g_lo + Gs);
@@ -36,12 +37,12 @@ __global__ __launch_bounds__(64 * kSmallMWaves) void gemm_smallm_kernel(
     smallm_engine<R, STEPS8>(
         codes, steps, N, K, g_lo, g_hi,
         [&](int m) __attribute__((always_inline)) { return X + (long)m * ldx; }, xvec, dt, M,
-        blockIdx.x * kSmallMWaves, gridDim.x * kSmallMWaves,
+        mp_log2, KW, blockIdx.x, gridDim.x,
         [&](int m, int n, float v) __attribute__((always_inline)) {
             if (direct) Y[(long)m * ldy + n] = v;
             else ws[((long)slice * M + m) * N + n] = v;
         },
-        sh);
+        sh, smallm_a);
 }
 
 // Y[m][n] = sum over slices s = 0, 1, ... of ws[s][m][n], in that order.
@@ -61,7 +62,7 @@ __global__ __launch_bounds__(256) void smallm_slices_kernel(const float *__restr
 namespace {
 
 typedef void (*GemmFn)(const uint4 *, const uint16_t *, int, int, const uint16_t *, long, int, int,
-                       float *, long, float *, int);
+                       float *, long, float *, int, int, int);
 
 template <bool S8>
 GemmFn pick_gemm_s(int R) {
@@ -77,13 +78,13 @@ GemmFn pick_gemm_s(int R) {
 }  // namespace
 
 size_t gemm_smallm_workspace(int N, int K, int M) {
-    const SmallMPlan p = smallm_plan(K);
+    const SmallMPlan p = smallm_plan(N, K, M, 1);
     return p.S > 1 ? (size_t)p.S * M * N * sizeof(float) : 0;
 }
 
-int smallm_grid_x(int N) {
-    const int ntiles = (N + 15) / 16;
-    int bx = (ntiles + kSmallMWaves - 1) / kSmallMWaves;
+int smallm_grid_x(int N, int KW) {
+    const int ntiles = (N + 15) / 16, tpw = kSmallMWaves / KW;
+    int bx = (ntiles + tpw - 1) / tpw;
     if (bx > 2048) bx = 2048;
     return bx < 1 ? 1 : bx;
 }
@@ -91,13 +92,13 @@ int smallm_grid_x(int N) {
 hipError_t launch_gemm_smallm(const uint32_t *codes, const uint16_t *steps, int N, int K,
                               const uint16_t *X, long ldx, int dt, int M, float *Y, long ldy,
                               float *ws, hipStream_t stream) {
-    const SmallMPlan p = smallm_plan(K);
+    const SmallMPlan p = smallm_plan(N, K, M, 1);
     const bool steps8 = (K / 32) % 4 == 0 && (reinterpret_cast<uintptr_t>(steps) & 7) == 0;
     GemmFn fn = steps8 ? pick_gemm_s<true>(p.R) : pick_gemm_s<false>(p.R);
     if (!fn || (p.S > 1 && !ws)) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(fn, dim3(smallm_grid_x(N), p.S), dim3(64 * kSmallMWaves), 0, stream,
-                       reinterpret_cast<const uint4 *>(codes), steps, N, K, X, ldx, dt, M, Y, ldy,
-                       ws, p.Gs);
+    hipLaunchKernelGGL(fn, dim3(smallm_grid_x(N, p.KW), p.S), dim3(64 * kSmallMWaves), p.lds_a,
+                       stream, reinterpret_cast<const uint4 *>(codes), steps, N, K, X, ldx, dt, M, Y,
+                       ldy, ws, p.Gs, p.mp_log2, p.KW);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.S == 1) return e;
     const long total = (long)M * N;

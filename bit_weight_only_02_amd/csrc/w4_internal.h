@@ -24,7 +24,7 @@ hipError_t launch_gemv(const uint32_t *codes, const uint16_t *steps, int N, int 
 // splits K (and, for the expert product, when route weights are given);
 // *_workspace() returns its size in bytes (0: none).
 size_t gemm_smallm_workspace(int N, int K, int M);
-int smallm_grid_x(int N);
+int smallm_grid_x(int N, int KW);
 
 hipError_t launch_gemm_smallm(const uint32_t *codes, const uint16_t *steps, int N, int K,
                               const uint16_t *X, long ldx, int dt, int M, float *Y, long ldy,

@@ -38,9 +38,10 @@ __global__ __launch_bounds__(64 * kSmallMWaves) void moe_kernel(
     int64_t stride_c4, int64_t stride_s, int N, int K, const uint16_t *__restrict__ X, long ldx,
     int dt, int x_per_pair, const int32_t *__restrict__ ids, int P, int topk,
     const int32_t *__restrict__ slot_of, int n_experts, int n_slots,
-    const float *__restrict__ row_scale, float *__restrict__ out, int direct, int Gs,
+    const float *__restrict__ row_scale, float *__restrict__ out, int direct, int Gs, int KW,
     int32_t *__restrict__ dev_err) {
     __shared__ SmallMShared sh;
+    extern __shared__ uint4 smallm_a[];
     __shared__ int ids_s[kMaxPairs];
     __shared__ unsigned char first_s[kMaxPairs];
     __shared__ int pairs_s[kMaxPairs];
@@ -93,12 +94,12 @@ __global__ __launch_bounds__(64 * kSmallMWaves) void moe_kernel(
     }
     if (!valid) {
         // never leave an untouched row behind: NaN rows and the error flag
-        // (the tiles this workgroup's waves own: kSmallMWaves consecutive ones)
-        constexpr int kCols = kSmallMWaves * 16;
-        for (int t0 = blockIdx.x * kSmallMWaves; t0 < ntiles; t0 += gridDim.x * kSmallMWaves)
-            for (int o = threadIdx.x; o < kCols * npairs; o += blockDim.x) {
-                const int n = t0 * 16 + o % kCols;
-                if (n < N) dst(pairs_s[o / kCols], n) = __builtin_nanf("");
+        // (the tiles this workgroup owns: kSmallMWaves/KW consecutive ones per step)
+        const int tpw = kSmallMWaves / KW, cols = tpw * 16;
+        for (int t0 = blockIdx.x * tpw; t0 < ntiles; t0 += gridDim.x * tpw)
+            for (int o = threadIdx.x; o < cols * npairs; o += blockDim.x) {
+                const int n = t0 * 16 + o % cols;
+                if (n < N) dst(pairs_s[o / cols], n) = __builtin_nanf("");
             }
         if (threadIdx.x == 0 && blockIdx.x == 0 && dev_err) *dev_err = 1;
         return;
@@ -110,6 +111,8 @@ __global__ __launch_bounds__(64 * kSmallMWaves) void moe_kernel(
     // up to 16 pairs per engine pass (one A row each)
     for (int c0 = 0; c0 < npairs; c0 += 16) {
         const int M = min(16, npairs - c0);
+        int mp_log2 = 0;
+        while ((1 << mp_log2) < M) ++mp_log2;
         auto xrow = [&](int m) __attribute__((always_inline)) {
             const int p = pairs_s[c0 + m];
             return X + (long)(x_per_pair ? p : p / topk) * ldx;
@@ -119,8 +122,8 @@ __global__ __launch_bounds__(64 * kSmallMWaves) void moe_kernel(
             if (direct && row_scale) v *= row_scale[(long)e * N + n];
             dst(p, n) = v;
         };
-        smallm_engine<R, STEPS8>(codes, steps, N, K, g_lo, g_hi, xrow, xvec, dt, M,
-                                 blockIdx.x * kSmallMWaves, gridDim.x * kSmallMWaves, store, sh);
+        smallm_engine<R, STEPS8>(codes, steps, N, K, g_lo, g_hi, xrow, xvec, dt, M, mp_log2, KW,
+                                 blockIdx.x, gridDim.x, store, sh, smallm_a);
         lds_barrier();  // the engine's shared memory is reused by the next pass
     }
 }
@@ -164,7 +167,7 @@ namespace {
 
 typedef void (*MoeFn)(const uint4 *, const uint16_t *, int64_t, int64_t, int, int, const uint16_t *,
                       long, int, int, const int32_t *, int, int, const int32_t *, int, int,
-                      const float *, float *, int, int, int32_t *);
+                      const float *, float *, int, int, int, int32_t *);
 
 template <bool S8>
 MoeFn pick_moe_s(int R) {
@@ -179,8 +182,15 @@ MoeFn pick_moe_s(int R) {
 
 }  // namespace
 
+// Plan of an expert launch: rows per engine pass are at most min(16, P) (the
+// pairs that chose one expert), and up to P experts run side by side.
+static SmallMPlan moe_plan(int N, int K, int T, int topk) {
+    const int P = T * topk;
+    return smallm_plan(N, K, P < 16 ? P : 16, P);
+}
+
 size_t moe_workspace(int N, int K, int T, int topk, bool route) {
-    const SmallMPlan p = smallm_plan(K);
+    const SmallMPlan p = moe_plan(N, K, T, topk);
     if (p.S == 1 && !route) return 0;
     return (size_t)p.S * T * topk * N * sizeof(float);
 }
@@ -191,17 +201,18 @@ hipError_t launch_moe(const uint32_t *codes_base, const uint16_t *steps_base,
                       const int32_t *ids, int T, int topk, const int32_t *slot_of,
                       int n_experts, int n_slots, const float *row_scale, const float *route_w,
                       float *Y, float *ws, int32_t *dev_err, hipStream_t stream) {
-    const SmallMPlan p = smallm_plan(K);
+    const SmallMPlan p = moe_plan(N, K, T, topk);
     const bool steps8 = (K / 32) % 4 == 0 && (reinterpret_cast<uintptr_t>(steps_base) & 7) == 0 &&
                         (stride_steps % 4) == 0;
     MoeFn fn = steps8 ? pick_moe_s<true>(p.R) : pick_moe_s<false>(p.R);
     const int direct = (p.S == 1 && !route_w) ? 1 : 0;
     if (!fn || (!direct && !ws)) return hipErrorInvalidConfiguration;
     const int P = T * topk;
-    hipLaunchKernelGGL(fn, dim3(smallm_grid_x(N), P, p.S), dim3(64 * kSmallMWaves), 0, stream,
-                       reinterpret_cast<const uint4 *>(codes_base), steps_base, stride_codes / 4,
-                       stride_steps, N, K, X, ldx, dt, x_per_pair, ids, P, topk, slot_of,
-                       n_experts, n_slots, row_scale, direct ? Y : ws, direct, p.Gs, dev_err);
+    hipLaunchKernelGGL(fn, dim3(smallm_grid_x(N, p.KW), P, p.S), dim3(64 * kSmallMWaves), p.lds_a,
+                       stream, reinterpret_cast<const uint4 *>(codes_base), steps_base,
+                       stride_codes / 4, stride_steps, N, K, X, ldx, dt, x_per_pair, ids, P, topk,
+                       slot_of, n_experts, n_slots, row_scale, direct ? Y : ws, direct, p.Gs, p.KW,
+                       dev_err);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || direct) return e;
     const long total = (long)(route_w ? T : P) * N;

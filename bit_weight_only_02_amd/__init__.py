@@ -38,7 +38,7 @@ W4_MAX_K_SMALLM = 16384
 W4_MAX_K_CHAIN = 8192
 W4_MAX_M = 16
 W4_MAX_TOPK = 32
-W4_CHAIN_SYNC_BYTES = 8192
+W4_CHAIN_SYNC_BYTES = 131328
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with bit_weight_only_02_amd/build.py "

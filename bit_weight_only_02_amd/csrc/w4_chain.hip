@@ -9,21 +9,24 @@
 // matrix i, and a grid-wide barrier separates matrix i from matrix i+1 (whose
 // input is the renormalised output of matrix i and so needs all of it).
 //
-// Per step:
+// Per step i (one workgroup of eight waves per CU; workgroup b owns the
+// contiguous row block [b*ceil(N/nwg), ...) of every matrix):
 //   1. input: x0 for the first matrix, else the leading K entries of the
 //      previous output divided by their RMS and rounded to fp16 (the same
 //      arithmetic as w4_rms_renorm, bit for bit), read with agent-coherent
-//      16-byte loads all issued at once; fp16 operands are exact as they are,
-//      so each wave only permutes them into the pair layout of the GEMV;
-//   2. the rows of this workgroup (a row mapping chosen from the shape), the
-//      results written with agent-scope stores;
-//   3. the barrier: every wave waits for its stores, the workgroup stores its
-//      generation into its own flag and wave 0 polls all flags (agent scope,
-//      bounded; no contended read-modify-write), while waves 1..3 pull this
-//      workgroup's share of the NEXT matrix into L2 with LDS-DMA loads into a
-//      scratch LDS area, so that the next step reads its weights from L2.
+//      16-byte loads all issued at once;
+//   2. waves 0..3 compute the block's rows of matrix i from an LDS weight
+//      buffer (codes and steps staged there in advance) and store them with
+//      agent-scope stores, while waves 4..7 stage the block of matrix i+1 into
+//      the other buffer with direct-to-LDS loads, so the weight stream of the
+//      next step overlaps this step's compute, the barrier and the next
+//      renormalisation;
+//   3. the barrier: each workgroup stores its generation into its own flag
+//      and wave 0 polls all flags (agent scope, bounded; no contended
+//      read-modify-write).
 // Outputs of every step are read back with agent-scope loads, which see the
-// stores of workgroups on other XCDs.  One workgroup of eight waves per CU.
+// stores of workgroups on other XCDs.  Rows beyond what one buffer holds are
+// read from memory directly.
 #include <cstdio>
 #include <cstdlib>
 #include <type_traits>
@@ -43,14 +46,20 @@ struct ChainMat {
 };
 static_assert(sizeof(ChainMat) == sizeof(w4_chain_mat), "descriptor layout");
 
-constexpr int kChainThreads = 512;  // eight waves; the renorm uses the first four
+constexpr int kChainThreads = 512;  // eight waves
+constexpr int kComputeWaves = 7;    // waves 0..6 compute rows (0..3 also renormalise); 7 copies weights
 constexpr int kChainMaxK = 8192;
-constexpr int kPrefetchBytes = 32768;  // LDS scratch for the L2 prefetch
+constexpr int kWeightBuf = 64 * 1024;  // bytes of each of the two LDS weight buffers
+constexpr int kCopyEarly = 16;         // copy instructions per wave issued before the rows
 // sync buffer: word 0 exit counter, word 1 epoch (barrier generations used by
 // earlier calls), word 2 error; from word 64 on, one arrival flag per
-// workgroup (the generation it last reached).
+// workgroup (the generation it last reached), kFlagStride words apart.
+// Each flag has a 256-byte line of its own: the pollers' reads then spread over
+// many memory channels instead of queueing on the one or two that would hold
+// a packed array (measured: 3.0 against 3.8 us per barrier at 256 workgroups).
 constexpr int kSyncExit = 0, kSyncEpoch = 1, kSyncError = 2, kSyncFlags = 64;
-constexpr int kMaxChainWG = (W4_CHAIN_SYNC_BYTES / 4) - kSyncFlags;
+constexpr int kFlagStride = 64;  // words
+constexpr int kMaxChainWG = (W4_CHAIN_SYNC_BYTES / 4 - kSyncFlags) / kFlagStride;
 
 __device__ __forceinline__ float load_agent(const float *p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -58,177 +67,232 @@ __device__ __forceinline__ float load_agent(const float *p) {
 __device__ __forceinline__ void store_agent(float *p, float v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// Pointers read from the descriptors are generic; the weights are in global
+// memory, and saying so keeps their loads off the flat path.
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_global_u4(const uint4 *p, long i) {
+    const u32x4 v = ((const __attribute__((address_space(1))) u32x4 *)p)[i];
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint32_t load_global_u16(const uint16_t *p, long i) {
+    return ((const __attribute__((address_space(1))) uint16_t *)p)[i];
+}
+
+// One output, stored so that loads with agent scope on any XCD see it.
+__device__ __forceinline__ void store_y(float *y, int n, int row, float v) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), buffer_rsrc(y, n * 4), row * 4, 0, 16);
+}
 __device__ __forceinline__ unsigned load_agent_u(unsigned *p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Row mapping of one step: lanes per row L and groups per lane NG.
-struct ChainVariant {
-    int L, NG;
+// Rows of one step that this workgroup computes: a contiguous block
+// [rb, re); the first nlds of them are staged in an LDS weight buffer (codes,
+// then -- when lds_steps -- their steps), the rest are read from memory.
+struct RowBlock {
+    int rb, re, nlds;
+    int steps_chunk;  // uint4 index of the staged steps inside the buffer
+    bool lds_steps;
 };
 
-__device__ __forceinline__ int chain_variant(int N, int G, int nwg) {
-    // Few lane-tasks (one 16-byte group each): spread them, 64 lanes per row.
-    // Many: 16 or 32 lanes per row with several groups per lane.
-    const long tasks = (long)N * G, lanes = (long)nwg * kChainThreads;
-    if (tasks <= 2 * lanes) return G <= 64 ? 0 : (G <= 128 ? 1 : 2);
-    if (G <= 48) return 3;
-    if (G <= 64) return 4;
-    if (G <= 128) return 5;
-    return 2;
+__device__ __forceinline__ RowBlock chain_block(const ChainMat &m, int nwg) {
+    const int G = m.K >> 5;
+    const int rpw = (m.N + nwg - 1) / nwg;
+    RowBlock b;
+    b.rb = min(m.N, (int)blockIdx.x * rpw);
+    b.re = min(m.N, b.rb + rpw);
+    // steps travel as 4-byte words: the block's steps must start on one
+    b.lds_steps = (G % 2) == 0 && (reinterpret_cast<uintptr_t>(m.steps) & 3) == 0;
+    auto bytes = [&](int rows) {
+        const int chunks = (rows * G + 63) / 64 * 64;
+        const int words = b.lds_steps ? (rows * G / 2 + 63) / 64 * 64 : 0;
+        return chunks * 16 + words * 4;
+    };
+    int n = min(b.re - b.rb, kWeightBuf / (G * 18));
+    while (n > 0 && bytes(n) > kWeightBuf) --n;
+    b.nlds = n;
+    b.steps_chunk = (n * G + 63) / 64 * 64;
+    return b;
 }
 
-__device__ __forceinline__ ChainVariant variant_shape(int v) {
-    switch (v) {
-        case 0: return {64, 1};
-        case 1: return {64, 2};
-        case 2: return {64, 4};
-        case 3: return {16, 3};
-        case 4: return {16, 4};
-        default: return {32, 4};
+// Copy waves: request the staged part of a block into `buf` (direct-to-LDS
+// loads; every lane moves 16 bytes of codes or 4 bytes of steps, and the last
+// instruction of each run lands its surplus lanes in the rounding padding).
+// Instructions [first, last) of the run are issued (codes first, then steps),
+// so that the copy can be split around a barrier.
+__device__ __forceinline__ void chain_copy(const ChainMat &m, const RowBlock &b, uint4 *buf,
+                                           int first, int last) {
+    const int w = (threadIdx.x >> 6) - kComputeWaves, lane = threadIdx.x & 63;
+    constexpr int nw = kChainThreads / 64 - kComputeWaves;
+    const int G = m.K >> 5;
+    const int n = b.nlds * G;
+    if (n == 0) return;
+    int k = 0;  // this wave's instruction count over the whole run
+    const uint4 *src = reinterpret_cast<const uint4 *>(m.codes) + (long)b.rb * G;
+    for (int c0 = w * 64; c0 < n; c0 += nw * 64, ++k) {
+        if (k < first) continue;
+        if (k >= last) return;
+        const int c = min(c0 + lane, n - 1);
+        __builtin_amdgcn_global_load_lds(
+            (const __attribute__((address_space(1))) void *)(src + c),
+            (__attribute__((address_space(3))) void *)(buf + c0), 16, 0, 0);
+    }
+    if (b.lds_steps) {
+        const uint32_t *ssrc = reinterpret_cast<const uint32_t *>(m.steps + (long)b.rb * G);
+        uint32_t *sdst = reinterpret_cast<uint32_t *>(buf + b.steps_chunk);
+        const int nd = n / 2;
+        for (int d0 = w * 64; d0 < nd; d0 += nw * 64, ++k) {
+            if (k < first) continue;
+            if (k >= last) return;
+            const int d = min(d0 + lane, nd - 1);
+            __builtin_amdgcn_global_load_lds(
+                (const __attribute__((address_space(1))) void *)(ssrc + d),
+                (__attribute__((address_space(3))) void *)(sdst + d0), 4, 0, 0);
+        }
     }
 }
 
+// Sum over each group of L consecutive lanes (L = 16, 32 or 64), left in the
+// group's last lane: shifted adds within 16-lane rows, then row broadcasts.
+template <int L>
+__device__ __forceinline__ float lane_group_sum(float v) {
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x111, 0xF, 0xF, true));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x112, 0xF, 0xF, true));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x114, 0xF, 0xF, true));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x118, 0xF, 0xF, true));
+    if (L >= 32)  // row_bcast:15 into rows 1 and 3
+        v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x142, 0xA, 0xF, false));
+    if (L == 64)  // row_bcast:31 into rows 2 and 3
+        v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x143, 0xC, 0xF, false));
+    return v;
+}
+
+// Compute waves: the rows of the block, L lanes per row, NG groups per lane;
+// codes and steps from the LDS buffer for staged rows, else from memory.
 template <int L, int NG>
-__device__ __forceinline__ void chain_rows(const uint4 *__restrict__ codes,
-                                           const uint16_t *__restrict__ steps, int N, int K,
-                                           const uint16_t *raw, float *y) {
+__device__ __forceinline__ void chain_rows(const ChainMat &m, const RowBlock &b, const uint4 *buf,
+                                           const uint16_t *raw) {
     constexpr int SLOTS = kWave / L;
-    const int G = K >> 5;
+    const int G = m.K >> 5;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int l = lane % L, slot = lane / L;
-    const int rows_per_iter = (kChainThreads / 64) * SLOTS;
-    int gc[NG];
-#pragma unroll
-    for (int i = 0; i < NG; ++i) gc[i] = min(l + i * L, G - 1);
-    // this wave's activations (fp16, staged as they are), LDS -> registers
+    const uint4 *codes = reinterpret_cast<const uint4 *>(m.codes);
+    const uint16_t *lsteps = reinterpret_cast<const uint16_t *>(buf + b.steps_chunk);
+    // this wave's activations, already in pair order in LDS -> registers
     h2 xr[NG][16];
+    const uint4 *r16 = reinterpret_cast<const uint4 *>(raw);
 #pragma unroll
     for (int i = 0; i < NG; ++i) {
         const int g = l + i * L;
-        if (g < G) {
-            permute_group_f16(raw, g, xr[i]);
-        } else {
 #pragma unroll
-            for (int p = 0; p < 16; ++p) xr[i][p] = h2{0, 0};
+        for (int w = 0; w < 4; ++w) {
+            const uint4 v = g < G ? r16[g * 4 + w] : make_uint4(0, 0, 0, 0);
+            xr[i][w * 4 + 0] = as_h2(v.x);
+            xr[i][w * 4 + 1] = as_h2(v.y);
+            xr[i][w * 4 + 2] = as_h2(v.z);
+            xr[i][w * 4 + 3] = as_h2(v.w);
         }
     }
-    for (int row0 = blockIdx.x * rows_per_iter; row0 < N; row0 += gridDim.x * rows_per_iter) {
-        const int row = row0 + wave * SLOTS + slot;
-        const int rc = min(row, N - 1);
-        uint4 q[NG];
-        uint32_t sv[NG];
-#pragma unroll
-        for (int i = 0; i < NG; ++i) {
-            q[i] = codes[(size_t)rc * G + gc[i]];
-            sv[i] = steps[(size_t)rc * G + gc[i]];
-        }
+    // Rows [rb, rb + nlds) from the buffer, the rest from memory (two loops,
+    // so that every load has a known address space).
+    auto finish = [&](int row, const uint4 (&q)[NG], const uint32_t (&sv)[NG]) __attribute__((always_inline)) {
         float acc = 0.0f;
 #pragma unroll
         for (int i = 0; i < NG; ++i) {
             const int g = l + i * L;
             acc = (g < G) ? __builtin_fmaf(group_dot(q[i], xr[i]), bf16_to_f32(sv[i]), acc) : acc;
         }
-#pragma unroll
-        for (int off = L / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, kWave);
-        if (l == 0 && row < N) store_agent(y + row, acc);
-    }
-}
-
-// Pull this workgroup's rows of the next matrix (codes, then steps) into L2
-// (waves 1.. only; the data land in a scratch LDS area that nobody reads).
-__device__ __forceinline__ void chain_prefetch(const ChainMat &m, int nwg, uint4 *scratch) {
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int nw = kChainThreads / 64 - 1;  // prefetching waves
-    if (wave == 0) return;
-    const int G = m.K >> 5;
-    const ChainVariant vs = variant_shape(chain_variant(m.N, G, nwg));
-    const int rows_per_iter = (kChainThreads / 64) * (kWave / vs.L);
-    int budget = kPrefetchBytes / 16;  // 16-byte chunks this workgroup may pull
-    int dst = 0;
-    auto pull = [&](const uint4 *base, long first, int chunks) __attribute__((always_inline)) {
-        for (int c0 = (wave - 1) * 64; c0 < chunks; c0 += nw * 64) {
-            const int c = min(c0 + lane, chunks - 1);
-            const int d = (dst + c0) % (kPrefetchBytes / 16 - 63);
-            __builtin_amdgcn_global_load_lds(
-                (const __attribute__((address_space(1))) void *)(base + first + c),
-                (__attribute__((address_space(3))) void *)(scratch + d), 16, 0, 0);
-        }
-        dst += chunks;
+        acc = lane_group_sum<L>(acc);
+        if (l == L - 1 && row < b.re) store_y(m.y, m.N, row, acc);
     };
-    for (int row0 = blockIdx.x * rows_per_iter; row0 < m.N && budget > 0; row0 += nwg * rows_per_iter) {
-        const int nrows = min(rows_per_iter, m.N - row0);
-        const int chunks = min(nrows * G, budget);
-        pull(reinterpret_cast<const uint4 *>(m.codes), (long)row0 * G, chunks);
-        budget -= chunks;
-        // the steps of these rows: the 16-byte chunks lying wholly inside
-        // their nrows*G bf16 values (never past the end of the step array)
-        const long s_first = ((long)row0 * G * 2 + 15) / 16;
-        const long s_end = ((long)(row0 + nrows) * G * 2) / 16;
-        const int s_chunks = (int)min((long)budget, s_end - s_first);
-        if (s_chunks > 0 && (reinterpret_cast<uintptr_t>(m.steps) & 15) == 0) {
-            pull(reinterpret_cast<const uint4 *>(m.steps), s_first, s_chunks);
-            budget -= s_chunks;
+    const int staged_end = b.rb + b.nlds;
+    for (int r0 = b.rb; r0 < staged_end; r0 += kComputeWaves * SLOTS) {
+        const int row = r0 + wave * SLOTS + slot;
+        const int rl = min(row, staged_end - 1) - b.rb;
+        uint4 q[NG];
+        uint32_t sv[NG];
+#pragma unroll
+        for (int i = 0; i < NG; ++i) q[i] = buf[rl * G + min(l + i * L, G - 1)];
+        if (b.lds_steps) {
+#pragma unroll
+            for (int i = 0; i < NG; ++i) sv[i] = lsteps[rl * G + min(l + i * L, G - 1)];
+        } else {
+#pragma unroll
+            for (int i = 0; i < NG; ++i) sv[i] = load_global_u16(m.steps, (long)(b.rb + rl) * G + min(l + i * L, G - 1));
         }
+        finish(row < staged_end ? row : b.re, q, sv);
+    }
+    for (int r0 = staged_end; r0 < b.re; r0 += kComputeWaves * SLOTS) {
+        const int row = r0 + wave * SLOTS + slot;
+        const int rc = min(row, b.re - 1);
+        uint4 q[NG];
+        uint32_t sv[NG];
+#pragma unroll
+        for (int i = 0; i < NG; ++i) {
+            const int g = min(l + i * L, G - 1);
+            q[i] = load_global_u4(codes, (long)rc * G + g);
+            sv[i] = load_global_u16(m.steps, (long)rc * G + g);
+        }
+        finish(row, q, sv);
     }
 }
 
-// Grid barrier to generation `gen`.  No read-modify-write on a shared word:
-// each workgroup stores `gen` into its own flag, then wave 0 reads every
-// workgroup's flag (agent-coherent loads, all issued at once, one or more per
-// lane) until all have reached `gen`, with a bounded number of polls; a
-// timeout sets the error word.  Meanwhile waves 1..3 pull this workgroup's
-// share of the next matrix into L2.  Returns false if the chain must stop.
-__device__ __forceinline__ bool chain_barrier(unsigned *sync, unsigned gen, unsigned spin_limit,
-                                              const ChainMat *next, int nwg, uint4 *scratch) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's stores are done
-    lds_barrier();
-    __shared__ int stop_s;
-    unsigned *flags = sync + kSyncFlags;
-    if (threadIdx.x == 0)
-        __hip_atomic_store(flags + blockIdx.x, gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (next) chain_prefetch(*next, nwg, scratch);
-    if (threadIdx.x < 64) {
-        const int lane = threadIdx.x;
-        const __amdgpu_buffer_rsrc_t fr = buffer_rsrc(flags, nwg * 4);
-        unsigned it = 0;
-        int stop = 0;
-        for (;;) {
-            // lane l checks flags l, l+64, ... (four at a time per load)
-            int behind = 0;
-            for (int f0 = lane * 4; f0 < nwg; f0 += 256) {
-                const float4 v = load_coherent_f4(fr, f0 * 4);
-                const unsigned a = __float_as_uint(v.x), b = __float_as_uint(v.y);
-                const unsigned c = __float_as_uint(v.z), d = __float_as_uint(v.w);
-                // generations only grow; compare with wrap-around arithmetic
-                behind |= (int)(a - gen) < 0 && f0 + 0 < nwg;
-                behind |= (int)(b - gen) < 0 && f0 + 1 < nwg;
-                behind |= (int)(c - gen) < 0 && f0 + 2 < nwg;
-                behind |= (int)(d - gen) < 0 && f0 + 3 < nwg;
-            }
-            if (!wave_or_i32(behind)) break;
-            if (++it > spin_limit) {
-                if (lane == 0)
-                    __hip_atomic_store(sync + kSyncError, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                stop = 1;
-                break;
-            }
-        }
-        if (lane == 0) stop_s = stop || load_agent_u(sync + kSyncError) != 0;
+__device__ __forceinline__ void chain_rows_any(const ChainMat &m, const RowBlock &b, const uint4 *buf,
+                                               const uint16_t *raw) {
+    const int G = m.K >> 5;
+    const int L = G <= 64 ? 16 : (G <= 128 ? 32 : 64);
+    const int NG = (G + L - 1) / L;
+    switch (__builtin_amdgcn_readfirstlane(L * 8 + NG)) {
+        case 16 * 8 + 1: chain_rows<16, 1>(m, b, buf, raw); break;
+        case 16 * 8 + 2: chain_rows<16, 2>(m, b, buf, raw); break;
+        case 16 * 8 + 3: chain_rows<16, 3>(m, b, buf, raw); break;
+        case 16 * 8 + 4: chain_rows<16, 4>(m, b, buf, raw); break;
+        case 32 * 8 + 3: chain_rows<32, 3>(m, b, buf, raw); break;
+        case 32 * 8 + 4: chain_rows<32, 4>(m, b, buf, raw); break;
+        case 64 * 8 + 3: chain_rows<64, 3>(m, b, buf, raw); break;
+        default: chain_rows<64, 4>(m, b, buf, raw); break;
     }
-    lds_barrier();
-    return stop_s == 0;
+}
+
+// Wave 0: wait until every workgroup's flag has reached generation `gen`
+// (agent-coherent loads, all issued at once, one or more per lane), with a
+// bounded number of polls; a timeout sets the error word.  Returns 1 if the
+// chain must stop.
+__device__ __forceinline__ int chain_poll(unsigned *sync, unsigned gen, unsigned spin_limit, int nwg) {
+    const int lane = threadIdx.x;
+    const __amdgpu_buffer_rsrc_t fr = buffer_rsrc(sync + kSyncFlags, nwg * kFlagStride * 4);
+    unsigned it = 0;
+    int stop = 0;
+    for (;;) {
+        // lane l checks the flags of workgroups l, l+64, ... (one load each)
+        int behind = 0;
+        for (int f = lane; f < nwg; f += 64) {
+            const unsigned a = __builtin_amdgcn_raw_buffer_load_b32(fr, f * kFlagStride * 4, 0, 16);
+            // generations only grow; compare with wrap-around arithmetic
+            behind |= (int)(a - gen) < 0;
+        }
+        if (!wave_or_i32(behind)) break;
+        if (++it > spin_limit) {
+            if (lane == 0)
+                __hip_atomic_store(sync + kSyncError, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            stop = 1;
+            break;
+        }
+    }
+    return stop || load_agent_u(sync + kSyncError) != 0;
 }
 
 __global__ __launch_bounds__(kChainThreads) void chain_kernel(const ChainMat *__restrict__ desc,
                                                               int n, const uint16_t *__restrict__ x0,
                                                               unsigned *sync, unsigned spin_limit) {
     extern __shared__ uint4 smem[];
-    uint16_t *raw = reinterpret_cast<uint16_t *>(smem);          // kChainMaxK halves
-    uint4 *scratch = smem + (kChainMaxK * 2) / 16;                // kPrefetchBytes
+    uint16_t *raw = reinterpret_cast<uint16_t *>(smem);   // kChainMaxK halves
+    uint4 *bufs = smem + (kChainMaxK * 2) / 16;            // two weight buffers
     __shared__ double dred[8];
+    __shared__ int stop_s;
     const int nwg = gridDim.x;
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, wave = tid >> 6;
+    const bool copier = wave >= kComputeWaves;
 
     // Every workgroup checks the descriptors (same answer everywhere).
     bool ok = n >= 1;
@@ -243,55 +307,83 @@ __global__ __launch_bounds__(kChainThreads) void chain_kernel(const ChainMat *__
     // barrier generations of this call continue from those of earlier calls
     const unsigned epoch = load_agent_u(sync + kSyncEpoch);
     if (ok) {
+        if (copier) chain_copy(desc[0], chain_block(desc[0], nwg), bufs, 0, 1 << 30);
         for (int i = 0; i < n; ++i) {
             const ChainMat m = desc[i];
-            const int K = m.K, G = K >> 5;
+            const int K = m.K;
             // 1. input into LDS (raw fp16)
             uint4 *r16 = reinterpret_cast<uint4 *>(raw);
+            // (both paths leave each 8-value block in the pair order
+            // (x0,x4)(x1,x5)(x2,x6)(x3,x7) that the unpack of a packed word uses)
             if (i == 0) {
                 const uint4 *x16 = reinterpret_cast<const uint4 *>(x0);
-                for (int c = tid; c < (K >> 3); c += kChainThreads) r16[c] = x16[c];
+                for (int c = tid; c < (K >> 3); c += kChainThreads) {
+                    const uint4 v = x16[c];
+                    r16[c] = make_uint4(__builtin_amdgcn_perm(v.z, v.x, 0x05040100u),
+                                        __builtin_amdgcn_perm(v.z, v.x, 0x07060302u),
+                                        __builtin_amdgcn_perm(v.w, v.y, 0x05040100u),
+                                        __builtin_amdgcn_perm(v.w, v.y, 0x07060302u));
+                }
             } else {
-                // previous output: all of this thread's chunks requested at
-                // once with agent-coherent loads, then the canonical sum
+                // previous output: the chunks of the canonical 256-thread
+                // order, all requested at once with agent-coherent loads
                 const __amdgpu_buffer_rsrc_t pr = buffer_rsrc(desc[i - 1].y, K * 4);
                 constexpr int J = kChainMaxK / 4 / 256;
                 float4 v[J];
-                const bool rn = tid < 256;  // the canonical 256-thread order
+                const bool rn = tid < 256;
 #pragma unroll
                 for (int j = 0; j < J; ++j) {
-                    const int c = min((rn ? tid : 0) + 256 * j, (K >> 2) - 1);
-                    v[j] = load_coherent_f4(pr, c * 16);
+                    const int c = tid + 256 * j;
+                    v[j] = (rn && c < (K >> 2)) ? load_coherent_f4(pr, c * 16)
+                                                : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
                 }
-                const double ss = sum_squares_256_regs(K, v, dred, rn);
+                const double inv = renorm_scale(sum_squares_256_regs(K, v, dred, rn), K);
                 if (rn) {
 #pragma unroll
                     for (int j = 0; j < J; ++j) {
                         const int c = tid + 256 * j;
                         if (c < (K >> 2)) {
-                            const uint32_t lo = renorm_value(v[j].x, ss, K, 0) | ((uint32_t)renorm_value(v[j].y, ss, K, 0) << 16);
-                            const uint32_t hi = renorm_value(v[j].z, ss, K, 0) | ((uint32_t)renorm_value(v[j].w, ss, K, 0) << 16);
-                            reinterpret_cast<uint2 *>(raw)[c] = make_uint2(lo, hi);
+                            // chunk c holds values 4(c&1)..+3 of block c>>1:
+                            // value e of a block sits at position 2(e&3) + (e>>2)
+                            uint16_t *blk = raw + (c >> 1) * 8 + (c & 1);
+                            blk[0] = renorm_value(v[j].x, inv, 0);
+                            blk[2] = renorm_value(v[j].y, inv, 0);
+                            blk[4] = renorm_value(v[j].z, inv, 0);
+                            blk[6] = renorm_value(v[j].w, inv, 0);
                         }
                     }
                 }
             }
+            // input staged, and this step's weights landed (the copy waves
+            // have no loads outstanding past this point)
             __syncthreads();
-            // 2. rows
-            const uint4 *codes = reinterpret_cast<const uint4 *>(m.codes);
-            switch (__builtin_amdgcn_readfirstlane(chain_variant(m.N, G, nwg))) {
-                case 0: chain_rows<64, 1>(codes, m.steps, m.N, K, raw, m.y); break;
-                case 1: chain_rows<64, 2>(codes, m.steps, m.N, K, raw, m.y); break;
-                case 2: chain_rows<64, 4>(codes, m.steps, m.N, K, raw, m.y); break;
-                case 3: chain_rows<16, 3>(codes, m.steps, m.N, K, raw, m.y); break;
-                case 4: chain_rows<16, 4>(codes, m.steps, m.N, K, raw, m.y); break;
-                default: chain_rows<32, 4>(codes, m.steps, m.N, K, raw, m.y); break;
+            // 2. copy waves fetch the next step's block; compute waves run this one
+            // (the copy wave issues the first kCopyEarly instructions of the next
+            // block now and the rest after the pre-flag barrier below, so that
+            // it reaches that barrier without delay)
+            uint4 *next_buf = bufs + ((i + 1) & 1) * (kWeightBuf / 16);
+            if (copier) {
+                if (i + 1 < n) chain_copy(desc[i + 1], chain_block(desc[i + 1], nwg), next_buf, 0, kCopyEarly);
+            } else {
+                chain_rows_any(m, chain_block(m, nwg), bufs + (i & 1) * (kWeightBuf / 16), raw);
             }
-            // 3. barrier before the next matrix reads this output
-            if (i + 1 < n) {
-                const ChainMat next = desc[i + 1];
-                if (!chain_barrier(sync, epoch + (unsigned)(i + 1), spin_limit, &next, nwg, scratch)) break;
+            if (i + 1 == n) break;
+            // 3. grid barrier before the next step reads this output
+            if (!copier) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // outputs stored
+            lds_barrier();
+            if (tid == 0)
+                __hip_atomic_store(sync + kSyncFlags + blockIdx.x * kFlagStride, epoch + (unsigned)(i + 1),
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (copier) {
+                chain_copy(desc[i + 1], chain_block(desc[i + 1], nwg), next_buf, kCopyEarly, 1 << 30);
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // next block landed
             }
+            if (wave == 0) {
+                const int stop = chain_poll(sync, epoch + (unsigned)(i + 1), spin_limit, nwg);
+                if (tid == 0) stop_s = stop;
+            }
+            lds_barrier();
+            if (stop_s) break;
         }
     } else if (blockIdx.x == 0 && tid == 0) {
         __hip_atomic_store(sync + kSyncError, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -312,7 +404,7 @@ __global__ __launch_bounds__(kChainThreads) void chain_kernel(const ChainMat *__
     }
 }
 
-size_t chain_lds_bytes() { return (size_t)kChainMaxK * 2 + kPrefetchBytes; }
+size_t chain_lds_bytes() { return (size_t)kChainMaxK * 2 + 2 * (size_t)kWeightBuf; }
 
 hipError_t launch_chain(const void *desc, int n, const uint16_t *x0, void *sync, unsigned spin_limit,
                         hipStream_t stream) {

@@ -30,6 +30,17 @@ typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
 
+// Workgroup barrier that orders LDS accesses only.  __syncthreads() also makes
+// the wave wait for every outstanding global load (its release fence covers all
+// address spaces), which would stall on weight loads that were deliberately
+// left in flight across the barrier.
+// Written as one asm statement with a memory clobber: the compiler neither
+// moves memory accesses across it nor adds waits for loads still in flight.
+// LDS written by global_load_lds must be waited for (wait_vmcnt) beforehand.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 __device__ __forceinline__ h2 as_h2(uint32_t u) { return __builtin_bit_cast(h2, u); }
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits) {
@@ -170,9 +181,9 @@ __device__ __forceinline__ double sum_squares_256_regs(int K, const float4 (&v)[
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off, kWave);
     if ((tid & 63) == 0 && tid < 256) red[tid >> 6] = ss;
-    __syncthreads();
+    lds_barrier();
     const double tot = ((red[0] + red[1]) + red[2]) + red[3];
-    __syncthreads();
+    lds_barrier();
     return tot;
 }
 
@@ -187,11 +198,17 @@ __device__ __forceinline__ float4 load_coherent_f4(__amdgpu_buffer_rsrc_t r, int
     return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_offset, 0, 16));
 }
 
-// u / sqrt(ss / K) rounded to nearest-even in fp16 (dt 0) or bf16 (dt 1),
-// zero when the vector is zero.
-__device__ __forceinline__ uint16_t renorm_value(float u, double ss, int K, int dt) {
+// Renormalisation of one entry: u / sqrt(ss / K), formed as u times the fp64
+// reciprocal 1 / sqrt(ss / K) (computed once per vector), rounded to fp32 and
+// then to nearest-even in fp16 (dt 0) or bf16 (dt 1); zero when the vector is
+// zero.  Within one unit in the last place of the exactly rounded quotient.
+__device__ __forceinline__ double renorm_scale(double ss, int K) {
     const double r = sqrt(ss / (double)K);
-    const float q = r > 0.0 ? (float)((double)u / r) : 0.0f;
+    return r > 0.0 ? 1.0 / r : 0.0;
+}
+
+__device__ __forceinline__ uint16_t renorm_value(float u, double inv, int dt) {
+    const float q = (float)((double)u * inv);
     return dt == 0 ? __builtin_bit_cast(uint16_t, (_Float16)q) : __builtin_bit_cast(uint16_t, (__bf16)q);
 }
 
@@ -307,16 +324,6 @@ __device__ __forceinline__ void stage_issue(const uint16_t *__restrict__ x, int 
     }
 }
 
-// Workgroup barrier that orders LDS accesses only.  __syncthreads() also makes
-// the wave wait for every outstanding global load (its release fence covers all
-// address spaces), which would stall on weight loads that were deliberately
-// left in flight across the barrier.
-// Written as one asm statement with a memory clobber: the compiler neither
-// moves memory accesses across it nor adds waits for loads still in flight.
-// LDS written by global_load_lds must be waited for (wait_vmcnt) beforehand.
-__device__ __forceinline__ void lds_barrier() {
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
 
 // Wait until at most `pending` vector-memory loads are outstanding (gfx9
 // s_waitcnt encoding: vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt left at

@@ -19,8 +19,8 @@ __global__ __launch_bounds__(256) void rms_renorm_kernel(const float *__restrict
         return vec ? reinterpret_cast<const float4 *>(v)[c]
                    : make_float4(v[4 * c], v[4 * c + 1], v[4 * c + 2], v[4 * c + 3]);
     };
-    const double ss = sum_squares_256(K, load4, red);
-    for (int k = threadIdx.x; k < K; k += 256) out[k] = renorm_value(v[k], ss, K, out_dt);
+    const double inv = renorm_scale(sum_squares_256(K, load4, red), K);
+    for (int k = threadIdx.x; k < K; k += 256) out[k] = renorm_value(v[k], inv, out_dt);
 }
 
 hipError_t launch_rms_renorm(const float *v, long ldv, int K, int rows, void *out, long ldo,

@@ -161,8 +161,10 @@ int w4_embed_gather(const uint32_t *codes, const uint16_t *steps, int32_t V, int
  * once (K a multiple of 4): for each row r, take the leading K entries u of
  * the fp32 vector
  * v + r*ldv, r_rms = sqrt(mean(u^2)), and write (out + r*ldo)[k] = u[k] / r_rms
- * rounded to nearest-even in dtype out_dt (zeros if r_rms == 0).  The sum of
- * squares is taken in fp64.  One workgroup per row.
+ * in dtype out_dt (zeros if r_rms == 0): u[k] times the fp64 reciprocal of
+ * r_rms, rounded to fp32 and then to nearest-even in out_dt, which is within
+ * one unit in the last place of the exactly rounded quotient.  The sum of
+ * squares is taken in fp64 in one fixed order.  One workgroup per row.
  */
 int w4_rms_renorm(const float *v, int64_t ldv, int32_t K, int32_t rows, void *out, int64_t ldo,
                   int32_t out_dt, void *stream);
@@ -189,7 +191,7 @@ int w4_rms_renorm(const float *v, int64_t ldv, int32_t K, int32_t rows, void *ou
  * they cannot all run together the bounded barrier waits end with error 1
  * rather than a hang.  Concurrent chains must use different sync buffers.
  */
-#define W4_CHAIN_SYNC_BYTES 8192
+#define W4_CHAIN_SYNC_BYTES 131328 /* 256 + 512 flags of 256 bytes */
 typedef struct {
     const uint32_t *codes; /* device, 16-byte aligned */
     const uint16_t *steps; /* device */

@@ -69,7 +69,6 @@ __device__ __forceinline__ void store_agent(float *p, float v) {
 }
 // Pointers read from the descriptors are generic; the weights are in global
 // memory, and saying so keeps their loads off the flat path.
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ uint4 load_global_u4(const uint4 *p, long i) {
     const u32x4 v = ((const __attribute__((address_space(1))) u32x4 *)p)[i];
     return make_uint4(v.x, v.y, v.z, v.w);
@@ -152,21 +151,6 @@ __device__ __forceinline__ void chain_copy(const ChainMat &m, const RowBlock &b,
     }
 }
 
-// Sum over each group of L consecutive lanes (L = 16, 32 or 64), left in the
-// group's last lane: shifted adds within 16-lane rows, then row broadcasts.
-template <int L>
-__device__ __forceinline__ float lane_group_sum(float v) {
-    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x111, 0xF, 0xF, true));
-    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x112, 0xF, 0xF, true));
-    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x114, 0xF, 0xF, true));
-    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x118, 0xF, 0xF, true));
-    if (L >= 32)  // row_bcast:15 into rows 1 and 3
-        v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x142, 0xA, 0xF, false));
-    if (L == 64)  // row_bcast:31 into rows 2 and 3
-        v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x143, 0xC, 0xF, false));
-    return v;
-}
-
 // Compute waves: the rows of the block, L lanes per row, NG groups per lane;
 // codes and steps from the LDS buffer for staged rows, else from memory.
 template <int L, int NG>
@@ -203,7 +187,7 @@ __device__ __forceinline__ void chain_rows(const ChainMat &m, const RowBlock &b,
             acc = (g < G) ? __builtin_fmaf(group_dot(q[i], xr[i]), bf16_to_f32(sv[i]), acc) : acc;
         }
         acc = lane_group_sum<L>(acc);
-        if (l == L - 1 && row < b.re) store_y(m.y, m.N, row, acc);
+        if (l == L - 1 && row < b.re) store_y(m.y, m.N, row, __builtin_ldexpf(acc, kGroupDotExp));
     };
     const int staged_end = b.rb + b.nlds;
     for (int r0 = b.rb; r0 < staged_end; r0 += kComputeWaves * SLOTS) {

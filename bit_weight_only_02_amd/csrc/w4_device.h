@@ -7,11 +7,12 @@
 // Exact operands.  The dev.to page "Gemma 4 on a 4 GB GPU in Plain PyTorch"
 // (section "Step 3 - Multiply Straight From the Packed Weights") turns a code
 // into a float by OR-ing it into the bits of 2^23 and subtracting 2^23 + 8.
-// Here the same idea runs two lanes at a time in fp16: OR-ing a nibble into
-// the mantissa of 1024.0h gives 1024 + c exactly, and one packed subtract of
-// 1032 gives c - 8 exactly.  A nibble sitting four bits higher gives 1024 + 16c,
-// and one packed FMA (x 1/16, - 72) gives c - 8 exactly.  The packed pairs then
-// feed v_dot2_f32_f16, which multiplies fp16 pairs and accumulates in fp32.
+// The same idea is used here two codes at a time in fp16, one step further:
+// with a zero exponent field a masked nibble already IS a float (the subnormal
+// c * 2^-24), so a single AND yields two codes and one packed subtract of
+// 8 * 2^-24 yields two exact (c - 8) * 2^-24.  The pairs feed v_dot2_f32_f16,
+// which multiplies fp16 pairs exactly and accumulates in fp32; the finished
+// row is scaled back by 2^24.
 //
 // Activations are staged as fp16 scaled by a power of two 2^s chosen from the
 // vector's largest exponent (so that every staged value is a normal fp16 equal
@@ -27,6 +28,7 @@
 namespace w4 {
 
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
 
@@ -61,41 +63,70 @@ __device__ __forceinline__ int f32_exponent(float v) {
     return (int)((__float_as_uint(v) >> 23) & 0xFFu) - 127;
 }
 
-// Eight codes of one packed word -> four exact fp16 pairs (c - 8), ordered
-// (c0,c4), (c1,c5), (c2,c6), (c3,c7).
+// Eight codes of one packed word -> four fp16 pairs holding exactly
+// (c - 8) * 2^-24 -- fp16 subnormals -- ordered (c0,c4), (c1,c5), (c2,c6),
+// (c3,c7); the pairs p1 and p3 hold 16 times that, (c - 8) * 2^-20.
+// A nibble masked into the low mantissa bits of an fp16 with a zero exponent
+// field is the subnormal c * 2^-24 (or 16c * 2^-24 four bits higher), so one
+// AND and one packed subtract of 8 * 2^-24 (or 128 * 2^-24) give the exact
+// operand; no OR of an exponent is needed.  Every step is exact as long as fp16
+// subnormals are kept (the default floating-point mode of these kernels).
 __device__ __forceinline__ void unpack_word(uint32_t w, h2 &p0, h2 &p1, h2 &p2, h2 &p3) {
-    const h2 kSub = {(_Float16)-1032.0f, (_Float16)-1032.0f};
-    const h2 kInv16 = {(_Float16)0.0625f, (_Float16)0.0625f};
-    const h2 kSub72 = {(_Float16)-72.0f, (_Float16)-72.0f};
+    const h2 k8 = __builtin_bit_cast(h2, 0x00080008u);    // 8 * 2^-24
+    const h2 k128 = __builtin_bit_cast(h2, 0x00800080u);  // 128 * 2^-24
     const uint32_t u = w >> 8;
-    p0 = as_h2((w & 0x000F000Fu) | 0x64006400u) + kSub;
-    p1 = as_h2((w & 0x00F000F0u) | 0x64006400u) * kInv16 + kSub72;
-    p2 = as_h2((u & 0x000F000Fu) | 0x64006400u) + kSub;
-    p3 = as_h2((u & 0x00F000F0u) | 0x64006400u) * kInv16 + kSub72;
+    p0 = as_h2(w & 0x000F000Fu) - k8;
+    p1 = as_h2(w & 0x00F000F0u) - k128;
+    p2 = as_h2(u & 0x000F000Fu) - k8;
+    p3 = as_h2(u & 0x00F000F0u) - k128;
 }
 
 __device__ __forceinline__ float dot2(h2 a, h2 b, float c) {
     return __builtin_amdgcn_fdot2(a, b, c, false);
 }
 
-// Sum over one group of 32 codes: q holds the 4 packed words, xr the 16 staged
-// activation pairs of the group in the order unpack_word produces.
+// group_dot returns its sum scaled by 2^-kGroupDotExp; the caller multiplies
+// the finished row by 2^kGroupDotExp (exact, a power of two).
+constexpr int kGroupDotExp = 24;
+
+// Sum over one group of 32 codes, times 2^-24: q holds the 4 packed words, xr
+// the 16 staged activation pairs of the group in the order unpack_word
+// produces.  Every product (c - 8) * 2^-24 * x is exact in fp32; the pairs
+// p0/p2 and p1/p3 go to separate fp32 accumulators, joined with a factor 1/16.
 __device__ __forceinline__ float group_dot(uint4 q, const h2 *xr) {
     h2 a0, a1, a2, a3;
-    float s0 = 0.0f, s1 = 0.0f;
+    float lo = 0.0f, hi = 0.0f;
     unpack_word(q.x, a0, a1, a2, a3);
-    s0 = dot2(a0, xr[0], s0); s1 = dot2(a1, xr[1], s1);
-    s0 = dot2(a2, xr[2], s0); s1 = dot2(a3, xr[3], s1);
+    lo = dot2(a0, xr[0], lo); hi = dot2(a1, xr[1], hi);
+    lo = dot2(a2, xr[2], lo); hi = dot2(a3, xr[3], hi);
     unpack_word(q.y, a0, a1, a2, a3);
-    s0 = dot2(a0, xr[4], s0); s1 = dot2(a1, xr[5], s1);
-    s0 = dot2(a2, xr[6], s0); s1 = dot2(a3, xr[7], s1);
+    lo = dot2(a0, xr[4], lo); hi = dot2(a1, xr[5], hi);
+    lo = dot2(a2, xr[6], lo); hi = dot2(a3, xr[7], hi);
     unpack_word(q.z, a0, a1, a2, a3);
-    s0 = dot2(a0, xr[8], s0); s1 = dot2(a1, xr[9], s1);
-    s0 = dot2(a2, xr[10], s0); s1 = dot2(a3, xr[11], s1);
+    lo = dot2(a0, xr[8], lo); hi = dot2(a1, xr[9], hi);
+    lo = dot2(a2, xr[10], lo); hi = dot2(a3, xr[11], hi);
     unpack_word(q.w, a0, a1, a2, a3);
-    s0 = dot2(a0, xr[12], s0); s1 = dot2(a1, xr[13], s1);
-    s0 = dot2(a2, xr[14], s0); s1 = dot2(a3, xr[15], s1);
-    return s0 + s1;
+    lo = dot2(a0, xr[12], lo); hi = dot2(a1, xr[13], hi);
+    lo = dot2(a2, xr[14], lo); hi = dot2(a3, xr[15], hi);
+    return __builtin_fmaf(hi, 0.0625f, lo);
+}
+
+// Sum over each group of L consecutive lanes (L = 8, 16, 32 or 64), left in
+// the group's last lane: shifted adds within rows of 16 lanes (DPP row_shr),
+// then row broadcasts across rows.  A fixed order, so results are reproducible.
+template <int L>
+__device__ __forceinline__ float lane_group_sum(float v) {
+    static_assert(L == 8 || L == 16 || L == 32 || L == 64, "lanes per group");
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x111, 0xF, 0xF, true));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x112, 0xF, 0xF, true));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x114, 0xF, 0xF, true));
+    if (L >= 16)
+        v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x118, 0xF, 0xF, true));
+    if (L >= 32)  // row_bcast:15 into rows 1 and 3
+        v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x142, 0xA, 0xF, false));
+    if (L == 64)  // row_bcast:31 into rows 2 and 3
+        v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x143, 0xC, 0xF, false));
+    return v;
 }
 
 // Exact fp32 group sum for the fallback path: activations read as fp32 from a
@@ -121,14 +152,6 @@ __device__ __forceinline__ int wave_max_i32(int v) {
 
 __device__ __forceinline__ int wave_or_i32(int v) {
     return __builtin_amdgcn_ballot_w64(v != 0) != 0 ? 1 : 0;
-}
-
-// max over the four lanes l, l^16, l^32, l^48 (the 16-lane groups of a wave)
-__device__ __forceinline__ int max_across_lane_groups(int v) {
-    auto a = __builtin_amdgcn_permlane32_swap(v, v, false, false);
-    v = max((int)a[0], (int)a[1]);
-    auto b = __builtin_amdgcn_permlane16_swap(v, v, false, false);
-    return max((int)b[0], (int)b[1]);
 }
 
 // Sum of squares of v[0..K) (K a multiple of 4) in fp64 with one fixed order,
@@ -212,88 +235,99 @@ __device__ __forceinline__ uint16_t renorm_value(float u, double inv, int dt) {
     return dt == 0 ? __builtin_bit_cast(uint16_t, (_Float16)q) : __builtin_bit_cast(uint16_t, (__bf16)q);
 }
 
-// ---- per-wave activation staging -------------------------------------------
-// Every wave scans the whole raw vector itself (no cross-wave reduction), then
-// each lane converts only the groups it owns, straight from LDS into its
-// registers.  The staged value is x * 2^s with s = 14 - (largest exponent):
-// every nonzero value must land in the normal fp16 range, i.e. lie within 2^28
-// of the largest; otherwise (or with inf/NaN) the wave takes the fp32 path.
-struct WaveScale {
-    int scale;  // s
-    int emax;   // largest exponent (-100000: all zero)
-    int bad;    // inf/NaN present
-};
-
-// raw: K halves in LDS, 16-byte aligned, K a multiple of 32.
-__device__ __forceinline__ WaveScale wave_scan(const uint16_t *raw, int K, int dt) {
-    const int lane = threadIdx.x & 63;
-    const uint4 *r16 = reinterpret_cast<const uint4 *>(raw);
-    int emax = -100000, bad = 0;
-    for (int c = lane; c < (K >> 3); c += 64) {
-        const uint4 v = r16[c];
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float f = act_to_f32((w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu, dt);
-            if (!__builtin_isfinite(f)) bad = 1;
-            else if (f != 0.0f) emax = max(emax, f32_exponent(f));
-        }
-    }
-    WaveScale ws;
-    ws.emax = wave_max_i32(emax);
-    ws.bad = wave_or_i32(bad);
-    ws.scale = ws.emax == -100000 ? 0 : 14 - ws.emax;
-    return ws;
-}
-
-// Group g of raw -> 16 staged pairs in unpack_word order; returns 1 if a value
-// cannot be staged exactly.
-__device__ __forceinline__ int convert_group(const uint16_t *raw, int g, int dt, const WaveScale &ws,
-                                             h2 *xr) {
-    const uint4 *r16 = reinterpret_cast<const uint4 *>(raw) + g * 4;
-    int lost = 0;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-        const uint4 v = r16[w];
-        const uint32_t b[4] = {v.x, v.y, v.z, v.w};
-        float f[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            f[e] = act_to_f32((b[e >> 1] >> (16 * (e & 1))) & 0xFFFFu, dt);
-            if (f[e] != 0.0f && f32_exponent(f[e]) < ws.emax - 28) lost = 1;
-        }
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            h2 t;
-            t[0] = (_Float16)__builtin_ldexpf(f[p], ws.scale);
-            t[1] = (_Float16)__builtin_ldexpf(f[p + 4], ws.scale);
-            xr[w * 4 + p] = t;
-        }
-    }
-    return lost;
-}
-
-// fp16 activations need no scaling: v_dot2_f32_f16 and the f16 MFMA take
-// fp16 subnormals as they are (measured on gfx950), so (c - 8) * x is exact in
-// fp32 for every fp16 x.  Staging is then only the pair permutation:
-// words (x0,x1) (x2,x3) (x4,x5) (x6,x7) -> (x0,x4) (x1,x5) (x2,x6) (x3,x7).
-__device__ __forceinline__ void permute_group_f16(const uint16_t *raw, int g, h2 *xr) {
-    const uint4 *r16 = reinterpret_cast<const uint4 *>(raw) + g * 4;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-        const uint4 v = r16[w];
-        // v_perm_b32 selector: bytes 0-3 from src1, 4-7 from src0
-        xr[w * 4 + 0] = as_h2(__builtin_amdgcn_perm(v.z, v.x, 0x05040100u));
-        xr[w * 4 + 1] = as_h2(__builtin_amdgcn_perm(v.z, v.x, 0x07060302u));
-        xr[w * 4 + 2] = as_h2(__builtin_amdgcn_perm(v.w, v.y, 0x05040100u));
-        xr[w * 4 + 3] = as_h2(__builtin_amdgcn_perm(v.w, v.y, 0x07060302u));
-    }
-}
-
 struct Staging {
     int scale;     // s: staged value = x * 2^s
     int fallback;  // 1: the vector cannot be staged exactly; use the fp32 path
 };
+
+// Workgroup-wide staging: the raw vector (K halves in LDS, landed and visible
+// to every wave) is converted once per workgroup -- every thread takes whole
+// 8-value chunks -- into staged[c], chunk c as four fp16 pairs in unpack_word
+// order, (x0,x4) (x1,x5) (x2,x6) (x3,x7).  fp16 values are only permuted; bf16
+// values are scaled by 2^s, s = 14 - (largest exponent of the vector), exactly.
+// Every thread returns the same {s, fallback}; fallback is set when some value
+// cannot be staged exactly (inf/NaN, or a nonzero more than 2^28 below the
+// largest), and then staged[] is not to be used.  Up to 16 waves.
+__device__ __forceinline__ Staging stage_x_workgroup(const uint16_t *raw, uint4 *staged, int K, int dt) {
+    __shared__ int red[48];
+    const int tid = threadIdx.x, nthr = blockDim.x, nw = nthr >> 6, wave = tid >> 6;
+    const uint4 *r16 = reinterpret_cast<const uint4 *>(raw);
+    const int n8 = K >> 3;
+    int emax = -100000, bad = 0;
+    if (dt != 0) {
+        for (int c = tid; c < n8; c += nthr) {
+            const uint4 v = r16[c];
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float f = act_to_f32((w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu, dt);
+                if (!__builtin_isfinite(f)) bad = 1;
+                else if (f != 0.0f) emax = max(emax, f32_exponent(f));
+            }
+        }
+        emax = wave_max_i32(emax);
+        bad = wave_or_i32(bad);
+        if ((tid & 63) == 0) {
+            red[wave] = emax;
+            red[16 + wave] = bad;
+        }
+        lds_barrier();
+        emax = -100000;
+        bad = 0;
+        for (int i = 0; i < nw; ++i) {
+            emax = max(emax, red[i]);
+            bad |= red[16 + i];
+        }
+    }
+    const int scale = (dt == 0 || emax == -100000) ? 0 : 14 - emax;
+    int lost = bad;
+    if (!bad) {
+        for (int c = tid; c < n8; c += nthr) {
+            const uint4 v = r16[c];
+            if (dt == 0) {
+                staged[c] = make_uint4(__builtin_amdgcn_perm(v.z, v.x, 0x05040100u),
+                                       __builtin_amdgcn_perm(v.z, v.x, 0x07060302u),
+                                       __builtin_amdgcn_perm(v.w, v.y, 0x05040100u),
+                                       __builtin_amdgcn_perm(v.w, v.y, 0x07060302u));
+            } else {
+                const uint32_t b[4] = {v.x, v.y, v.z, v.w};
+                float f[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    f[e] = act_to_f32((b[e >> 1] >> (16 * (e & 1))) & 0xFFFFu, dt);
+                    if (f[e] != 0.0f && f32_exponent(f[e]) < emax - 28) lost = 1;
+                }
+                uint32_t o[4];
+#pragma unroll
+                for (int p = 0; p < 4; ++p) {
+                    h2 t;
+                    t[0] = (_Float16)__builtin_ldexpf(f[p], scale);
+                    t[1] = (_Float16)__builtin_ldexpf(f[p + 4], scale);
+                    o[p] = __builtin_bit_cast(uint32_t, t);
+                }
+                staged[c] = make_uint4(o[0], o[1], o[2], o[3]);
+            }
+        }
+    }
+    lost = wave_or_i32(lost);
+    if ((tid & 63) == 0) red[32 + wave] = lost;
+    lds_barrier();
+    int fallback = 0;
+    for (int i = 0; i < nw; ++i) fallback |= red[32 + i];
+    return Staging{scale, fallback};
+}
+
+// The staged pairs of group g (4 chunks) into registers.
+__device__ __forceinline__ void load_staged_group(const uint4 *staged, int g, h2 *xr) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        const uint4 v = staged[g * 4 + w];
+        xr[w * 4 + 0] = as_h2(v.x);
+        xr[w * 4 + 1] = as_h2(v.y);
+        xr[w * 4 + 2] = as_h2(v.z);
+        xr[w * 4 + 3] = as_h2(v.w);
+    }
+}
 
 // Staging of a raw activation vector: stage_issue() requests all of x straight
 // into LDS (global_load_lds_dwordx4: no registers; each wave moves 64 chunks of
@@ -324,6 +358,36 @@ __device__ __forceinline__ void stage_issue(const uint16_t *__restrict__ x, int 
     }
 }
 
+
+// Direct-to-LDS 16-byte load written as inline assembly, for pipelines that
+// keep several such loads in flight and wait for them by count themselves
+// (wait_vmcnt_mem).  Given the builtin, the compiler's wait insertion treats
+// every later LDS read as possibly reading this load's destination and waits for
+// all outstanding loads before it, which would drain the pipeline each step.
+// Lane i writes 16 bytes at lds + 16*i; `lds` must be wave-uniform.  M0 carries
+// the LDS address and is set here; none of the kernels using this keeps a
+// compiler-managed M0 value live across it.
+__device__ __forceinline__ void lds_dma16(const void *g, void *lds) {
+    const uint32_t m = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void *)lds;
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(m) : "memory");
+}
+
+// The same load with a wave-uniform 64-bit base in scalar registers and a
+// per-lane 32-bit byte offset, marked non-temporal (the data are read once:
+// measured on MI355X, streaming reads run markedly faster with this hint).
+__device__ __forceinline__ void lds_dma16_nt(const void *sbase, uint32_t voff, void *lds) {
+    const uint32_t m = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void *)lds;
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1 nt" ::"v"(voff), "s"(sbase), "s"(m)
+                 : "memory");
+}
+
+// Wait until at most `pending` vector-memory operations are outstanding, as an
+// asm statement with a memory clobber, so that no LDS read is moved above it.
+template <int pending>
+__device__ __forceinline__ void wait_vmcnt_mem() {
+    static_assert(pending >= 0 && pending < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(pending) : "memory");
+}
 
 // Wait until at most `pending` vector-memory loads are outstanding (gfx9
 // s_waitcnt encoding: vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt left at

@@ -22,7 +22,7 @@
 
 namespace w4 {
 
-template <int L, int NG, int R>
+template <int L, int NG, int R, int PF>
 __global__ __launch_bounds__(256) void gemv_kernel(const uint4 *__restrict__ codes,
                                                    const uint16_t *__restrict__ steps,
                                                    int N, int K,
@@ -58,17 +58,18 @@ __global__ __launch_bounds__(256) void gemv_kernel(const uint4 *__restrict__ cod
             const uint16_t *sp = steps + (size_t)row * G;
 #pragma unroll
             for (int i = 0; i < NG; ++i) {
-                q[r][i] = cp[gc[i]];
-                sv[r][i] = sp[gc[i]];
+                // read once: non-temporal loads
+                const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(cp) + gc[i]);
+                q[r][i] = make_uint4(v.x, v.y, v.z, v.w);
+                sv[r][i] = __builtin_nontemporal_load(sp + gc[i]);
             }
         }
     };
 
     // The activations go to LDS by DMA with the first rows' weights requested
-    // right behind them; one barrier later every wave stages its own lanes'
-    // activations into registers (wave_scan / convert_group) -- no further
-    // workgroup-wide step.  A wave that cannot stage exactly takes the fp32
-    // path on its own.
+    // right behind them; the workgroup then stages them once (exact fp16
+    // pairs, or the fp32 path for the whole workgroup when they cannot be
+    // staged exactly) and every lane copies its own groups into registers.
     uint16_t *raw = reinterpret_cast<uint16_t *>(xs);
     stage_issue(x, K, raw);
     int row0 = blockIdx.x * rows_per_iter;
@@ -80,31 +81,22 @@ __global__ __launch_bounds__(256) void gemv_kernel(const uint4 *__restrict__ cod
     wait_vmcnt<0>();
     lds_barrier();
 
-    // fp16: the values are staged as they are (scale 0, never the fp32 path);
-    // bf16: scaled into fp16 after a per-wave exponent scan.
-    WaveScale ws{0, 0, 0};
-    if (dt != 0) ws = wave_scan(raw, K, dt);
+    // x staged once per workgroup, then each lane takes its own groups
+    uint4 *staged = reinterpret_cast<uint4 *>(raw + stage_raw_halves(K));
+    const Staging st = stage_x_workgroup(raw, staged, K, dt);
     h2 xr[NG][16];
-    int lost = ws.bad;
-    auto load_xr = [&]() __attribute__((always_inline)) {
+    if (!st.fallback) {
 #pragma unroll
         for (int i = 0; i < NG; ++i) {
             const int g = l + i * L;
             if (g < G) {
-                if (dt == 0)
-                    permute_group_f16(raw, g, xr[i]);
-                else
-                    lost |= convert_group(raw, g, dt, ws, xr[i]);
+                load_staged_group(staged, g, xr[i]);
             } else {
 #pragma unroll
                 for (int p = 0; p < 16; ++p) xr[i][p] = h2{0, 0};
             }
         }
-    };
-    if (!ws.bad) load_xr();
-    Staging st;
-    st.scale = ws.scale;
-    st.fallback = wave_or_i32(lost);
+    }
 
     auto compute_rows = [&](const uint4 (&q)[R][NG], const uint32_t (&sv)[R][NG], int r0,
                             auto exact_f32) __attribute__((always_inline)) {
@@ -125,11 +117,10 @@ __global__ __launch_bounds__(256) void gemv_kernel(const uint4 *__restrict__ cod
         }
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-#pragma unroll
-            for (int off = L / 2; off > 0; off >>= 1) acc[r] += __shfl_xor(acc[r], off, kWave);
+            acc[r] = lane_group_sum<L>(acc[r]);
             const int row = r0 + (r * nwaves + wave) * SLOTS + slot;
-            if (l == 0 && row < N)
-                y[row] = decltype(exact_f32)::value ? acc[r] : __builtin_ldexpf(acc[r], -st.scale);
+            if (l == L - 1 && row < N)
+                y[row] = decltype(exact_f32)::value ? acc[r] : __builtin_ldexpf(acc[r], kGroupDotExp - st.scale);
         }
     };
 
@@ -137,12 +128,32 @@ __global__ __launch_bounds__(256) void gemv_kernel(const uint4 *__restrict__ cod
     // so none sits behind a branch), then does the math; other waves on the
     // CU keep the memory system busy meanwhile.  The first step's loads were
     // issued before the staging.
+    // With PF, the loads of the next step are issued before the math of this
+    // one (two register sets, alternating), so that each wave keeps a step of
+    // weights in flight while it computes.
     auto row_loop = [&](auto exact_f32) __attribute__((always_inline)) {
         if (row0 >= N) return;
-        compute_rows(qa, sa, row0, exact_f32);
-        for (row0 += gstride; row0 < N; row0 += gstride) {
-            load_rows(qa, sa, row0);
+        if constexpr (PF == 0) {
             compute_rows(qa, sa, row0, exact_f32);
+            for (row0 += gstride; row0 < N; row0 += gstride) {
+                load_rows(qa, sa, row0);
+                compute_rows(qa, sa, row0, exact_f32);
+            }
+        } else {
+            uint4 qb[R][NG];
+            uint32_t sb[R][NG];
+            for (;;) {
+                int nxt = row0 + gstride;
+                if (nxt < N) load_rows(qb, sb, nxt);
+                compute_rows(qa, sa, row0, exact_f32);
+                row0 = nxt;
+                if (row0 >= N) break;
+                nxt = row0 + gstride;
+                if (nxt < N) load_rows(qa, sa, nxt);
+                compute_rows(qb, sb, row0, exact_f32);
+                row0 = nxt;
+                if (row0 >= N) break;
+            }
         }
     };
     // The staging outcome is uniform within the wave: branch on it once, in a
@@ -153,6 +164,148 @@ __global__ __launch_bounds__(256) void gemv_kernel(const uint4 *__restrict__ cod
         row_loop(std::false_type{});
 }
 
+// ---- streaming variant -------------------------------------------------------
+//
+// The same row mapping, fed through LDS.  A tile is SLOTS consecutive rows (one
+// per row slot of a wave): their codes, SLOTS*G 16-byte groups, and their steps,
+// SLOTS*G bf16 values, are contiguous in memory.  Tiles are dealt to waves
+// round-robin over the whole grid, and every wave keeps a private ring of D tile
+// buffers in LDS that it fills with direct-to-LDS loads (no registers held while
+// the data are in flight) D-1 tiles ahead of the tile it computes.  One
+// workgroup of eight waves per CU then keeps about 100 KB of weights in flight
+// per CU, which the plain register loads of gemv_kernel cannot.  No workgroup
+// barrier is needed after the staging of x: each wave waits only for its own
+// loads (vmcnt; loads complete in issue order), and the output stores issued
+// between tiles are younger than the tile being waited for.
+//
+// Preconditions (checked by the host): G = K/32 is a multiple of 8 (every row's
+// steps are whole 16-byte chunks), the steps are 16-byte aligned, NG = ceil(G/L),
+// so that a tile takes exactly NG code instructions and one step instruction.
+template <int L, int NG, int D>
+__global__ __launch_bounds__(512) void gemv_ring_kernel(const uint4 *__restrict__ codes,
+                                                        const uint16_t *__restrict__ steps,
+                                                        int N, int K,
+                                                        const uint16_t *__restrict__ x, int dt,
+                                                        float *__restrict__ y) {
+    constexpr int SLOTS = kWave / L;
+    constexpr int kPerTile = NG + 1;  // load instructions per tile
+    static_assert((D - 1) * kPerTile <= 63, "vmcnt range");
+    extern __shared__ uint4 smem[];
+    const int G = K >> 5;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar tile loop
+    const int nwaves = blockDim.x >> 6;
+    const int l = lane % L, slot = lane / L;
+
+    uint16_t *raw = reinterpret_cast<uint16_t *>(smem);
+    const int cchunks = SLOTS * G;      // code chunks of a tile
+    const int schunks = SLOTS * G / 8;  // step chunks of a tile (<= 64)
+    const int tile_chunks = cchunks + schunks;
+    uint4 *staged = smem + stage_raw_halves(K) / 8;
+    uint4 *ring = staged + stage_raw_halves(K) / 8 + (long)wave * D * tile_chunks;
+
+    const long ntiles = ((long)N + SLOTS - 1) / SLOTS;
+    const long tstride = (long)gridDim.x * nwaves;
+    const long last_c = (long)N * G - 1, last_s = (long)N * G / 8 - 1;
+    const uint4 *steps16 = reinterpret_cast<const uint4 *>(steps);
+
+    // Request tile t into ring buffer b: NG code instructions (lanes past the
+    // tile's chunks idle) and one step instruction; rows past N are clamped to
+    // the last row (their results are not stored).
+    auto issue = [&](long t, int b) __attribute__((always_inline)) {
+        uint4 *dst = ring + b * tile_chunks;
+        const long c_base = t * cchunks;
+        if (c_base + cchunks - 1 <= last_c) {
+            // a whole tile: scalar base, fixed lane offsets
+            const uint4 *cb = codes + c_base;
+#pragma unroll
+            for (int i = 0; i < NG; ++i)
+                if (i * 64 + lane < cchunks) lds_dma16_nt(cb, (uint32_t)(i * 64 + lane) * 16u, dst + i * 64);
+            if (lane < schunks) lds_dma16_nt(steps16 + c_base / 8, (uint32_t)lane * 16u, dst + cchunks);
+        } else {
+            // the last tile, cut by N: chunks past the end are clamped
+#pragma unroll
+            for (int i = 0; i < NG; ++i) {
+                const int c = i * 64 + lane;
+                if (c < cchunks) lds_dma16(codes + min(c_base + c, last_c), dst + i * 64);
+            }
+            if (lane < schunks) lds_dma16(steps16 + min(c_base / 8 + lane, last_s), dst + cchunks);
+        }
+    };
+
+    // x to LDS first, then the first D-1 tiles of this wave.
+    stage_issue(x, K, raw);
+    if (!stage_vector_path(x))
+        for (int i = threadIdx.x; i < K; i += blockDim.x) raw[i] = x[i];
+    long t = (long)blockIdx.x * nwaves + wave;
+#pragma unroll
+    for (int p = 0; p < D - 1; ++p)
+        if (t + p * tstride < ntiles) issue(t + p * tstride, p);
+    // x has landed once at most the tiles' loads are outstanding
+    if (t + (long)(D - 2) * tstride < ntiles)
+        wait_vmcnt_mem<(D - 1) * kPerTile>();
+    else
+        wait_vmcnt_mem<0>();
+    wait_vmcnt<0>();  // (no-op by now; tells the compiler that x has landed)
+    lds_barrier();
+
+    const Staging st = stage_x_workgroup(raw, staged, K, dt);
+    h2 xr[NG][16];
+    if (!st.fallback) {
+#pragma unroll
+        for (int i = 0; i < NG; ++i) {
+            const int g = l + i * L;
+            if (g < G) {
+                load_staged_group(staged, g, xr[i]);
+            } else {
+#pragma unroll
+                for (int p = 0; p < 16; ++p) xr[i][p] = h2{0, 0};
+            }
+        }
+    }
+    const int scale = st.scale;
+    const int fallback = st.fallback;
+
+    auto tile_loop = [&](auto exact_f32) __attribute__((always_inline)) {
+        int b = 0, bn = D - 1;  // ring buffers of the tile computed and of the one requested
+        for (; t < ntiles; t += tstride) {
+            const long tn = t + (long)(D - 1) * tstride;
+            if (tn < ntiles) {
+                issue(tn, bn);
+                wait_vmcnt_mem<(D - 1) * kPerTile>();
+            } else {
+                wait_vmcnt_mem<0>();
+            }
+            const uint4 *tc = ring + b * tile_chunks + slot * G;
+            const uint16_t *ts = reinterpret_cast<const uint16_t *>(ring + b * tile_chunks + cchunks) + slot * G;
+            float acc = 0.0f;
+#pragma unroll
+            for (int i = 0; i < NG; ++i) {
+                const int g = l + i * L;
+                const int gc = min(g, G - 1);
+                const uint4 q = tc[gc];
+                const uint32_t sv = ts[gc];
+                float part;
+                if constexpr (decltype(exact_f32)::value)
+                    part = group_dot_f32(q, raw + gc * 32, dt);
+                else
+                    part = group_dot(q, xr[i]);
+                acc = (g < G) ? __builtin_fmaf(part, bf16_to_f32(sv), acc) : acc;
+            }
+            acc = lane_group_sum<L>(acc);
+            const long row = t * SLOTS + slot;
+            if (l == L - 1 && row < N)
+                y[row] = decltype(exact_f32)::value ? acc : __builtin_ldexpf(acc, kGroupDotExp - scale);
+            b = b + 1 == D ? 0 : b + 1;
+            bn = bn + 1 == D ? 0 : bn + 1;
+        }
+    };
+    if (__builtin_amdgcn_readfirstlane(fallback))
+        tile_loop(std::true_type{});
+    else
+        tile_loop(std::false_type{});
+}
+
 // ---- tiling table ------------------------------------------------------------
 
 namespace {
@@ -160,36 +313,69 @@ namespace {
 typedef void (*GemvFn)(const uint4 *, const uint16_t *, int, int, const uint16_t *, int, float *);
 
 template <int L, int NG>
-GemvFn pick_r(int R) {
-    switch (R) {
-        case 1: return gemv_kernel<L, NG, 1>;
-        case 2: return gemv_kernel<L, NG, 2>;
-        case 4: return gemv_kernel<L, NG, 4>;
+GemvFn pick_r(int R, int pf) {
+    switch (R * 2 + (pf ? 1 : 0)) {
+        case 2: return gemv_kernel<L, NG, 1, 0>;
+        case 3: return gemv_kernel<L, NG, 1, 1>;
+        case 4: return gemv_kernel<L, NG, 2, 0>;
     }
     return nullptr;
 }
 
 template <int L>
-GemvFn pick_ng(int NG, int R) {
+GemvFn pick_ng(int NG, int R, int pf) {
     switch (NG) {
-        case 1: return pick_r<L, 1>(R);
-        case 2: return pick_r<L, 2>(R);
-        case 3: return pick_r<L, 3>(R);
-        case 4: return pick_r<L, 4>(R);
-        case 6: return pick_r<L, 6>(R);
-        case 8: return pick_r<L, 8>(R);
+        case 1: return pick_r<L, 1>(R, pf);
+        case 2: return pick_r<L, 2>(R, pf);
+        case 3: return pick_r<L, 3>(R, pf);
+        case 4: return pick_r<L, 4>(R, pf);
+        case 6: return pick_r<L, 6>(R, pf);
+        case 8: return pick_r<L, 8>(R, pf);
     }
     return nullptr;
 }
 
-GemvFn pick(int L, int NG, int R) {
+GemvFn pick(int L, int NG, int R, int pf) {
     switch (L) {
-        case 8: return pick_ng<8>(NG, R);
-        case 16: return pick_ng<16>(NG, R);
-        case 32: return pick_ng<32>(NG, R);
-        case 64: return pick_ng<64>(NG, R);
+        case 8: return pick_ng<8>(NG, R, pf);
+        case 16: return pick_ng<16>(NG, R, pf);
+        case 32: return pick_ng<32>(NG, R, pf);
+        case 64: return pick_ng<64>(NG, R, pf);
     }
     return nullptr;
+}
+
+template <int L, int NG>
+GemvFn pick_ring_d(int D) {
+    switch (D) {
+        case 2: return gemv_ring_kernel<L, NG, 2>;
+        case 3: return gemv_ring_kernel<L, NG, 3>;
+        case 4: return gemv_ring_kernel<L, NG, 4>;
+        case 5: return gemv_ring_kernel<L, NG, 5>;
+        case 6: return gemv_ring_kernel<L, NG, 6>;
+    }
+    return nullptr;
+}
+
+GemvFn pick_ring(int L, int NG, int D) {
+    switch (L * 16 + NG) {
+        case 16 * 16 + 3: return pick_ring_d<16, 3>(D);
+        case 16 * 16 + 4: return pick_ring_d<16, 4>(D);
+        case 32 * 16 + 3: return pick_ring_d<32, 3>(D);
+        case 32 * 16 + 4: return pick_ring_d<32, 4>(D);
+        case 64 * 16 + 3: return pick_ring_d<64, 3>(D);
+        case 64 * 16 + 4: return pick_ring_d<64, 4>(D);
+    }
+    return nullptr;
+}
+
+constexpr int kLdsBytes = 160 * 1024;  // LDS of one CU (gfx950)
+constexpr int kRingMaxD = 6;
+
+// Bytes of one ring buffer (a tile of 64/L rows: codes then steps).
+int ring_tile_bytes(int L, int K) {
+    const int G = K / 32;
+    return (64 / L) * G * 16 + (64 / L) * G * 2;
 }
 
 }  // namespace
@@ -223,23 +409,60 @@ GemvTile gemv_tile(int N, int K) {
     const long rows_per_iter = (long)(64 / best.L) * best.R * best.waves;
     const long blocks = (N + rows_per_iter - 1) / rows_per_iter;
     best.blocks = (int)(blocks < 1 ? 1 : (blocks > 1024 ? 1024 : blocks));
+    best.ring = 0;
+    // The streaming variant: eight waves per CU-sized workgroup, each with a
+    // ring as deep as the LDS allows (up to kRingMaxD tiles), when the shape
+    // meets its preconditions and there are enough tiles to keep every wave of
+    // the chip busy.
+    if (G > 0 && G % 8 == 0 && best.NG == (G + best.L - 1) / best.L &&
+        pick_ring(best.L, best.NG, 2) != nullptr) {
+        const int waves = 8;
+        const int per_wave = (kLdsBytes - stage_raw_halves(K) * 4) / waves;
+        int D = per_wave / ring_tile_bytes(best.L, K);
+        if (D > kRingMaxD) D = kRingMaxD;
+        const long tiles = (N + (64 / best.L) - 1) / (64 / best.L);
+        if (D >= 2 && tiles >= 256L * waves && getenv("W4_GEMV_RING_DEFAULT")) {
+            best.ring = D;
+            best.waves = waves;
+            best.R = 1;
+            best.blocks = 256;
+        }
+    }
     return best;
 }
 
 hipError_t launch_gemv(const uint32_t *codes, const uint16_t *steps, int N, int K,
                        const uint16_t *x, int dt, float *y, hipStream_t stream) {
     GemvTile t = gemv_tile(N, K);
-    // W4_GEMV_TILE="L,NG,R,waves,blocks" overrides the table (tile sweeps);
+    // W4_GEMV_TILE="L,NG,R,waves,blocks[,ring depth[,prefetch]]" overrides the table (tile sweeps);
     // it changes only the schedule, never what is computed.
     if (const char *e = getenv("W4_GEMV_TILE")) {
         GemvTile o;
-        if (sscanf(e, "%d,%d,%d,%d,%d", &o.L, &o.NG, &o.R, &o.waves, &o.blocks) == 5 &&
-            o.L * o.NG * 32 >= K && o.waves >= 1 && o.waves <= 4 && o.blocks >= 1)
+        o.ring = 0;
+        o.pf = 0;
+        const int nf = sscanf(e, "%d,%d,%d,%d,%d,%d,%d", &o.L, &o.NG, &o.R, &o.waves, &o.blocks, &o.ring,
+                              &o.pf);
+        if (nf >= 5 && o.L * o.NG * 32 >= K && o.waves >= 1 && o.waves <= (o.ring ? 8 : 4) &&
+            o.blocks >= 1 && o.ring >= 0 && o.ring <= kRingMaxD)
             t = o;
     }
-    GemvFn fn = pick(t.L, t.NG, t.R);
+    if (t.ring) {
+        // the ring kernel's preconditions (a bad override is refused)
+        const int G = K / 32;
+        GemvFn fn = pick_ring(t.L, t.NG, t.ring);
+        if (!fn || G == 0 || G % 8 != 0 || t.NG != (G + t.L - 1) / t.L ||
+            (reinterpret_cast<uintptr_t>(steps) & 15) != 0 || t.waves < 1 || t.waves > 8)
+            return hipErrorInvalidConfiguration;
+        const size_t lds = (size_t)stage_raw_halves(K) * 4 +
+                           (size_t)t.waves * t.ring * ring_tile_bytes(t.L, K);
+        if (lds > (size_t)kLdsBytes) return hipErrorInvalidConfiguration;
+        hipLaunchKernelGGL(fn, dim3(t.blocks), dim3(64 * t.waves), lds, stream,
+                           reinterpret_cast<const uint4 *>(codes), steps, N, K, x, dt, y);
+        return hipGetLastError();
+    }
+    GemvFn fn = pick(t.L, t.NG, t.R, t.pf);
     if (!fn) return hipErrorInvalidConfiguration;
-    const size_t lds = (size_t)(stage_raw_halves(K) + 8) * sizeof(_Float16);
+    const size_t lds = (size_t)2 * stage_raw_halves(K) * sizeof(_Float16);
     hipLaunchKernelGGL(fn, dim3(t.blocks), dim3(64 * t.waves), lds, stream,
                        reinterpret_cast<const uint4 *>(codes), steps, N, K, x, dt, y);
     return hipGetLastError();

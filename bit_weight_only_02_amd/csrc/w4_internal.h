@@ -13,6 +13,8 @@ struct GemvTile {
     int R;       // rows per slot in flight
     int waves;   // waves per workgroup
     int blocks;  // workgroups
+    int ring;    // streaming variant: ring depth in tiles (0: register variant)
+    int pf;      // register variant: next step's loads issued before this step's math
 };
 
 GemvTile gemv_tile(int N, int K);

@@ -42,6 +42,59 @@ def test_gemv_shapes_vs_oracle(w4, N, K, dt):
     assert ok, f"worst |err|/sum|wx| = {worst}"
 
 
+# The streaming (LDS ring) variant, forced through the tile override
+# "L,NG,R,waves,blocks,ring depth" on shapes that span several tiles per wave,
+# a ragged last tile, waves without any tile, and every ring depth.
+RING_CASES = [(1000, 1536, "16,3,1,8,3,4"), (257, 2048, "16,4,1,8,2,3"),
+              (129, 8192, "64,4,1,8,5,2"), (1000, 2816, "32,3,1,8,4,5"), (700, 1536, "16,3,1,4,3,6"),
+              (33, 1536, "16,3,1,8,64,5"), (4097, 4096, "32,4,1,4,7,5"),
+              (20001, 1536, "16,3,1,8,256,5")]
+
+
+@pytest.mark.parametrize("dt", [F16, BF16])
+@pytest.mark.parametrize("N,K,tile", RING_CASES)
+def test_gemv_streaming_variant_vs_oracle(w4, monkeypatch, N, K, tile, dt):
+    print(f"gemv ring N={N} K={K} tile={tile} dt={dt}", flush=True)
+    monkeypatch.setenv("W4_GEMV_TILE", tile)
+    rng = np.random.default_rng(N * 11 + K + dt)
+    codes, steps = synth.w4_matrix(rng, N, K)
+    x = synth.activations(rng, K, dt)
+    y = run_gemv(w4, codes, steps, x, dt)
+    yo, ao = oracle.gemv(codes, steps, N, K, x, dt, threads=True)
+    ok, worst = within_bound(y, yo, ao)
+    assert ok, f"worst |err|/sum|wx| = {worst}"
+
+
+def test_gemv_streaming_variant_exact_cases(w4, monkeypatch):
+    """Integer inputs (bit-exact), a one-hot subnormal x (bit-exact) and a
+    vector too wide for fp16 staging (the exact fp32 path) through the ring."""
+    monkeypatch.setenv("W4_GEMV_TILE", "16,4,1,8,2,4")
+    rng = np.random.default_rng(14)
+    N, K = 300, 2048
+    codes, _ = synth.w4_matrix(rng, N, K)
+    steps = (0x3F80 - 0x80 * rng.integers(0, 5, size=(N, K // 32))).astype(np.uint16)
+    x = rng.choice(np.array([0xBC00, 0x0000, 0x3C00], dtype=np.uint16), size=K)
+    y = run_gemv(w4, codes, steps, x, F16)
+    yo, _ = oracle.gemv(codes, steps, N, K, x, F16)
+    assert np.array_equal(y.astype(np.float64), yo)
+    x = np.zeros(K, dtype=np.uint16)
+    x[1999] = 0x0001
+    y = run_gemv(w4, codes, steps, x, F16)
+    yo, _ = oracle.gemv(codes, steps, N, K, x, F16)
+    assert np.array_equal(y.astype(np.float64), yo)
+    monkeypatch.setenv("W4_GEMV_TILE", "16,3,1,8,2,5")
+    N, K = 129, 1536
+    codes, steps = synth.w4_matrix(rng, N, K)
+    v = rng.normal(0, 1, K)
+    v[::7] *= 2.0**12
+    v[3::11] *= 2.0**-20
+    for dt in (F16, BF16):
+        x = synth.act_bits(v, dt)
+        y = run_gemv(w4, codes, steps, x, dt)
+        yo, ao = oracle.gemv(codes, steps, N, K, x, dt)
+        assert within_bound(y, yo, ao)[0], dt
+
+
 def test_gemv_config_single_2048x1536_f16(w4):
     """Single W4A16 GEMV: 2048 x 1536, fp16 x, seed 0 -- every output."""
     rng = np.random.default_rng(0)

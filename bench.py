@@ -211,7 +211,7 @@ def extra_sweep(w4, torch, np, synth, timer, reps: int = 20):
     x0 = torch.from_numpy(synth.activations(np.random.default_rng(0), 1536, synth.F16).view(np.int16)
                           ).cuda().view(torch.float16)
     desc = w4.w4_chain_desc(mats, ys)
-    sync = w4.w4_chain_sync()
+    sync = w4.w4_chain_sync(len(shapes))
     chain = timer.per_call(lambda i: w4.w4_gemv_chain(desc, x0, sync), reps)
     err = int(sync[2].item())
 

@@ -38,7 +38,6 @@ W4_MAX_K_SMALLM = 16384
 W4_MAX_K_CHAIN = 8192
 W4_MAX_M = 16
 W4_MAX_TOPK = 32
-W4_CHAIN_SYNC_BYTES = 131328
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with bit_weight_only_02_amd/build.py "
@@ -57,7 +56,7 @@ _SIGNATURES = {
                         _P, _I32, _I32, _P, _P, _P, _P, _P],
     "w4_embed_gather": [_P, _P, _I32, _I32, _P, _I32, _P, _P, _P],
     "w4_rms_renorm": [_P, _I64, _I32, _I32, _P, _I64, _I32, _P],
-    "w4_gemv_chain": [_P, _I32, _P, _P, _P],
+    "w4_gemv_chain": [_P, _I32, _P, _P, _I64, _P],
     "w4_probe_stream": [_P, _I64, _P, _P],
 }
 for _name, _args in _SIGNATURES.items():
@@ -202,16 +201,23 @@ def w4_chain_desc(mats, ys):
     return torch.tensor(rec, dtype=torch.int64).cuda()
 
 
-def w4_chain_sync(device="cuda"):
-    """A zeroed sync buffer for w4_gemv_chain."""
-    return torch.zeros(W4_CHAIN_SYNC_BYTES // 4, dtype=torch.int32, device=device)
+def w4_chain_sync_bytes(n_mats: int) -> int:
+    """Bytes of the sync buffer of a chain of n_mats matrices
+    (W4_CHAIN_SYNC_BYTES(n_mats) of w4.h)."""
+    return 256 + n_mats * 65536
+
+
+def w4_chain_sync(n_mats: int, device="cuda"):
+    """A zeroed sync buffer for a w4_gemv_chain of n_mats matrices."""
+    return torch.zeros(w4_chain_sync_bytes(n_mats) // 4, dtype=torch.int32, device=device)
 
 
 def w4_gemv_chain(desc, x0, sync, stream=None):
     """Run the chain described by ``desc`` (from w4_chain_desc) on fp16 ``x0``."""
     if x0.dtype != torch.float16:
         raise TypeError("x0 must be float16")
-    _check(lib.w4_gemv_chain(_ptr(desc), desc.shape[0], _ptr(x0), _ptr(sync), _stream(stream)),
+    _check(lib.w4_gemv_chain(_ptr(desc), desc.shape[0], _ptr(x0), _ptr(sync),
+                             sync.numel() * sync.element_size(), _stream(stream)),
            "w4_gemv_chain")
 
 

@@ -242,15 +242,18 @@ int w4_moe_gemv_ids(const uint32_t *codes_base, const uint16_t *steps_base,
 }
 
 int w4_gemv_chain(const w4_chain_mat *desc, int32_t n_mats, const uint16_t *x0, void *sync,
-                  void *stream) {
+                  int64_t sync_bytes, void *stream) {
     int st;
     if (n_mats < 1) return fail(W4_ERR_INVALID_ARG, "n_mats must be >= 1");
     if (!desc || !x0 || !sync) return fail(W4_ERR_INVALID_ARG, "null desc/x0/sync");
+    if (sync_bytes < W4_CHAIN_SYNC_BYTES(n_mats))
+        return fail(W4_ERR_INVALID_ARG, "sync buffer of %lld bytes, %lld needed", (long long)sync_bytes,
+                    (long long)W4_CHAIN_SYNC_BYTES(n_mats));
     if (!aligned(desc, 8) || !aligned(x0, 16) || !aligned(sync, 16))
         return fail(W4_ERR_ALIGNMENT, "desc, x0 or sync misaligned");
     if ((st = device_ready())) return st;
     if (forced_launch_error()) return fail(W4_ERR_HIP, "forced launch error (test hook)");
-    // W4_CHAIN_SPIN_LIMIT bounds each barrier wait (polls); tests set it tiny to
+    // W4_CHAIN_SPIN_LIMIT bounds each wait for exchange cells (read rounds); tests set it tiny to
     // exercise the timeout path without a hang.
     unsigned spin = 1u << 22;
     if (const char *e = getenv("W4_CHAIN_SPIN_LIMIT")) spin = (unsigned)strtoul(e, nullptr, 10);

@@ -5,28 +5,32 @@
 // hundreds of small kernels and that launching them one by one costs more than
 // running them; its tip "Merge the Small Projections" merges q/k/v and gate/up
 // into one matrix each.  Here the whole chain of merged matrices runs inside
-// one kernel: every workgroup stays resident, takes its share of the rows of
-// matrix i, and a grid-wide barrier separates matrix i from matrix i+1 (whose
-// input is the renormalised output of matrix i and so needs all of it).
+// one kernel: every workgroup stays resident and takes its share of the rows
+// of matrix i; matrix i+1 needs all of the renormalised output of matrix i.
+//
+// Exchange.  There is no separate grid barrier: every output that the next
+// matrix needs is published as one 8-byte cell {value, tag} (a single store),
+// the tag naming the call and the step.  A consumer reads the cells it needs
+// and accepts each one whose tag is the expected one; cells with an older tag
+// are read again (bounded; a timeout sets the error word).  One round trip
+// through memory thus both waits for the producers and brings their values.
+// Each step has its own cell region, so a fast workgroup can never overwrite
+// values that a slow one has yet to read.
 //
 // Per step i (one workgroup of eight waves per CU; workgroup b owns the
 // contiguous row block [b*ceil(N/nwg), ...) of every matrix):
-//   1. input: x0 for the first matrix, else the leading K entries of the
-//      previous output divided by their RMS and rounded to fp16 (the same
-//      arithmetic as w4_rms_renorm, bit for bit), read with agent-coherent
-//      16-byte loads all issued at once;
-//   2. waves 0..3 compute the block's rows of matrix i from an LDS weight
-//      buffer (codes and steps staged there in advance) and store them with
-//      agent-scope stores, while waves 4..7 stage the block of matrix i+1 into
-//      the other buffer with direct-to-LDS loads, so the weight stream of the
-//      next step overlaps this step's compute, the barrier and the next
-//      renormalisation;
-//   3. the barrier: each workgroup stores its generation into its own flag
-//      and wave 0 polls all flags (agent scope, bounded; no contended
-//      read-modify-write).
-// Outputs of every step are read back with agent-scope loads, which see the
-// stores of workgroups on other XCDs.  Rows beyond what one buffer holds are
-// read from memory directly.
+//   1. input: x0 for the first matrix; else waves 0..3 read the leading K
+//      cells of step i-1 (agent-coherent loads), the workgroup takes their sum
+//      of squares in fp64 in the fixed order of w4_rms_renorm and writes
+//      u / rms rounded to fp16 into LDS (bit for bit what w4_rms_renorm gives);
+//      meanwhile waves 6..7 wait for their copy of this step's weights;
+//   2. waves 6..7 request the next step's weight block into the other LDS
+//      buffer (direct-to-LDS loads that only they wait for, at the start of
+//      the next step: neither the exchange loads of waves 0..3 nor any row
+//      computation queue behind weight traffic);
+//   3. waves 0..5 compute the block's rows from LDS and store y, and the
+//      cells of the rows the next step needs.
+// The descriptors are copied into LDS once (the first kDescCache of them).
 #include <cstdio>
 #include <cstdlib>
 #include <type_traits>
@@ -47,19 +51,19 @@ struct ChainMat {
 static_assert(sizeof(ChainMat) == sizeof(w4_chain_mat), "descriptor layout");
 
 constexpr int kChainThreads = 512;  // eight waves
-constexpr int kComputeWaves = 7;    // waves 0..6 compute rows (0..3 also renormalise); 7 copies weights
+constexpr int kChainWaves = kChainThreads / 64;
+constexpr int kPollThreads = 256;   // waves 0..3 read the exchange cells and renormalise
+constexpr int kCopyWave0 = 6;       // waves 6..7 copy weight blocks and compute nothing
+constexpr int kComputeWaves = kCopyWave0;  // waves 0..5 compute rows
+constexpr int kDescCache = 256;     // descriptors kept in LDS
 constexpr int kChainMaxK = 8192;
 constexpr int kWeightBuf = 64 * 1024;  // bytes of each of the two LDS weight buffers
-constexpr int kCopyEarly = 16;         // copy instructions per wave issued before the rows
-// sync buffer: word 0 exit counter, word 1 epoch (barrier generations used by
-// earlier calls), word 2 error; from word 64 on, one arrival flag per
-// workgroup (the generation it last reached), kFlagStride words apart.
-// Each flag has a 256-byte line of its own: the pollers' reads then spread over
-// many memory channels instead of queueing on the one or two that would hold
-// a packed array (measured: 3.0 against 3.8 us per barrier at 256 workgroups).
-constexpr int kSyncExit = 0, kSyncEpoch = 1, kSyncError = 2, kSyncFlags = 64;
-constexpr int kFlagStride = 64;  // words
-constexpr int kMaxChainWG = (W4_CHAIN_SYNC_BYTES / 4 - kSyncFlags) / kFlagStride;
+// sync buffer: bytes [0, 256) a header (word 0 exit counter, word 1 epoch --
+// the tags used by earlier calls --, word 2 error); from byte 256, one region
+// of kChainMaxK 8-byte cells per matrix.
+constexpr int kSyncExit = 0, kSyncEpoch = 1, kSyncError = 2;
+constexpr long kExchOffset = 256, kExchBytes = (long)kChainMaxK * 8;
+static_assert(W4_CHAIN_SYNC_BYTES(1) == kExchOffset + kExchBytes, "sync layout");
 
 __device__ __forceinline__ float load_agent(const float *p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -107,64 +111,66 @@ __device__ __forceinline__ RowBlock chain_block(const ChainMat &m, int nwg) {
         const int words = b.lds_steps ? (rows * G / 2 + 63) / 64 * 64 : 0;
         return chunks * 16 + words * 4;
     };
-    int n = min(b.re - b.rb, kWeightBuf / (G * 18));
+    // (rows are staged only together with their steps)
+    int n = b.lds_steps ? min(b.re - b.rb, kWeightBuf / (G * 18)) : 0;
     while (n > 0 && bytes(n) > kWeightBuf) --n;
     b.nlds = n;
     b.steps_chunk = (n * G + 63) / 64 * 64;
     return b;
 }
 
-// Copy waves: request the staged part of a block into `buf` (direct-to-LDS
-// loads; every lane moves 16 bytes of codes or 4 bytes of steps, and the last
-// instruction of each run lands its surplus lanes in the rounding padding).
-// Instructions [first, last) of the run are issued (codes first, then steps),
-// so that the copy can be split around a barrier.
-__device__ __forceinline__ void chain_copy(const ChainMat &m, const RowBlock &b, uint4 *buf,
-                                           int first, int last) {
-    const int w = (threadIdx.x >> 6) - kComputeWaves, lane = threadIdx.x & 63;
-    constexpr int nw = kChainThreads / 64 - kComputeWaves;
+// Copy waves: request the staged part of a block into `buf` with
+// direct-to-LDS loads (every lane moves 16 bytes of codes or 4 bytes of steps;
+// the last instruction of each run lands its surplus lanes in the rounding
+// padding).  Written with the asm form of the load, so that the compiler adds
+// no waits for it; the copy waves wait for it themselves (vmcnt 0) before the
+// workgroup barrier that precedes the block's use.
+__device__ __forceinline__ void chain_copy(const ChainMat &m, const RowBlock &b, uint4 *buf) {
+    const int w = (threadIdx.x >> 6) - kCopyWave0, lane = threadIdx.x & 63;
+    constexpr int nw = kChainWaves - kCopyWave0;
     const int G = m.K >> 5;
     const int n = b.nlds * G;
     if (n == 0) return;
-    int k = 0;  // this wave's instruction count over the whole run
     const uint4 *src = reinterpret_cast<const uint4 *>(m.codes) + (long)b.rb * G;
-    for (int c0 = w * 64; c0 < n; c0 += nw * 64, ++k) {
-        if (k < first) continue;
-        if (k >= last) return;
-        const int c = min(c0 + lane, n - 1);
-        __builtin_amdgcn_global_load_lds(
-            (const __attribute__((address_space(1))) void *)(src + c),
-            (__attribute__((address_space(3))) void *)(buf + c0), 16, 0, 0);
-    }
+    for (int c0 = w * 64; c0 < n; c0 += nw * 64) lds_dma16(src + min(c0 + lane, n - 1), buf + c0);
     if (b.lds_steps) {
         const uint32_t *ssrc = reinterpret_cast<const uint32_t *>(m.steps + (long)b.rb * G);
         uint32_t *sdst = reinterpret_cast<uint32_t *>(buf + b.steps_chunk);
         const int nd = n / 2;
-        for (int d0 = w * 64; d0 < nd; d0 += nw * 64, ++k) {
-            if (k < first) continue;
-            if (k >= last) return;
-            const int d = min(d0 + lane, nd - 1);
-            __builtin_amdgcn_global_load_lds(
-                (const __attribute__((address_space(1))) void *)(ssrc + d),
-                (__attribute__((address_space(3))) void *)(sdst + d0), 4, 0, 0);
-        }
+        for (int d0 = w * 64; d0 < nd; d0 += nw * 64) lds_dma4(ssrc + min(d0 + lane, nd - 1), sdst + d0);
     }
 }
 
-// Compute waves: the rows of the block, L lanes per row, NG groups per lane;
-// codes and steps from the LDS buffer for staged rows, else from memory.
+// One exchange cell {value, tag}, published with a single 8-byte store that
+// agent-scope loads on any XCD see.
+__device__ __forceinline__ void store_cell(uint2 *cells, int row, float v, unsigned tag) {
+    const uint64_t c = (uint64_t)__float_as_uint(v) | ((uint64_t)tag << 32);
+    __hip_atomic_store(reinterpret_cast<uint64_t *>(cells + row), c, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Where the rows of one step go: y, and the cells of rows < k_next (the
+// leading entries the next step reads; k_next 0 for the last step).
+struct RowSink {
+    uint2 *cells;
+    int k_next;
+    unsigned tag;
+};
+
+// Computing waves: the rows of the block, L lanes per row, NG groups per lane;
+// rows staged in the LDS buffer first (a loop with no global loads), then any
+// rows read from memory.
 template <int L, int NG>
 __device__ __forceinline__ void chain_rows(const ChainMat &m, const RowBlock &b, const uint4 *buf,
-                                           const uint16_t *raw) {
+                                           const uint16_t *xin, const RowSink &sink) {
     constexpr int SLOTS = kWave / L;
     const int G = m.K >> 5;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int l = lane % L, slot = lane / L;
-    const uint4 *codes = reinterpret_cast<const uint4 *>(m.codes);
     const uint16_t *lsteps = reinterpret_cast<const uint16_t *>(buf + b.steps_chunk);
-    // this wave's activations, already in pair order in LDS -> registers
+    // the activations, already in pair order in LDS -> registers
     h2 xr[NG][16];
-    const uint4 *r16 = reinterpret_cast<const uint4 *>(raw);
+    const uint4 *r16 = reinterpret_cast<const uint4 *>(xin);
 #pragma unroll
     for (int i = 0; i < NG; ++i) {
         const int g = l + i * L;
@@ -177,8 +183,6 @@ __device__ __forceinline__ void chain_rows(const ChainMat &m, const RowBlock &b,
             xr[i][w * 4 + 3] = as_h2(v.w);
         }
     }
-    // Rows [rb, rb + nlds) from the buffer, the rest from memory (two loops,
-    // so that every load has a known address space).
     auto finish = [&](int row, const uint4 (&q)[NG], const uint32_t (&sv)[NG]) __attribute__((always_inline)) {
         float acc = 0.0f;
 #pragma unroll
@@ -187,7 +191,13 @@ __device__ __forceinline__ void chain_rows(const ChainMat &m, const RowBlock &b,
             acc = (g < G) ? __builtin_fmaf(group_dot(q[i], xr[i]), bf16_to_f32(sv[i]), acc) : acc;
         }
         acc = lane_group_sum<L>(acc);
-        if (l == L - 1 && row < b.re) store_y(m.y, m.N, row, __builtin_ldexpf(acc, kGroupDotExp));
+        if (l == L - 1 && row < b.re) {
+            const float v = __builtin_ldexpf(acc, kGroupDotExp);
+            // (a global store: through the generic pointer it would be a flat
+            // store, which every later LDS read would have to wait for)
+            ((__attribute__((address_space(1))) float *)m.y)[row] = v;
+            if (row < sink.k_next) store_cell(sink.cells, row, v, sink.tag);
+        }
     };
     const int staged_end = b.rb + b.nlds;
     for (int r0 = b.rb; r0 < staged_end; r0 += kComputeWaves * SLOTS) {
@@ -196,111 +206,183 @@ __device__ __forceinline__ void chain_rows(const ChainMat &m, const RowBlock &b,
         uint4 q[NG];
         uint32_t sv[NG];
 #pragma unroll
-        for (int i = 0; i < NG; ++i) q[i] = buf[rl * G + min(l + i * L, G - 1)];
-        if (b.lds_steps) {
-#pragma unroll
-            for (int i = 0; i < NG; ++i) sv[i] = lsteps[rl * G + min(l + i * L, G - 1)];
-        } else {
-#pragma unroll
-            for (int i = 0; i < NG; ++i) sv[i] = load_global_u16(m.steps, (long)(b.rb + rl) * G + min(l + i * L, G - 1));
+        for (int i = 0; i < NG; ++i) {
+            const int g = min(l + i * L, G - 1);
+            q[i] = buf[rl * G + g];
+            sv[i] = lsteps[rl * G + g];
         }
         finish(row < staged_end ? row : b.re, q, sv);
     }
-    for (int r0 = staged_end; r0 < b.re; r0 += kComputeWaves * SLOTS) {
-        const int row = r0 + wave * SLOTS + slot;
-        const int rc = min(row, b.re - 1);
-        uint4 q[NG];
-        uint32_t sv[NG];
+    if (staged_end < b.re) {
+        const uint4 *codes = reinterpret_cast<const uint4 *>(m.codes);
+        for (int r0 = staged_end; r0 < b.re; r0 += kComputeWaves * SLOTS) {
+            const int row = r0 + wave * SLOTS + slot;
+            const int rc = min(row, b.re - 1);
+            uint4 q[NG];
+            uint32_t sv[NG];
 #pragma unroll
-        for (int i = 0; i < NG; ++i) {
-            const int g = min(l + i * L, G - 1);
-            q[i] = load_global_u4(codes, (long)rc * G + g);
-            sv[i] = load_global_u16(m.steps, (long)rc * G + g);
+            for (int i = 0; i < NG; ++i) {
+                const int g = min(l + i * L, G - 1);
+                q[i] = load_global_u4(codes, (long)rc * G + g);
+                sv[i] = load_global_u16(m.steps, (long)rc * G + g);
+            }
+            finish(row, q, sv);
         }
-        finish(row, q, sv);
     }
 }
 
 __device__ __forceinline__ void chain_rows_any(const ChainMat &m, const RowBlock &b, const uint4 *buf,
-                                               const uint16_t *raw) {
+                                               const uint16_t *xin, const RowSink &sink) {
+    if (b.re <= b.rb) return;
+    // Lanes per row from the row length alone: 16 lanes up to 64 groups, 32
+    // up to 128, else 64.  (Choosing by the least work per lane -- 64 lanes
+    // for a block of six 64-group rows, say -- measured slower over the whole
+    // decode sweep: passes are latency-bound, not arithmetic-bound.)
     const int G = m.K >> 5;
     const int L = G <= 64 ? 16 : (G <= 128 ? 32 : 64);
     const int NG = (G + L - 1) / L;
     switch (__builtin_amdgcn_readfirstlane(L * 8 + NG)) {
-        case 16 * 8 + 1: chain_rows<16, 1>(m, b, buf, raw); break;
-        case 16 * 8 + 2: chain_rows<16, 2>(m, b, buf, raw); break;
-        case 16 * 8 + 3: chain_rows<16, 3>(m, b, buf, raw); break;
-        case 16 * 8 + 4: chain_rows<16, 4>(m, b, buf, raw); break;
-        case 32 * 8 + 3: chain_rows<32, 3>(m, b, buf, raw); break;
-        case 32 * 8 + 4: chain_rows<32, 4>(m, b, buf, raw); break;
-        case 64 * 8 + 3: chain_rows<64, 3>(m, b, buf, raw); break;
-        default: chain_rows<64, 4>(m, b, buf, raw); break;
+        case 16 * 8 + 1: chain_rows<16, 1>(m, b, buf, xin, sink); break;
+        case 16 * 8 + 2: chain_rows<16, 2>(m, b, buf, xin, sink); break;
+        case 16 * 8 + 3: chain_rows<16, 3>(m, b, buf, xin, sink); break;
+        case 16 * 8 + 4: chain_rows<16, 4>(m, b, buf, xin, sink); break;
+        case 32 * 8 + 3: chain_rows<32, 3>(m, b, buf, xin, sink); break;
+        case 32 * 8 + 4: chain_rows<32, 4>(m, b, buf, xin, sink); break;
+        case 64 * 8 + 3: chain_rows<64, 3>(m, b, buf, xin, sink); break;
+        default: chain_rows<64, 4>(m, b, buf, xin, sink); break;
     }
 }
 
-// Wave 0: wait until every workgroup's flag has reached generation `gen`
-// (agent-coherent loads, all issued at once, one or more per lane), with a
-// bounded number of polls; a timeout sets the error word.  Returns 1 if the
-// chain must stop.
-__device__ __forceinline__ int chain_poll(unsigned *sync, unsigned gen, unsigned spin_limit, int nwg) {
-    const int lane = threadIdx.x;
-    const __amdgpu_buffer_rsrc_t fr = buffer_rsrc(sync + kSyncFlags, nwg * kFlagStride * 4);
-    unsigned it = 0;
-    int stop = 0;
-    for (;;) {
-        // lane l checks the flags of workgroups l, l+64, ... (one load each)
-        int behind = 0;
-        for (int f = lane; f < nwg; f += 64) {
-            const unsigned a = __builtin_amdgcn_raw_buffer_load_b32(fr, f * kFlagStride * 4, 0, 16);
-            // generations only grow; compare with wrap-around arithmetic
-            behind |= (int)(a - gen) < 0;
+// Waves 0..3: read the K cells of one region until every tag equals `tag`.
+// Thread t owns the 4-value chunks c = t, t+256, ... (the order of the sum of
+// squares) and re-reads only chunks not yet complete.  A bounded number of
+// rounds; a timeout (or an error raised elsewhere) returns 1.
+constexpr int kPollJ = kChainMaxK / 4 / kPollThreads;
+
+__device__ __forceinline__ int chain_read_cells(const uint2 *cells, int K, unsigned tag,
+                                                unsigned spin_limit, unsigned *sync,
+                                                float4 (&v)[kPollJ]) {
+    const int tid = threadIdx.x;
+    const __amdgpu_buffer_rsrc_t r = buffer_rsrc(cells, K * 8);
+    unsigned pend = 0;
+#pragma unroll
+    for (int j = 0; j < kPollJ; ++j) {
+        v[j] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        if (tid + kPollThreads * j < (K >> 2)) pend |= 1u << j;
+    }
+    for (unsigned it = 0;; ++it) {
+        uint4 a[kPollJ], b[kPollJ];
+#pragma unroll
+        for (int j = 0; j < kPollJ; ++j) {
+            if (pend & (1u << j)) {
+                const int off = (tid + kPollThreads * j) * 32;
+                a[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 16));
+                b[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off + 16, 0, 16));
+            }
         }
-        if (!wave_or_i32(behind)) break;
-        if (++it > spin_limit) {
-            if (lane == 0)
+#pragma unroll
+        for (int j = 0; j < kPollJ; ++j) {
+            if ((pend & (1u << j)) && a[j].y == tag && a[j].w == tag && b[j].y == tag && b[j].w == tag) {
+                v[j] = make_float4(__uint_as_float(a[j].x), __uint_as_float(a[j].z),
+                                   __uint_as_float(b[j].x), __uint_as_float(b[j].z));
+                pend &= ~(1u << j);
+            }
+        }
+        if (!wave_or_i32(pend != 0)) return 0;
+        if (it >= spin_limit || ((it & 63) == 63 && load_agent_u(sync + kSyncError) != 0)) {
+            if ((tid & 63) == 0)
                 __hip_atomic_store(sync + kSyncError, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            stop = 1;
-            break;
+            return 1;
         }
     }
-    return stop || load_agent_u(sync + kSyncError) != 0;
+}
+
+// Sum of squares over the poll waves' values, in the fixed order of
+// sum_squares_256 (thread t: chunks t, t+256, ... ascending; xor folds 32..1;
+// wave sums added in wave order) -- bit for bit the w4_rms_renorm value --
+// with a single workgroup barrier: the wave sums go to one of two LDS slots,
+// alternating from step to step, so a slot is rewritten only two barriers
+// after it was read.
+__device__ __forceinline__ double chain_sum_squares(int K, const float4 (&v)[kPollJ], double *red,
+                                                    bool active, int parity) {
+    const int tid = threadIdx.x;
+    double ss = 0.0;
+    if (active) {
+#pragma unroll
+        for (int j = 0; j < kPollJ; ++j) {
+            if (tid + kPollThreads * j < (K >> 2)) {
+                ss += (double)v[j].x * (double)v[j].x;
+                ss += (double)v[j].y * (double)v[j].y;
+                ss += (double)v[j].z * (double)v[j].z;
+                ss += (double)v[j].w * (double)v[j].w;
+            }
+        }
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off, kWave);
+    double *r = red + parity * 4;
+    if ((tid & 63) == 0 && tid < kPollThreads) r[tid >> 6] = ss;
+    lds_barrier();
+    return ((r[0] + r[1]) + r[2]) + r[3];
 }
 
 __global__ __launch_bounds__(kChainThreads) void chain_kernel(const ChainMat *__restrict__ desc,
                                                               int n, const uint16_t *__restrict__ x0,
                                                               unsigned *sync, unsigned spin_limit) {
     extern __shared__ uint4 smem[];
-    uint16_t *raw = reinterpret_cast<uint16_t *>(smem);   // kChainMaxK halves
+    uint16_t *xin = reinterpret_cast<uint16_t *>(smem);   // kChainMaxK halves, pair order
     uint4 *bufs = smem + (kChainMaxK * 2) / 16;            // two weight buffers
+    ChainMat *dtab = reinterpret_cast<ChainMat *>(bufs + 2 * (kWeightBuf / 16));
     __shared__ double dred[8];
-    __shared__ int stop_s;
+    __shared__ int stop_s, bad_s;
     const int nwg = gridDim.x;
     const int tid = threadIdx.x, wave = tid >> 6;
-    const bool copier = wave >= kComputeWaves;
+    const bool copier = wave >= kCopyWave0;
+    uint2 *regions = reinterpret_cast<uint2 *>(reinterpret_cast<char *>(sync) + kExchOffset);
+    // tags of this call continue from those of earlier calls
+    const unsigned epoch = load_agent_u(sync + kSyncEpoch);
 
-    // Every workgroup checks the descriptors (same answer everywhere).
-    bool ok = n >= 1;
-    for (int i = 0; i < n && ok; ++i) {
-        const ChainMat m = desc[i];
+    // Descriptors: the first kDescCache into an LDS table (entry i in slot
+    // i % kDescCache); later ones are brought in kDescCache/2 steps ahead of
+    // use (see the end of the step loop).  Every workgroup checks them all
+    // (same answer everywhere).
+    typedef const __attribute__((address_space(1))) uint32_t gword;
+    constexpr int kWords = sizeof(ChainMat) / 4;
+    gword *dsrc = (gword *)desc;
+    uint32_t *dwords = reinterpret_cast<uint32_t *>(dtab);
+    for (int k = tid; k < min(n, kDescCache) * kWords; k += kChainThreads) dwords[k] = dsrc[k];
+    if (tid == 0) {
+        stop_s = 0;
+        bad_s = n < 1;
+    }
+    auto load_desc = [&](int i) __attribute__((always_inline)) {
+        uint32_t w[kWords];
+#pragma unroll
+        for (int k = 0; k < kWords; ++k) w[k] = dsrc[(long)i * kWords + k];
+        ChainMat m;
+        __builtin_memcpy(&m, w, sizeof(m));
+        return m;
+    };
+    for (int i = tid; i < n; i += kChainThreads) {
+        const ChainMat m = load_desc(i);
+        const int prevN = i > 0 ? load_desc(i - 1).N : 0;
         if (m.N < 1 || m.K < 32 || (m.K & 31) || m.K > kChainMaxK || !m.codes || !m.steps || !m.y ||
             (reinterpret_cast<uintptr_t>(m.codes) & 15) || (reinterpret_cast<uintptr_t>(m.y) & 15) ||
-            (i > 0 && m.K > desc[i - 1].N))
-            ok = false;
+            (i > 0 && m.K > prevN))
+            bad_s = 1;
     }
-    if (nwg > kMaxChainWG) ok = false;
-    // barrier generations of this call continue from those of earlier calls
-    const unsigned epoch = load_agent_u(sync + kSyncEpoch);
-    if (ok) {
-        if (copier) chain_copy(desc[0], chain_block(desc[0], nwg), bufs, 0, 1 << 30);
+    __syncthreads();
+    auto get = [&](int i) __attribute__((always_inline)) { return dtab[i % kDescCache]; };
+    if (!bad_s) {
+        if (copier) chain_copy(get(0), chain_block(get(0), nwg), bufs);
         for (int i = 0; i < n; ++i) {
-            const ChainMat m = desc[i];
+            const ChainMat m = get(i);
             const int K = m.K;
-            // 1. input into LDS (raw fp16)
-            uint4 *r16 = reinterpret_cast<uint4 *>(raw);
-            // (both paths leave each 8-value block in the pair order
-            // (x0,x4)(x1,x5)(x2,x6)(x3,x7) that the unpack of a packed word uses)
+            // 1. input into LDS, in the pair order (x0,x4)(x1,x5)(x2,x6)(x3,x7)
+            // of each 8-value block that the unpack of a packed word uses
             if (i == 0) {
                 const uint4 *x16 = reinterpret_cast<const uint4 *>(x0);
+                uint4 *r16 = reinterpret_cast<uint4 *>(xin);
                 for (int c = tid; c < (K >> 3); c += kChainThreads) {
                     const uint4 v = x16[c];
                     r16[c] = make_uint4(__builtin_amdgcn_perm(v.z, v.x, 0x05040100u),
@@ -308,28 +390,30 @@ __global__ __launch_bounds__(kChainThreads) void chain_kernel(const ChainMat *__
                                         __builtin_amdgcn_perm(v.w, v.y, 0x05040100u),
                                         __builtin_amdgcn_perm(v.w, v.y, 0x07060302u));
                 }
+                if (copier) wait_vmcnt_mem<0>();  // block 0 landed
             } else {
-                // previous output: the chunks of the canonical 256-thread
-                // order, all requested at once with agent-coherent loads
-                const __amdgpu_buffer_rsrc_t pr = buffer_rsrc(desc[i - 1].y, K * 4);
-                constexpr int J = kChainMaxK / 4 / 256;
-                float4 v[J];
-                const bool rn = tid < 256;
+                float4 v[kPollJ];
+                const bool rn = tid < kPollThreads;
+                if (rn) {
+                    const int stop = chain_read_cells(regions + (long)(i - 1) * kChainMaxK, K,
+                                                      epoch + (unsigned)i, spin_limit, sync, v);
+                    if (stop) stop_s = 1;
+                } else {
 #pragma unroll
-                for (int j = 0; j < J; ++j) {
-                    const int c = tid + 256 * j;
-                    v[j] = (rn && c < (K >> 2)) ? load_coherent_f4(pr, c * 16)
-                                                : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+                    for (int j = 0; j < kPollJ; ++j) v[j] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+                    if (copier) wait_vmcnt_mem<0>();  // this step's block landed
                 }
-                const double inv = renorm_scale(sum_squares_256_regs(K, v, dred, rn), K);
+                // (its barriers also publish stop_s)
+                const double inv = renorm_scale(chain_sum_squares(K, v, dred, rn, i & 1), K);
+                if (stop_s) break;
                 if (rn) {
 #pragma unroll
-                    for (int j = 0; j < J; ++j) {
-                        const int c = tid + 256 * j;
+                    for (int j = 0; j < kPollJ; ++j) {
+                        const int c = tid + kPollThreads * j;
                         if (c < (K >> 2)) {
                             // chunk c holds values 4(c&1)..+3 of block c>>1:
                             // value e of a block sits at position 2(e&3) + (e>>2)
-                            uint16_t *blk = raw + (c >> 1) * 8 + (c & 1);
+                            uint16_t *blk = xin + (c >> 1) * 8 + (c & 1);
                             blk[0] = renorm_value(v[j].x, inv, 0);
                             blk[2] = renorm_value(v[j].y, inv, 0);
                             blk[4] = renorm_value(v[j].z, inv, 0);
@@ -338,43 +422,31 @@ __global__ __launch_bounds__(kChainThreads) void chain_kernel(const ChainMat *__
                     }
                 }
             }
-            // input staged, and this step's weights landed (the copy waves
-            // have no loads outstanding past this point)
-            __syncthreads();
-            // 2. copy waves fetch the next step's block; compute waves run this one
-            // (the copy wave issues the first kCopyEarly instructions of the next
-            // block now and the rest after the pre-flag barrier below, so that
-            // it reaches that barrier without delay)
-            uint4 *next_buf = bufs + ((i + 1) & 1) * (kWeightBuf / 16);
+            // input staged, and this step's weights landed
+            lds_barrier();
             if (copier) {
-                if (i + 1 < n) chain_copy(desc[i + 1], chain_block(desc[i + 1], nwg), next_buf, 0, kCopyEarly);
+                // 2. the copy waves request the next step's block
+                if (i + 1 < n)
+                    chain_copy(get(i + 1), chain_block(get(i + 1), nwg), bufs + ((i + 1) & 1) * (kWeightBuf / 16));
             } else {
-                chain_rows_any(m, chain_block(m, nwg), bufs + (i & 1) * (kWeightBuf / 16), raw);
+                // 3. this step's rows
+                RowSink sink;
+                sink.cells = regions + (long)i * kChainMaxK;
+                sink.k_next = i + 1 < n ? get(i + 1).K : 0;
+                sink.tag = epoch + (unsigned)(i + 1);
+                chain_rows_any(m, chain_block(m, nwg), bufs + (i & 1) * (kWeightBuf / 16), xin, sink);
+                // refill: descriptor i + kDescCache/2 into the slot of i - kDescCache/2
+                const int j = i + kDescCache / 2;
+                if (wave == kComputeWaves - 1 && j >= kDescCache && j < n && (tid & 63) < kWords)
+                    dwords[(j % kDescCache) * kWords + (tid & 63)] = dsrc[(long)j * kWords + (tid & 63)];
             }
-            if (i + 1 == n) break;
-            // 3. grid barrier before the next step reads this output
-            if (!copier) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // outputs stored
-            lds_barrier();
-            if (tid == 0)
-                __hip_atomic_store(sync + kSyncFlags + blockIdx.x * kFlagStride, epoch + (unsigned)(i + 1),
-                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            if (copier) {
-                chain_copy(desc[i + 1], chain_block(desc[i + 1], nwg), next_buf, kCopyEarly, 1 << 30);
-                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // next block landed
-            }
-            if (wave == 0) {
-                const int stop = chain_poll(sync, epoch + (unsigned)(i + 1), spin_limit, nwg);
-                if (tid == 0) stop_s = stop;
-            }
-            lds_barrier();
-            if (stop_s) break;
         }
     } else if (blockIdx.x == 0 && tid == 0) {
         __hip_atomic_store(sync + kSyncError, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    // Exit: the last workgroup out (every other one is past its last barrier
-    // and has read the epoch) advances the epoch past this call's generations
-    // and returns the exit counter to zero.
+    // Exit: the last workgroup out (every other one has finished and has read
+    // the epoch) advances the epoch past this call's tags and returns the exit
+    // counter to zero.
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     lds_barrier();
     if (tid == 0) {
@@ -388,14 +460,14 @@ __global__ __launch_bounds__(kChainThreads) void chain_kernel(const ChainMat *__
     }
 }
 
-size_t chain_lds_bytes() { return (size_t)kChainMaxK * 2 + 2 * (size_t)kWeightBuf; }
+size_t chain_lds_bytes() { return (size_t)kChainMaxK * 2 + 2 * (size_t)kWeightBuf + kDescCache * sizeof(ChainMat); }
 
 hipError_t launch_chain(const void *desc, int n, const uint16_t *x0, void *sync, unsigned spin_limit,
                         hipStream_t stream) {
     // One workgroup per CU, all resident together on an otherwise idle device
     // (the occupancy check makes sure one fits per CU).  A plain launch: if
-    // some workgroups could not start while others wait, the bounded barrier
-    // waits end with the timeout error instead of a hang.
+    // some workgroups could not start while others wait, the bounded waits for
+    // their cells end with the timeout error instead of a hang.
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
@@ -405,7 +477,7 @@ hipError_t launch_chain(const void *desc, int n, const uint16_t *x0, void *sync,
     const size_t lds = chain_lds_bytes();
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, chain_kernel, kChainThreads, lds);
     if (e != hipSuccess) return e;
-    if (per_cu < 1 || cus > kMaxChainWG) return hipErrorInvalidConfiguration;
+    if (per_cu < 1) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(chain_kernel, dim3(cus), dim3(kChainThreads), lds, stream,
                        static_cast<const ChainMat *>(desc), n, x0, static_cast<unsigned *>(sync),
                        spin_limit);

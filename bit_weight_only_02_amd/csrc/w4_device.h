@@ -231,6 +231,10 @@ __device__ __forceinline__ double renorm_scale(double ss, int K) {
 }
 
 __device__ __forceinline__ uint16_t renorm_value(float u, double inv, int dt) {
+    // Two separate roundings, fp64 -> fp32 -> 16 bits: with contraction allowed
+    // the compiler fuses them into one software fp64 -> fp16 conversion (some
+    // forty instructions, and a different rounding).
+#pragma clang fp contract(off)
     const float q = (float)((double)u * inv);
     return dt == 0 ? __builtin_bit_cast(uint16_t, (_Float16)q) : __builtin_bit_cast(uint16_t, (__bf16)q);
 }
@@ -364,19 +368,32 @@ __device__ __forceinline__ void stage_issue(const uint16_t *__restrict__ x, int 
 // (wait_vmcnt_mem).  Given the builtin, the compiler's wait insertion treats
 // every later LDS read as possibly reading this load's destination and waits for
 // all outstanding loads before it, which would drain the pipeline each step.
-// Lane i writes 16 bytes at lds + 16*i; `lds` must be wave-uniform.  M0 carries
+// Lane i writes 16 bytes at lds + 16*i; `lds` must be wave-uniform; the loads
+// are marked non-temporal (weights are read once).  M0 carries
 // the LDS address and is set here; none of the kernels using this keeps a
 // compiler-managed M0 value live across it.
 __device__ __forceinline__ void lds_dma16(const void *g, void *lds) {
-    const uint32_t m = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void *)lds;
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(m) : "memory");
+    const uint32_t m = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) void *)lds);
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off nt" ::"v"(g), "s"(m) : "memory");
+}
+
+// The 4-byte form (lane i writes 4 bytes at lds + 4*i).
+__device__ __forceinline__ void lds_dma4(const void *g, void *lds) {
+    const uint32_t m = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) void *)lds);
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off nt" ::"v"(g), "s"(m) : "memory");
 }
 
 // The same load with a wave-uniform 64-bit base in scalar registers and a
 // per-lane 32-bit byte offset, marked non-temporal (the data are read once:
 // measured on MI355X, streaming reads run markedly faster with this hint).
 __device__ __forceinline__ void lds_dma16_nt(const void *sbase, uint32_t voff, void *lds) {
-    const uint32_t m = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void *)lds;
+    // (readfirstlane returns a signed int: widen each half as unsigned, or the
+    // low half would be sign-extended into the high one)
+    const uint64_t b = (uint64_t)(uintptr_t)sbase;
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+    sbase = (const void *)(uintptr_t)(((uint64_t)hi << 32) | (uint64_t)lo);
+    const uint32_t m = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) void *)lds);
     asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1 nt" ::"v"(voff), "s"(sbase), "s"(m)
                  : "memory");
 }

@@ -179,19 +179,21 @@ int w4_rms_renorm(const float *v, int64_t ldv, int32_t K, int32_t rows, void *ou
  * mapping (and so the order of its fp32 sums) is chosen per matrix for the
  * whole-chip launch and can differ from w4_gemv's.
  *   desc: DEVICE array of n_mats records (it is read by the kernel).
- *   sync: device buffer of W4_CHAIN_SYNC_BYTES bytes, all zero before the
- *         first call and then owned by the chain (it carries barrier
- *         generations from call to call; reuse it only for chains run one
- *         after another on one stream).  Word 2 is an error word written by
- *         the kernel: 1 if a grid barrier timed out (results incomplete), 2 if
- *         a record was invalid (N < 1, K not a multiple of 32, K larger than
- *         W4_MAX_K_CHAIN or than the previous N, a null or misaligned
- *         pointer; nothing computed).  The caller clears it after reading it.
+ *   sync: device buffer of sync_bytes >= W4_CHAIN_SYNC_BYTES(n_mats) bytes,
+ *         16-byte aligned, all zero before the first call and then owned by
+ *         the chain (it carries the tags of earlier calls and one region of
+ *         exchange cells per matrix; reuse it only for chains run one after
+ *         another on one stream).  Word 2 is an error word written by the
+ *         kernel: 1 if a wait for another workgroup's outputs timed out
+ *         (results incomplete), 2 if a record was invalid (N < 1, K not a
+ *         multiple of 32, K larger than W4_MAX_K_CHAIN or than the previous N,
+ *         a null or misaligned pointer; nothing computed).  The caller clears
+ *         it after reading it.
  * One workgroup per CU, all resident at once on an otherwise idle device; if
- * they cannot all run together the bounded barrier waits end with error 1
- * rather than a hang.  Concurrent chains must use different sync buffers.
+ * they cannot all run together the bounded waits end with error 1 rather than
+ * a hang.  Concurrent chains must use different sync buffers.
  */
-#define W4_CHAIN_SYNC_BYTES 131328 /* 256 + 512 flags of 256 bytes */
+#define W4_CHAIN_SYNC_BYTES(n_mats) (256 + (int64_t)(n_mats) * 65536)
 typedef struct {
     const uint32_t *codes; /* device, 16-byte aligned */
     const uint16_t *steps; /* device */
@@ -200,7 +202,7 @@ typedef struct {
     int32_t K;
 } w4_chain_mat;
 int w4_gemv_chain(const w4_chain_mat *desc, int32_t n_mats, const uint16_t *x0, void *sync,
-                  void *stream);
+                  int64_t sync_bytes, void *stream);
 
 /*
  * Plain streaming read of `bytes` bytes (a multiple of 16, buf 16-byte aligned):

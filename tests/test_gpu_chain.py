@@ -65,7 +65,7 @@ def test_chain_ragged_shapes(w4):
     rng = np.random.default_rng(1)
     x0 = dev_act(synth.activations(rng, 64, F16), F16)
     desc = w4.w4_chain_desc(mats, ys)
-    sync = w4.w4_chain_sync()
+    sync = w4.w4_chain_sync(len(shapes))
     w4.w4_gemv_chain(desc, x0, sync)
     torch.cuda.synchronize()
     assert sync[0].item() == 0 and sync[2].item() == 0
@@ -87,7 +87,7 @@ def test_chain_decode_sweep_35_layers(w4):
     ys = [torch.empty(N, device="cuda") for N, _ in shapes]
     x0 = dev_act(synth.activations(np.random.default_rng(0), 1536, F16), F16)
     desc = w4.w4_chain_desc(mats, ys)
-    sync = w4.w4_chain_sync()
+    sync = w4.w4_chain_sync(len(shapes))
     w4.w4_gemv_chain(desc, x0, sync)
     torch.cuda.synchronize()
     assert sync[0].item() == 0 and sync[2].item() == 0
@@ -97,12 +97,26 @@ def test_chain_decode_sweep_35_layers(w4):
     check_teacher_forced(w4, mats, x0, ys, rows=rows, full_upto=4)
 
 
+def test_chain_longer_than_descriptor_cache(w4):
+    """300 small matrices: descriptors past the first 256 are brought into the
+    kernel's table while the chain runs."""
+    shapes = [(96, 64), (64, 96), (160, 64)] * 100
+    mats = make_mats(shapes, 4)
+    ys = [torch.full((N,), float("nan"), device="cuda") for N, _ in shapes]
+    x0 = dev_act(synth.activations(np.random.default_rng(4), 64, F16), F16)
+    sync = w4.w4_chain_sync(len(shapes))
+    w4.w4_gemv_chain(w4.w4_chain_desc(mats, ys), x0, sync)
+    torch.cuda.synchronize()
+    assert sync[0].item() == 0 and sync[2].item() == 0
+    check_teacher_forced(w4, mats, x0, ys)
+
+
 def test_chain_invalid_descriptor_sets_error_word(w4):
     shapes = [(64, 64), (64, 128)]          # K of matrix 1 exceeds N of matrix 0
     mats = make_mats(shapes, 2)
     ys = [torch.full((N,), float("nan"), device="cuda") for N, _ in shapes]
     x0 = torch.zeros(64, dtype=torch.float16, device="cuda")
-    sync = w4.w4_chain_sync()
+    sync = w4.w4_chain_sync(len(shapes))
     w4.w4_gemv_chain(w4.w4_chain_desc(mats, ys), x0, sync)
     torch.cuda.synchronize()
     assert sync[2].item() == 2 and sync[0].item() == 0
@@ -115,7 +129,7 @@ def test_chain_barrier_timeout_is_reported_and_recovers(w4, monkeypatch):
     ys = [torch.zeros(N, device="cuda") for N, _ in shapes]
     x0 = dev_act(synth.activations(np.random.default_rng(3), 64, F16), F16)
     desc = w4.w4_chain_desc(mats, ys)
-    sync = w4.w4_chain_sync()
+    sync = w4.w4_chain_sync(len(shapes))
     monkeypatch.setenv("W4_CHAIN_SPIN_LIMIT", "0")   # host-forced: every barrier wait gives up
     w4.w4_gemv_chain(desc, x0, sync)
     torch.cuda.synchronize()

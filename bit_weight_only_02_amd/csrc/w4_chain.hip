@@ -298,7 +298,7 @@ __device__ __forceinline__ int chain_read_cells(const uint2 *cells, int K, unsig
 }
 
 // Sum of squares over the poll waves' values, in the fixed order of
-// sum_squares_256 (thread t: chunks t, t+256, ... ascending; xor folds 32..1;
+// sum_squares_256 (thread t: chunks t, t+256, ... ascending; wave_sum_f64;
 // wave sums added in wave order) -- bit for bit the w4_rms_renorm value --
 // with a single workgroup barrier: the wave sums go to one of two LDS slots,
 // alternating from step to step, so a slot is rewritten only two barriers
@@ -318,8 +318,7 @@ __device__ __forceinline__ double chain_sum_squares(int K, const float4 (&v)[kPo
             }
         }
     }
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off, kWave);
+    ss = wave_sum_f64(ss);
     double *r = red + parity * 4;
     if ((tid & 63) == 0 && tid < kPollThreads) r[tid >> 6] = ss;
     lds_barrier();

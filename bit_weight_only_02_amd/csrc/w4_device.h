@@ -154,13 +154,57 @@ __device__ __forceinline__ int wave_or_i32(int v) {
     return __builtin_amdgcn_ballot_w64(v != 0) != 0 ? 1 : 0;
 }
 
+// Sum of a double over the 64 lanes of a wave, the same bits in every lane:
+// a butterfly of exchanges -- lanes 1 apart, 2 apart (quad permutes), the two
+// halves of each 8-lane group and of each 16-lane row (mirrors), then pairs of
+// rows 16 and 32 apart (permlane swaps) -- each adding the two operands of a
+// pair in the same order on both sides.  The exchanges move the two 32-bit
+// halves of the double with DPP and permlane instructions, so no LDS traffic.
+template <int ctrl>
+__device__ __forceinline__ double dpp_f64(double v) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, ctrl, 0xF, 0xF, false);
+    const uint32_t hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), ctrl, 0xF, 0xF, false);
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+__device__ __forceinline__ double wave_sum_f64(double v) {
+    // pair (a, b) is added as min-lane + max-lane in both lanes: a + b is
+    // commutative in IEEE arithmetic, so both lanes get the same bits
+    v = v + dpp_f64<0xB1>(v);   // quad_perm [1,0,3,2]
+    v = v + dpp_f64<0x4E>(v);   // quad_perm [2,3,0,1]
+    v = v + dpp_f64<0x141>(v);  // row_half_mirror
+    v = v + dpp_f64<0x140>(v);  // row_mirror
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    auto swap_sum = [](uint64_t x, bool rows32) __attribute__((always_inline)) {
+        const uint32_t lo = (uint32_t)x, hi = (uint32_t)(x >> 32);
+        uint32_t a_lo, b_lo, a_hi, b_hi;
+        if (rows32) {
+            const auto pl = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+            const auto ph = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+            a_lo = pl[0]; b_lo = pl[1]; a_hi = ph[0]; b_hi = ph[1];
+        } else {
+            const auto pl = __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+            const auto ph = __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+            a_lo = pl[0]; b_lo = pl[1]; a_hi = ph[0]; b_hi = ph[1];
+        }
+        // a holds the lower row of each swapped pair in both rows, b the upper
+        const double a = __builtin_bit_cast(double, ((uint64_t)a_hi << 32) | a_lo);
+        const double b = __builtin_bit_cast(double, ((uint64_t)b_hi << 32) | b_lo);
+        return a + b;
+    };
+    v = swap_sum(u, false);
+    v = swap_sum(__builtin_bit_cast(uint64_t, v), true);
+    return v;
+}
+
 // Sum of squares of v[0..K) (K a multiple of 4) in fp64 with one fixed order,
 // shared by every kernel that renormalises (so that they agree bit for bit):
 // thread t of a 256-thread workgroup owns the 4-element chunks c = t, t+256,
 // ... and adds their squares in ascending (c, element) order; the 64 lanes of
-// a wave are folded by xor shuffles 32, 16, ..., 1; the four wave sums are
-// added in wave order.  load4(c) returns chunk c as a float4.  Every thread
-// gets the total.  `red` is 4 doubles of shared scratch.
+// a wave are combined by wave_sum_f64; the four wave sums are added in wave
+// order.  load4(c) returns chunk c as a float4.  Every thread gets the total.
+// `red` is 4 doubles of shared scratch.
 template <class Load4>
 __device__ __forceinline__ double sum_squares_256(int K, Load4 load4, double *red) {
     const int tid = threadIdx.x;
@@ -172,41 +216,11 @@ __device__ __forceinline__ double sum_squares_256(int K, Load4 load4, double *re
         ss += (double)v.z * (double)v.z;
         ss += (double)v.w * (double)v.w;
     }
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off, kWave);
+    ss = wave_sum_f64(ss);
     if ((tid & 63) == 0) red[tid >> 6] = ss;
     __syncthreads();
     const double tot = ((red[0] + red[1]) + red[2]) + red[3];
     __syncthreads();
-    return tot;
-}
-
-// The same sum over chunks already in registers: v[j] is chunk tid + 256*j
-// (valid while tid + 256*j < K/4), up to J chunks per thread.  Threads with
-// `active` false (beyond the first 256 of a larger workgroup) add nothing and
-// only take part in the barriers; `red` holds one double per wave.
-template <int J>
-__device__ __forceinline__ double sum_squares_256_regs(int K, const float4 (&v)[J], double *red,
-                                                       bool active = true) {
-    const int tid = threadIdx.x;
-    double ss = 0.0;
-    if (active) {
-#pragma unroll
-        for (int j = 0; j < J; ++j) {
-            if (tid + 256 * j < (K >> 2)) {
-                ss += (double)v[j].x * (double)v[j].x;
-                ss += (double)v[j].y * (double)v[j].y;
-                ss += (double)v[j].z * (double)v[j].z;
-                ss += (double)v[j].w * (double)v[j].w;
-            }
-        }
-    }
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off, kWave);
-    if ((tid & 63) == 0 && tid < 256) red[tid >> 6] = ss;
-    lds_barrier();
-    const double tot = ((red[0] + red[1]) + red[2]) + red[3];
-    lds_barrier();
     return tot;
 }
 

@@ -8,7 +8,8 @@ dev.to page "Gemma 4 on a 4 GB GPU in Plain PyTorch", section "Step 2 - Keep
 the Vocabulary Tables in 4-Bit").  Three copies of the table are rotated so that
 the 256 MB Infinity Cache cannot hold the working set.
 
-`value` = algorithmic HBM bytes of one step / measured step time (GB/s, 1e9 B).
+`value` = algorithmic HBM bytes of one step / measured step time (GB/s, 1e9 B),
+each step replayed as one HIP graph.
 Printed as ONE JSON line, with the dominant kernel's roofline, the CPU oracle's
 time on a bounded sample of the same workload, and (under "extra") the other
 workloads of this path: the single 2048 x 1536 GEMV, the 35-layer decode-step
@@ -390,17 +391,34 @@ def main(argv=None):
         w4.w4_gemv(dcodes[c], dsteps[c], dx, y)
         w4.w4_embed_gather(dcodes[c], dsteps[c], dids, gout)
 
+    # One decode step is replayed as one HIP graph (as the dev.to page does per
+    # decode step); one graph per table copy, replayed in rotation.
+    side = torch.cuda.Stream()
+    graphs = []
+    for c in range(COPIES):
+        step(c)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(g, stream=side):
+                step(c)
+        graphs.append(g)
+    torch.cuda.synchronize()
     for i in range(args.warmup):
-        step(i)
+        graphs[i % COPIES].replay()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    step_s = timer.per_call(step, args.steps, warmup=0)
+    step_s = timer.per_call(lambda i: graphs[i % COPIES].replay(), args.steps, warmup=0)
     wall = time.perf_counter() - t0
-    # dominant kernel: the GEMV alone, back to back on the same stream
-    gemv_s = timer.per_call(lambda i: w4.w4_gemv(dcodes[i % COPIES], dsteps[i % COPIES], dx, y),
-                            args.steps, warmup=0)
-    gather_s = timer.per_call(lambda i: w4.w4_embed_gather(dcodes[i % COPIES], dsteps[i % COPIES],
-                                                            dids, gout), args.steps, warmup=0)
+    step_eager_s = timer.per_call(step, args.steps, warmup=0)
+    # dominant kernel: the GEMV alone, launched back to back on the stream
+    # (measured closest to the kernel's own duration in a rocprofv3 trace of
+    # this command; a graph of the same launches adds a gap per node)
+    gemv_call = lambda i: w4.w4_gemv(dcodes[i % COPIES], dsteps[i % COPIES], dx, y)  # noqa: E731
+    gemv_s = timer.per_call(gemv_call, args.steps, warmup=2)
+    gemv_graph_s = timer.graph_per_call(gemv_call, args.steps)
+    gather_s = timer.graph_per_call(lambda i: w4.w4_embed_gather(dcodes[i % COPIES], dsteps[i % COPIES],
+                                                                  dids, gout), args.steps)
     ceiling = probe_ceiling(w4, torch)
     achieved = gbps(gemv_bytes(V, K), gemv_s)
     traffic, kname = measured_traffic()
@@ -426,12 +444,14 @@ def main(argv=None):
                      "bytes_per_launch": gemv_bytes(V, K),
                      "avg_launch_us": round(gemv_s * 1e6, 3)},
         "extra": {"gemv_weight_GBps": round(gbps(w4_bytes(V, K), gemv_s), 2),
+                  "gemv_us_graph": round(gemv_graph_s * 1e6, 3),
+                  "ms_per_step_eager": round(step_eager_s * 1e3, 5),
                   "gather_us": round(gather_s * 1e6, 3),
                   "probe_read_ceiling_GBps": round(ceiling, 1),
                   "gemv_frac_of_probe": round(achieved / ceiling, 4),
                   "timed_wall_s": round(wall, 4)},
     }
-    del dcodes, dsteps
+    del dcodes, dsteps, graphs
     torch.cuda.empty_cache()
     if not args.no_extra:
         ex = result["extra"]

@@ -136,6 +136,22 @@ def test_magic_float_conversions_are_exact():
         assert float(f16 - np.float16(1032)) == c - 8
         f16hi = np.array([0x6400 | (c << 4)], dtype=np.uint16).view(np.float16)[0]
         assert float(np.float16(f16hi * np.float16(1 / 16)) - np.float16(72)) == c - 8
+        # The form the GPU kernels use: a nibble in the low mantissa bits with a
+        # zero exponent field is the subnormal c * 2^-24 (16c * 2^-24 four bits
+        # higher), and one fp16 subtraction of 8 * 2^-24 (128 * 2^-24) gives
+        # (c - 8) * 2^-24 (16 (c - 8) * 2^-24) exactly, as a subnormal.
+        lo = np.array([c], dtype=np.uint16).view(np.float16)[0]
+        hi = np.array([c << 4], dtype=np.uint16).view(np.float16)[0]
+        assert float(lo) == c * 2.0**-24 and float(hi) == 16 * c * 2.0**-24
+        d_lo = np.float16(lo - np.array([8], dtype=np.uint16).view(np.float16)[0])
+        d_hi = np.float16(hi - np.array([128], dtype=np.uint16).view(np.float16)[0])
+        assert float(d_lo) == (c - 8) * 2.0**-24
+        assert float(d_hi) == 16 * (c - 8) * 2.0**-24
+        # and the product with any fp16 x is exact in fp32 (at most 4 + 11 bits)
+        for xb in (0x0001, 0x03FF, 0x3C00, 0x7BFF, 0xB555):
+            x = np.array([xb], dtype=np.uint16).view(np.float16)[0]
+            prod = np.float32(d_lo) * np.float32(x)
+            assert float(prod) == (c - 8) * 2.0**-24 * float(x)
 
 
 # --- matrix-vector product --------------------------------------------------

@@ -101,6 +101,12 @@ int staging_buffer(size_t bytes, hipStream_t stream, void **out) {
     void *p = nullptr;
     e = hipMalloc(&p, bytes);
     if (e != hipSuccess) return fail(W4_ERR_HIP, "hipMalloc(%zu): %s", bytes, hipGetErrorString(e));
+    // the counter area at its start must read zero before first use
+    e = hipMemsetAsync(p, 0, w4::kWsCounterBytes, stream);
+    if (e != hipSuccess) {
+        (void)hipFree(p);
+        return fail(W4_ERR_HIP, "hipMemsetAsync: %s", hipGetErrorString(e));
+    }
     g_ws_ptr[dev] = p;
     g_ws_bytes[dev] = bytes;
     *out = p;
@@ -153,10 +159,10 @@ int w4_gemm_smallM(const uint32_t *codes, const uint16_t *steps, int32_t N, int3
     }
     void *ws = nullptr;
     const size_t ws_bytes = w4::gemm_smallm_workspace(N, K, M);
-    if (ws_bytes && (st = staging_buffer(ws_bytes, static_cast<hipStream_t>(stream), &ws)))
+    if (ws_bytes && (st = staging_buffer(w4::kWsCounterBytes + ws_bytes, static_cast<hipStream_t>(stream), &ws)))
         return st;
     return launched(w4::launch_gemm_smallm(codes, steps, N, K, static_cast<const uint16_t *>(X), ldx,
-                                           xdt, M, Y, ldy, static_cast<float *>(ws),
+                                           xdt, M, Y, ldy, ws,
                                            static_cast<hipStream_t>(stream)),
                     "w4_gemm_smallM");
 }
@@ -232,12 +238,12 @@ int w4_moe_gemv_ids(const uint32_t *codes_base, const uint16_t *steps_base,
     hipStream_t s = static_cast<hipStream_t>(stream);
     void *ws = nullptr;
     const size_t ws_bytes = w4::moe_workspace(N, K, T, topk, route_w != nullptr);
-    if (ws_bytes && (st = staging_buffer(ws_bytes, s, &ws))) return st;
+    if (ws_bytes && (st = staging_buffer(w4::kWsCounterBytes + ws_bytes, s, &ws))) return st;
     if (forced_launch_error()) return fail(W4_ERR_HIP, "forced launch error (test hook)");
     return launched(w4::launch_moe(codes_base, steps_base, expert_stride_codes, expert_stride_steps,
                                    N, K, static_cast<const uint16_t *>(X), ldx, xdt, x_per_pair, ids,
                                    T, topk, slot_of, n_experts, n_slots, row_scale, route_w, Y,
-                                   static_cast<float *>(ws), dev_err, s),
+                                   ws, dev_err, s),
                     "w4_moe_gemv_ids");
 }
 

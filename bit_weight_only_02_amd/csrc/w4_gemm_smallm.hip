@@ -5,12 +5,15 @@
 // writing a 16-bit copy; its section "Step 5 - Attention for One Token at a
 // Time" notes that without matrix units a dot-product instruction lost to a
 // plain multiply-and-sum.  Here the M activation rows make the product a real
-// (if thin) contraction, so it runs on MFMA (engine in w4_mfma.h).
+// (if thin) contraction, so it runs on MFMA (engine in w4_mfma.h); a single row
+// goes to the batch-1 kernel instead.
 //
 // Grid: x = steps of kSmallMWaves/KW 16-row tiles, y = the K-slice.  With one
-// slice the engine stores Y directly; with several, each slice writes its
-// partial sums to a workspace [S][M][N] and a second kernel adds them in slice
-// order.
+// slice the engine stores Y directly.  With several, each slice stores its
+// partial sums to a workspace [S][M][N] (agent-coherent stores) and counts
+// itself in on a per-column-of-the-grid counter; the last slice to arrive adds
+// the S partials in slice order (so the result does not depend on the order of
+// arrival), writes Y and puts the counter back to zero.
 #include <cstdio>
 #include <cstdlib>
 
@@ -21,48 +24,64 @@
 namespace w4 {
 
 // Activation row m at X + m*ldx.  S == 1: output Y[m*ldy + n]; otherwise the
-// slice's partial to ws[(slice*M + m)*N + n].
+// slice's partial to part[(slice*M + m)*N + n], then the last slice of grid
+// column blockIdx.x sums them.  cnt: one counter per grid column.
 template <int R, bool STEPS8>
 __global__ __launch_bounds__(64 * kSmallMWaves) void gemm_smallm_kernel(
     const uint4 *__restrict__ codes, const uint16_t *__restrict__ steps, int N, int K,
     const uint16_t *__restrict__ X, long ldx, int dt, int M, float *__restrict__ Y, long ldy,
-    float *__restrict__ ws, int Gs, int mp_log2, int KW) {
+    float *__restrict__ part, unsigned *__restrict__ cnt, int Gs, int mp_log2, int KW) {
     __shared__ SmallMShared sh;
+    __shared__ int last_s;
     extern __shared__ uint4 smallm_a[];
     const int G = K >> 5;
-    const int slice = blockIdx.y;
+    const int slice = blockIdx.y, S = gridDim.y;
     const int g_lo = slice * Gs, g_hi = min(G, g_lo + Gs);
     const bool xvec = ((reinterpret_cast<uintptr_t>(X) & 15) == 0) && (ldx % 8 == 0);
-    const bool direct = gridDim.y == 1;
     smallm_engine<R, STEPS8>(
         codes, steps, N, K, g_lo, g_hi,
         [&](int m) __attribute__((always_inline)) { return X + (long)m * ldx; }, xvec, dt, M,
         mp_log2, KW, blockIdx.x, gridDim.x,
         [&](int m, int n, float v) __attribute__((always_inline)) {
-            if (direct) Y[(long)m * ldy + n] = v;
-            else ws[((long)slice * M + m) * N + n] = v;
+            if (S == 1)
+                Y[(long)m * ldy + n] = v;
+            else
+                __hip_atomic_store(part + ((long)slice * M + m) * N + n, v, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
         },
         sh, smallm_a);
-}
-
-// Y[m][n] = sum over slices s = 0, 1, ... of ws[s][m][n], in that order.
-__global__ __launch_bounds__(256) void smallm_slices_kernel(const float *__restrict__ ws, int S,
-                                                            int M, int N, float *__restrict__ Y,
-                                                            long ldy) {
-    const long total = (long)M * N;
-    for (long i = (long)blockIdx.x * blockDim.x + threadIdx.x; i < total;
-         i += (long)gridDim.x * blockDim.x) {
-        float s = ws[i];
-        for (int k = 1; k < S; ++k) s += ws[(long)k * total + i];
-        const int m = (int)(i / N), n = (int)(i % N);
-        Y[(long)m * ldy + n] = s;
+    if (S == 1) return;
+    // this slice's partials are stored (every wave waits for its own), then
+    // one count per workgroup
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (threadIdx.x == 0)
+        last_s = __hip_atomic_fetch_add(cnt + blockIdx.x, 1u, __ATOMIC_RELAXED,
+                                        __HIP_MEMORY_SCOPE_AGENT) == (unsigned)S - 1;
+    __syncthreads();
+    if (!last_s) return;
+    // the last slice of this grid column: its tiles, every (m, n), slices in order
+    const int tpw = kSmallMWaves / KW, ntiles = (N + 15) >> 4, cols = tpw * 16;
+    const long plane = (long)M * N;
+    for (int tg = blockIdx.x; tg * tpw < ntiles; tg += gridDim.x) {
+        for (int o = threadIdx.x; o < cols * M; o += blockDim.x) {
+            const int m = o / cols, n = tg * cols + o % cols;
+            if (n >= N) continue;
+            const float *pp = part + (long)m * N + n;
+            float v = __hip_atomic_load(pp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            for (int k = 1; k < S; ++k)
+                v += __hip_atomic_load(pp + k * plane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            Y[(long)m * ldy + n] = v;
+        }
     }
+    if (threadIdx.x == 0)
+        __hip_atomic_store(cnt + blockIdx.x, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 namespace {
 
 typedef void (*GemmFn)(const uint4 *, const uint16_t *, int, int, const uint16_t *, long, int, int,
-                       float *, long, float *, int, int, int);
+                       float *, long, float *, unsigned *, int, int, int);
 
 template <bool S8>
 GemmFn pick_gemm_s(int R) {
@@ -75,37 +94,76 @@ GemmFn pick_gemm_s(int R) {
     return nullptr;
 }
 
+SmallMPlan gemm_plan(int N, int K, int M) { return smallm_plan(N, K, M, 1, kSmallMLdsFast, true); }
+
+// W4_SMALLM_PLAN="KW,S,workgroups" overrides the plan's waves per tile, K-slices
+// and workgroup cap (schedule sweeps; what is computed does not change).
+// Returns the cap (0: the default).
+int plan_override(int N, int K, int M, SmallMPlan &p) {
+    const char *e = getenv("W4_SMALLM_PLAN");
+    int kw = 0, S = 0, cap = 0;
+    if (!e || sscanf(e, "%d,%d,%d", &kw, &S, &cap) != 3) return 0;
+    if ((kw != 1 && kw != 2 && kw != 4) || S < 1 || cap < 0) return 0;
+    const int G = K / 32;
+    int mp = 1, lg = 0;
+    while (mp < M) { mp <<= 1; ++lg; }
+    int gs = ((G + S - 1) / S + 3) / 4 * 4;
+    if (gs < 4) gs = 4;
+    const int nr = gs / 4;
+    if (nr * 4 * 4 * mp * 16 > kSmallMLdsA) return 0;  // does not fit: keep the plan
+    p.Gs = gs;
+    p.S = (G + gs - 1) / gs;
+    p.KW = kw;
+    while (p.KW > 1 && nr < p.KW) p.KW /= 2;
+    const int rpw = (nr + p.KW - 1) / p.KW;
+    p.R = rpw <= 4 ? 4 : rpw <= 8 ? 8 : rpw <= 16 ? 16 : 24;
+    p.lds_a = (nr * 4 * 4 * mp + 63) / 64 * 64 * 16;
+    p.mp_log2 = lg;
+    return cap;
+}
+
 }  // namespace
 
 size_t gemm_smallm_workspace(int N, int K, int M) {
-    const SmallMPlan p = smallm_plan(N, K, M, 1);
+    if (M == 1) return 0;  // the batch-1 product
+    SmallMPlan p = gemm_plan(N, K, M);
+    plan_override(N, K, M, p);
     return p.S > 1 ? (size_t)p.S * M * N * sizeof(float) : 0;
 }
 
 int smallm_grid_x(int N, int KW) {
     const int ntiles = (N + 15) / 16, tpw = kSmallMWaves / KW;
     int bx = (ntiles + tpw - 1) / tpw;
-    if (bx > 2048) bx = 2048;
+    if (bx > kMaxGridColumns) bx = kMaxGridColumns;
     return bx < 1 ? 1 : bx;
+}
+
+// Grid columns of a small-M launch of S slices: one per step of tiles, but
+// no more than `groups` workgroups in all, so that each workgroup stages its
+// activations once and then loops over several tiles.
+static int gemm_grid_x(int N, const SmallMPlan &p, int groups) {
+    int bx = smallm_grid_x(N, p.KW);
+    const int cap = (int)((groups + p.S - 1) / p.S);
+    return bx < cap ? bx : (cap < 1 ? 1 : cap);
 }
 
 hipError_t launch_gemm_smallm(const uint32_t *codes, const uint16_t *steps, int N, int K,
                               const uint16_t *X, long ldx, int dt, int M, float *Y, long ldy,
-                              float *ws, hipStream_t stream) {
-    const SmallMPlan p = smallm_plan(N, K, M, 1);
+                              void *ws, hipStream_t stream) {
+    // one activation row: the batch-1 kernel (no matrix-core padding)
+    if (M == 1) return launch_gemv(codes, steps, N, K, X, dt, Y, stream);
+    SmallMPlan p = gemm_plan(N, K, M);
+    const int cap = plan_override(N, K, M, p);
     const bool steps8 = (K / 32) % 4 == 0 && (reinterpret_cast<uintptr_t>(steps) & 7) == 0;
     GemmFn fn = steps8 ? pick_gemm_s<true>(p.R) : pick_gemm_s<false>(p.R);
     if (!fn || (p.S > 1 && !ws)) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(fn, dim3(smallm_grid_x(N, p.KW), p.S), dim3(64 * kSmallMWaves), p.lds_a,
+    unsigned *cnt = static_cast<unsigned *>(ws);
+    float *part = ws ? reinterpret_cast<float *>(static_cast<char *>(ws) + kWsCounterBytes) : nullptr;
+    const int groups = cap > 0 ? cap : (int)(p.KW == 1 && M >= 8 ? kSmallMWideGroups : kSmallMTargetGroups);
+    hipLaunchKernelGGL(fn, dim3(gemm_grid_x(N, p, groups), p.S),
+                       dim3(64 * kSmallMWaves), p.lds_a,
                        stream, reinterpret_cast<const uint4 *>(codes), steps, N, K, X, ldx, dt, M, Y,
-                       ldy, ws, p.Gs, p.mp_log2, p.KW);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess || p.S == 1) return e;
-    const long total = (long)M * N;
-    long blocks = (total + 255) / 256;
-    if (blocks > 2048) blocks = 2048;
-    hipLaunchKernelGGL(smallm_slices_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, ws, p.S,
-                       M, N, Y, ldy);
+                       ldy, part, cnt, p.Gs, p.mp_log2, p.KW);
     return hipGetLastError();
 }
 

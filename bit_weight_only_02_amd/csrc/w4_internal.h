@@ -24,13 +24,20 @@ hipError_t launch_gemv(const uint32_t *codes, const uint16_t *steps, int N, int 
 
 // Small-M products (w4_mfma.h engine).  A workspace is needed when the plan
 // splits K (and, for the expert product, when route weights are given);
-// *_workspace() returns its size in bytes (0: none).
+// *_workspace() returns the bytes of partial sums it needs (0: none).  The
+// workspace handed to the launchers starts with kWsCounterBytes of counters
+// (one per grid column, at most kMaxGridColumns; zero between calls: zeroed
+// when the buffer is allocated and left at zero by every kernel that uses
+// them); the partial sums follow.
+constexpr int kMaxGridColumns = 2048;
+constexpr size_t kWsCounterBytes = 16384;
+static_assert(kMaxGridColumns * 4 <= (int)kWsCounterBytes, "counter area");
 size_t gemm_smallm_workspace(int N, int K, int M);
 int smallm_grid_x(int N, int KW);
 
 hipError_t launch_gemm_smallm(const uint32_t *codes, const uint16_t *steps, int N, int K,
                               const uint16_t *X, long ldx, int dt, int M, float *Y, long ldy,
-                              float *ws, hipStream_t stream);
+                              void *ws, hipStream_t stream);
 
 hipError_t launch_gather(const uint32_t *codes, const uint16_t *steps, int V, int K,
                          const int32_t *ids, int n, uint16_t *out, int32_t *dev_err,
@@ -46,7 +53,7 @@ hipError_t launch_moe(const uint32_t *codes_base, const uint16_t *steps_base,
                       const uint16_t *X, long ldx, int dt, int x_per_pair,
                       const int32_t *ids, int T, int topk, const int32_t *slot_of,
                       int n_experts, int n_slots, const float *row_scale, const float *route_w,
-                      float *Y, float *ws, int32_t *dev_err, hipStream_t stream);
+                      float *Y, void *ws, int32_t *dev_err, hipStream_t stream);
 
 size_t chain_lds_bytes();
 hipError_t launch_chain(const void *desc, int n, const uint16_t *x0, void *sync, unsigned spin_limit,

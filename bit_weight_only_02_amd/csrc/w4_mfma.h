@@ -5,9 +5,10 @@
 // rows (B operand) by the same 32 columns of up to 16 activation rows (A
 // operand); its fp32 result is then scaled by the group's bf16 step, per weight
 // row, exactly where the step applies.  Operands are exact fp16: the weights
-// are c - 8 (the OR-into-1024 unpack of w4_device.h), and each activation row
-// is fp16 as given, or bf16 staged as x * 2^s with a power of two per row and
-// K-slice (undone once per output).
+// are (c - 8) * 2^-24 -- each nibble shifted to the low bits and masked is the
+// fp16 subnormal c * 2^-24, and one packed subtract of 8 * 2^-24 follows --
+// and each activation row is fp16 as given, or bf16 staged as x * 2^s with a
+// power of two per row and K-slice; both scalings are undone once per output.
 //
 // Register layout (lane i, 0..63): A holds X[m = i%16][k-slots 8(i/16)..+7],
 // B holds W[n = i%16][the same k-slots], D holds rows m = 4(i/16)..+3 of column
@@ -22,10 +23,14 @@
 // conversion pass), for Mp = M rounded up to a power of two rows, so that small
 // M needs little LDS.  KW waves share a 16-row tile, each taking a contiguous
 // run of the slice's rounds (4 groups each), and their partial tiles are added
-// in LDS in wave order; KW is 4 for small matrices (more SIMDs per tile) and 1
-// for large ones.  All weight loads of a wave's first tile are issued before
-// the staging starts, so their latency overlaps it.  Results of several
-// K-slices are summed by a separate pass in slice order (deterministic).
+// in LDS in wave order.  The plan picks KW and the number of K-slices so that
+// the chip holds about 16 waves per CU (a thin product is latency-bound: the
+// more independent waves, the more weight bytes in flight) without splitting K
+// across workgroups unless a wave would otherwise run a long serial chain of
+// rounds (the cross-workgroup sum costs a few memory round trips).  All weight
+// loads of a wave's first tile are issued before the staging starts, so their
+// latency overlaps it.  Results of several K-slices are summed in slice order
+// (deterministic) by the caller.
 #pragma once
 
 #include "w4_device.h"
@@ -38,6 +43,11 @@ typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kSmallMWaves = 4;           // waves per workgroup
 constexpr int kSmallMLdsA = 96 * 1024;    // largest staged A operand, bytes
+constexpr int kSmallMLdsFast = 48 * 1024; // staged A per workgroup that leaves room for 3 per CU
+constexpr long kSmallMTargetWaves = 4096; // 16 waves per CU on 256 CUs
+constexpr int kSmallMMaxRounds = 8;       // rounds per wave above which K is split further
+constexpr long kSmallMTargetGroups = 768; // workgroups: 3 per CU, each looping over its tiles
+constexpr long kSmallMWideGroups = 256;   // the same for 8 or more rows with one wave per tile
 
 // 4x4 transpose of words across the four 16-lane groups: on entry lane group
 // Q holds words 0..3 of group Q in v[0..3]; on exit lane group q holds word q
@@ -76,26 +86,46 @@ struct SmallMPlan {
 };
 
 // M: activation rows (largest per engine pass); units: independent problems
-// (experts) that run in the same launch.
-inline SmallMPlan smallm_plan(int N, int K, int M, int units) {
+// (experts) that run in the same launch; lds_budget: bytes of staged A per
+// workgroup; split: more K-slices may be used to reach the wave target.
+inline SmallMPlan smallm_plan(int N, int K, int M, int units, int lds_budget = kSmallMLdsA,
+                              bool split = false) {
     const int G = K / 32;
     SmallMPlan p;
     int mp = 1, lg = 0;
     while (mp < M) { mp <<= 1; ++lg; }
     p.mp_log2 = lg;
-    int max_gs = kSmallMLdsA / (64 * mp) / 4 * 4;   // one group = 4*Mp chunks of 16 bytes
-    p.S = (G + max_gs - 1) / max_gs;
-    if (p.S < 1) p.S = 1;
-    int gs = (G + p.S - 1) / p.S;
+    const long U = units > 0 ? units : 1;
+    const long ntiles = (N + 15) / 16;
+    const int nr_full = (G + 3) / 4;                        // rounds of 4 groups
+    const int max_gs = lds_budget / (64 * mp) / 4 * 4;      // one group = 4*Mp chunks of 16 bytes
+    // waves per tile: up to 4 while each wave keeps at least one round --
+    // except, when splitting is allowed, for 8 or more activation rows over
+    // enough tiles to give every wave of the chip its own: each workgroup then
+    // stages its (large) activation block once and its waves take separate
+    // tiles (measured 1.6x faster for 16 x 16384 x 1536)
+    p.KW = 1;
+    const bool wide = split && mp >= 8 && ntiles * U >= 4 * 256;
+    while (!wide && p.KW < kSmallMWaves && nr_full >= 2 * p.KW) p.KW *= 2;
+    int S = max_gs > 0 ? (G + max_gs - 1) / max_gs : G;
+    if (split && !wide && (nr_full + S * p.KW - 1) / (S * p.KW) > kSmallMMaxRounds &&
+        ntiles * U * S * p.KW < kSmallMTargetWaves) {
+        // long serial chains on too few waves: more slices, down to about
+        // kSmallMMaxRounds / 2 rounds per wave or the wave target
+        const long want = (kSmallMTargetWaves + ntiles * U * p.KW - 1) / (ntiles * U * p.KW);
+        const int s_rounds = (nr_full + p.KW * kSmallMMaxRounds / 2 - 1) / (p.KW * kSmallMMaxRounds / 2);
+        const int s_new = (int)(want < s_rounds ? want : s_rounds);
+        if (s_new > S) S = s_new;
+    }
+    if (S < 1) S = 1;
+    int gs = (G + S - 1) / S;
     gs = (gs + 3) / 4 * 4;
     if (gs < 4) gs = 4;
     p.Gs = gs;
     p.S = (G + gs - 1) / gs;
     if (p.S < 1) p.S = 1;
     const int nr = gs / 4;
-    const long tiles = (long)((N + 15) / 16) * p.S * (units > 0 ? units : 1);
-    p.KW = 1;
-    while (p.KW < kSmallMWaves && tiles * p.KW < 1024 && nr >= 2 * p.KW * 2) p.KW *= 2;
+    while (p.KW > 1 && nr < p.KW) p.KW /= 2;
     const int rpw = (nr + p.KW - 1) / p.KW;
     p.R = rpw <= 4 ? 4 : rpw <= 8 ? 8 : rpw <= 16 ? 16 : 24;
     const int chunks = nr * 4 * 4 * mp;
@@ -299,9 +329,7 @@ __device__ __forceinline__ void smallm_engine(const uint4 *__restrict__ codes,
         return;
     }
 
-    const h2 kSub = {(_Float16)-1032.0f, (_Float16)-1032.0f};
-    const h2 kInv16 = {(_Float16)0.0625f, (_Float16)0.0625f};
-    const h2 kSub72 = {(_Float16)-72.0f, (_Float16)-72.0f};
+    const h2 k8 = __builtin_bit_cast(h2, 0x00080008u);  // 8 * 2^-24 in both halves
     const h8 *Ah = reinterpret_cast<const h8 *>(A);
     const int arow = (q << mp_log2) + (n_l & mmask);   // this lane's A chunk within a group
 
@@ -323,11 +351,11 @@ __device__ __forceinline__ void smallm_engine(const uint4 *__restrict__ codes,
                         h8 b[4];
 #pragma unroll
                         for (int j = 0; j < 4; ++j) {
-                            const uint32_t u = w[j] >> 8;
-                            const h2 p0 = as_h2((w[j] & 0x000F000Fu) | 0x64006400u) + kSub;
-                            const h2 p1 = as_h2((w[j] & 0x00F000F0u) | 0x64006400u) * kInv16 + kSub72;
-                            const h2 p2 = as_h2((u & 0x000F000Fu) | 0x64006400u) + kSub;
-                            const h2 p3 = as_h2((u & 0x00F000F0u) | 0x64006400u) * kInv16 + kSub72;
+                            // (c - 8) * 2^-24 for the pairs (c0,c4) (c1,c5) (c2,c6) (c3,c7)
+                            const h2 p0 = as_h2(w[j] & 0x000F000Fu) - k8;
+                            const h2 p1 = as_h2((w[j] >> 4) & 0x000F000Fu) - k8;
+                            const h2 p2 = as_h2((w[j] >> 8) & 0x000F000Fu) - k8;
+                            const h2 p3 = as_h2((w[j] >> 12) & 0x000F000Fu) - k8;
                             b[j][0] = p0[0]; b[j][1] = p0[1]; b[j][2] = p1[0]; b[j][3] = p1[1];
                             b[j][4] = p2[0]; b[j][5] = p2[1]; b[j][6] = p3[0]; b[j][7] = p3[1];
                         }
@@ -369,7 +397,7 @@ __device__ __forceinline__ void smallm_engine(const uint4 *__restrict__ codes,
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int mm = 4 * q + j;
-                if (mm < M && n < N) store(mm, n, __builtin_ldexpf(acc[j], -sh.scale[mm]));
+                if (mm < M && n < N) store(mm, n, __builtin_ldexpf(acc[j], kGroupDotExp - sh.scale[mm]));
             }
         }
         const int next = (tg + tg_stride) * tpw + tsub;

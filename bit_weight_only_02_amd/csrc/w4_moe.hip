@@ -200,7 +200,9 @@ hipError_t launch_moe(const uint32_t *codes_base, const uint16_t *steps_base,
                       const uint16_t *X, long ldx, int dt, int x_per_pair,
                       const int32_t *ids, int T, int topk, const int32_t *slot_of,
                       int n_experts, int n_slots, const float *row_scale, const float *route_w,
-                      float *Y, float *ws, int32_t *dev_err, hipStream_t stream) {
+                      float *Y, void *wsv, int32_t *dev_err, hipStream_t stream) {
+    // partial sums after the workspace's counter area (which this kernel leaves alone)
+    float *ws = wsv ? reinterpret_cast<float *>(static_cast<char *>(wsv) + kWsCounterBytes) : nullptr;
     const SmallMPlan p = moe_plan(N, K, T, topk);
     const bool steps8 = (K / 32) % 4 == 0 && (reinterpret_cast<uintptr_t>(steps_base) & 7) == 0 &&
                         (stride_steps % 4) == 0;

@@ -98,10 +98,13 @@ int w4_gemv(const uint32_t *codes, const uint16_t *steps, int32_t N, int32_t K,
  *   Y[m*ldy + n] = sum_k w(n,k) * X[m*ldx + k]   for m < M, n < N.
  * Each weight is read from memory once for all M rows.  ldx >= K, ldy >= N,
  * K <= W4_MAX_K_SMALLM (larger K: W4_ERR_UNSUPPORTED).
- * For K > 3072 the product is summed over K-slices in a fixed order, through a
- * device buffer that the library allocates once per device and reuses (grown
- * on demand while no graph capture is active; such calls on one device from
- * different streams must not overlap).
+ * M == 1 runs the batch-1 kernel of w4_gemv.  Otherwise the product runs on
+ * the matrix cores; when the plan splits K into slices (to give the chip
+ * enough independent work, or to fit the staged activations), the slices are
+ * summed in a fixed order inside the same launch, through a device buffer that
+ * the library allocates once per device and reuses (grown on demand while no
+ * graph capture is active; such calls on one device from different streams
+ * must not overlap).
  */
 int w4_gemm_smallM(const uint32_t *codes, const uint16_t *steps, int32_t N, int32_t K,
                    const void *X, int32_t xdt, int32_t M, int64_t ldx,

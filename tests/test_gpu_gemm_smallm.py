@@ -69,6 +69,31 @@ def test_gemm_decode_sweep_shapes(w4, M):
         assert ok, (N, K, M, worst)
 
 
+def test_gemm_split_k_is_deterministic_and_survives_other_calls(w4):
+    """A product split into K-slices and summed by the last slice to arrive:
+    bitwise the same on every call, also when expert products (which share the
+    library's device buffer) run in between."""
+    rng = np.random.default_rng(11)
+    N, K, M = 1536, 8192, 4
+    codes, steps = synth.w4_matrix(rng, N, K)
+    X = synth.activations(rng, (M, K), BF16)
+    first = run_gemm(w4, codes, steps, X, BF16, M, K)
+    Yo, Ao = oracle_rows(codes, steps, N, K, X, BF16, M)
+    assert within_bound(first, Yo, Ao)[0]
+    # an expert product with route weights in between (it uses the same buffer)
+    E, Ne, Ke, topk = 4, 64, 256, 2
+    ec, es = synth.w4_matrix(rng, E * Ne, Ke)
+    ids = torch.tensor([[0, 3]], dtype=torch.int32, device="cuda")
+    route = torch.tensor([[0.25, 0.75]], dtype=torch.float32, device="cuda")
+    xe = dev_act(synth.activations(rng, (1, Ke), BF16), BF16)
+    Ye = torch.empty((1, Ne), device="cuda")
+    w4.w4_moe_gemv_ids(dev_codes(ec), dev_steps(es), Ne * Ke // 8, Ne * Ke // 32, Ne, Ke, xe, ids,
+                       n_experts=E, route_w=route, Y=Ye)
+    for _ in range(3):
+        again = run_gemm(w4, codes, steps, X, BF16, M, K)
+        assert again.tobytes() == first.tobytes()
+
+
 def test_gemm_leading_dimensions(w4):
     rng = np.random.default_rng(1)
     N, K, M, ldx, ldy = 300, 1536, 6, 1600, 333

@@ -106,7 +106,13 @@ inline SmallMPlan smallm_plan(int N, int K, int M, int units, int lds_budget = k
     // tiles (measured 1.6x faster for 16 x 16384 x 1536)
     p.KW = 1;
     const bool wide = split && mp >= 8 && ntiles * U >= 4 * 256;
-    while (!wide && p.KW < kSmallMWaves && nr_full >= 2 * p.KW) p.KW *= 2;
+    if (split) {
+        while (!wide && p.KW < kSmallMWaves && nr_full >= 2 * p.KW) p.KW *= 2;
+    } else {
+        // (expert launches: many units, each staging the rows of the largest
+        // pass; more waves per tile only while the launch is small)
+        while (p.KW < kSmallMWaves && ntiles * U * p.KW < 1024 && nr_full >= 4 * p.KW) p.KW *= 2;
+    }
     int S = max_gs > 0 ? (G + max_gs - 1) / max_gs : G;
     if (split && !wide && (nr_full + S * p.KW - 1) / (S * p.KW) > kSmallMMaxRounds &&
         ntiles * U * S * p.KW < kSmallMTargetWaves) {

@@ -9,7 +9,8 @@
 // (scales, biases) keeps the real expert id.
 //
 // Here: T tokens x topk choices = P pairs.  Each workgroup takes one DISTINCT
-// expert (deduplicated on the device, in order of first appearance), one
+// expert (deduplicated on the device, in order of first appearance -- with
+// wave ballots for up to 64 pairs), one
 // K-slice and a group of 16-row tiles, reads that part of the expert's packed
 // weights once, and runs the MFMA small-M engine with one A row per pair that
 // chose the expert.  The weight address is the only place where slot_of
@@ -51,6 +52,37 @@ __global__ __launch_bounds__(64 * kSmallMWaves) void moe_kernel(
     const int g_lo = slice * Gs, g_hi = min(G, g_lo + Gs);
 
     // ---- this workgroup's distinct expert and the pairs that chose it
+    if (P <= kWave) {
+        // one wave, in registers: lane p holds pair p's id; a pair is the first
+        // of its expert when no earlier lane holds the same id; ballots give
+        // the u-th first pair and the (ordered) pairs of that expert
+        if (threadIdx.x < kWave) {
+            const int lane = threadIdx.x;
+            const int e = lane < P ? ids[lane] : 0;
+            bool first = lane < P;
+            for (int q = 0; q < P; ++q) {
+                const int eq = __builtin_amdgcn_readlane(e, q);
+                first = first && !(q < lane && eq == e);
+            }
+            const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+            const uint64_t firsts = __builtin_amdgcn_ballot_w64(first);
+            const int rank = __builtin_popcountll(firsts & below);
+            const uint64_t pick = __builtin_amdgcn_ballot_w64(first && rank == u);
+            if (pick == 0) {
+                if (lane == 0) info_s[2] = 0;
+            } else {
+                const int eu = __builtin_amdgcn_readlane(e, __builtin_ctzll(pick));
+                const uint64_t mine = __builtin_amdgcn_ballot_w64(lane < P && e == eu);
+                if (lane < P && e == eu) pairs_s[__builtin_popcountll(mine & below)] = lane;
+                if (lane == 0) {
+                    info_s[0] = eu;
+                    info_s[1] = __builtin_popcountll(mine);
+                    info_s[2] = 1;
+                }
+            }
+        }
+        lds_barrier();
+    } else {
     for (int p = threadIdx.x; p < P; p += blockDim.x) ids_s[p] = ids[p];
     lds_barrier();
     for (int p = threadIdx.x; p < P; p += blockDim.x) {
@@ -77,6 +109,7 @@ __global__ __launch_bounds__(64 * kSmallMWaves) void moe_kernel(
         info_s[2] = found;
     }
     lds_barrier();
+    }
     if (!info_s[2]) return;  // fewer distinct experts than this grid row
     const int e = info_s[0], npairs = info_s[1];
     const int ntiles = (N + 15) >> 4;
@@ -186,7 +219,18 @@ MoeFn pick_moe_s(int R) {
 // pairs that chose one expert), and up to P experts run side by side.
 static SmallMPlan moe_plan(int N, int K, int T, int topk) {
     const int P = T * topk;
-    return smallm_plan(N, K, P < 16 ? P : 16, P);
+    SmallMPlan p = smallm_plan(N, K, P < 16 ? P : 16, P);
+    // W4_MOE_PLAN="KW,R" overrides the waves per tile and the rounds of loads
+    // a wave keeps in flight (schedule sweeps; what is computed does not change)
+    if (const char *e = getenv("W4_MOE_PLAN")) {
+        int kw = 0, r = 0;
+        if (sscanf(e, "%d,%d", &kw, &r) == 2 && (kw == 1 || kw == 2 || kw == 4) &&
+            (r == 4 || r == 8 || r == 16 || r == 24)) {
+            p.KW = kw;
+            p.R = r;
+        }
+    }
+    return p;
 }
 
 size_t moe_workspace(int N, int K, int T, int topk, bool route) {

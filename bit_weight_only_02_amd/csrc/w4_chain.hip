@@ -55,8 +55,16 @@ constexpr int kChainWaves = kChainThreads / 64;
 constexpr int kPollThreads = 256;   // waves 0..3 read the exchange cells and renormalise
 constexpr int kCopyWave0 = 6;       // waves 6..7 copy weight blocks and compute nothing
 constexpr int kComputeWaves = kCopyWave0;  // waves 0..5 compute rows
-constexpr int kDescCache = 256;     // descriptors kept in LDS
+constexpr int kDescCache = 128;     // descriptors kept in LDS
 constexpr int kChainMaxK = 8192;
+
+// The staged input is kept as four planes: plane w holds uint4 w (pair-order
+// fp16 values 8w..8w+7) of every group, so that lanes reading the same plane
+// for consecutive groups touch consecutive LDS banks.  The plane stride is
+// the group count rounded up to 8 modulo 16 uint4, which puts planes 1 and 3
+// on the other half of the banks from planes 0 and 2 when they are written.
+__device__ __forceinline__ int chain_plane(int G) { return ((G + 7) >> 4) * 16 + 8; }
+constexpr int kXinBytes = 4 * (((kChainMaxK / 32 + 7) >> 4) * 16 + 8) * 16;
 constexpr int kWeightBuf = 64 * 1024;  // bytes of each of the two LDS weight buffers
 // sync buffer: bytes [0, 256) a header (word 0 exit counter, word 1 epoch --
 // the tags used by earlier calls --, word 2 error); from byte 256, one region
@@ -89,33 +97,46 @@ __device__ __forceinline__ unsigned load_agent_u(unsigned *p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Rows of one step that this workgroup computes: a contiguous block
-// [rb, re); the first nlds of them are staged in an LDS weight buffer (codes,
-// then -- when lds_steps -- their steps), the rest are read from memory.
+// This workgroup's plan for one step: the rows it computes are a contiguous
+// block [rb, re); the first nlds of them are staged in an LDS weight buffer
+// (codes, then their steps), the rest are read from memory.  Worked out once
+// per descriptor, when the descriptor enters the LDS table, so that the step
+// itself starts computing at once.
 struct RowBlock {
     int rb, re, nlds;
     int steps_chunk;  // uint4 index of the staged steps inside the buffer
-    bool lds_steps;
+    int sel;          // row kernel: lanes per row * 8 + groups per lane
+    int k_next;       // K of the next step (the cells it reads), 0 after the last
+    int pad[2];
 };
+static_assert(sizeof(RowBlock) == 32, "plan entry");
 
-__device__ __forceinline__ RowBlock chain_block(const ChainMat &m, int nwg) {
+__device__ __forceinline__ RowBlock chain_plan(const ChainMat &m, int k_next, int nwg) {
     const int G = m.K >> 5;
     const int rpw = (m.N + nwg - 1) / nwg;
     RowBlock b;
     b.rb = min(m.N, (int)blockIdx.x * rpw);
     b.re = min(m.N, b.rb + rpw);
     // steps travel as 4-byte words: the block's steps must start on one
-    b.lds_steps = (G % 2) == 0 && (reinterpret_cast<uintptr_t>(m.steps) & 3) == 0;
+    const bool lds_steps = (G % 2) == 0 && (reinterpret_cast<uintptr_t>(m.steps) & 3) == 0;
     auto bytes = [&](int rows) {
         const int chunks = (rows * G + 63) / 64 * 64;
-        const int words = b.lds_steps ? (rows * G / 2 + 63) / 64 * 64 : 0;
+        const int words = (rows * G / 2 + 63) / 64 * 64;
         return chunks * 16 + words * 4;
     };
     // (rows are staged only together with their steps)
-    int n = b.lds_steps ? min(b.re - b.rb, kWeightBuf / (G * 18)) : 0;
+    int n = lds_steps ? min(b.re - b.rb, kWeightBuf / (G * 18)) : 0;
     while (n > 0 && bytes(n) > kWeightBuf) --n;
     b.nlds = n;
     b.steps_chunk = (n * G + 63) / 64 * 64;
+    // lanes per row from the row length alone: 16 lanes up to 64 groups, 32
+    // up to 128, else 64.  (Choosing by the least work per lane -- 64 lanes
+    // for a block of six 64-group rows, say -- measured slower over the whole
+    // decode sweep: passes are latency-bound, not arithmetic-bound.)
+    const int L = G <= 64 ? 16 : (G <= 128 ? 32 : 64);
+    b.sel = L * 8 + (G + L - 1) / L;
+    b.k_next = k_next;
+    b.pad[0] = b.pad[1] = 0;
     return b;
 }
 
@@ -133,7 +154,7 @@ __device__ __forceinline__ void chain_copy(const ChainMat &m, const RowBlock &b,
     if (n == 0) return;
     const uint4 *src = reinterpret_cast<const uint4 *>(m.codes) + (long)b.rb * G;
     for (int c0 = w * 64; c0 < n; c0 += nw * 64) lds_dma16(src + min(c0 + lane, n - 1), buf + c0);
-    if (b.lds_steps) {
+    {
         const uint32_t *ssrc = reinterpret_cast<const uint32_t *>(m.steps + (long)b.rb * G);
         uint32_t *sdst = reinterpret_cast<uint32_t *>(buf + b.steps_chunk);
         const int nd = n / 2;
@@ -153,7 +174,6 @@ __device__ __forceinline__ void store_cell(uint2 *cells, int row, float v, unsig
 // leading entries the next step reads; k_next 0 for the last step).
 struct RowSink {
     uint2 *cells;
-    int k_next;
     unsigned tag;
 };
 
@@ -171,12 +191,13 @@ __device__ __forceinline__ void chain_rows(const ChainMat &m, const RowBlock &b,
     // the activations, already in pair order in LDS -> registers
     h2 xr[NG][16];
     const uint4 *r16 = reinterpret_cast<const uint4 *>(xin);
+    const int Gs = chain_plane(G);
 #pragma unroll
     for (int i = 0; i < NG; ++i) {
         const int g = l + i * L;
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-            const uint4 v = g < G ? r16[g * 4 + w] : make_uint4(0, 0, 0, 0);
+            const uint4 v = g < G ? r16[w * Gs + g] : make_uint4(0, 0, 0, 0);
             xr[i][w * 4 + 0] = as_h2(v.x);
             xr[i][w * 4 + 1] = as_h2(v.y);
             xr[i][w * 4 + 2] = as_h2(v.z);
@@ -196,9 +217,13 @@ __device__ __forceinline__ void chain_rows(const ChainMat &m, const RowBlock &b,
             // (a global store: through the generic pointer it would be a flat
             // store, which every later LDS read would have to wait for)
             ((__attribute__((address_space(1))) float *)m.y)[row] = v;
-            if (row < sink.k_next) store_cell(sink.cells, row, v, sink.tag);
+            if (row < b.k_next) store_cell(sink.cells, row, v, sink.tag);
         }
     };
+    // A pass gives each computing wave SLOTS rows.  Waves whose rows are all
+    // past the end still run the pass on clamped rows and store nothing:
+    // skipping it (and giving the idle SIMD time to the wave beside it)
+    // measured slower over the decode sweep.
     const int staged_end = b.rb + b.nlds;
     for (int r0 = b.rb; r0 < staged_end; r0 += kComputeWaves * SLOTS) {
         const int row = r0 + wave * SLOTS + slot;
@@ -234,14 +259,7 @@ __device__ __forceinline__ void chain_rows(const ChainMat &m, const RowBlock &b,
 __device__ __forceinline__ void chain_rows_any(const ChainMat &m, const RowBlock &b, const uint4 *buf,
                                                const uint16_t *xin, const RowSink &sink) {
     if (b.re <= b.rb) return;
-    // Lanes per row from the row length alone: 16 lanes up to 64 groups, 32
-    // up to 128, else 64.  (Choosing by the least work per lane -- 64 lanes
-    // for a block of six 64-group rows, say -- measured slower over the whole
-    // decode sweep: passes are latency-bound, not arithmetic-bound.)
-    const int G = m.K >> 5;
-    const int L = G <= 64 ? 16 : (G <= 128 ? 32 : 64);
-    const int NG = (G + L - 1) / L;
-    switch (__builtin_amdgcn_readfirstlane(L * 8 + NG)) {
+    switch (__builtin_amdgcn_readfirstlane(b.sel)) {
         case 16 * 8 + 1: chain_rows<16, 1>(m, b, buf, xin, sink); break;
         case 16 * 8 + 2: chain_rows<16, 2>(m, b, buf, xin, sink); break;
         case 16 * 8 + 3: chain_rows<16, 3>(m, b, buf, xin, sink); break;
@@ -329,9 +347,10 @@ __global__ __launch_bounds__(kChainThreads) void chain_kernel(const ChainMat *__
                                                               int n, const uint16_t *__restrict__ x0,
                                                               unsigned *sync, unsigned spin_limit) {
     extern __shared__ uint4 smem[];
-    uint16_t *xin = reinterpret_cast<uint16_t *>(smem);   // kChainMaxK halves, pair order
-    uint4 *bufs = smem + (kChainMaxK * 2) / 16;            // two weight buffers
+    uint16_t *xin = reinterpret_cast<uint16_t *>(smem);   // the staged input, four planes
+    uint4 *bufs = smem + kXinBytes / 16;                   // two weight buffers
     ChainMat *dtab = reinterpret_cast<ChainMat *>(bufs + 2 * (kWeightBuf / 16));
+    RowBlock *ptab = reinterpret_cast<RowBlock *>(dtab + kDescCache);  // this workgroup's plans
     __shared__ double dred[8];
     __shared__ int stop_s, bad_s;
     const int nwg = gridDim.x;
@@ -362,6 +381,10 @@ __global__ __launch_bounds__(kChainThreads) void chain_kernel(const ChainMat *__
         __builtin_memcpy(&m, w, sizeof(m));
         return m;
     };
+    auto load_plan = [&](int i) __attribute__((always_inline)) {
+        return chain_plan(load_desc(i), i + 1 < n ? (int)dsrc[(long)(i + 1) * kWords + 7] : 0, nwg);
+    };
+    static_assert(offsetof(ChainMat, K) == 28, "K is word 7 of a descriptor");
     for (int i = tid; i < n; i += kChainThreads) {
         const ChainMat m = load_desc(i);
         const int prevN = i > 0 ? load_desc(i - 1).N : 0;
@@ -372,8 +395,12 @@ __global__ __launch_bounds__(kChainThreads) void chain_kernel(const ChainMat *__
     }
     __syncthreads();
     auto get = [&](int i) __attribute__((always_inline)) { return dtab[i % kDescCache]; };
+    auto plan = [&](int i) __attribute__((always_inline)) { return ptab[i % kDescCache]; };
     if (!bad_s) {
-        if (copier) chain_copy(get(0), chain_block(get(0), nwg), bufs);
+        // (plans only of checked descriptors)
+        for (int i = tid; i < min(n, kDescCache); i += kChainThreads) ptab[i] = load_plan(i);
+        lds_barrier();
+        if (copier) chain_copy(get(0), plan(0), bufs);
         for (int i = 0; i < n; ++i) {
             const ChainMat m = get(i);
             const int K = m.K;
@@ -382,9 +409,10 @@ __global__ __launch_bounds__(kChainThreads) void chain_kernel(const ChainMat *__
             if (i == 0) {
                 const uint4 *x16 = reinterpret_cast<const uint4 *>(x0);
                 uint4 *r16 = reinterpret_cast<uint4 *>(xin);
+                const int Gs = chain_plane(K >> 5);
                 for (int c = tid; c < (K >> 3); c += kChainThreads) {
                     const uint4 v = x16[c];
-                    r16[c] = make_uint4(__builtin_amdgcn_perm(v.z, v.x, 0x05040100u),
+                    r16[(c & 3) * Gs + (c >> 2)] = make_uint4(__builtin_amdgcn_perm(v.z, v.x, 0x05040100u),
                                         __builtin_amdgcn_perm(v.z, v.x, 0x07060302u),
                                         __builtin_amdgcn_perm(v.w, v.y, 0x05040100u),
                                         __builtin_amdgcn_perm(v.w, v.y, 0x07060302u));
@@ -406,13 +434,16 @@ __global__ __launch_bounds__(kChainThreads) void chain_kernel(const ChainMat *__
                 const double inv = renorm_scale(chain_sum_squares(K, v, dred, rn, i & 1), K);
                 if (stop_s) break;
                 if (rn) {
+                    const int Gs = chain_plane(K >> 5);
 #pragma unroll
                     for (int j = 0; j < kPollJ; ++j) {
                         const int c = tid + kPollThreads * j;
                         if (c < (K >> 2)) {
-                            // chunk c holds values 4(c&1)..+3 of block c>>1:
-                            // value e of a block sits at position 2(e&3) + (e>>2)
-                            uint16_t *blk = xin + (c >> 1) * 8 + (c & 1);
+                            // chunk c holds values 4(c&1)..+3 of block u = c>>1
+                            // (uint4 u & 3 of group u >> 2): value e of a block
+                            // sits at position 2(e&3) + (e>>2)
+                            const int u = c >> 1;
+                            uint16_t *blk = xin + ((u & 3) * Gs + (u >> 2)) * 8 + (c & 1);
                             blk[0] = renorm_value(v[j].x, inv, 0);
                             blk[2] = renorm_value(v[j].y, inv, 0);
                             blk[4] = renorm_value(v[j].z, inv, 0);
@@ -426,18 +457,21 @@ __global__ __launch_bounds__(kChainThreads) void chain_kernel(const ChainMat *__
             if (copier) {
                 // 2. the copy waves request the next step's block
                 if (i + 1 < n)
-                    chain_copy(get(i + 1), chain_block(get(i + 1), nwg), bufs + ((i + 1) & 1) * (kWeightBuf / 16));
+                    chain_copy(get(i + 1), plan(i + 1), bufs + ((i + 1) & 1) * (kWeightBuf / 16));
             } else {
                 // 3. this step's rows
                 RowSink sink;
                 sink.cells = regions + (long)i * kChainMaxK;
-                sink.k_next = i + 1 < n ? get(i + 1).K : 0;
                 sink.tag = epoch + (unsigned)(i + 1);
-                chain_rows_any(m, chain_block(m, nwg), bufs + (i & 1) * (kWeightBuf / 16), xin, sink);
-                // refill: descriptor i + kDescCache/2 into the slot of i - kDescCache/2
+                chain_rows_any(m, plan(i), bufs + (i & 1) * (kWeightBuf / 16), xin, sink);
+                // refill: descriptor i + kDescCache/2 (and its plan) into the
+                // slot of i - kDescCache/2
                 const int j = i + kDescCache / 2;
-                if (wave == kComputeWaves - 1 && j >= kDescCache && j < n && (tid & 63) < kWords)
-                    dwords[(j % kDescCache) * kWords + (tid & 63)] = dsrc[(long)j * kWords + (tid & 63)];
+                if (wave == kComputeWaves - 1 && j >= kDescCache && j < n) {
+                    if ((tid & 63) < kWords)
+                        dwords[(j % kDescCache) * kWords + (tid & 63)] = dsrc[(long)j * kWords + (tid & 63)];
+                    if ((tid & 63) == kWords) ptab[j % kDescCache] = load_plan(j);
+                }
             }
         }
     } else if (blockIdx.x == 0 && tid == 0) {
@@ -459,7 +493,11 @@ __global__ __launch_bounds__(kChainThreads) void chain_kernel(const ChainMat *__
     }
 }
 
-size_t chain_lds_bytes() { return (size_t)kChainMaxK * 2 + 2 * (size_t)kWeightBuf + kDescCache * sizeof(ChainMat); }
+static_assert(kXinBytes + 2 * kWeightBuf + kDescCache * 64 + 256 <= 160 * 1024, "LDS of one workgroup");
+
+size_t chain_lds_bytes() {
+    return (size_t)kXinBytes + 2 * (size_t)kWeightBuf + kDescCache * (sizeof(ChainMat) + sizeof(RowBlock));
+}
 
 hipError_t launch_chain(const void *desc, int n, const uint16_t *x0, void *sync, unsigned spin_limit,
                         hipStream_t stream) {

@@ -204,7 +204,7 @@ def w4_chain_desc(mats, ys):
 def w4_chain_sync_bytes(n_mats: int) -> int:
     """Bytes of the sync buffer of a chain of n_mats matrices
     (W4_CHAIN_SYNC_BYTES(n_mats) of w4.h)."""
-    return 256 + n_mats * 65536
+    return 256 + n_mats * 32768
 
 
 def w4_chain_sync(n_mats: int, device="cuda"):

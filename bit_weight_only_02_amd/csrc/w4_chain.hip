@@ -9,13 +9,17 @@
 // of matrix i; matrix i+1 needs all of the renormalised output of matrix i.
 //
 // Exchange.  There is no separate grid barrier: every output that the next
-// matrix needs is published as one 8-byte cell {value, tag} (a single store),
-// the tag naming the call and the step.  A consumer reads the cells it needs
-// and accepts each one whose tag is the expected one; cells with an older tag
-// are read again (bounded; a timeout sets the error word).  One round trip
-// through memory thus both waits for the producers and brings their values.
-// Each step has its own cell region, so a fast workgroup can never overwrite
-// values that a slow one has yet to read.
+// matrix needs is published as one 4-byte cell holding the bitwise complement
+// of the value (NaNs stored as one quiet NaN, so no written cell is zero),
+// and a cell that is still zero has not been written.  A consumer reads the
+// cells it needs until none is zero (bounded; a timeout sets the error word):
+// one round trip through memory both waits for the producers and brings
+// their values.  Each step has its own cell region, so a fast workgroup never
+// overwrites values that a slow one has yet to read.  Regions go back to zero
+// within the call: once a workgroup has read all of step s-1's cells, every
+// workgroup has finished reading step s-2's (each wrote its step s-1 cells
+// only after that), so it clears its own cells of step s-2; the last
+// workgroup out clears the last region that was read.
 //
 // Per step i (one workgroup of eight waves per CU; workgroup b owns the
 // contiguous row block [b*ceil(N/nwg), ...) of every matrix):
@@ -66,11 +70,10 @@ constexpr int kChainMaxK = 8192;
 __device__ __forceinline__ int chain_plane(int G) { return ((G + 7) >> 4) * 16 + 8; }
 constexpr int kXinBytes = 4 * (((kChainMaxK / 32 + 7) >> 4) * 16 + 8) * 16;
 constexpr int kWeightBuf = 64 * 1024;  // bytes of each of the two LDS weight buffers
-// sync buffer: bytes [0, 256) a header (word 0 exit counter, word 1 epoch --
-// the tags used by earlier calls --, word 2 error); from byte 256, one region
-// of kChainMaxK 8-byte cells per matrix.
-constexpr int kSyncExit = 0, kSyncEpoch = 1, kSyncError = 2;
-constexpr long kExchOffset = 256, kExchBytes = (long)kChainMaxK * 8;
+// sync buffer: bytes [0, 256) a header (word 0 exit counter, word 2 error);
+// from byte 256, one region of kChainMaxK 4-byte cells per matrix.
+constexpr int kSyncExit = 0, kSyncError = 2;
+constexpr long kExchOffset = 256, kExchBytes = (long)kChainMaxK * 4;
 static_assert(W4_CHAIN_SYNC_BYTES(1) == kExchOffset + kExchBytes, "sync layout");
 
 __device__ __forceinline__ float load_agent(const float *p) {
@@ -162,19 +165,21 @@ __device__ __forceinline__ void chain_copy(const ChainMat &m, const RowBlock &b,
     }
 }
 
-// One exchange cell {value, tag}, published with a single 8-byte store that
-// agent-scope loads on any XCD see.
-__device__ __forceinline__ void store_cell(uint2 *cells, int row, float v, unsigned tag) {
-    const uint64_t c = (uint64_t)__float_as_uint(v) | ((uint64_t)tag << 32);
-    __hip_atomic_store(reinterpret_cast<uint64_t *>(cells + row), c, __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
+// One exchange cell: the complement of the value's bits, published with a
+// single 4-byte store that agent-scope loads on any XCD see.
+__device__ __forceinline__ void store_cell(uint32_t *cells, int row, float v) {
+    const uint32_t bits = v == v ? __float_as_uint(v) : 0x7FC00000u;
+    __hip_atomic_store(cells + row, ~bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void clear_cell(uint32_t *cells, int row) {
+    __hip_atomic_store(cells + row, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Where the rows of one step go: y, and the cells of rows < k_next (the
 // leading entries the next step reads; k_next 0 for the last step).
 struct RowSink {
-    uint2 *cells;
-    unsigned tag;
+    uint32_t *cells;
 };
 
 // Computing waves: the rows of the block, L lanes per row, NG groups per lane;
@@ -217,7 +222,7 @@ __device__ __forceinline__ void chain_rows(const ChainMat &m, const RowBlock &b,
             // (a global store: through the generic pointer it would be a flat
             // store, which every later LDS read would have to wait for)
             ((__attribute__((address_space(1))) float *)m.y)[row] = v;
-            if (row < b.k_next) store_cell(sink.cells, row, v, sink.tag);
+            if (row < b.k_next) store_cell(sink.cells, row, v);
         }
     };
     // A pass gives each computing wave SLOTS rows.  Waves whose rows are all
@@ -271,17 +276,16 @@ __device__ __forceinline__ void chain_rows_any(const ChainMat &m, const RowBlock
     }
 }
 
-// Waves 0..3: read the K cells of one region until every tag equals `tag`.
-// Thread t owns the 4-value chunks c = t, t+256, ... (the order of the sum of
-// squares) and re-reads only chunks not yet complete.  A bounded number of
-// rounds; a timeout (or an error raised elsewhere) returns 1.
+// Waves 0..3: read the K cells of one region until none is zero.  Thread t
+// owns the 4-value chunks c = t, t+256, ... (the order of the sum of squares)
+// and re-reads only chunks not yet complete.  A bounded number of rounds; a
+// timeout (or an error raised elsewhere) returns 1.
 constexpr int kPollJ = kChainMaxK / 4 / kPollThreads;
 
-__device__ __forceinline__ int chain_read_cells(const uint2 *cells, int K, unsigned tag,
-                                                unsigned spin_limit, unsigned *sync,
-                                                float4 (&v)[kPollJ]) {
+__device__ __forceinline__ int chain_read_cells(const uint32_t *cells, int K, unsigned spin_limit,
+                                                unsigned *sync, float4 (&v)[kPollJ]) {
     const int tid = threadIdx.x;
-    const __amdgpu_buffer_rsrc_t r = buffer_rsrc(cells, K * 8);
+    const __amdgpu_buffer_rsrc_t r = buffer_rsrc(cells, K * 4);
     unsigned pend = 0;
 #pragma unroll
     for (int j = 0; j < kPollJ; ++j) {
@@ -289,20 +293,17 @@ __device__ __forceinline__ int chain_read_cells(const uint2 *cells, int K, unsig
         if (tid + kPollThreads * j < (K >> 2)) pend |= 1u << j;
     }
     for (unsigned it = 0;; ++it) {
-        uint4 a[kPollJ], b[kPollJ];
+        uint4 a[kPollJ];
+#pragma unroll
+        for (int j = 0; j < kPollJ; ++j)
+            if (pend & (1u << j))
+                a[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                     r, (tid + kPollThreads * j) * 16, 0, 16));
 #pragma unroll
         for (int j = 0; j < kPollJ; ++j) {
-            if (pend & (1u << j)) {
-                const int off = (tid + kPollThreads * j) * 32;
-                a[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 16));
-                b[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off + 16, 0, 16));
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < kPollJ; ++j) {
-            if ((pend & (1u << j)) && a[j].y == tag && a[j].w == tag && b[j].y == tag && b[j].w == tag) {
-                v[j] = make_float4(__uint_as_float(a[j].x), __uint_as_float(a[j].z),
-                                   __uint_as_float(b[j].x), __uint_as_float(b[j].z));
+            if ((pend & (1u << j)) && a[j].x != 0u && a[j].y != 0u && a[j].z != 0u && a[j].w != 0u) {
+                v[j] = make_float4(__uint_as_float(~a[j].x), __uint_as_float(~a[j].y),
+                                   __uint_as_float(~a[j].z), __uint_as_float(~a[j].w));
                 pend &= ~(1u << j);
             }
         }
@@ -356,9 +357,7 @@ __global__ __launch_bounds__(kChainThreads) void chain_kernel(const ChainMat *__
     const int nwg = gridDim.x;
     const int tid = threadIdx.x, wave = tid >> 6;
     const bool copier = wave >= kCopyWave0;
-    uint2 *regions = reinterpret_cast<uint2 *>(reinterpret_cast<char *>(sync) + kExchOffset);
-    // tags of this call continue from those of earlier calls
-    const unsigned epoch = load_agent_u(sync + kSyncEpoch);
+    uint32_t *regions = reinterpret_cast<uint32_t *>(reinterpret_cast<char *>(sync) + kExchOffset);
 
     // Descriptors: the first kDescCache into an LDS table (entry i in slot
     // i % kDescCache); later ones are brought in kDescCache/2 steps ahead of
@@ -423,7 +422,7 @@ __global__ __launch_bounds__(kChainThreads) void chain_kernel(const ChainMat *__
                 const bool rn = tid < kPollThreads;
                 if (rn) {
                     const int stop = chain_read_cells(regions + (long)(i - 1) * kChainMaxK, K,
-                                                      epoch + (unsigned)i, spin_limit, sync, v);
+                                                      spin_limit, sync, v);
                     if (stop) stop_s = 1;
                 } else {
 #pragma unroll
@@ -462,8 +461,14 @@ __global__ __launch_bounds__(kChainThreads) void chain_kernel(const ChainMat *__
                 // 3. this step's rows
                 RowSink sink;
                 sink.cells = regions + (long)i * kChainMaxK;
-                sink.tag = epoch + (unsigned)(i + 1);
                 chain_rows_any(m, plan(i), bufs + (i & 1) * (kWeightBuf / 16), xin, sink);
+                // step i-1's cells are all in: every workgroup is done with
+                // step i-2's, so this one clears its own
+                if (wave == kComputeWaves - 1 && i >= 2) {
+                    const RowBlock q = plan(i - 2);
+                    uint32_t *cells = regions + (long)(i - 2) * kChainMaxK;
+                    for (int r = q.rb + (tid & 63); r < min(q.re, q.k_next); r += 64) clear_cell(cells, r);
+                }
                 // refill: descriptor i + kDescCache/2 (and its plan) into the
                 // slot of i - kDescCache/2
                 const int j = i + kDescCache / 2;
@@ -477,19 +482,23 @@ __global__ __launch_bounds__(kChainThreads) void chain_kernel(const ChainMat *__
     } else if (blockIdx.x == 0 && tid == 0) {
         __hip_atomic_store(sync + kSyncError, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    // Exit: the last workgroup out (every other one has finished and has read
-    // the epoch) advances the epoch past this call's tags and returns the exit
-    // counter to zero.
+    // Exit: the last workgroup out (every other one has finished, so all
+    // reading is over) clears the cells of the last step that were read and
+    // returns the exit counter to zero.
+    __shared__ int last_s;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     lds_barrier();
     if (tid == 0) {
         const unsigned prev = __hip_atomic_fetch_add(sync + kSyncExit, 1u, __ATOMIC_RELAXED,
                                                      __HIP_MEMORY_SCOPE_AGENT);
-        if (prev == (unsigned)nwg - 1) {
-            __hip_atomic_store(sync + kSyncEpoch, epoch + (unsigned)n, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(sync + kSyncExit, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
+        last_s = prev == (unsigned)nwg - 1;
+        if (last_s) __hip_atomic_store(sync + kSyncExit, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    lds_barrier();
+    if (last_s && !bad_s && n >= 2) {
+        const int kl = (int)dsrc[(long)(n - 1) * kWords + 7];
+        uint32_t *cells = regions + (long)(n - 2) * kChainMaxK;
+        for (int r = tid; r < kl; r += kChainThreads) clear_cell(cells, r);
     }
 }
 

@@ -184,19 +184,20 @@ int w4_rms_renorm(const float *v, int64_t ldv, int32_t K, int32_t rows, void *ou
  *   desc: DEVICE array of n_mats records (it is read by the kernel).
  *   sync: device buffer of sync_bytes >= W4_CHAIN_SYNC_BYTES(n_mats) bytes,
  *         16-byte aligned, all zero before the first call and then owned by
- *         the chain (it carries the tags of earlier calls and one region of
- *         exchange cells per matrix; reuse it only for chains run one after
- *         another on one stream).  Word 2 is an error word written by the
- *         kernel: 1 if a wait for another workgroup's outputs timed out
- *         (results incomplete), 2 if a record was invalid (N < 1, K not a
- *         multiple of 32, K larger than W4_MAX_K_CHAIN or than the previous N,
- *         a null or misaligned pointer; nothing computed).  The caller clears
- *         it after reading it.
+ *         the chain (a header and one region of exchange cells per matrix; a
+ *         call that ends without error leaves it all zero again, so it can be
+ *         reused by chains run one after another on one stream).  Word 2 is
+ *         an error word written by the kernel: 1 if a wait for another
+ *         workgroup's outputs timed out (results incomplete), 2 if a record
+ *         was invalid (N < 1, K not a multiple of 32, K larger than
+ *         W4_MAX_K_CHAIN or than the previous N, a null or misaligned pointer;
+ *         nothing computed).  After an error the caller zeroes the whole
+ *         buffer before the next call.
  * One workgroup per CU, all resident at once on an otherwise idle device; if
  * they cannot all run together the bounded waits end with error 1 rather than
  * a hang.  Concurrent chains must use different sync buffers.
  */
-#define W4_CHAIN_SYNC_BYTES(n_mats) (256 + (int64_t)(n_mats) * 65536)
+#define W4_CHAIN_SYNC_BYTES(n_mats) (256 + (int64_t)(n_mats) * 32768)
 typedef struct {
     const uint32_t *codes; /* device, 16-byte aligned */
     const uint16_t *steps; /* device */

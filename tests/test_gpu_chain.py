@@ -69,6 +69,8 @@ def test_chain_ragged_shapes(w4):
     w4.w4_gemv_chain(desc, x0, sync)
     torch.cuda.synchronize()
     assert sync[0].item() == 0 and sync[2].item() == 0
+    # a call that ends without error leaves every exchange cell cleared
+    assert int(torch.count_nonzero(sync)) == 0
     check_teacher_forced(w4, mats, x0, ys)
     # a second call reuses the sync buffer and reproduces every output bitwise
     first = [y.clone() for y in ys]
@@ -91,6 +93,7 @@ def test_chain_decode_sweep_35_layers(w4):
     w4.w4_gemv_chain(desc, x0, sync)
     torch.cuda.synchronize()
     assert sync[0].item() == 0 and sync[2].item() == 0
+    assert int(torch.count_nonzero(sync)) == 0
 
     def rows(N):
         return [(0, 64), (N // 2, N // 2 + 64), (N - 64, N)]

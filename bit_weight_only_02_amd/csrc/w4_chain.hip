@@ -327,9 +327,12 @@ __device__ __forceinline__ double chain_sum_squares(int K, const float4 (&v)[kPo
     const int tid = threadIdx.x;
     double ss = 0.0;
     if (active) {
+        // chunks past the end hold zeros, and adding +0 leaves the sum's bits
+        // unchanged: the bound is the wave-uniform chunk count, no lane test
+        const int jn = ((K >> 2) + kPollThreads - 1) / kPollThreads;
 #pragma unroll
         for (int j = 0; j < kPollJ; ++j) {
-            if (tid + kPollThreads * j < (K >> 2)) {
+            if (j < jn) {
                 ss += (double)v[j].x * (double)v[j].x;
                 ss += (double)v[j].y * (double)v[j].y;
                 ss += (double)v[j].z * (double)v[j].z;
@@ -434,19 +437,26 @@ __global__ __launch_bounds__(kChainThreads) void chain_kernel(const ChainMat *__
                 if (stop_s) break;
                 if (rn) {
                     const int Gs = chain_plane(K >> 5);
+                    const int jn = ((K >> 2) + kPollThreads - 1) / kPollThreads;
+                    uint2 *x8 = reinterpret_cast<uint2 *>(xin);
 #pragma unroll
                     for (int j = 0; j < kPollJ; ++j) {
-                        const int c = tid + kPollThreads * j;
-                        if (c < (K >> 2)) {
+                        if (j < jn) {
                             // chunk c holds values 4(c&1)..+3 of block u = c>>1
-                            // (uint4 u & 3 of group u >> 2): value e of a block
-                            // sits at position 2(e&3) + (e>>2)
+                            // (uint4 u & 3 of group u >> 2), whose pair order is
+                            // (x0,x4)(x1,x5)(x2,x6)(x3,x7): the even lane of a
+                            // pair writes the first two words, the odd lane the
+                            // last two, each taking two halves from the other
+                            const int c = tid + kPollThreads * j;
+                            const uint32_t h0 = renorm_value(v[j].x, inv, 0), h1 = renorm_value(v[j].y, inv, 0);
+                            const uint32_t h2 = renorm_value(v[j].z, inv, 0), h3 = renorm_value(v[j].w, inv, 0);
+                            const bool odd = c & 1;
+                            const uint32_t give = odd ? (h0 | (h1 << 16)) : (h2 | (h3 << 16));
+                            const uint32_t got = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)give, 0xB1, 0xF, 0xF, false);
+                            const uint2 w = odd ? make_uint2((got & 0xFFFFu) | (h2 << 16), (got >> 16) | (h3 << 16))
+                                                : make_uint2(h0 | (got << 16), h1 | (got & 0xFFFF0000u));
                             const int u = c >> 1;
-                            uint16_t *blk = xin + ((u & 3) * Gs + (u >> 2)) * 8 + (c & 1);
-                            blk[0] = renorm_value(v[j].x, inv, 0);
-                            blk[2] = renorm_value(v[j].y, inv, 0);
-                            blk[4] = renorm_value(v[j].z, inv, 0);
-                            blk[6] = renorm_value(v[j].w, inv, 0);
+                            if (c < (K >> 2)) x8[((u & 3) * Gs + (u >> 2)) * 2 + (c & 1)] = w;
                         }
                     }
                 }

@@ -111,6 +111,40 @@ __device__ __forceinline__ float group_dot(uint4 q, const h2 *xr) {
     return __builtin_fmaf(hi, 0.0625f, lo);
 }
 
+// The same sum with the offset taken out of the loop: sum_k (c_k - 8) x_k =
+// sum_k c_k x_k - 8 sum_k x_k.  group_dot_raw returns the two raw partial
+// sums {even nibbles, odd nibbles (times 16)} of c * 2^-24 * x, in a fixed
+// order; group_offset is the same computation on codes that are all 8, done
+// once per activation vector.  The difference of the two, taken per partial
+// sum, is exact whenever the sums are (integer or one-hot inputs), and is 0
+// exactly for a group whose codes are all 8.  Per packed word: one shift, four
+// ands and four dot2 (the subtractions of 8 move out of the row loop).
+__device__ __forceinline__ float2 group_dot_raw(uint4 q, const h2 *xr) {
+    float lo = 0.0f, hi = 0.0f;
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const uint32_t u = w[k] >> 8;
+        lo = dot2(as_h2(w[k] & 0x000F000Fu), xr[4 * k + 0], lo);
+        hi = dot2(as_h2(w[k] & 0x00F000F0u), xr[4 * k + 1], hi);
+        lo = dot2(as_h2(u & 0x000F000Fu), xr[4 * k + 2], lo);
+        hi = dot2(as_h2(u & 0x00F000F0u), xr[4 * k + 3], hi);
+    }
+    return make_float2(lo, hi);
+}
+
+__device__ __forceinline__ float2 group_offset(const h2 *xr) {
+    // (an opaque all-8 word, so that the compiler emits the very same dot2
+    // sequence rather than folding it into something else)
+    const uint32_t w8 = __builtin_amdgcn_readfirstlane(0x88888888u);
+    return group_dot_raw(make_uint4(w8, w8, w8, w8), xr);
+}
+
+__device__ __forceinline__ float group_dot_off(uint4 q, const h2 *xr, float2 off) {
+    const float2 s = group_dot_raw(q, xr);
+    return __builtin_fmaf(s.y - off.y, 0.0625f, s.x - off.x);
+}
+
 // Sum over each group of L consecutive lanes (L = 8, 16, 32 or 64), left in
 // the group's last lane: shifted adds within rows of 16 lanes (DPP row_shr),
 // then row broadcasts across rows.  A fixed order, so results are reproducible.

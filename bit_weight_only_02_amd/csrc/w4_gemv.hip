@@ -85,6 +85,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(const uint4 *__restrict__ cod
     uint4 *staged = reinterpret_cast<uint4 *>(raw + stage_raw_halves(K));
     const Staging st = stage_x_workgroup(raw, staged, K, dt);
     h2 xr[NG][16];
+    float2 xo[NG];
     if (!st.fallback) {
 #pragma unroll
         for (int i = 0; i < NG; ++i) {
@@ -95,6 +96,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(const uint4 *__restrict__ cod
 #pragma unroll
                 for (int p = 0; p < 16; ++p) xr[i][p] = h2{0, 0};
             }
+            xo[i] = group_offset(xr[i]);
         }
     }
 
@@ -111,7 +113,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(const uint4 *__restrict__ cod
                 if constexpr (decltype(exact_f32)::value)
                     part = group_dot_f32(q[r][i], raw + gc[i] * 32, dt);
                 else
-                    part = group_dot(q[r][i], xr[i]);
+                    part = group_dot_off(q[r][i], xr[i], xo[i]);
                 acc[r] = (g < G) ? __builtin_fmaf(part, bf16_to_f32(sv[r][i]), acc[r]) : acc[r];
             }
         }
@@ -251,6 +253,7 @@ __global__ __launch_bounds__(512) void gemv_ring_kernel(const uint4 *__restrict_
 
     const Staging st = stage_x_workgroup(raw, staged, K, dt);
     h2 xr[NG][16];
+    float2 xo[NG];
     if (!st.fallback) {
 #pragma unroll
         for (int i = 0; i < NG; ++i) {
@@ -261,6 +264,7 @@ __global__ __launch_bounds__(512) void gemv_ring_kernel(const uint4 *__restrict_
 #pragma unroll
                 for (int p = 0; p < 16; ++p) xr[i][p] = h2{0, 0};
             }
+            xo[i] = group_offset(xr[i]);
         }
     }
     const int scale = st.scale;
@@ -289,7 +293,7 @@ __global__ __launch_bounds__(512) void gemv_ring_kernel(const uint4 *__restrict_
                 if constexpr (decltype(exact_f32)::value)
                     part = group_dot_f32(q, raw + gc * 32, dt);
                 else
-                    part = group_dot(q, xr[i]);
+                    part = group_dot_off(q, xr[i], xo[i]);
                 acc = (g < G) ? __builtin_fmaf(part, bf16_to_f32(sv), acc) : acc;
             }
             acc = lane_group_sum<L>(acc);

@@ -209,12 +209,15 @@ __device__ __forceinline__ void chain_rows(const ChainMat &m, const RowBlock &b,
             xr[i][w * 4 + 3] = as_h2(v.w);
         }
     }
+    float2 xo[NG];
+#pragma unroll
+    for (int i = 0; i < NG; ++i) xo[i] = group_offset(xr[i]);
     auto finish = [&](int row, const uint4 (&q)[NG], const uint32_t (&sv)[NG]) __attribute__((always_inline)) {
         float acc = 0.0f;
 #pragma unroll
         for (int i = 0; i < NG; ++i) {
             const int g = l + i * L;
-            acc = (g < G) ? __builtin_fmaf(group_dot(q[i], xr[i]), bf16_to_f32(sv[i]), acc) : acc;
+            acc = (g < G) ? __builtin_fmaf(group_dot_off(q[i], xr[i], xo[i]), bf16_to_f32(sv[i]), acc) : acc;
         }
         acc = lane_group_sum<L>(acc);
         if (l == L - 1 && row < b.re) {
@@ -471,7 +474,12 @@ __global__ __launch_bounds__(kChainThreads) void chain_kernel(const ChainMat *__
                 // 3. this step's rows
                 RowSink sink;
                 sink.cells = regions + (long)i * kChainMaxK;
+                // waves 4 and 5 share SIMDs with waves 0 and 1, and issue
+                // after them at equal priority; raised, they finish their rows
+                // no later than the others
+                if (wave >= 4) __builtin_amdgcn_s_setprio(2);
                 chain_rows_any(m, plan(i), bufs + (i & 1) * (kWeightBuf / 16), xin, sink);
+                __builtin_amdgcn_s_setprio(0);
                 // step i-1's cells are all in: every workgroup is done with
                 // step i-2's, so this one clears its own
                 if (wave == kComputeWaves - 1 && i >= 2) {

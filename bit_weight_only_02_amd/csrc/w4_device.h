@@ -63,62 +63,33 @@ __device__ __forceinline__ int f32_exponent(float v) {
     return (int)((__float_as_uint(v) >> 23) & 0xFFu) - 127;
 }
 
-// Eight codes of one packed word -> four fp16 pairs holding exactly
-// (c - 8) * 2^-24 -- fp16 subnormals -- ordered (c0,c4), (c1,c5), (c2,c6),
-// (c3,c7); the pairs p1 and p3 hold 16 times that, (c - 8) * 2^-20.
-// A nibble masked into the low mantissa bits of an fp16 with a zero exponent
-// field is the subnormal c * 2^-24 (or 16c * 2^-24 four bits higher), so one
-// AND and one packed subtract of 8 * 2^-24 (or 128 * 2^-24) give the exact
-// operand; no OR of an exponent is needed.  Every step is exact as long as fp16
-// subnormals are kept (the default floating-point mode of these kernels).
-__device__ __forceinline__ void unpack_word(uint32_t w, h2 &p0, h2 &p1, h2 &p2, h2 &p3) {
-    const h2 k8 = __builtin_bit_cast(h2, 0x00080008u);    // 8 * 2^-24
-    const h2 k128 = __builtin_bit_cast(h2, 0x00800080u);  // 128 * 2^-24
-    const uint32_t u = w >> 8;
-    p0 = as_h2(w & 0x000F000Fu) - k8;
-    p1 = as_h2(w & 0x00F000F0u) - k128;
-    p2 = as_h2(u & 0x000F000Fu) - k8;
-    p3 = as_h2(u & 0x00F000F0u) - k128;
-}
+// Unpack.  A nibble masked into the low mantissa bits of an fp16 with a zero
+// exponent field is the subnormal c * 2^-24 (or 16c * 2^-24 when it sits four
+// bits higher), so one AND turns codes into exact fp16 operands, two per
+// 32-bit lane: w & 0x000F000F gives (c0, c4), w & 0x00F000F0 gives 16 (c1, c5),
+// and the same masks on w >> 8 give (c2, c6) and 16 (c3, c7).  Every step is
+// exact as long as fp16 subnormals are kept (the default floating-point mode
+// of these kernels).  The activations are staged in the matching pair order
+// (x0,x4) (x1,x5) (x2,x6) (x3,x7) of each 8-value block.
 
 __device__ __forceinline__ float dot2(h2 a, h2 b, float c) {
     return __builtin_amdgcn_fdot2(a, b, c, false);
 }
 
-// group_dot returns its sum scaled by 2^-kGroupDotExp; the caller multiplies
-// the finished row by 2^kGroupDotExp (exact, a power of two).
+// Group sums come out scaled by 2^-kGroupDotExp; the caller multiplies the
+// finished row by 2^kGroupDotExp (exact, a power of two).
 constexpr int kGroupDotExp = 24;
 
-// Sum over one group of 32 codes, times 2^-24: q holds the 4 packed words, xr
-// the 16 staged activation pairs of the group in the order unpack_word
-// produces.  Every product (c - 8) * 2^-24 * x is exact in fp32; the pairs
-// p0/p2 and p1/p3 go to separate fp32 accumulators, joined with a factor 1/16.
-__device__ __forceinline__ float group_dot(uint4 q, const h2 *xr) {
-    h2 a0, a1, a2, a3;
-    float lo = 0.0f, hi = 0.0f;
-    unpack_word(q.x, a0, a1, a2, a3);
-    lo = dot2(a0, xr[0], lo); hi = dot2(a1, xr[1], hi);
-    lo = dot2(a2, xr[2], lo); hi = dot2(a3, xr[3], hi);
-    unpack_word(q.y, a0, a1, a2, a3);
-    lo = dot2(a0, xr[4], lo); hi = dot2(a1, xr[5], hi);
-    lo = dot2(a2, xr[6], lo); hi = dot2(a3, xr[7], hi);
-    unpack_word(q.z, a0, a1, a2, a3);
-    lo = dot2(a0, xr[8], lo); hi = dot2(a1, xr[9], hi);
-    lo = dot2(a2, xr[10], lo); hi = dot2(a3, xr[11], hi);
-    unpack_word(q.w, a0, a1, a2, a3);
-    lo = dot2(a0, xr[12], lo); hi = dot2(a1, xr[13], hi);
-    lo = dot2(a2, xr[14], lo); hi = dot2(a3, xr[15], hi);
-    return __builtin_fmaf(hi, 0.0625f, lo);
-}
-
-// The same sum with the offset taken out of the loop: sum_k (c_k - 8) x_k =
-// sum_k c_k x_k - 8 sum_k x_k.  group_dot_raw returns the two raw partial
-// sums {even nibbles, odd nibbles (times 16)} of c * 2^-24 * x, in a fixed
-// order; group_offset is the same computation on codes that are all 8, done
-// once per activation vector.  The difference of the two, taken per partial
-// sum, is exact whenever the sums are (integer or one-hot inputs), and is 0
-// exactly for a group whose codes are all 8.  Per packed word: one shift, four
-// ands and four dot2 (the subtractions of 8 move out of the row loop).
+// Sum over one group of 32 codes, sum_k (c_k - 8) x_k times 2^-24, with the
+// offset taken out of the row loop: sum_k c_k x_k - 8 sum_k x_k.  q holds the
+// group's 4 packed words, xr its 16 staged activation pairs.
+// group_dot_raw returns the two raw partial sums {even nibbles, odd nibbles
+// (times 16)} of c * 2^-24 * x -- every product exact in fp32 -- in a fixed
+// order of dot2 steps; group_offset is the same computation on codes that are
+// all 8, done once per activation vector.  The difference of the two, taken
+// per partial sum and joined with a factor 1/16, is exact whenever the sums
+// are (integer or one-hot inputs), and is exactly 0 for a group whose codes
+// are all 8.  Per packed word: one shift, four ands and four dot2.
 __device__ __forceinline__ float2 group_dot_raw(uint4 q, const h2 *xr) {
     float lo = 0.0f, hi = 0.0f;
     const uint32_t w[4] = {q.x, q.y, q.z, q.w};
@@ -294,7 +265,7 @@ struct Staging {
 
 // Workgroup-wide staging: the raw vector (K halves in LDS, landed and visible
 // to every wave) is converted once per workgroup -- every thread takes whole
-// 8-value chunks -- into staged[c], chunk c as four fp16 pairs in unpack_word
+// 8-value chunks -- into staged[c], chunk c as four fp16 pairs in unpack
 // order, (x0,x4) (x1,x5) (x2,x6) (x3,x7).  fp16 values are only permuted; bf16
 // values are scaled by 2^s, s = 14 - (largest exponent of the vector), exactly.
 // Every thread returns the same {s, fallback}; fallback is set when some value

@@ -22,14 +22,54 @@
 
 namespace w4 {
 
+// Expert-indexed use of the same kernel (see launch_gemv_pairs): pair
+// p = blockIdx.y reads the matrix of expert a = ids[p] (slot_of[ids[p]] with a
+// slot pool) at codes + a*stride_c4, steps + a*stride_s, multiplies the
+// activation row p (x_per_pair) or p / topk, and writes row p of the output
+// (times row_scale[ids[p]] when given).  ids == nullptr: a plain product.
+struct GemvPairs {
+    const int32_t *ids;
+    const int32_t *slot_of;
+    const float *row_scale;
+    int32_t *dev_err;
+    int64_t stride_c4, stride_s;
+    long ldx;
+    int n_experts, n_slots, x_per_pair, topk;
+};
+
 template <int L, int NG, int R, int PF>
 __global__ __launch_bounds__(256) void gemv_kernel(const uint4 *__restrict__ codes,
                                                    const uint16_t *__restrict__ steps,
                                                    int N, int K,
                                                    const uint16_t *__restrict__ x, int dt,
-                                                   float *__restrict__ y) {
+                                                   float *__restrict__ y, const GemvPairs bp) {
     constexpr int SLOTS = kWave / L;
     extern __shared__ _Float16 xs[];  // the raw activations (stage_raw_halves(K))
+    // This workgroup's expert (uniform: scalar loads).  An id or slot out of
+    // range leaves no row untouched: the pair's rows become NaN and the error
+    // word is set.  The weight address is the only place the slot enters.
+    const float *rs = nullptr;
+    if (bp.ids) {
+        const int p = blockIdx.y;
+        const int e = bp.ids[p];
+        int a = e;
+        bool bad = e < 0 || e >= bp.n_experts;
+        if (!bad && bp.slot_of) {
+            a = bp.slot_of[e];
+            bad = a < 0 || a >= bp.n_slots;
+        }
+        y += (long)p * N;
+        if (bad) {
+            for (int n = blockIdx.x * blockDim.x + threadIdx.x; n < N; n += gridDim.x * blockDim.x)
+                y[n] = __builtin_nanf("");
+            if (blockIdx.x == 0 && threadIdx.x == 0 && bp.dev_err) *bp.dev_err = 1;
+            return;
+        }
+        codes += a * bp.stride_c4;
+        steps += a * bp.stride_s;
+        x += (long)(bp.x_per_pair ? p : p / bp.topk) * bp.ldx;
+        if (bp.row_scale) rs = bp.row_scale + (long)e * N;
+    }
     const int G = K >> 5;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int nwaves = blockDim.x >> 6;
@@ -121,8 +161,10 @@ __global__ __launch_bounds__(256) void gemv_kernel(const uint4 *__restrict__ cod
         for (int r = 0; r < R; ++r) {
             acc[r] = lane_group_sum<L>(acc[r]);
             const int row = r0 + (r * nwaves + wave) * SLOTS + slot;
-            if (l == L - 1 && row < N)
-                y[row] = decltype(exact_f32)::value ? acc[r] : __builtin_ldexpf(acc[r], kGroupDotExp - st.scale);
+            if (l == L - 1 && row < N) {
+                const float v = decltype(exact_f32)::value ? acc[r] : __builtin_ldexpf(acc[r], kGroupDotExp - st.scale);
+                y[row] = rs ? v * rs[row] : v;
+            }
         }
     };
 
@@ -314,7 +356,9 @@ __global__ __launch_bounds__(512) void gemv_ring_kernel(const uint4 *__restrict_
 
 namespace {
 
-typedef void (*GemvFn)(const uint4 *, const uint16_t *, int, int, const uint16_t *, int, float *);
+typedef void (*GemvFn)(const uint4 *, const uint16_t *, int, int, const uint16_t *, int, float *,
+                       const GemvPairs);
+typedef void (*RingFn)(const uint4 *, const uint16_t *, int, int, const uint16_t *, int, float *);
 
 template <int L, int NG>
 GemvFn pick_r(int R, int pf) {
@@ -350,7 +394,7 @@ GemvFn pick(int L, int NG, int R, int pf) {
 }
 
 template <int L, int NG>
-GemvFn pick_ring_d(int D) {
+RingFn pick_ring_d(int D) {
     switch (D) {
         case 2: return gemv_ring_kernel<L, NG, 2>;
         case 3: return gemv_ring_kernel<L, NG, 3>;
@@ -361,7 +405,7 @@ GemvFn pick_ring_d(int D) {
     return nullptr;
 }
 
-GemvFn pick_ring(int L, int NG, int D) {
+RingFn pick_ring(int L, int NG, int D) {
     switch (L * 16 + NG) {
         case 16 * 16 + 3: return pick_ring_d<16, 3>(D);
         case 16 * 16 + 4: return pick_ring_d<16, 4>(D);
@@ -453,7 +497,7 @@ hipError_t launch_gemv(const uint32_t *codes, const uint16_t *steps, int N, int 
     if (t.ring) {
         // the ring kernel's preconditions (a bad override is refused)
         const int G = K / 32;
-        GemvFn fn = pick_ring(t.L, t.NG, t.ring);
+        RingFn fn = pick_ring(t.L, t.NG, t.ring);
         if (!fn || G == 0 || G % 8 != 0 || t.NG != (G + t.L - 1) / t.L ||
             (reinterpret_cast<uintptr_t>(steps) & 15) != 0 || t.waves < 1 || t.waves > 8)
             return hipErrorInvalidConfiguration;
@@ -468,7 +512,47 @@ hipError_t launch_gemv(const uint32_t *codes, const uint16_t *steps, int N, int 
     if (!fn) return hipErrorInvalidConfiguration;
     const size_t lds = (size_t)2 * stage_raw_halves(K) * sizeof(_Float16);
     hipLaunchKernelGGL(fn, dim3(t.blocks), dim3(64 * t.waves), lds, stream,
-                       reinterpret_cast<const uint4 *>(codes), steps, N, K, x, dt, y);
+                       reinterpret_cast<const uint4 *>(codes), steps, N, K, x, dt, y, GemvPairs{});
+    return hipGetLastError();
+}
+
+// Expert-indexed products with one activation row per pair: P products of
+// [N][K] matrices in one launch, gridDim.y = P, the tile of a single [N][K]
+// product; about 1024 workgroups in all, so that each loops over a couple of
+// row steps (the activation staging is paid once per workgroup).
+// W4_MOE_GEMV_BLOCKS overrides the workgroups per pair (schedule sweeps).
+hipError_t launch_gemv_pairs(const uint32_t *codes_base, const uint16_t *steps_base, int64_t stride_codes,
+                             int64_t stride_steps, int N, int K, const uint16_t *X, long ldx, int dt,
+                             int x_per_pair, const int32_t *ids, int P, int topk, const int32_t *slot_of,
+                             int n_experts, int n_slots, const float *row_scale, float *out,
+                             int32_t *dev_err, hipStream_t stream) {
+    const GemvTile t = gemv_tile(N, K);
+    int R = 1, pf = 0;
+    // W4_MOE_GEMV_RPF="R,pf": rows per slot in flight and prefetch (sweeps)
+    if (const char *e = getenv("W4_MOE_GEMV_RPF")) sscanf(e, "%d,%d", &R, &pf);
+    GemvFn fn = pick(t.L, t.NG, R, pf);
+    if (!fn || P < 1 || P > 65535) return hipErrorInvalidConfiguration;
+    const long rows_per_iter = (long)(64 / t.L) * t.waves * R;
+    const long need = (N + rows_per_iter - 1) / rows_per_iter;
+    long bx = (1024 + P - 1) / P;
+    if (const char *e = getenv("W4_MOE_GEMV_BLOCKS")) bx = atol(e);
+    if (bx > need) bx = need;
+    if (bx < 1) bx = 1;
+    GemvPairs bp;
+    bp.ids = ids;
+    bp.slot_of = slot_of;
+    bp.row_scale = row_scale;
+    bp.dev_err = dev_err;
+    bp.stride_c4 = stride_codes / 4;
+    bp.stride_s = stride_steps;
+    bp.ldx = ldx;
+    bp.n_experts = n_experts;
+    bp.n_slots = n_slots;
+    bp.x_per_pair = x_per_pair;
+    bp.topk = topk;
+    const size_t lds = (size_t)2 * stage_raw_halves(K) * sizeof(_Float16);
+    hipLaunchKernelGGL(fn, dim3((unsigned)bx, (unsigned)P), dim3(64 * t.waves), lds, stream,
+                       reinterpret_cast<const uint4 *>(codes_base), steps_base, N, K, X, dt, out, bp);
     return hipGetLastError();
 }
 

@@ -23,10 +23,73 @@ __global__ __launch_bounds__(256) void rms_renorm_kernel(const float *__restrict
     for (int k = threadIdx.x; k < K; k += 256) out[k] = renorm_value(v[k], inv, out_dt);
 }
 
+// The same for K <= 8192, with each thread's chunks kept in registers between
+// the sum of squares (the same order: chunks t, t+256, ... ascending, then
+// wave_sum_f64, then the four wave sums in order) and the writes, and a single
+// workgroup barrier.  Bitwise the result of rms_renorm_kernel.
+constexpr int kRenormRegJ = 8;  // chunks per thread: K <= 256 * 4 * 8
+
+__global__ __launch_bounds__(256) void rms_renorm_reg_kernel(const float *__restrict__ v0, long ldv,
+                                                             int K, uint16_t *__restrict__ out0,
+                                                             long ldo, int out_dt) {
+    __shared__ double red[4];
+    const int tid = threadIdx.x;
+    const float *v = v0 + (long)blockIdx.x * ldv;
+    uint16_t *out = out0 + (long)blockIdx.x * ldo;
+    const bool vec = (reinterpret_cast<uintptr_t>(v) & 15) == 0;
+    const bool ovec = (reinterpret_cast<uintptr_t>(out) & 7) == 0;
+    const int n4 = K >> 2;
+    const int jn = (n4 + 255) >> 8;  // uniform
+    float4 x[kRenormRegJ];
+#pragma unroll
+    for (int j = 0; j < kRenormRegJ; ++j) {
+        const int c = tid + 256 * j;
+        x[j] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        if (j < jn && c < n4)
+            x[j] = vec ? reinterpret_cast<const float4 *>(v)[c]
+                       : make_float4(v[4 * c], v[4 * c + 1], v[4 * c + 2], v[4 * c + 3]);
+    }
+    // (chunks past the end are zeros: adding +0 leaves the sum's bits alone)
+    double ss = 0.0;
+#pragma unroll
+    for (int j = 0; j < kRenormRegJ; ++j) {
+        if (j < jn) {
+            ss += (double)x[j].x * (double)x[j].x;
+            ss += (double)x[j].y * (double)x[j].y;
+            ss += (double)x[j].z * (double)x[j].z;
+            ss += (double)x[j].w * (double)x[j].w;
+        }
+    }
+    ss = wave_sum_f64(ss);
+    if ((tid & 63) == 0) red[tid >> 6] = ss;
+    __syncthreads();
+    const double inv = renorm_scale(((red[0] + red[1]) + red[2]) + red[3], K);
+#pragma unroll
+    for (int j = 0; j < kRenormRegJ; ++j) {
+        const int c = tid + 256 * j;
+        if (j < jn && c < n4) {
+            const uint32_t h0 = renorm_value(x[j].x, inv, out_dt), h1 = renorm_value(x[j].y, inv, out_dt);
+            const uint32_t h2 = renorm_value(x[j].z, inv, out_dt), h3 = renorm_value(x[j].w, inv, out_dt);
+            if (ovec) {
+                reinterpret_cast<uint2 *>(out)[c] = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
+            } else {
+                out[4 * c] = (uint16_t)h0;
+                out[4 * c + 1] = (uint16_t)h1;
+                out[4 * c + 2] = (uint16_t)h2;
+                out[4 * c + 3] = (uint16_t)h3;
+            }
+        }
+    }
+}
+
 hipError_t launch_rms_renorm(const float *v, long ldv, int K, int rows, void *out, long ldo,
                              int out_dt, hipStream_t stream) {
-    hipLaunchKernelGGL(rms_renorm_kernel, dim3(rows), dim3(256), 0, stream, v, ldv, K,
-                       static_cast<uint16_t *>(out), ldo, out_dt);
+    if (K <= 256 * 4 * kRenormRegJ)
+        hipLaunchKernelGGL(rms_renorm_reg_kernel, dim3(rows), dim3(256), 0, stream, v, ldv, K,
+                           static_cast<uint16_t *>(out), ldo, out_dt);
+    else
+        hipLaunchKernelGGL(rms_renorm_kernel, dim3(rows), dim3(256), 0, stream, v, ldv, K,
+                           static_cast<uint16_t *>(out), ldo, out_dt);
     return hipGetLastError();
 }
 

@@ -128,11 +128,13 @@ int w4_gemm_smallM(const uint32_t *codes, const uint16_t *steps, int32_t N, int3
  *   route_w: optional float[T][topk].  NULL: Y is float[T*topk][N], one row per
  *      choice.  Non-NULL: Y is float[T][N] = sum over j = 0..topk-1 (ascending)
  *      of route_w[t][j] * (choice j's row).
- *   A choice used by several tokens reads its expert's weights once.
+ *   Up to 4 tokens every choice is its own matrix-vector product (an expert
+ *   chosen by several tokens is read once per token); with more tokens the
+ *   matrix engine reads each distinct expert once for all its tokens.
  *   dev_err: optional device int32; an id or slot out of range sets it to 1 and
  *      fills the affected output rows with NaN (never leaves them untouched).
- *   The combined form (route_w != NULL), and any K > 3072 (summed over
- *   K-slices in a fixed order), stage per-choice rows in a device buffer the
+ *   The combined form (route_w != NULL), and from 5 tokens any K > 3072
+ *   (summed over K-slices in a fixed order), stage per-choice rows in a device buffer the
  *   library allocates once per device and reuses (grown on demand while no
  *   graph capture is active; such calls on one device from different streams
  *   must not overlap).

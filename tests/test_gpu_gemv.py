@@ -214,7 +214,7 @@ def test_gemv_failed_launch_leaves_poisoned_output(w4, monkeypatch):
 
 def test_rms_renorm_within_one_ulp(w4):
     rng = np.random.default_rng(9)
-    for K, dt in [(1536, F16), (2048, F16), (8192, BF16), (704, BF16)]:
+    for K, dt in [(1536, F16), (2048, F16), (8192, BF16), (704, BF16), (12288, F16), (4, BF16)]:
         v = (rng.normal(0, 5, size=K + 100)).astype(np.float32)
         out = w4.w4_rms_renorm(torch.from_numpy(v).cuda(), K,
                                out_dtype=torch.float16 if dt == F16 else torch.bfloat16)

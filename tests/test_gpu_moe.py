@@ -74,13 +74,22 @@ def test_moe_small_vs_oracle_and_pool_identity(w4, T, topk, xpp, dt):
         assert ok, worst
 
 
+def test_moe_few_tokens_on_the_matrix_engine(w4, monkeypatch):
+    """Four tokens forced onto the matrix engine (the path of larger batches):
+    the same parity and pool identity as the default matrix-vector path."""
+    monkeypatch.setenv("W4_MOE_PAIRS_MAX_T", "0")
+    test_moe_small_vs_oracle_and_pool_identity(w4, 4, 8, 1, F16)
+    test_moe_small_vs_oracle_and_pool_identity(w4, 1, 8, 0, BF16)
+
+
 @pytest.mark.parametrize("dt", [F16, BF16])
 def test_moe_long_rows_summed_over_k_slices(w4, dt):
-    """K = 3200 (100 groups) is split into two K-slices whose partial rows are
-    added in order by the finishing pass; also with a bad id (NaN rows)."""
+    """K = 3200 (100 groups) on the matrix engine (five tokens) is split into
+    two K-slices whose partial rows are added in order by the finishing pass;
+    also with a bad id (NaN rows)."""
     print(f"moe k-slices dt={dt}", flush=True)
     rng = np.random.default_rng(40 + dt)
-    E, N, K, S, T, topk = 12, 70, 3200, 12, 3, 4
+    E, N, K, S, T, topk = 12, 70, 3200, 12, 5, 4
     codes, steps = experts(rng, E, N, K)
     ids, route = synth.expert_choice(rng, T, E, topk)
     slot_of, used = synth.slot_map(rng, ids, E, S)
@@ -148,6 +157,30 @@ def test_moe_bad_id_and_missing_slot_give_nan_and_flag(w4):
     Y = run(w4, codes, steps, N, K, X, BF16, ids2, 0, slot_of=slot_of, n_slots=8, err=err)
     assert err.item() == 1
     assert np.all(np.isnan(Y[3])) and not np.any(np.isnan(Y[[0, 1, 2]]))
+
+
+def test_moe_single_token_bad_id_and_missing_slot(w4):
+    """One token runs as side-by-side matrix-vector products: a bad id or a
+    missing slot still gives NaN rows (and the route-weighted row) and the flag."""
+    rng = np.random.default_rng(8)
+    E, N, K = 8, 300, 512
+    codes, steps = experts(rng, E, N, K)
+    X = synth.activations(rng, (1, K), BF16)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ids = np.array([[0, 9, 2]], dtype=np.int32)                # 9 is out of range
+    Y = run(w4, codes, steps, N, K, X, BF16, ids, 0, err=err)
+    assert err.item() == 1
+    assert np.all(np.isnan(Y[1])) and not np.any(np.isnan(Y[[0, 2]]))
+    err.zero_()
+    route = np.array([[0.5, 0.25, 0.25]], dtype=np.float32)
+    Y = run(w4, codes, steps, N, K, X, BF16, ids, 0, route=route, err=err)
+    assert err.item() == 1 and np.all(np.isnan(Y))
+    slot_of = np.array([0, 1, -1, 3, 4, 5, 6, 7], dtype=np.int32)   # expert 2 not resident
+    err.zero_()
+    ids2 = np.array([[0, 1, 2]], dtype=np.int32)
+    Y = run(w4, codes, steps, N, K, X, BF16, ids2, 0, slot_of=slot_of, n_slots=8, err=err)
+    assert err.item() == 1
+    assert np.all(np.isnan(Y[2])) and not np.any(np.isnan(Y[[0, 1]]))
 
 
 def test_moe_many_pairs_share_an_expert(w4):
@@ -235,3 +268,11 @@ def test_rms_renorm_rows(w4):
     for r in range(5):
         ref = oracle.rms_renorm(v[r], 704, BF16).astype(np.int64)
         assert np.all(np.abs(got[r] - ref) <= 1)
+    # odd output row stride: rows 1, 3 start 2 bytes off an 8-byte boundary
+    o = torch.zeros((5, 705), dtype=torch.float16, device="cuda")
+    w4.w4_rms_renorm(torch.from_numpy(v).cuda(), 704, out=o[:, :704])
+    torch.cuda.synchronize()
+    got2 = o.view(torch.int16).cpu().numpy().view(np.uint16).astype(np.int64)
+    for r in range(5):
+        ref = oracle.rms_renorm(v[r], 704, F16).astype(np.int64)
+        assert np.all(np.abs(got2[r, :704] - ref) <= 1) and got2[r, 704] == 0

@@ -359,6 +359,8 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extra", action="store_true", help="only the vocabulary-head step")
+    ap.add_argument("--only", choices=["single", "sweep", "small_m", "moe"],
+                    help="run one secondary workload alone (kernel traces) and print its JSON")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
@@ -373,6 +375,11 @@ def main(argv=None):
 
     torch.cuda.set_device(0)
     timer = Timer(torch)
+    if args.only:
+        run = {"single": extra_single_gemv, "sweep": extra_sweep, "small_m": extra_small_m,
+               "moe": extra_moe}[args.only]
+        print(json.dumps({"workload": args.only, "result": run(w4, torch, np, synth, timer)}), flush=True)
+        return 0
     rng = np.random.default_rng(0)
     codes, steps = synth.w4_matrix(rng, V, K)
     x = synth.activations(rng, K, synth.BF16)

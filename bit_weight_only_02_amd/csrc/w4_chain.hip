@@ -32,8 +32,12 @@
 //      buffer (direct-to-LDS loads that only they wait for, at the start of
 //      the next step: neither the exchange loads of waves 0..3 nor any row
 //      computation queue behind weight traffic);
-//   3. waves 0..5 compute the block's rows from LDS and store y, and the
-//      cells of the rows the next step needs.
+//   3. waves 0..3 compute the block's rows from LDS and store y, and the
+//      cells of the rows the next step needs.  Wave w runs on SIMD w mod 4,
+//      so these are one wave per SIMD; a second computing wave on a SIMD
+//      (waves 4 and 5 did so) measured slower over the decode sweep: its
+//      rows finish last and hold up the next exchange.  Waves 4..5 only
+//      join the workgroup barriers.
 // The descriptors are copied into LDS once (the first kDescCache of them).
 #include <cstdio>
 #include <cstdlib>
@@ -58,7 +62,7 @@ constexpr int kChainThreads = 512;  // eight waves
 constexpr int kChainWaves = kChainThreads / 64;
 constexpr int kPollThreads = 256;   // waves 0..3 read the exchange cells and renormalise
 constexpr int kCopyWave0 = 6;       // waves 6..7 copy weight blocks and compute nothing
-constexpr int kComputeWaves = kCopyWave0;  // waves 0..5 compute rows
+constexpr int kComputeWaves = 4;    // waves 0..3 compute rows (one per SIMD); waves 4..5 only join barriers
 constexpr int kDescCache = 128;     // descriptors kept in LDS
 constexpr int kChainMaxK = 8192;
 
@@ -470,16 +474,11 @@ __global__ __launch_bounds__(kChainThreads) void chain_kernel(const ChainMat *__
                 // 2. the copy waves request the next step's block
                 if (i + 1 < n)
                     chain_copy(get(i + 1), plan(i + 1), bufs + ((i + 1) & 1) * (kWeightBuf / 16));
-            } else {
+            } else if (wave < kComputeWaves) {
                 // 3. this step's rows
                 RowSink sink;
                 sink.cells = regions + (long)i * kChainMaxK;
-                // waves 4 and 5 share SIMDs with waves 0 and 1, and issue
-                // after them at equal priority; raised, they finish their rows
-                // no later than the others
-                if (wave >= 4) __builtin_amdgcn_s_setprio(2);
                 chain_rows_any(m, plan(i), bufs + (i & 1) * (kWeightBuf / 16), xin, sink);
-                __builtin_amdgcn_s_setprio(0);
                 // step i-1's cells are all in: every workgroup is done with
                 // step i-2's, so this one clears its own
                 if (wave == kComputeWaves - 1 && i >= 2) {

@@ -33,6 +33,7 @@ W4_ERR_NODEV = -5
 W4_ERR_HIP = -6
 W4_F16 = 0
 W4_BF16 = 1
+W4_F32_RMS = 2  # w4_moe_gemv_ids: fp32 rows renormalised on load
 W4_MAX_K = 16384
 W4_MAX_K_SMALLM = 16384
 W4_MAX_K_CHAIN = 8192
@@ -144,7 +145,9 @@ def w4_moe_gemv_ids(codes_base, steps_base, expert_stride_codes, expert_stride_s
                     row_scale=None, route_w=None, Y=None, dev_err=None, stream=None):
     """Expert-indexed product (see w4.h).  ``ids`` int32 [T, topk] of real ids;
     strides in uint32 words / uint16 elements; ``slot_of`` int32 [n_experts]
-    selects pool addressing."""
+    selects pool addressing.  A float32 ``X`` is renormalised on load (each
+    row's leading K entries divided by their RMS and rounded to fp16, as
+    w4_rms_renorm does)."""
     T, topk = ids.shape
     if n_experts is None:
         raise ValueError("n_experts is required")
@@ -154,7 +157,8 @@ def w4_moe_gemv_ids(codes_base, steps_base, expert_stride_codes, expert_stride_s
     if Y is None:
         Y = torch.empty((rows, N), dtype=torch.float32, device=X.device)
     _check(lib.w4_moe_gemv_ids(_ptr(codes_base), _ptr(steps_base), expert_stride_codes,
-                               expert_stride_steps, N, K, _ptr(X), _act_dtype(X),
+                               expert_stride_steps, N, K, _ptr(X),
+                               W4_F32_RMS if X.dtype == torch.float32 else _act_dtype(X),
                                1 if x_per_pair else 0, X.stride(0), _ptr(ids), T, topk,
                                _ptr(slot_of), n_experts, n_slots, _ptr(row_scale),
                                _ptr(route_w), _ptr(Y), _ptr(dev_err), _stream(stream)),

@@ -143,7 +143,8 @@ int w4_gemm_smallM(const uint32_t *codes, const uint16_t *steps, int32_t N, int3
     if (K > W4_MAX_K_SMALLM) return fail(W4_ERR_UNSUPPORTED, "K=%d exceeds %d", K, W4_MAX_K_SMALLM);
     if (ldx < K || ldy < N) return fail(W4_ERR_INVALID_ARG, "ldx < K or ldy < N");
     if (N > 0 && (!Y || (K > 0 && !X))) return fail(W4_ERR_INVALID_ARG, "null X/Y");
-    if (X && !aligned(X, 2)) return fail(W4_ERR_ALIGNMENT, "X not 2-byte aligned");
+    if (X && !aligned(X, xdt == W4_F32_RMS ? 4 : 2)) return fail(W4_ERR_ALIGNMENT, "X misaligned");
+    if (xdt == W4_F32_RMS && K % 4) return fail(W4_ERR_INVALID_ARG, "K must be a multiple of 4");
     if (Y && !aligned(Y, 4)) return fail(W4_ERR_ALIGNMENT, "Y not 4-byte aligned");
     if (N == 0) return W4_OK;
     if ((st = device_ready())) return st;
@@ -215,7 +216,7 @@ int w4_moe_gemv_ids(const uint32_t *codes_base, const uint16_t *steps_base,
                     float *Y, int32_t *dev_err, void *stream) {
     int st;
     if ((st = check_matrix(codes_base, steps_base, N, K))) return st;
-    if ((st = check_dtype(xdt))) return st;
+    if (xdt != W4_F32_RMS && (st = check_dtype(xdt))) return st;
     if (K > W4_MAX_K_SMALLM) return fail(W4_ERR_UNSUPPORTED, "K=%d exceeds %d", K, W4_MAX_K_SMALLM);
     if (T < 0 || topk < 1 || topk > W4_MAX_TOPK)
         return fail(W4_ERR_INVALID_ARG, "T=%d topk=%d (topk must be 1..%d)", T, topk, W4_MAX_TOPK);
@@ -229,7 +230,8 @@ int w4_moe_gemv_ids(const uint32_t *codes_base, const uint16_t *steps_base,
         return fail(W4_ERR_INVALID_ARG, "expert strides smaller than one expert matrix");
     if (ldx < K) return fail(W4_ERR_INVALID_ARG, "ldx < K");
     if (T > 0 && N > 0 && (!ids || !Y || (K > 0 && !X))) return fail(W4_ERR_INVALID_ARG, "null ids/X/Y");
-    if (X && !aligned(X, 2)) return fail(W4_ERR_ALIGNMENT, "X not 2-byte aligned");
+    if (X && !aligned(X, xdt == W4_F32_RMS ? 4 : 2)) return fail(W4_ERR_ALIGNMENT, "X misaligned");
+    if (xdt == W4_F32_RMS && K % 4) return fail(W4_ERR_INVALID_ARG, "K must be a multiple of 4");
     if (Y && !aligned(Y, 4)) return fail(W4_ERR_ALIGNMENT, "Y not 4-byte aligned");
     if (ids && !aligned(ids, 4)) return fail(W4_ERR_ALIGNMENT, "ids not 4-byte aligned");
     if (T == 0 || N == 0) return W4_OK;
@@ -237,11 +239,28 @@ int w4_moe_gemv_ids(const uint32_t *codes_base, const uint16_t *steps_base,
     if ((st = device_ready())) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     void *ws = nullptr;
-    const size_t ws_bytes = w4::moe_workspace(N, K, T, topk, route_w != nullptr);
+    size_t ws_bytes = w4::moe_workspace(N, K, T, topk, route_w != nullptr);
+    // fp32 rows on the matrix engine: renormalised into the buffer, after the
+    // engine's part, as fp16 rows of K (16-byte aligned)
+    const int xrows = x_per_pair ? T * topk : T;
+    const bool pre_rms = xdt == W4_F32_RMS && !w4::moe_by_pairs(T);
+    const size_t xoff = (ws_bytes + 15) / 16 * 16;
+    if (pre_rms) ws_bytes = xoff + (size_t)xrows * K * 2;
     if (ws_bytes && (st = staging_buffer(w4::kWsCounterBytes + ws_bytes, s, &ws))) return st;
     if (forced_launch_error()) return fail(W4_ERR_HIP, "forced launch error (test hook)");
+    const void *Xk = X;
+    int64_t ldk = ldx;
+    int dtk = xdt;
+    if (pre_rms) {
+        uint16_t *xr = reinterpret_cast<uint16_t *>(static_cast<char *>(ws) + w4::kWsCounterBytes + xoff);
+        hipError_t e = w4::launch_rms_renorm(static_cast<const float *>(X), ldx, K, xrows, xr, K, W4_F16, s);
+        if (e != hipSuccess) return launched(e, "w4_moe_gemv_ids");
+        Xk = xr;
+        ldk = K;
+        dtk = W4_F16;
+    }
     return launched(w4::launch_moe(codes_base, steps_base, expert_stride_codes, expert_stride_steps,
-                                   N, K, static_cast<const uint16_t *>(X), ldx, xdt, x_per_pair, ids,
+                                   N, K, static_cast<const uint16_t *>(Xk), ldk, dtk, x_per_pair, ids,
                                    T, topk, slot_of, n_experts, n_slots, row_scale, route_w, Y,
                                    ws, dev_err, s),
                     "w4_moe_gemv_ids");

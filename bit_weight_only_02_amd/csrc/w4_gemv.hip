@@ -37,7 +37,11 @@ struct GemvPairs {
     int n_experts, n_slots, x_per_pair, topk;
 };
 
-template <int L, int NG, int R, int PF>
+// RN: the activations are fp32 rows (x points at floats; the pair's row is
+// ldx floats apart), renormalised on load: the leading K entries divided by
+// their RMS, with the sum of squares in the order of w4_rms_renorm and the
+// same two roundings, so the staged fp16 values are bitwise that kernel's.
+template <int L, int NG, int R, int PF, bool RN = false>
 __global__ __launch_bounds__(256) void gemv_kernel(const uint4 *__restrict__ codes,
                                                    const uint16_t *__restrict__ steps,
                                                    int N, int K,
@@ -67,7 +71,11 @@ __global__ __launch_bounds__(256) void gemv_kernel(const uint4 *__restrict__ cod
         }
         codes += a * bp.stride_c4;
         steps += a * bp.stride_s;
-        x += (long)(bp.x_per_pair ? p : p / bp.topk) * bp.ldx;
+        if constexpr (RN)
+            x = reinterpret_cast<const uint16_t *>(reinterpret_cast<const float *>(x) +
+                                                   (long)(bp.x_per_pair ? p : p / bp.topk) * bp.ldx);
+        else
+            x += (long)(bp.x_per_pair ? p : p / bp.topk) * bp.ldx;
         if (bp.row_scale) rs = bp.row_scale + (long)e * N;
     }
     const int G = K >> 5;
@@ -111,19 +119,44 @@ __global__ __launch_bounds__(256) void gemv_kernel(const uint4 *__restrict__ cod
     // pairs, or the fp32 path for the whole workgroup when they cannot be
     // staged exactly) and every lane copies its own groups into registers.
     uint16_t *raw = reinterpret_cast<uint16_t *>(xs);
-    stage_issue(x, K, raw);
+    uint4 *staged = reinterpret_cast<uint4 *>(raw + stage_raw_halves(K));
     int row0 = blockIdx.x * rows_per_iter;
     uint4 qa[R][NG];
     uint32_t sa[R][NG];
-    if (row0 < N) load_rows(qa, sa, row0);
-    if (!stage_vector_path(x))
-        for (int i = threadIdx.x; i < K; i += blockDim.x) raw[i] = x[i];
-    wait_vmcnt<0>();
-    lds_barrier();
-
-    // x staged once per workgroup, then each lane takes its own groups
-    uint4 *staged = reinterpret_cast<uint4 *>(raw + stage_raw_halves(K));
-    const Staging st = stage_x_workgroup(raw, staged, K, dt);
+    Staging st;
+    if constexpr (RN) {
+        // the fp32 row is read twice from memory (it is small and was just
+        // written): for the sum of squares, then for the staged fp16 pairs
+        __shared__ double red_rn[4];
+        if (row0 < N) load_rows(qa, sa, row0);
+        const float *xf = reinterpret_cast<const float *>(x);
+        const bool vec = (reinterpret_cast<uintptr_t>(xf) & 15) == 0;
+        auto load4 = [&](int c) __attribute__((always_inline)) {
+            return vec ? reinterpret_cast<const float4 *>(xf)[c]
+                       : make_float4(xf[4 * c], xf[4 * c + 1], xf[4 * c + 2], xf[4 * c + 3]);
+        };
+        const double inv = renorm_scale(sum_squares_256(K, load4, red_rn), K);
+        for (int c = threadIdx.x; c < (K >> 3); c += blockDim.x) {
+            const float4 a = load4(2 * c), b = load4(2 * c + 1);
+            const uint32_t h0 = renorm_value(a.x, inv, 0), h1 = renorm_value(a.y, inv, 0);
+            const uint32_t h2v = renorm_value(a.z, inv, 0), h3 = renorm_value(a.w, inv, 0);
+            const uint32_t h4 = renorm_value(b.x, inv, 0), h5 = renorm_value(b.y, inv, 0);
+            const uint32_t h6 = renorm_value(b.z, inv, 0), h7 = renorm_value(b.w, inv, 0);
+            staged[c] = make_uint4(h0 | (h4 << 16), h1 | (h5 << 16), h2v | (h6 << 16), h3 | (h7 << 16));
+        }
+        lds_barrier();
+        st.scale = 0;  // fp16 values staged as they are
+        st.fallback = 0;
+    } else {
+        stage_issue(x, K, raw);
+        if (row0 < N) load_rows(qa, sa, row0);
+        if (!stage_vector_path(x))
+            for (int i = threadIdx.x; i < K; i += blockDim.x) raw[i] = x[i];
+        wait_vmcnt<0>();
+        lds_barrier();
+        // x staged once per workgroup, then each lane takes its own groups
+        st = stage_x_workgroup(raw, staged, K, dt);
+    }
     h2 xr[NG][16];
     float2 xo[NG];
     if (!st.fallback) {
@@ -358,6 +391,30 @@ namespace {
 
 typedef void (*GemvFn)(const uint4 *, const uint16_t *, int, int, const uint16_t *, int, float *,
                        const GemvPairs);
+template <int L>
+GemvFn pick_rn_ng(int NG) {
+    switch (NG) {
+        case 1: return gemv_kernel<L, 1, 1, 0, true>;
+        case 2: return gemv_kernel<L, 2, 1, 0, true>;
+        case 3: return gemv_kernel<L, 3, 1, 0, true>;
+        case 4: return gemv_kernel<L, 4, 1, 0, true>;
+        case 6: return gemv_kernel<L, 6, 1, 0, true>;
+        case 8: return gemv_kernel<L, 8, 1, 0, true>;
+    }
+    return nullptr;
+}
+
+// the kernels that renormalise fp32 rows on load (one row per slot, no prefetch)
+GemvFn pick_rn(int L, int NG) {
+    switch (L) {
+        case 8: return pick_rn_ng<8>(NG);
+        case 16: return pick_rn_ng<16>(NG);
+        case 32: return pick_rn_ng<32>(NG);
+        case 64: return pick_rn_ng<64>(NG);
+    }
+    return nullptr;
+}
+
 typedef void (*RingFn)(const uint4 *, const uint16_t *, int, int, const uint16_t *, int, float *);
 
 template <int L, int NG>
@@ -543,7 +600,9 @@ hipError_t launch_gemv_pairs(const uint32_t *codes_base, const uint16_t *steps_b
     int R = 1, pf = 0;
     // W4_MOE_GEMV_RPF="R,pf": rows per slot in flight and prefetch (sweeps)
     if (const char *e = getenv("W4_MOE_GEMV_RPF")) sscanf(e, "%d,%d", &R, &pf);
-    GemvFn fn = pick(t.L, t.NG, R, pf);
+    // dt 2: fp32 rows renormalised on load
+    GemvFn fn = dt == 2 ? (R == 1 && pf == 0 && t.waves == 4 ? pick_rn(t.L, t.NG) : nullptr)
+                        : pick(t.L, t.NG, R, pf);
     if (!fn || P < 1 || P > 65535) return hipErrorInvalidConfiguration;
     const long rows_per_iter = (long)(64 / t.L) * t.waves * R;
     const long need = (N + rows_per_iter - 1) / rows_per_iter;

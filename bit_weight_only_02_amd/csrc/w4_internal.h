@@ -53,6 +53,7 @@ hipError_t launch_gemv_pairs(const uint32_t *codes_base, const uint16_t *steps_b
                              int x_per_pair, const int32_t *ids, int P, int topk, const int32_t *slot_of,
                              int n_experts, int n_slots, const float *row_scale, float *out,
                              int32_t *dev_err, hipStream_t stream);
+bool moe_by_pairs(int T);
 hipError_t launch_moe(const uint32_t *codes_base, const uint16_t *steps_base,
                       int64_t stride_codes, int64_t stride_steps, int N, int K,
                       const uint16_t *X, long ldx, int dt, int x_per_pair,

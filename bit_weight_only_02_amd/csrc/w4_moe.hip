@@ -245,7 +245,7 @@ static SmallMPlan moe_plan(int N, int K, int T, int topk) {
 // few experts shared by two tokens are read twice.
 // W4_MOE_PAIRS_MAX_T overrides the token bound (0: always the engine).
 constexpr int kPairsMaxT = 4;
-static bool moe_by_pairs(int T) {
+bool moe_by_pairs(int T) {
     const char *e = getenv("W4_MOE_PAIRS_MAX_T");
     return T <= (e ? atoi(e) : kPairsMaxT);
 }
@@ -279,6 +279,7 @@ hipError_t launch_moe(const uint32_t *codes_base, const uint16_t *steps_base,
                            n_experts, row_scale, route_w, T, topk, Y);
         return hipGetLastError();
     }
+    if (dt == 2) return hipErrorInvalidConfiguration;  // fp32 rows are renormalised by the caller here
     const SmallMPlan p = moe_plan(N, K, T, topk);
     const bool steps8 = (K / 32) % 4 == 0 && (reinterpret_cast<uintptr_t>(steps_base) & 7) == 0 &&
                         (stride_steps % 4) == 0;

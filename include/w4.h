@@ -75,7 +75,11 @@ typedef enum {
     W4_ERR_HIP = -6          /* a HIP call or kernel launch failed */
 } w4_status;
 
-typedef enum { W4_F16 = 0, W4_BF16 = 1 } w4_dtype;
+typedef enum { W4_F16 = 0, W4_BF16 = 1, W4_F32_RMS = 2 } w4_dtype;
+/* W4_F32_RMS (w4_moe_gemv_ids only): the activation rows are fp32, and each
+ * row's leading K entries are renormalised as part of the product -- divided
+ * by their RMS and rounded to fp16 bit for bit as w4_rms_renorm(..., W4_F16)
+ * would -- so no separate renormalisation pass runs between two products. */
 
 #define W4_MAX_K 16384       /* largest K of w4_gemv and w4_embed_gather */
 #define W4_MAX_K_SMALLM 16384 /* largest K of w4_gemm_smallM and w4_moe_gemv_ids */
@@ -122,7 +126,10 @@ int w4_gemm_smallM(const uint32_t *codes, const uint16_t *steps, int32_t N, int3
  * with the same reduction order, so equal bytes give bitwise equal results.
  *
  *   X: activation rows, ldx apart: row t (x_per_pair == 0, the same input for
- *      all choices of a token) or row t*topk + j (x_per_pair == 1).
+ *      all choices of a token) or row t*topk + j (x_per_pair == 1).  xdt
+ *      W4_F16 or W4_BF16 (2-byte aligned), or W4_F32_RMS (fp32 rows, 4-byte
+ *      aligned, ldx in floats, renormalised on load; from 5 tokens the rows
+ *      are renormalised into the library's device buffer first).
  *   row_scale: optional float[n_experts][N] per-expert output scale, ALWAYS
  *      indexed by the real id (only the weight read goes through slot_of).
  *   route_w: optional float[T][topk].  NULL: Y is float[T*topk][N], one row per

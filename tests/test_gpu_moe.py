@@ -183,6 +183,41 @@ def test_moe_single_token_bad_id_and_missing_slot(w4):
     assert np.all(np.isnan(Y[2])) and not np.any(np.isnan(Y[[0, 1]]))
 
 
+@pytest.mark.parametrize("T,xpp", [(1, 0), (1, 1), (3, 1), (5, 0), (5, 1)])
+def test_moe_fp32_rows_renormalised_on_load(w4, T, xpp):
+    """fp32 activation rows renormalised as part of the product give the bits
+    of w4_rms_renorm (fp16) followed by the product, with and without route
+    weights, on both paths (up to four tokens fused; from five the rows are
+    renormalised into the library's buffer first)."""
+    rng = np.random.default_rng(60 + T * 2 + xpp)
+    E, N, K, topk, ld = 16, 200, 704, 4, 1408
+    codes, steps = experts(rng, E, N, K)
+    ids, route = synth.expert_choice(rng, T, E, topk)
+    rows = T * topk if xpp else T
+    X32 = torch.from_numpy((rng.normal(0, 3, size=(rows, ld))).astype(np.float32)).cuda()
+    Xh = w4.w4_rms_renorm(X32, K, out_dtype=torch.float16)
+    dc, ds = dev_codes(codes.reshape(-1, K // 8)), dev_steps(steps.reshape(-1, K // 32))
+    dids = torch.from_numpy(ids.astype(np.int32)).cuda()
+    for rw in (None, torch.from_numpy(route).cuda()):
+        out = []
+        for X in (X32, Xh):
+            Y = torch.full((T * topk if rw is None else T, N), float("nan"), device="cuda")
+            w4.w4_moe_gemv_ids(dc, ds, N * K // 8, N * K // 32, N, K, X, dids, x_per_pair=bool(xpp),
+                               n_experts=E, route_w=rw, Y=Y)
+            out.append(Y)
+        torch.cuda.synchronize()
+        assert torch.equal(out[0].view(torch.int32), out[1].view(torch.int32)), (T, xpp, rw is None)
+    # and the product itself against the oracle on the renormalised rows
+    Xo = Xh.view(torch.int16).cpu().numpy().view(np.uint16)
+    Yo, Ao = oracle.moe(codes, steps, N * K // 8, N * K // 32, N, K, Xo, F16, xpp, ids, topk, n_experts=E)
+    Y = torch.empty((T * topk, N), device="cuda")
+    w4.w4_moe_gemv_ids(dc, ds, N * K // 8, N * K // 32, N, K, X32, dids, x_per_pair=bool(xpp),
+                       n_experts=E, Y=Y)
+    torch.cuda.synchronize()
+    ok, worst = within_bound(Y.cpu().numpy(), Yo, Ao)
+    assert ok, worst
+
+
 def test_moe_many_pairs_share_an_expert(w4):
     # 20 tokens all choose expert 3 first: more pairs than one MFMA tile of rows
     rng = np.random.default_rng(6)

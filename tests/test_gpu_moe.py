@@ -183,14 +183,15 @@ def test_moe_single_token_bad_id_and_missing_slot(w4):
     assert np.all(np.isnan(Y[2])) and not np.any(np.isnan(Y[[0, 1]]))
 
 
-@pytest.mark.parametrize("T,xpp", [(1, 0), (1, 1), (3, 1), (5, 0), (5, 1)])
-def test_moe_fp32_rows_renormalised_on_load(w4, T, xpp):
+@pytest.mark.parametrize("T,xpp,K", [(1, 0, 704), (1, 1, 704), (3, 1, 704), (5, 0, 704), (5, 1, 704),
+                                     (1, 0, 2816), (2, 1, 2816), (1, 0, 8192)])
+def test_moe_fp32_rows_renormalised_on_load(w4, T, xpp, K):
     """fp32 activation rows renormalised as part of the product give the bits
     of w4_rms_renorm (fp16) followed by the product, with and without route
     weights, on both paths (up to four tokens fused; from five the rows are
     renormalised into the library's buffer first)."""
-    rng = np.random.default_rng(60 + T * 2 + xpp)
-    E, N, K, topk, ld = 16, 200, 704, 4, 1408
+    rng = np.random.default_rng(60 + T * 2 + xpp + K)
+    E, N, topk, ld = 16, 200, 4, K + 64
     codes, steps = experts(rng, E, N, K)
     ids, route = synth.expert_choice(rng, T, E, topk)
     rows = T * topk if xpp else T

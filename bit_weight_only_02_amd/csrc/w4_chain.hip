@@ -97,75 +97,116 @@ __device__ __forceinline__ uint32_t load_global_u16(const uint16_t *p, long i) {
 }
 
 // One output, stored so that loads with agent scope on any XCD see it.
-__device__ __forceinline__ void store_y(float *y, int n, int row, float v) {
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), buffer_rsrc(y, n * 4), row * 4, 0, 16);
-}
 __device__ __forceinline__ unsigned load_agent_u(unsigned *p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// This workgroup's plan for one step: the rows it computes are a contiguous
-// block [rb, re); the first nlds of them are staged in an LDS weight buffer
-// (codes, then their steps), the rest are read from memory.  Worked out once
-// per descriptor, when the descriptor enters the LDS table, so that the step
-// itself starts computing at once.
+// This workgroup's plan for one step.  Its rows are range A, [ra, ra + na),
+// then range B, [rb2, rb2 + nb).  When the next step reads only the leading
+// k_next < N outputs (the gate half of gate/up), A is this workgroup's share of
+// those rows and B its share of the rest, so every workgroup publishes the
+// exchanged rows first and computes the others while they travel; otherwise A
+// is a contiguous block and B is empty.  The first nlds rows of A ++ B are
+// staged in an LDS weight buffer -- A's codes at 0, B's at offb, then the
+// steps (A's, then B's at sbo words) -- and the rest are read from memory.
+// Worked out once per descriptor, when the descriptor enters the LDS table.
 struct RowBlock {
-    int rb, re, nlds;
-    int steps_chunk;  // uint4 index of the staged steps inside the buffer
-    int sel;          // row kernel: lanes per row * 8 + groups per lane
-    int k_next;       // K of the next step (the cells it reads), 0 after the last
-    int pad[2];
+    int ra, na, rb2, nb;
+    int nlds;
+    int sel;     // row kernel: lanes per row * 8 + groups per lane
+    int k_next;  // K of the next step (the cells it reads), 0 after the last
+    int pad;
 };
 static_assert(sizeof(RowBlock) == 32, "plan entry");
 
+__device__ __forceinline__ int round64(int v) { return (v + 63) & ~63; }
+
+// LDS layout of a plan's staged rows (uint4 chunks for codes, 4-byte words
+// for steps; every run rounded to 64, so that the surplus lanes of a copy
+// instruction land in padding)
+struct StagedLayout {
+    int na_st, nb_st;  // staged rows of A and B
+    int offb;          // chunk offset of B's codes
+    int sc;            // chunk offset of the steps
+    int sbo;           // word offset of B's steps inside the steps
+};
+__device__ __forceinline__ StagedLayout staged_layout(const RowBlock &b, int G) {
+    StagedLayout s;
+    s.na_st = min(b.na, b.nlds);
+    s.nb_st = b.nlds - s.na_st;
+    s.offb = round64(s.na_st * G);
+    s.sc = s.offb + round64(s.nb_st * G);
+    s.sbo = round64(s.na_st * G / 2);
+    return s;
+}
+
 __device__ __forceinline__ RowBlock chain_plan(const ChainMat &m, int k_next, int nwg) {
     const int G = m.K >> 5;
-    const int rpw = (m.N + nwg - 1) / nwg;
-    RowBlock b;
-    b.rb = min(m.N, (int)blockIdx.x * rpw);
-    b.re = min(m.N, b.rb + rpw);
-    // steps travel as 4-byte words: the block's steps must start on one
+    const int b = blockIdx.x;
+    RowBlock p;
+    const int kn = (k_next > 0 && k_next < m.N) ? k_next : 0;
+    if (kn) {
+        const int ra_w = (kn + nwg - 1) / nwg, rb_w = (m.N - kn + nwg - 1) / nwg;
+        p.ra = min(kn, b * ra_w);
+        p.na = min(kn, p.ra + ra_w) - p.ra;
+        p.rb2 = kn + min(m.N - kn, b * rb_w);
+        p.nb = min(m.N, p.rb2 + rb_w) - p.rb2;
+    } else {
+        const int rpw = (m.N + nwg - 1) / nwg;
+        p.ra = min(m.N, b * rpw);
+        p.na = min(m.N, p.ra + rpw) - p.ra;
+        p.rb2 = m.N;
+        p.nb = 0;
+    }
+    // steps travel as 4-byte words: every row's steps must start on one
     const bool lds_steps = (G % 2) == 0 && (reinterpret_cast<uintptr_t>(m.steps) & 3) == 0;
     auto bytes = [&](int rows) {
-        const int chunks = (rows * G + 63) / 64 * 64;
-        const int words = (rows * G / 2 + 63) / 64 * 64;
-        return chunks * 16 + words * 4;
+        const int a = min(p.na, rows), c = rows - a;
+        return (round64(a * G) + round64(c * G)) * 16 + (round64(a * G / 2) + round64(c * G / 2)) * 4;
     };
     // (rows are staged only together with their steps)
-    int n = lds_steps ? min(b.re - b.rb, kWeightBuf / (G * 18)) : 0;
+    int n = lds_steps ? min(p.na + p.nb, kWeightBuf / (G * 18)) : 0;
     while (n > 0 && bytes(n) > kWeightBuf) --n;
-    b.nlds = n;
-    b.steps_chunk = (n * G + 63) / 64 * 64;
+    p.nlds = n;
     // lanes per row from the row length alone: 16 lanes up to 64 groups, 32
     // up to 128, else 64.  (Choosing by the least work per lane -- 64 lanes
     // for a block of six 64-group rows, say -- measured slower over the whole
     // decode sweep: passes are latency-bound, not arithmetic-bound.)
     const int L = G <= 64 ? 16 : (G <= 128 ? 32 : 64);
-    b.sel = L * 8 + (G + L - 1) / L;
-    b.k_next = k_next;
-    b.pad[0] = b.pad[1] = 0;
-    return b;
+    p.sel = L * 8 + (G + L - 1) / L;
+    p.k_next = k_next;
+    p.pad = 0;
+    return p;
 }
 
-// Copy waves: request the staged part of a block into `buf` with
-// direct-to-LDS loads (every lane moves 16 bytes of codes or 4 bytes of steps;
-// the last instruction of each run lands its surplus lanes in the rounding
-// padding).  Written with the asm form of the load, so that the compiler adds
-// no waits for it; the copy waves wait for it themselves (vmcnt 0) before the
-// workgroup barrier that precedes the block's use.
+// Copy waves: request the staged rows into `buf` with direct-to-LDS loads
+// (every lane moves 16 bytes of codes or 4 bytes of steps; the last
+// instruction of each run lands its surplus lanes in the run's padding).
+// Written with the asm form of the load, so that the compiler adds no waits
+// for it; the copy waves wait for it themselves (vmcnt 0) before the workgroup
+// barrier that precedes the block's use.
 __device__ __forceinline__ void chain_copy(const ChainMat &m, const RowBlock &b, uint4 *buf) {
     const int w = (threadIdx.x >> 6) - kCopyWave0, lane = threadIdx.x & 63;
     constexpr int nw = kChainWaves - kCopyWave0;
     const int G = m.K >> 5;
-    const int n = b.nlds * G;
-    if (n == 0) return;
-    const uint4 *src = reinterpret_cast<const uint4 *>(m.codes) + (long)b.rb * G;
-    for (int c0 = w * 64; c0 < n; c0 += nw * 64) lds_dma16(src + min(c0 + lane, n - 1), buf + c0);
-    {
-        const uint32_t *ssrc = reinterpret_cast<const uint32_t *>(m.steps + (long)b.rb * G);
-        uint32_t *sdst = reinterpret_cast<uint32_t *>(buf + b.steps_chunk);
-        const int nd = n / 2;
-        for (int d0 = w * 64; d0 < nd; d0 += nw * 64) lds_dma4(ssrc + min(d0 + lane, nd - 1), sdst + d0);
+    if (b.nlds == 0) return;
+    const StagedLayout sl = staged_layout(b, G);
+    auto codes_run = [&](int row0, int rows, uint4 *dst) __attribute__((always_inline)) {
+        const int n = rows * G;
+        const uint4 *src = reinterpret_cast<const uint4 *>(m.codes) + (long)row0 * G;
+        for (int c0 = w * 64; c0 < n; c0 += nw * 64) lds_dma16(src + min(c0 + lane, n - 1), dst + c0);
+    };
+    auto steps_run = [&](int row0, int rows, uint32_t *dst) __attribute__((always_inline)) {
+        const int nd = rows * G / 2;
+        const uint32_t *src = reinterpret_cast<const uint32_t *>(m.steps + (long)row0 * G);
+        for (int d0 = w * 64; d0 < nd; d0 += nw * 64) lds_dma4(src + min(d0 + lane, nd - 1), dst + d0);
+    };
+    uint32_t *sdst = reinterpret_cast<uint32_t *>(buf + sl.sc);
+    codes_run(b.ra, sl.na_st, buf);
+    steps_run(b.ra, sl.na_st, sdst);
+    if (sl.nb_st > 0) {
+        codes_run(b.rb2, sl.nb_st, buf + sl.offb);
+        steps_run(b.rb2, sl.nb_st, sdst + sl.sbo);
     }
 }
 
@@ -196,7 +237,11 @@ __device__ __forceinline__ void chain_rows(const ChainMat &m, const RowBlock &b,
     const int G = m.K >> 5;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int l = lane % L, slot = lane / L;
-    const uint16_t *lsteps = reinterpret_cast<const uint16_t *>(buf + b.steps_chunk);
+    const StagedLayout sl = staged_layout(b, G);
+    const uint16_t *lsteps = reinterpret_cast<const uint16_t *>(buf + sl.sc);
+    const int nrows = b.na + b.nb;
+    // local row lr of A ++ B -> its global row
+    auto global_row = [&](int lr) __attribute__((always_inline)) { return lr < b.na ? b.ra + lr : b.rb2 + (lr - b.na); };
     // the activations, already in pair order in LDS -> registers
     h2 xr[NG][16];
     const uint4 *r16 = reinterpret_cast<const uint4 *>(xin);
@@ -224,7 +269,7 @@ __device__ __forceinline__ void chain_rows(const ChainMat &m, const RowBlock &b,
             acc = (g < G) ? __builtin_fmaf(group_dot_off(q[i], xr[i], xo[i]), bf16_to_f32(sv[i]), acc) : acc;
         }
         acc = lane_group_sum<L>(acc);
-        if (l == L - 1 && row < b.re) {
+        if (l == L - 1 && row >= 0) {
             const float v = __builtin_ldexpf(acc, kGroupDotExp);
             // (a global store: through the generic pointer it would be a flat
             // store, which every later LDS read would have to wait for)
@@ -236,25 +281,27 @@ __device__ __forceinline__ void chain_rows(const ChainMat &m, const RowBlock &b,
     // past the end still run the pass on clamped rows and store nothing:
     // skipping it (and giving the idle SIMD time to the wave beside it)
     // measured slower over the decode sweep.
-    const int staged_end = b.rb + b.nlds;
-    for (int r0 = b.rb; r0 < staged_end; r0 += kComputeWaves * SLOTS) {
-        const int row = r0 + wave * SLOTS + slot;
-        const int rl = min(row, staged_end - 1) - b.rb;
+    for (int l0 = 0; l0 < b.nlds; l0 += kComputeWaves * SLOTS) {
+        const int lr = l0 + wave * SLOTS + slot;
+        const int lc = min(lr, b.nlds - 1);
+        // staged position: A's rows from 0, B's from offb (codes) / 2 sbo (steps)
+        const int cbase = lc < sl.na_st ? lc * G : sl.offb + (lc - sl.na_st) * G;
+        const int sbase = lc < sl.na_st ? lc * G : 2 * sl.sbo + (lc - sl.na_st) * G;
         uint4 q[NG];
         uint32_t sv[NG];
 #pragma unroll
         for (int i = 0; i < NG; ++i) {
             const int g = min(l + i * L, G - 1);
-            q[i] = buf[rl * G + g];
-            sv[i] = lsteps[rl * G + g];
+            q[i] = buf[cbase + g];
+            sv[i] = lsteps[sbase + g];
         }
-        finish(row < staged_end ? row : b.re, q, sv);
+        finish(lr < b.nlds ? global_row(lr) : -1, q, sv);
     }
-    if (staged_end < b.re) {
+    if (b.nlds < nrows) {
         const uint4 *codes = reinterpret_cast<const uint4 *>(m.codes);
-        for (int r0 = staged_end; r0 < b.re; r0 += kComputeWaves * SLOTS) {
-            const int row = r0 + wave * SLOTS + slot;
-            const int rc = min(row, b.re - 1);
+        for (int l0 = b.nlds; l0 < nrows; l0 += kComputeWaves * SLOTS) {
+            const int lr = l0 + wave * SLOTS + slot;
+            const int rc = global_row(min(lr, nrows - 1));
             uint4 q[NG];
             uint32_t sv[NG];
 #pragma unroll
@@ -263,14 +310,14 @@ __device__ __forceinline__ void chain_rows(const ChainMat &m, const RowBlock &b,
                 q[i] = load_global_u4(codes, (long)rc * G + g);
                 sv[i] = load_global_u16(m.steps, (long)rc * G + g);
             }
-            finish(row, q, sv);
+            finish(lr < nrows ? global_row(lr) : -1, q, sv);
         }
     }
 }
 
 __device__ __forceinline__ void chain_rows_any(const ChainMat &m, const RowBlock &b, const uint4 *buf,
                                                const uint16_t *xin, const RowSink &sink) {
-    if (b.re <= b.rb) return;
+    if (b.na + b.nb == 0) return;
     switch (__builtin_amdgcn_readfirstlane(b.sel)) {
         case 16 * 8 + 1: chain_rows<16, 1>(m, b, buf, xin, sink); break;
         case 16 * 8 + 2: chain_rows<16, 2>(m, b, buf, xin, sink); break;
@@ -484,7 +531,7 @@ __global__ __launch_bounds__(kChainThreads) void chain_kernel(const ChainMat *__
                 if (wave == kComputeWaves - 1 && i >= 2) {
                     const RowBlock q = plan(i - 2);
                     uint32_t *cells = regions + (long)(i - 2) * kChainMaxK;
-                    for (int r = q.rb + (tid & 63); r < min(q.re, q.k_next); r += 64) clear_cell(cells, r);
+                    for (int r = q.ra + (tid & 63); r < min(q.ra + q.na, q.k_next); r += 64) clear_cell(cells, r);
                 }
                 // refill: descriptor i + kDescCache/2 (and its plan) into the
                 // slot of i - kDescCache/2

@@ -588,8 +588,11 @@ hipError_t launch_gemv(const uint32_t *codes, const uint16_t *steps, int N, int 
 
 // Expert-indexed products with one activation row per pair: P products of
 // [N][K] matrices in one launch, gridDim.y = P, the tile of a single [N][K]
-// product; about 1024 workgroups in all, so that each loops over a couple of
-// row steps (the activation staging is paid once per workgroup).
+// product; 512 workgroups in all up to 8 pairs, 768 beyond, so that each
+// loops over a few row steps (the activation staging is paid once per
+// workgroup).  Measured over an expert token: at 8 pairs (one token) 64 per
+// pair gave 566-579 us against 625 us with 72 and 629 us with 128; at 32
+// pairs 24 per pair gave 976-982 us against 999 with 32 and 1013 with 16.
 // W4_MOE_GEMV_BLOCKS overrides the workgroups per pair (schedule sweeps).
 hipError_t launch_gemv_pairs(const uint32_t *codes_base, const uint16_t *steps_base, int64_t stride_codes,
                              int64_t stride_steps, int N, int K, const uint16_t *X, long ldx, int dt,
@@ -606,7 +609,7 @@ hipError_t launch_gemv_pairs(const uint32_t *codes_base, const uint16_t *steps_b
     if (!fn || P < 1 || P > 65535) return hipErrorInvalidConfiguration;
     const long rows_per_iter = (long)(64 / t.L) * t.waves * R;
     const long need = (N + rows_per_iter - 1) / rows_per_iter;
-    long bx = (1024 + P - 1) / P;
+    long bx = ((P <= 8 ? 512 : 768) + P - 1) / P;
     if (const char *e = getenv("W4_MOE_GEMV_BLOCKS")) bx = atol(e);
     if (bx > need) bx = need;
     if (bx < 1) bx = 1;

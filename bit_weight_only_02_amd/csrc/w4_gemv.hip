@@ -173,9 +173,11 @@ __global__ __launch_bounds__(256) void gemv_kernel(const uint4 *__restrict__ cod
         }
     }
 
-    auto compute_rows = [&](const uint4 (&q)[R][NG], const uint32_t (&sv)[R][NG], int r0,
-                            auto exact_f32) __attribute__((always_inline)) {
-        float acc[R];
+    // dot_rows: the lane's partial sums of its R rows; store_rows: reduce them
+    // over the row's lanes and store.  (The next rows' loads go out between
+    // the two: the weight registers are free once the partial sums exist.)
+    auto dot_rows = [&](const uint4 (&q)[R][NG], const uint32_t (&sv)[R][NG], float (&acc)[R],
+                        auto exact_f32) __attribute__((always_inline)) {
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             acc[r] = 0.0f;
@@ -190,6 +192,8 @@ __global__ __launch_bounds__(256) void gemv_kernel(const uint4 *__restrict__ cod
                 acc[r] = (g < G) ? __builtin_fmaf(part, bf16_to_f32(sv[r][i]), acc[r]) : acc[r];
             }
         }
+    };
+    auto store_rows = [&](float (&acc)[R], int r0, auto exact_f32) __attribute__((always_inline)) {
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             acc[r] = lane_group_sum<L>(acc[r]);
@@ -208,13 +212,23 @@ __global__ __launch_bounds__(256) void gemv_kernel(const uint4 *__restrict__ cod
     // With PF, the loads of the next step are issued before the math of this
     // one (two register sets, alternating), so that each wave keeps a step of
     // weights in flight while it computes.
+    auto compute_rows = [&](const uint4 (&q)[R][NG], const uint32_t (&sv)[R][NG], int r0,
+                            auto exact_f32) __attribute__((always_inline)) {
+        float acc[R];
+        dot_rows(q, sv, acc, exact_f32);
+        store_rows(acc, r0, exact_f32);
+    };
     auto row_loop = [&](auto exact_f32) __attribute__((always_inline)) {
         if (row0 >= N) return;
         if constexpr (PF == 0) {
-            compute_rows(qa, sa, row0, exact_f32);
-            for (row0 += gstride; row0 < N; row0 += gstride) {
-                load_rows(qa, sa, row0);
-                compute_rows(qa, sa, row0, exact_f32);
+            for (;;) {
+                float acc[R];
+                dot_rows(qa, sa, acc, exact_f32);
+                const int nxt = row0 + gstride;
+                if (nxt < N) load_rows(qa, sa, nxt);
+                store_rows(acc, row0, exact_f32);
+                row0 = nxt;
+                if (row0 >= N) break;
             }
         } else {
             uint4 qb[R][NG];

@@ -143,8 +143,7 @@ int w4_gemm_smallM(const uint32_t *codes, const uint16_t *steps, int32_t N, int3
     if (K > W4_MAX_K_SMALLM) return fail(W4_ERR_UNSUPPORTED, "K=%d exceeds %d", K, W4_MAX_K_SMALLM);
     if (ldx < K || ldy < N) return fail(W4_ERR_INVALID_ARG, "ldx < K or ldy < N");
     if (N > 0 && (!Y || (K > 0 && !X))) return fail(W4_ERR_INVALID_ARG, "null X/Y");
-    if (X && !aligned(X, xdt == W4_F32_RMS ? 4 : 2)) return fail(W4_ERR_ALIGNMENT, "X misaligned");
-    if (xdt == W4_F32_RMS && K % 4) return fail(W4_ERR_INVALID_ARG, "K must be a multiple of 4");
+    if (X && !aligned(X, 2)) return fail(W4_ERR_ALIGNMENT, "X not 2-byte aligned");
     if (Y && !aligned(Y, 4)) return fail(W4_ERR_ALIGNMENT, "Y not 4-byte aligned");
     if (N == 0) return W4_OK;
     if ((st = device_ready())) return st;

@@ -124,8 +124,18 @@ int plan_override(int N, int K, int M, SmallMPlan &p) {
 
 }  // namespace
 
+// Up to four rows: M batch-1 products side by side, their weights read from
+// HBM about once (the workgroups of a row block run together); on a set of
+// the four sweep shapes 28.1 against 32.3 us at M = 2, 34.3 against 37.9 us at
+// M = 4.  From 8 rows the matrix cores win (45.9 against 48.9 us at M = 8).
+// W4_SMALLM_ROWS_MAX overrides the bound (0: always the matrix cores).
+static bool smallm_by_rows(int M) {
+    const char *e = getenv("W4_SMALLM_ROWS_MAX");
+    return M <= (e ? atoi(e) : 4);
+}
+
 size_t gemm_smallm_workspace(int N, int K, int M) {
-    if (M == 1) return 0;  // the batch-1 product
+    if (M == 1 || smallm_by_rows(M)) return 0;  // batch-1 products
     SmallMPlan p = gemm_plan(N, K, M);
     plan_override(N, K, M, p);
     return p.S > 1 ? (size_t)p.S * M * N * sizeof(float) : 0;
@@ -152,6 +162,7 @@ hipError_t launch_gemm_smallm(const uint32_t *codes, const uint16_t *steps, int 
                               void *ws, hipStream_t stream) {
     // one activation row: the batch-1 kernel (no matrix-core padding)
     if (M == 1) return launch_gemv(codes, steps, N, K, X, dt, Y, stream);
+    if (smallm_by_rows(M)) return launch_gemv_rows(codes, steps, N, K, X, ldx, dt, M, Y, ldy, stream);
     SmallMPlan p = gemm_plan(N, K, M);
     const int cap = plan_override(N, K, M, p);
     const bool steps8 = (K / 32) % 4 == 0 && (reinterpret_cast<uintptr_t>(steps) & 7) == 0;

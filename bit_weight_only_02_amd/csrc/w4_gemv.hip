@@ -35,6 +35,7 @@ struct GemvPairs {
     int64_t stride_c4, stride_s;
     long ldx;
     int n_experts, n_slots, x_per_pair, topk;
+    long ldy;  // ids == nullptr and ldy != 0: gridDim.y activation rows (X ldx, Y ldy apart)
 };
 
 // RN: the activations are fp32 rows (x points at floats; the pair's row is
@@ -77,6 +78,10 @@ __global__ __launch_bounds__(256) void gemv_kernel(const uint4 *__restrict__ cod
         else
             x += (long)(bp.x_per_pair ? p : p / bp.topk) * bp.ldx;
         if (bp.row_scale) rs = bp.row_scale + (long)e * N;
+    } else if (bp.ldy) {
+        // several activation rows against one matrix: row blockIdx.y
+        x += (long)blockIdx.y * bp.ldx;
+        y += (long)blockIdx.y * bp.ldy;
     }
     const int G = K >> 5;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -597,6 +602,29 @@ hipError_t launch_gemv(const uint32_t *codes, const uint16_t *steps, int N, int 
     const size_t lds = (size_t)2 * stage_raw_halves(K) * sizeof(_Float16);
     hipLaunchKernelGGL(fn, dim3(t.blocks), dim3(64 * t.waves), lds, stream,
                        reinterpret_cast<const uint4 *>(codes), steps, N, K, x, dt, y, GemvPairs{});
+    return hipGetLastError();
+}
+
+// M activation rows against one matrix, as M batch-1 products side by side
+// (gridDim.y = M): the M workgroups of a row block run together, so the
+// weights come from HBM about once and from the caches for the other rows.
+hipError_t launch_gemv_rows(const uint32_t *codes, const uint16_t *steps, int N, int K, const uint16_t *X,
+                            long ldx, int dt, int M, float *Y, long ldy, hipStream_t stream) {
+    const GemvTile t = gemv_tile(N, K);
+    GemvFn fn = pick(t.L, t.NG, 1, 0);
+    if (!fn || M < 1 || M > 65535 || ldy < 1) return hipErrorInvalidConfiguration;
+    const long rows_per_iter = (long)(64 / t.L) * t.waves;
+    const long need = (N + rows_per_iter - 1) / rows_per_iter;
+    long bx = (512 + M - 1) / M;  // 512 in all: measured best at M = 2 and 4
+    if (const char *e = getenv("W4_ROWS_GEMV_BLOCKS")) bx = atol(e);
+    if (bx > need) bx = need;
+    if (bx < 1) bx = 1;
+    GemvPairs bp{};
+    bp.ldx = ldx;
+    bp.ldy = ldy;
+    const size_t lds = (size_t)2 * stage_raw_halves(K) * sizeof(_Float16);
+    hipLaunchKernelGGL(fn, dim3((unsigned)bx, (unsigned)M), dim3(64 * t.waves), lds, stream,
+                       reinterpret_cast<const uint4 *>(codes), steps, N, K, X, dt, Y, bp);
     return hipGetLastError();
 }
 

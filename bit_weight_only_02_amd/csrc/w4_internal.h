@@ -48,6 +48,8 @@ hipError_t launch_rms_renorm(const float *v, long ldv, int K, int rows, void *ou
 
 size_t moe_workspace(int N, int K, int T, int topk, bool route);
 
+hipError_t launch_gemv_rows(const uint32_t *codes, const uint16_t *steps, int N, int K, const uint16_t *X,
+                            long ldx, int dt, int M, float *Y, long ldy, hipStream_t stream);
 hipError_t launch_gemv_pairs(const uint32_t *codes_base, const uint16_t *steps_base, int64_t stride_codes,
                              int64_t stride_steps, int N, int K, const uint16_t *X, long ldx, int dt,
                              int x_per_pair, const int32_t *ids, int P, int topk, const int32_t *slot_of,

@@ -100,10 +100,12 @@ int w4_gemv(const uint32_t *codes, const uint16_t *steps, int32_t N, int32_t K,
 /*
  * Small-batch product [P1-S3] with M activation rows, 1 <= M <= W4_MAX_M:
  *   Y[m*ldy + n] = sum_k w(n,k) * X[m*ldx + k]   for m < M, n < N.
- * Each weight is read from memory once for all M rows.  ldx >= K, ldy >= N,
- * K <= W4_MAX_K_SMALLM (larger K: W4_ERR_UNSUPPORTED).
- * M == 1 runs the batch-1 kernel of w4_gemv.  Otherwise the product runs on
- * the matrix cores; when the plan splits K into slices (to give the chip
+ * ldx >= K, ldy >= N, K <= W4_MAX_K_SMALLM (larger K: W4_ERR_UNSUPPORTED).
+ * M <= 4 runs M batch-1 products of w4_gemv's kernel side by side in one
+ * launch (row m has the bits w4_gemv gives for that row with the same tile;
+ * the workgroups of a row block run together, so the weights come from memory
+ * about once).  M >= 5 runs on the matrix cores, each weight read from memory
+ * once for all M rows; when the plan splits K into slices (to give the chip
  * enough independent work, or to fit the staged activations), the slices are
  * summed in a fixed order inside the same launch, through a device buffer that
  * the library allocates once per device and reuses (grown on demand while no

@@ -69,10 +69,11 @@ def test_gemm_decode_sweep_shapes(w4, M):
         assert ok, (N, K, M, worst)
 
 
-def test_gemm_split_k_is_deterministic_and_survives_other_calls(w4):
+def test_gemm_split_k_is_deterministic_and_survives_other_calls(w4, monkeypatch):
     """A product split into K-slices and summed by the last slice to arrive:
     bitwise the same on every call, also when expert products (which share the
-    library's device buffer) run in between."""
+    library's device buffer) run in between.  (Four rows on the matrix cores.)"""
+    monkeypatch.setenv("W4_SMALLM_ROWS_MAX", "0")
     rng = np.random.default_rng(11)
     N, K, M = 1536, 8192, 4
     codes, steps = synth.w4_matrix(rng, N, K)
@@ -159,3 +160,31 @@ def test_gemm_rejects_k_beyond_limit(w4):
     with pytest.raises(w4.W4Error) as e:
         w4.w4_gemm_smallM(codes, steps, X)
     assert e.value.status == w4.W4_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("M", [2, 3, 4])
+def test_gemm_few_rows_match_batch1_bitwise(w4, M):
+    """Up to four rows run as batch-1 products side by side: every row has the
+    bits of w4_gemv on that row alone."""
+    rng = np.random.default_rng(40 + M)
+    N, K = 5000, 1536
+    codes, steps = synth.w4_matrix(rng, N, K)
+    X = synth.activations(rng, (M, K), BF16)
+    Y = run_gemm(w4, codes, steps, X, BF16, M, K)
+    for m in range(M):
+        y = torch.empty(N, device="cuda")
+        w4.w4_gemv(dev_codes(codes), dev_steps(steps), dev_act(X[m], BF16), y)
+        torch.cuda.synchronize()
+        assert y.cpu().numpy().tobytes() == Y[m].tobytes(), m
+
+
+def test_gemm_few_rows_on_the_matrix_cores(w4, monkeypatch):
+    """Two to four rows forced onto the MFMA engine (the path from 5 rows)."""
+    monkeypatch.setenv("W4_SMALLM_ROWS_MAX", "0")
+    rng = np.random.default_rng(30)
+    for N, K, M in [(2560, 1536, 2), (1536, 2048, 4), (97, 704, 3), (1536, 8192, 4)]:
+        codes, steps = synth.w4_matrix(rng, N, K)
+        X = synth.activations(rng, (M, K), BF16)
+        Y = run_gemm(w4, codes, steps, X, BF16, M, K)
+        Yo, Ao = oracle_rows(codes, steps, N, K, X, BF16, M)
+        assert within_bound(Y, Yo, Ao)[0], (N, K, M)

@@ -176,26 +176,50 @@ __global__ __launch_bounds__(256) void moe_finish_kernel(const float *__restrict
                                                          const float *__restrict__ route_w, int T,
                                                          int topk, float *__restrict__ Y) {
     const int rows = route_w ? T : P;
-    const long total = (long)rows * N;
+    const int total = rows * N;  // <= 1024 * N rows of pairs, well inside int
     const long plane = (long)P * N;
-    for (long i = (long)blockIdx.x * blockDim.x + threadIdx.x; i < total;
-         i += (long)gridDim.x * blockDim.x) {
-        const int r = (int)(i / N), n = (int)(i % N);
-        auto pair_value = [&](int p) __attribute__((always_inline)) {
-            const long o = (long)p * N + n;
-            float v = ws[o];
-            for (int s = 1; s < S; ++s) v += ws[(long)s * plane + o];
-            const int e = ids[p];
-            if (row_scale && e >= 0 && e < n_experts) v *= row_scale[(long)e * N + n];
-            return v;
-        };
-        if (route_w) {
+    // one pair's value: its slices in order, then row_scale of the real id
+    auto pair_value = [&](int p, int n) __attribute__((always_inline)) {
+        const long o = (long)p * N + n;
+        float v = ws[o];
+        for (int s = 1; s < S; ++s) v += ws[(long)s * plane + o];
+        const int e = ids[p];
+        if (row_scale && e >= 0 && e < n_experts) v *= row_scale[(long)e * N + n];
+        return v;
+    };
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < total; i += gridDim.x * blockDim.x) {
+        const int r = i / N, n = i - r * N;
+        if (route_w && S == 1) {
+            // every choice's value and weight requested before any is used
+            // (eight at a time), then row_scale, then the sum in ascending j
+            float s = 0.0f;
+            for (int j0 = 0; j0 < topk; j0 += 8) {
+                float v[8], w[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int p = r * topk + min(j0 + u, topk - 1);
+                    v[u] = ws[(long)p * N + n];
+                    w[u] = route_w[p];
+                }
+                if (row_scale) {
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) {
+                        const int e = ids[r * topk + min(j0 + u, topk - 1)];
+                        if (e >= 0 && e < n_experts) v[u] *= row_scale[(long)e * N + n];
+                    }
+                }
+#pragma unroll
+                for (int u = 0; u < 8; ++u)
+                    if (j0 + u < topk) s = __builtin_fmaf(w[u], v[u], s);
+            }
+            Y[i] = s;
+        } else if (route_w) {
             float s = 0.0f;
             for (int j = 0; j < topk; ++j)
-                s = __builtin_fmaf(route_w[r * topk + j], pair_value(r * topk + j), s);
+                s = __builtin_fmaf(route_w[r * topk + j], pair_value(r * topk + j, n), s);
             Y[i] = s;
         } else {
-            Y[i] = pair_value(r);
+            Y[i] = pair_value(r, n);
         }
     }
 }

@@ -39,6 +39,7 @@ W4_MAX_K_SMALLM = 16384
 W4_MAX_K_CHAIN = 8192
 W4_MAX_M = 16
 W4_MAX_TOPK = 32
+W4_MAX_M_PROMPT = 4096
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with bit_weight_only_02_amd/build.py "
@@ -53,6 +54,7 @@ lib = ctypes.CDLL(LIB_PATH)
 _SIGNATURES = {
     "w4_gemv": [_P, _P, _I32, _I32, _P, _I32, _P, _P],
     "w4_gemm_smallM": [_P, _P, _I32, _I32, _P, _I32, _I32, _I64, _P, _I64, _P],
+    "w4_gemm_prompt": [_P, _P, _I32, _I32, _P, _I32, _I32, _I64, _P, _I64, _P],
     "w4_moe_gemv_ids": [_P, _P, _I64, _I64, _I32, _I32, _P, _I32, _I32, _I64, _P, _I32, _I32,
                         _P, _I32, _I32, _P, _P, _P, _P, _P],
     "w4_embed_gather": [_P, _P, _I32, _I32, _P, _I32, _P, _P, _P],
@@ -137,6 +139,23 @@ def w4_gemm_smallM(codes, steps, X, Y=None, stream=None):
     _check(lib.w4_gemm_smallM(_ptr(codes), _ptr(steps), N, K, _ptr(X), _act_dtype(X), M,
                               X.stride(0), _ptr(Y), Y.stride(0), _stream(stream)),
            "w4_gemm_smallM")
+    return Y
+
+
+def w4_gemm_prompt(codes, steps, X, Y=None, stream=None):
+    """Prompt-chunk product: Y[m, n] for the M rows of X ([M, ldx], ldx >= K,
+    M up to W4_MAX_M_PROMPT) on the matrix cores; Y fp32 [M, N]."""
+    N, K = _matrix(codes, steps)
+    if X.dim() != 2 or X.stride(1) != 1 or X.shape[1] < K:
+        raise ValueError("X must be [M, >=K] with unit column stride")
+    M = X.shape[0]
+    if Y is None:
+        Y = torch.empty((M, N), dtype=torch.float32, device=codes.device)
+    if Y.dim() != 2 or Y.stride(1) != 1 or Y.shape[0] != M or Y.shape[1] < N:
+        raise ValueError("Y must be [M, >=N] with unit column stride")
+    _check(lib.w4_gemm_prompt(_ptr(codes), _ptr(steps), N, K, _ptr(X), _act_dtype(X), M,
+                              X.stride(0), _ptr(Y), Y.stride(0), _stream(stream)),
+           "w4_gemm_prompt")
     return Y
 
 

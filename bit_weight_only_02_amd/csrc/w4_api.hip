@@ -167,6 +167,41 @@ int w4_gemm_smallM(const uint32_t *codes, const uint16_t *steps, int32_t N, int3
                     "w4_gemm_smallM");
 }
 
+int w4_gemm_prompt(const uint32_t *codes, const uint16_t *steps, int32_t N, int32_t K,
+                   const void *X, int32_t xdt, int32_t M, int64_t ldx,
+                   float *Y, int64_t ldy, void *stream) {
+    int st;
+    if ((st = check_matrix(codes, steps, N, K))) return st;
+    if ((st = check_dtype(xdt))) return st;
+    if (M < 1 || M > W4_MAX_M_PROMPT) return fail(W4_ERR_INVALID_ARG, "M=%d outside 1..%d", M, W4_MAX_M_PROMPT);
+    if (K > W4_MAX_K_SMALLM) return fail(W4_ERR_UNSUPPORTED, "K=%d exceeds %d", K, W4_MAX_K_SMALLM);
+    if (ldx < K || ldy < N) return fail(W4_ERR_INVALID_ARG, "ldx < K or ldy < N");
+    if (N > 0 && (!Y || (K > 0 && !X))) return fail(W4_ERR_INVALID_ARG, "null X/Y");
+    if (X && !aligned(X, 2)) return fail(W4_ERR_ALIGNMENT, "X not 2-byte aligned");
+    if (Y && !aligned(Y, 4)) return fail(W4_ERR_ALIGNMENT, "Y not 4-byte aligned");
+    if (N == 0) return W4_OK;
+    if ((st = device_ready())) return st;
+    if (forced_launch_error()) return fail(W4_ERR_HIP, "forced launch error (test hook)");
+    if (K == 0) {
+        // empty sums: zeros through the batch-1 kernel, row by row
+        for (int m = 0; m < M; ++m) {
+            hipError_t e = w4::launch_gemv(codes, steps, N, 0, static_cast<const uint16_t *>(X), xdt,
+                                           Y + (int64_t)m * ldy, static_cast<hipStream_t>(stream));
+            if (e != hipSuccess) return launched(e, "w4_gemm_prompt");
+        }
+        return launched(hipSuccess, "w4_gemm_prompt");
+    }
+    void *ws = nullptr;
+    if ((st = staging_buffer(w4::kWsCounterBytes + w4::gemm_prompt_workspace(N, K, M),
+                             static_cast<hipStream_t>(stream), &ws)))
+        return st;
+    // the staged rows go after the counter area, which other calls keep at zero
+    return launched(w4::launch_gemm_prompt(codes, steps, N, K, static_cast<const uint16_t *>(X), ldx, xdt, M,
+                                           Y, ldy, static_cast<char *>(ws) + w4::kWsCounterBytes,
+                                           static_cast<hipStream_t>(stream)),
+                    "w4_gemm_prompt");
+}
+
 int w4_embed_gather(const uint32_t *codes, const uint16_t *steps, int32_t V, int32_t K,
                     const int32_t *ids, int32_t n, uint16_t *out_bf16, int32_t *dev_err,
                     void *stream) {

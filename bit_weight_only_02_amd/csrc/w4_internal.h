@@ -33,6 +33,11 @@ constexpr int kMaxGridColumns = 2048;
 constexpr size_t kWsCounterBytes = 16384;
 static_assert(kMaxGridColumns * 4 <= (int)kWsCounterBytes, "counter area");
 size_t gemm_smallm_workspace(int N, int K, int M);
+// prompt-chunk product (w4_gemm_prompt.hip): staged activations, row scales and flags
+size_t gemm_prompt_workspace(int N, int K, int M);
+hipError_t launch_gemm_prompt(const uint32_t *codes, const uint16_t *steps, int N, int K,
+                              const uint16_t *X, long ldx, int dt, int M, float *Y, long ldy,
+                              void *ws, hipStream_t stream);
 int smallm_grid_x(int N, int KW);
 
 hipError_t launch_gemm_smallm(const uint32_t *codes, const uint16_t *steps, int N, int K,

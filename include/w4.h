@@ -19,6 +19,9 @@
  *   [P1-S4] same page, "Step 4 - Replay Each Decode Step as One CUDA Graph" and
  *           the tip "Merge the Small Projections": a decode step is a long chain
  *           of small products, run without host launches in between.
+ *   [P1-S6] same page, "Step 6 - Read Prompts in 32-Bit on a Card Without Tensor
+ *           Cores": a prompt is read in chunks of 256 tokens, each chunk a
+ *           product of many activation rows with every weight matrix.
  *   [P3]    anyesh.me, "Running a 26B MoE on an 8 GB Jetson by streaming experts
  *           from SSD", section "Streaming without touching a single GPU kernel":
  *           the expert matmul addresses expert id as base + id * stride; a pool
@@ -86,6 +89,7 @@ typedef enum { W4_F16 = 0, W4_BF16 = 1, W4_F32_RMS = 2 } w4_dtype;
 #define W4_MAX_K_CHAIN 8192   /* largest K of a w4_gemv_chain record */
 #define W4_MAX_M 16     /* largest M of w4_gemm_smallM */
 #define W4_MAX_TOPK 32  /* largest experts per token of w4_moe_gemv_ids */
+#define W4_MAX_M_PROMPT 4096 /* largest M of w4_gemm_prompt */
 
 /*
  * Batch-1 product [P1-S3]:  y[n] = sum_k w(n,k) * x[k]  for n in [0, N).
@@ -113,6 +117,30 @@ int w4_gemv(const uint32_t *codes, const uint16_t *steps, int32_t N, int32_t K,
  * must not overlap).
  */
 int w4_gemm_smallM(const uint32_t *codes, const uint16_t *steps, int32_t N, int32_t K,
+                   const void *X, int32_t xdt, int32_t M, int64_t ldx,
+                   float *Y, int64_t ldy, void *stream);
+
+/*
+ * Prompt-chunk product [P1-S6] with M activation rows, 1 <= M <= W4_MAX_M_PROMPT
+ * (a chunk of prompt tokens, e.g. 256):
+ *   Y[m*ldy + n] = sum_k w(n,k) * X[m*ldx + k]   for m < M, n < N.
+ * [P1-S6] is the same page's "Step 6 - Read Prompts in 32-Bit on a Card
+ * Without Tensor Cores": prompts are read in chunks of 256 tokens, and the
+ * product [256, 1536] x [1536, 24576] is quoted in TFLOP/s.  Here it runs on
+ * the matrix cores straight from the packed words (no 16-bit weight matrix).
+ *   X: fp16 or bf16 (xdt), 2-byte aligned, ldx >= K.  Y: fp32, ldy >= N,
+ *      4-byte aligned; written, never read.  K <= W4_MAX_K_SMALLM.
+ * Each weight (c - 8) * step, scaled by a power of two per weight row, and
+ * each activation, scaled by a power of two per activation row, is an exact
+ * fp16 operand; the products sum in fp32.  Rows outside those exponent ranges
+ * (weight steps spanning more than 2^25, or a bf16 subnormal/inf/NaN step;
+ * bf16 activation rows spanning more than 2^31, or holding inf/NaN or a
+ * subnormal) take slower exact paths, so the bound above holds for all inputs.
+ * Two kernels run: the activations are first staged as fp16 into the device
+ * buffer that the library allocates once per device and reuses (see
+ * w4_gemm_smallM; 2*K*M bytes, rounded up), then the product.
+ */
+int w4_gemm_prompt(const uint32_t *codes, const uint16_t *steps, int32_t N, int32_t K,
                    const void *X, int32_t xdt, int32_t M, int64_t ldx,
                    float *Y, int64_t ldy, void *stream);
 

@@ -19,7 +19,7 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("w4_gemv", "w4_gemm_smallM", "w4_moe_gemv_ids", "w4_embed_gather",
+    for n in ("w4_gemv", "w4_gemm_smallM", "w4_gemm_prompt", "w4_moe_gemv_ids", "w4_embed_gather",
               "w4_rms_renorm", "w4_gemv_chain", "w4_probe_stream", "w4_strerror"):
         assert n in names
 
@@ -76,6 +76,23 @@ def test_gather_and_renorm_argument_errors():
     assert L.w4_rms_renorm(None, 64, 64, 1, FAKE, 64, 0, None) == -1
     assert L.w4_rms_renorm(FAKE, 32, 64, 2, FAKE, 64, 0, None) == -1   # ldv < K
     assert L.w4_probe_stream(FAKE, 17, FAKE, None) == -1
+
+
+def test_gemm_argument_errors():
+    import bit_weight_only_02_amd as w4
+    L = w4.lib
+    for fn, mmax in ((L.w4_gemm_smallM, 16), (L.w4_gemm_prompt, 4096)):
+        # codes, steps, N, K, X, xdt, M, ldx, Y, ldy, stream
+        assert fn(FAKE, FAKE, 64, 64, FAKE, 0, 0, 64, FAKE, 64, None) == -1          # M = 0
+        assert fn(FAKE, FAKE, 64, 64, FAKE, 0, mmax + 1, 64, FAKE, 64, None) == -1   # M too large
+        assert fn(FAKE, FAKE, 64, 48, FAKE, 0, 2, 64, FAKE, 64, None) == -1          # K % 32
+        assert fn(FAKE, FAKE, 64, 64, FAKE, 0, 2, 32, FAKE, 64, None) == -1          # ldx < K
+        assert fn(FAKE, FAKE, 64, 64, FAKE, 0, 2, 64, FAKE, 32, None) == -1          # ldy < N
+        assert fn(FAKE, FAKE, 64, 64, FAKE, 9, 2, 64, FAKE, 64, None) == -3          # dtype
+        assert fn(FAKE, FAKE, 64, 64, FAKE + 1, 0, 2, 64, FAKE, 64, None) == -2      # X alignment
+        assert fn(FAKE, FAKE, 64, 64, FAKE, 0, 2, 64, FAKE + 2, 64, None) == -2      # Y alignment
+        assert fn(FAKE, FAKE, 64, 32768, FAKE, 0, 2, 32768, FAKE, 64, None) == -4    # K too large
+        assert fn(FAKE, FAKE, 0, 64, FAKE, 0, 2, 64, FAKE, 64, None) == 0            # N = 0
 
 
 def test_moe_argument_errors():

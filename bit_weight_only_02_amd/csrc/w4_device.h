@@ -396,6 +396,13 @@ __device__ __forceinline__ void lds_dma16(const void *g, void *lds) {
     asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off nt" ::"v"(g), "s"(m) : "memory");
 }
 
+// The same without the non-temporal hint, for data that other workgroups read
+// again soon (it stays in the caches).
+__device__ __forceinline__ void lds_dma16_keep(const void *g, void *lds) {
+    const uint32_t m = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) void *)lds);
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(m) : "memory");
+}
+
 // The 4-byte form (lane i writes 4 bytes at lds + 4*i).
 __device__ __forceinline__ void lds_dma4(const void *g, void *lds) {
     const uint32_t m = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) void *)lds);
@@ -415,6 +422,24 @@ __device__ __forceinline__ void lds_dma16_nt(const void *sbase, uint32_t voff, v
     const uint32_t m = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) void *)lds);
     asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1 nt" ::"v"(voff), "s"(sbase), "s"(m)
                  : "memory");
+}
+
+// Direct-to-LDS load with a wave-uniform base (scalar registers), a per-lane
+// 32-bit byte offset and a wave-uniform LDS byte address (lane i writes 16
+// bytes at lds_addr + 16*i); NT marks it non-temporal.
+template <bool NT>
+__device__ __forceinline__ void lds_dma16_so(const void *sbase, uint32_t voff, uint32_t lds_addr) {
+    const uint64_t b = (uint64_t)(uintptr_t)sbase;
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+    sbase = (const void *)(uintptr_t)(((uint64_t)hi << 32) | (uint64_t)lo);
+    const uint32_t m = __builtin_amdgcn_readfirstlane(lds_addr);
+    if constexpr (NT)
+        asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1 nt" ::"v"(voff), "s"(sbase), "s"(m)
+                     : "memory");
+    else
+        asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(m)
+                     : "memory");
 }
 
 // Wait until at most `pending` vector-memory operations are outstanding, as an

@@ -14,7 +14,7 @@
 // bf16 step 8, so the product fits fp16's 11 bits exactly whenever it is a
 // normal fp16 number.  t_n is a power of two per weight row, chosen from the
 // row's largest step so that every product lies in [2^-14, 2^15); a row whose
-// steps span more than 2^25 (or hold a bf16 subnormal, inf or NaN) cannot be
+// steps span more than 2^21 (or hold a bf16 subnormal, inf or NaN) cannot be
 // scaled that way, and the 16-row tile holding it instead multiplies (c - 8)
 // alone and applies each group's step to the fp32 MFMA result (the small-M
 // engine's form: exact, but one VALU multiply-add per output per group).  The
@@ -42,19 +42,75 @@ namespace w4 {
 
 constexpr int kPromptNT = 3;  // 16-row weight tiles per wave
 
-// ---- staging pass: one workgroup per (padded) activation row ---------------
-// Xt chunk (p, m) at Xt[p*Mp + m]: columns 8p..8p+7 of row m (p = 4g + q), in
-// the pair order (x0,x4)(x1,x5)(x2,x6)(x3,x7) of the weight unpack, scaled by
-// 2^xs[m]; rows m >= M and columns >= K are zeros.  xbad[m] = 1 when row m
-// cannot be staged exactly (bf16 only).
-__global__ __launch_bounds__(256) void prompt_stage_kernel(const uint16_t *__restrict__ X, long ldx,
-                                                           int dt, int M, int K, int Gp, int Mp,
-                                                           uint4 *__restrict__ Xt,
-                                                           int *__restrict__ xs,
-                                                           int *__restrict__ xbad) {
+// ---- staging pass ---------------------------------------------------------
+// Workgroups 0 .. Mp-1 stage one activation row each; the next Np/16 each
+// prepare one 16-row tile of the weight steps.
+//
+// Activation row m: Xt chunk (p, m) at Xt[p*Mp + m] holds columns 8p..8p+7
+// (p = 4g + q) in the pair order (x0,x4)(x1,x5)(x2,x6)(x3,x7) of the weight
+// unpack, scaled by 2^xs[m]; rows m >= M and columns >= K are zeros.
+// xbad[m] = 1 when the bf16 row cannot be staged exactly (its chunks are then
+// zeros and the product reads the row itself).
+//
+// Weight tile T (rows 16T .. 16T+15, rows >= N as all-zero steps): per row the
+// scale t_n = 138 - (largest biased step exponent), so that every |c - 8| *
+// step * 2^t_n lies below 2^15; the tile is fast (tfast[T] = 1) when every row
+// has no subnormal, inf or NaN step and its nonzero steps span at most 2^21
+// (every product then at least 2^-14, a normal fp16 number).  For a fast tile,
+// St[(r*Np + n)*4 + j] = fp16(step(n, 4r + j) * 2^t_n), exact (8 significant
+// bits in fp16's normal range), and 0 for groups past K.
+__global__ __launch_bounds__(256) void prompt_stage_kernel(
+    const uint16_t *__restrict__ X, long ldx, int dt, int M, int K, int Gp, int Mp,
+    uint4 *__restrict__ Xt, int *__restrict__ xs, int *__restrict__ xbad,
+    const uint16_t *__restrict__ steps, int N, int Np, _Float16 *__restrict__ St,
+    int *__restrict__ tn, int *__restrict__ tfast) {
     __shared__ uint32_t red_mx[4], red_mn[4];
-    const int m = blockIdx.x;
+    __shared__ int red_bad[4];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int G = K >> 5;
+
+    if ((int)blockIdx.x >= Mp) {
+        // ---- one 16-row tile of weight steps: 16 threads per row ----
+        const int T = blockIdx.x - Mp;
+        const int r16 = tid >> 4, k = tid & 15;
+        const int n = T * 16 + r16;
+        const uint16_t *sp = steps + (long)min(n, N - 1) * G;
+        int emax = 0, emin = 255, bad = 0;
+        if (n < N) {
+            for (int g = k; g < G; g += 16) {
+                const int mag = sp[g] & 0x7FFF;
+                if (mag == 0) continue;
+                const int e = mag >> 7;
+                if (e == 0 || e == 255) bad = 1;
+                emax = max(emax, e);
+                emin = min(emin, e);
+            }
+        }
+#pragma unroll
+        for (int off = 1; off < 16; off <<= 1) {
+            emax = max(emax, __shfl_xor(emax, off, kWave));
+            emin = min(emin, __shfl_xor(emin, off, kWave));
+            bad |= __shfl_xor(bad, off, kWave);
+        }
+        if (emax > 0 && emax - emin > 21) bad = 1;
+        const int t = emax > 0 ? 138 - emax : 0;
+        const int wbad = wave_or_i32(bad);
+        if (lane == 0) red_bad[wave] = wbad;
+        __syncthreads();
+        const bool fast = !(red_bad[0] | red_bad[1] | red_bad[2] | red_bad[3]);
+        if (k == 0) tn[n] = fast ? t : 0;
+        if (tid == 0) tfast[T] = fast ? 1 : 0;
+        // scaled steps of every round, 4 per row and round; 0 past K and past N
+        for (int gg = k; gg < Gp; gg += 16) {
+            _Float16 v = (_Float16)0.0f;
+            if (fast && n < N && gg < G) v = (_Float16)__builtin_ldexpf(bf16_to_f32(sp[gg]), t);
+            St[((long)(gg >> 2) * Np + n) * 4 + (gg & 3)] = v;
+        }
+        return;
+    }
+
+    // ---- one activation row ----
+    const int m = blockIdx.x;
     const int nch = Gp * 4, kch = K >> 3;
     if (m >= M) {
         for (int p = tid; p < nch; p += 256) Xt[(long)p * Mp + m] = make_uint4(0, 0, 0, 0);
@@ -131,20 +187,31 @@ __global__ __launch_bounds__(256) void prompt_stage_kernel(const uint16_t *__res
 
 // ---- the product -------------------------------------------------------------
 // Grid: x = blocks of BN = 64*NT weight rows, y = blocks of BM = 16*MT
-// activation rows.  Dynamic LDS: two buffers of one round (4 groups) of the
-// staged activations, 16*BM chunks of 16 bytes each, chunk (p, m) of the round
-// at p*BM + m.
-template <int MT>
-__global__ __launch_bounds__(256) void prompt_kernel(const uint4 *__restrict__ codes,
-                                                     const uint16_t *__restrict__ steps, int N, int K,
-                                                     const uint4 *__restrict__ Xt,
-                                                     const int *__restrict__ xs,
-                                                     const int *__restrict__ xbad,
-                                                     const uint16_t *__restrict__ X, long ldx, int dt,
-                                                     int M, int Mp, int Gp, float *__restrict__ Y,
-                                                     long ldy) {
-    constexpr int NT = kPromptNT, BM = 16 * MT, BN = 64 * NT;
-    extern __shared__ uint4 prompt_a[];
+// activation rows.  Every operand goes through a ring of D stages in LDS, each
+// holding one round (4 groups) and filled by direct-to-LDS loads D-1 rounds
+// ahead of the round computed:
+//   A:  16*BM chunks, chunk (p, m) of the round at p*BM + m (p = 4j + q);
+//   B:  4*BN chunks of codes, group 4r + Q of block row rl at 4*rl + Q (each
+//       row's 64 bytes are read by 4 adjacent lanes);
+//   S:  the scaled steps of the round, 4 fp16 per block row (BN*8 bytes,
+//       padded to 64 chunks per wave so that every wave issues one full
+//       instruction).
+// W waves, each with NT 16-row weight tiles and all MT activation tiles.
+// Each wave issues the same number of load instructions per round, so "round
+// r has landed" is a count of outstanding loads.
+template <int MT, int D, int W>
+__global__ __launch_bounds__(64 * W) void prompt_kernel(
+    const uint4 *__restrict__ codes, const uint16_t *__restrict__ steps, int N, int K,
+    const uint4 *__restrict__ Xt, const int *__restrict__ xs, const int *__restrict__ xbad,
+    const uint4 *__restrict__ St, const int *__restrict__ tn, const int *__restrict__ tfast,
+    const uint16_t *__restrict__ X, long ldx, int dt, int M, int Mp, int Gp, int Np,
+    float *__restrict__ Y, long ldy) {
+    constexpr int NT = kPromptNT, BM = 16 * MT, BN = 16 * W * NT, TH = 64 * W;
+    constexpr int SA = 16 * BM, SB = 4 * BN, SS = TH, STAGE = SA + SB + SS;  // chunks
+    constexpr int PER = SA / TH + SB / TH + 1;  // load instructions per wave and round
+    static_assert(SA % TH == 0 && SB % TH == 0 && BN * 8 <= SS * 16, "stage layout");
+    static_assert((D - 2) * PER < 64, "vmcnt range");
+    extern __shared__ uint4 prompt_lds[];
     __shared__ int sh_xs[BM];
     __shared__ int sh_bad;
     const int G = K >> 5;
@@ -154,7 +221,7 @@ __global__ __launch_bounds__(256) void prompt_kernel(const uint4 *__restrict__ c
 
     if (tid == 0) sh_bad = 0;
     __syncthreads();
-    for (int i = tid; i < BM; i += 256) {
+    for (int i = tid; i < BM; i += TH) {
         sh_xs[i] = xs[m0 + i];
         if (m0 + i < M && xbad[m0 + i]) sh_bad = 1;
     }
@@ -163,7 +230,7 @@ __global__ __launch_bounds__(256) void prompt_kernel(const uint4 *__restrict__ c
     if (sh_bad) {
         // Rare exact path: a row of this block could not be staged as fp16.
         // Plain fp32 products and group sums, one output per thread at a time.
-        for (int o = tid; o < BM * BN; o += 256) {
+        for (int o = tid; o < BM * BN; o += TH) {
             const int mm = m0 + o / BN, n = nb0 + o % BN;
             if (mm >= M || n >= N) continue;
             float acc = 0.0f;
@@ -175,75 +242,67 @@ __global__ __launch_bounds__(256) void prompt_kernel(const uint4 *__restrict__ c
         return;
     }
 
-    // Rows of this wave's NT tiles (clamped for loads; stored only below N).
-    int row[NT];
+    // the wave's tiles: fast when the staging pass found all of them scalable
+    int fast_i = 1;
 #pragma unroll
-    for (int t = 0; t < NT; ++t) row[t] = min(nb0 + (wave * NT + t) * 16 + n_l, N - 1);
+    for (int t = 0; t < NT; ++t) fast_i &= tfast[(nb0 >> 4) + wave * NT + t];
+    const bool fast = __builtin_amdgcn_readfirstlane(fast_i) != 0;
 
-    // Per-row scale t_n from the exponents of the row's nonzero steps; a row
-    // that cannot be scaled makes its wave take the per-group path.
-    int tn[NT];
-    int wave_bad = 0;
+    // Request round r into stage b.  Per-lane byte offsets are fixed; the
+    // round enters through the wave-uniform bases.  Every address is in
+    // bounds: codes rows are clamped to N - 1, and in a last round cut by K the
+    // groups too; S padding lanes re-read the first chunk.
+    const uint32_t wave_u = __builtin_amdgcn_readfirstlane(wave);
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void *)prompt_lds;
+    uint32_t offa[SA / TH], offb[SB / TH];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-        int emax = 0, emin = 255, bad = 0;
-        const uint16_t *sp = steps + (long)row[t] * G;
-        for (int g = q; g < G; g += 4) {
-            const int mag = sp[g] & 0x7FFF;
-            if (mag == 0) continue;
-            const int e = mag >> 7;
-            if (e == 0 || e == 255) bad = 1;
-            emax = max(emax, e);
-            emin = min(emin, e);
-        }
-        emax = max(emax, __shfl_xor(emax, 16, kWave));
-        emax = max(emax, __shfl_xor(emax, 32, kWave));
-        emin = min(emin, __shfl_xor(emin, 16, kWave));
-        emin = min(emin, __shfl_xor(emin, 32, kWave));
-        if (emax > 0 && emax - emin > 25) bad = 1;
-        tn[t] = emax > 0 ? 138 - emax : 0;  // largest |c - 8| * step * 2^t below 2^15
-        wave_bad |= bad;
+    for (int i = 0; i < SA / TH; ++i) {
+        const int c = wave * 64 + TH * i + lane;
+        offa[i] = (uint32_t)((c / BM) * Mp + c % BM) * 16u;
     }
-    const bool fast = !wave_or_i32(wave_bad);
-
-    // Loads of one round (4 groups): lane (n_l, q) reads group 4r + q of its
-    // rows (clamped: groups past G multiply zero activations, and their steps
-    // read as 0), and the 4 steps of the round.
-    uint4 qw[NT];
-    uint2 sw[NT];
-    const bool steps8 = (G & 3) == 0 && (reinterpret_cast<uintptr_t>(steps) & 7) == 0;
-    auto load_b = [&](int r) __attribute__((always_inline)) {
-        const int g0 = 4 * r;
+    int brow[SB / TH], bq[SB / TH];
 #pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            qw[t] = codes[(long)row[t] * G + min(g0 + q, G - 1)];
-            const uint16_t *sp = steps + (long)row[t] * G + g0;
-            if (steps8) {
-                sw[t] = *reinterpret_cast<const uint2 *>(sp);
-            } else {
-                const uint32_t s0 = g0 < G ? sp[0] : 0u, s1 = g0 + 1 < G ? sp[1] : 0u;
-                const uint32_t s2 = g0 + 2 < G ? sp[2] : 0u, s3 = g0 + 3 < G ? sp[3] : 0u;
-                sw[t] = make_uint2(s0 | (s1 << 16), s2 | (s3 << 16));
-            }
+    for (int i = 0; i < SB / TH; ++i) {
+        const int c = wave * 64 + TH * i + lane;
+        brow[i] = min(nb0 + (c >> 2), N - 1) - nb0;  // a row's 4 groups from 4 adjacent lanes
+        bq[i] = c & 3;
+        offb[i] = (uint32_t)(brow[i] * G + bq[i]) * 16u;
+    }
+    const uint32_t offs = (uint32_t)((wave * 64 + lane) < BN / 2 ? (wave * 64 + lane) : 0) * 16u;
+    const uint4 *codes_blk = codes + (long)nb0 * G;
+    auto issue = [&](int r, int b) __attribute__((always_inline)) {
+        const uint32_t st = lds0 + (uint32_t)(b * STAGE) * 16u;
+#pragma unroll
+        for (int i = 0; i < SA / TH; ++i)
+            lds_dma16_so<false>(Xt + (long)16 * r * Mp + m0, offa[i], st + (wave_u * 64 + TH * i) * 16u);
+        if (4 * r + 3 < G) {
+#pragma unroll
+            for (int i = 0; i < SB / TH; ++i)
+                lds_dma16_so<true>(codes_blk + 4 * r, offb[i], st + (SA + wave_u * 64 + TH * i) * 16u);
+        } else {
+#pragma unroll
+            for (int i = 0; i < SB / TH; ++i)
+                lds_dma16_so<true>(codes_blk, (uint32_t)(brow[i] * G + min(4 * r + bq[i], G - 1)) * 16u,
+                                   st + (SA + wave_u * 64 + TH * i) * 16u);
         }
-    };
-    // Direct-to-LDS copy of round r's activations into buffer b: 16*BM chunks,
-    // 64 per instruction (BM is a multiple of 16, so every lane has one).
-    auto load_a = [&](int r, int b) __attribute__((always_inline)) {
-        uint4 *dst = prompt_a + b * 16 * BM;
-        for (int c0 = wave * 64; c0 < 16 * BM; c0 += 256) {
-            const int c = c0 + lane;
-            const int p = c / BM, mm = c % BM;
-            const uint4 *src = Xt + (long)(16 * r + p) * Mp + m0 + mm;
-            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)src,
-                                             (__attribute__((address_space(3))) void *)(dst + c0), 16,
-                                             0, 0);
-        }
+        lds_dma16_so<false>(St + ((long)r * Np + nb0) / 2, offs, st + (SA + SB + wave_u * 64) * 16u);
     };
 
     const int rounds = Gp >> 2;
-    const uint32_t k_or = 0x64006400u;                   // 1024 in both fp16 halves
+    // Unpack: a nibble masked into the low mantissa of an fp16 1024 gives
+    // 1024 + c (low nibble of a byte) or 1024 + 16c (high nibble); subtracting
+    // 1032 or 1152 leaves (c - 8) or 16 (c - 8), and the step factor (divided
+    // by 16 for the high nibbles) follows.  One AND-OR per pair, one shift per
+    // word.
+    const uint32_t k_or = 0x64006400u, m_lo = 0x000F000Fu, m_hi = 0x00F000F0u;
     const h2 k1032 = __builtin_bit_cast(h2, 0x64086408u);  // 1032 in both halves
+    const h2 k1152 = __builtin_bit_cast(h2, 0x64806480u);  // 1152 in both halves
+    const h2 k16th = __builtin_bit_cast(h2, 0x2C002C00u);  // 1/16 in both halves
+    auto and_or = [](uint32_t x, uint32_t m, uint32_t k) __attribute__((always_inline)) {
+        uint32_t r;
+        asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "v"(m), "v"(k));
+        return r;
+    };
     f4 acc[MT][NT];
 #pragma unroll
     for (int i = 0; i < MT; ++i)
@@ -252,58 +311,89 @@ __global__ __launch_bounds__(256) void prompt_kernel(const uint4 *__restrict__ c
 
     auto main_loop = [&](auto fast_t) __attribute__((always_inline)) {
         constexpr bool FAST = decltype(fast_t)::value;
-        load_a(0, 0);
-        load_b(0);
+#pragma unroll
+        for (int s = 0; s < D - 1; ++s)
+            if (s < rounds) issue(s, s);
         for (int r = 0; r < rounds; ++r) {
-            wait_vmcnt<0>();
-            lds_barrier();  // round r staged by every wave; buffer (r+1)&1 free
-            // this round's weight fragments, built before the next loads go out
-            h8 bf[4][NT];
-            float st[4][NT];
+            // round r landed (for this wave; the barrier then for all waves),
+            // and every wave is done with round r - 1, whose stage is refilled
+            if (r + D - 2 < rounds)
+                wait_vmcnt_mem<(D - 2) * PER>();
+            else
+                wait_vmcnt_mem<0>();
+            lds_barrier();
+            if (r + D - 1 < rounds) issue(r + D - 1, (r + D - 1) % D);
+            const uint4 *st = prompt_lds + (r % D) * STAGE;
+            const h8 *Ah = reinterpret_cast<const h8 *>(st);
+            const uint4 *Bc = st + SA;
+            const uint2 *Sc = reinterpret_cast<const uint2 *>(st + SA + SB);
+            // the round's raw words (word q of each of the 4 groups) and steps
+            uint32_t w[NT][4];
+            h2 sc[NT][4];
+            float sf[NT][4];
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
-                uint32_t w[4] = {qw[t].x, qw[t].y, qw[t].z, qw[t].w};
-                transpose_lane_groups(w);
-                const uint32_t sv[4] = {sw[t].x & 0xFFFFu, sw[t].x >> 16, sw[t].y & 0xFFFFu,
-                                        sw[t].y >> 16};
+                const int rl = (wave * NT + t) * 16 + n_l;
+                const uint4 qv = Bc[4 * rl + q];
+                w[t][0] = qv.x;
+                w[t][1] = qv.y;
+                w[t][2] = qv.z;
+                w[t][3] = qv.w;
+                if constexpr (FAST) {
+                    const uint2 sv = Sc[rl];
+                    sc[t][0] = as_h2(__builtin_amdgcn_perm(sv.x, sv.x, 0x01000100u));
+                    sc[t][1] = as_h2(__builtin_amdgcn_perm(sv.x, sv.x, 0x03020302u));
+                    sc[t][2] = as_h2(__builtin_amdgcn_perm(sv.y, sv.y, 0x01000100u));
+                    sc[t][3] = as_h2(__builtin_amdgcn_perm(sv.y, sv.y, 0x03020302u));
+                } else {
+                    const long rowoff = (long)min(nb0 + rl, N - 1) * G;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    h2 sc = {(_Float16)1.0f, (_Float16)1.0f};
-                    if constexpr (FAST) {
-                        const _Float16 s = (_Float16)__builtin_ldexpf(bf16_to_f32(sv[j]), tn[t]);
-                        sc = h2{s, s};
-                    } else {
-                        st[j][t] = bf16_to_f32(sv[j]);
+                    for (int j = 0; j < 4; ++j) {
+                        const int g = 4 * r + j;
+                        sf[t][j] = g < G ? bf16_to_f32(steps[rowoff + g]) : 0.0f;
+                        sc[t][j] = h2{(_Float16)1.0f, (_Float16)1.0f};
                     }
-                    // (c - 8) [* step * 2^t_n] for the pairs (c0,c4) (c1,c5) (c2,c6) (c3,c7)
-                    const h2 p0 = (as_h2((w[j] & 0x000F000Fu) | k_or) - k1032) * sc;
-                    const h2 p1 = (as_h2(((w[j] >> 4) & 0x000F000Fu) | k_or) - k1032) * sc;
-                    const h2 p2 = (as_h2(((w[j] >> 8) & 0x000F000Fu) | k_or) - k1032) * sc;
-                    const h2 p3 = (as_h2(((w[j] >> 12) & 0x000F000Fu) | k_or) - k1032) * sc;
-                    bf[j][t] = h8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
                 }
             }
-            if (r + 1 < rounds) {
-                load_a(r + 1, (r + 1) & 1);
-                load_b(r + 1);
-            }
-            const h8 *Ah = reinterpret_cast<const h8 *>(prompt_a + (r & 1) * 16 * BM);
+            // A fragments of group j + 1 are requested before the weight
+            // unpack and the MFMAs of group j
+            h8 a[2][MT];
+#pragma unroll
+            for (int i = 0; i < MT; ++i) a[0][i] = Ah[q * BM + 16 * i + n_l];
+#pragma unroll
+            for (int t = 0; t < NT; ++t) transpose_lane_groups(w[t]);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
+                if (j + 1 < 4) {
+#pragma unroll
+                    for (int i = 0; i < MT; ++i) a[(j + 1) & 1][i] = Ah[(4 * (j + 1) + q) * BM + 16 * i + n_l];
+                }
+                h8 bf[NT];
+#pragma unroll
+                for (int t = 0; t < NT; ++t) {
+                    // (c - 8) [* step * 2^t_n] for the pairs (c0,c4) (c1,c5) (c2,c6) (c3,c7)
+                    const uint32_t wj = w[t][j];
+                    const uint32_t u = wj >> 8;
+                    const h2 s16 = sc[t][j] * k16th;
+                    const h2 p0 = (as_h2(and_or(wj, m_lo, k_or)) - k1032) * sc[t][j];
+                    const h2 p1 = (as_h2(and_or(wj, m_hi, k_or)) - k1152) * s16;
+                    const h2 p2 = (as_h2(and_or(u, m_lo, k_or)) - k1032) * sc[t][j];
+                    const h2 p3 = (as_h2(and_or(u, m_hi, k_or)) - k1152) * s16;
+                    bf[t] = h8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+                }
 #pragma unroll
                 for (int i = 0; i < MT; ++i) {
-                    const h8 a = Ah[(4 * j + q) * BM + 16 * i + n_l];
 #pragma unroll
                     for (int t = 0; t < NT; ++t) {
                         if constexpr (FAST) {
-                            acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bf[j][t], acc[i][t], 0, 0, 0);
+                            acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[j & 1][i], bf[t], acc[i][t], 0, 0, 0);
                         } else {
                             const f4 d = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                                a, bf[j][t], f4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
-                            acc[i][t][0] = __builtin_fmaf(d[0], st[j][t], acc[i][t][0]);
-                            acc[i][t][1] = __builtin_fmaf(d[1], st[j][t], acc[i][t][1]);
-                            acc[i][t][2] = __builtin_fmaf(d[2], st[j][t], acc[i][t][2]);
-                            acc[i][t][3] = __builtin_fmaf(d[3], st[j][t], acc[i][t][3]);
+                                a[j & 1][i], bf[t], f4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+                            acc[i][t][0] = __builtin_fmaf(d[0], sf[t][j], acc[i][t][0]);
+                            acc[i][t][1] = __builtin_fmaf(d[1], sf[t][j], acc[i][t][1]);
+                            acc[i][t][2] = __builtin_fmaf(d[2], sf[t][j], acc[i][t][2]);
+                            acc[i][t][3] = __builtin_fmaf(d[3], sf[t][j], acc[i][t][3]);
                         }
                     }
                 }
@@ -320,7 +410,7 @@ __global__ __launch_bounds__(256) void prompt_kernel(const uint4 *__restrict__ c
     for (int t = 0; t < NT; ++t) {
         const int n = nb0 + (wave * NT + t) * 16 + n_l;
         if (n >= N) continue;
-        const int e_n = fast ? tn[t] : 0;
+        const int e_n = fast ? tn[n] : 0;
 #pragma unroll
         for (int i = 0; i < MT; ++i) {
 #pragma unroll
@@ -336,60 +426,112 @@ __global__ __launch_bounds__(256) void prompt_kernel(const uint4 *__restrict__ c
 namespace {
 
 typedef void (*PromptFn)(const uint4 *, const uint16_t *, int, int, const uint4 *, const int *,
-                         const int *, const uint16_t *, long, int, int, int, int, float *, long);
+                         const int *, const uint4 *, const int *, const int *, const uint16_t *, long,
+                         int, int, int, int, int, float *, long);
+
+constexpr int kPromptD = 3;  // ring stages
 
 struct PromptPlan {
     int MT;      // 16-row activation tiles per workgroup
+    int W;       // waves per workgroup
     int Mp;      // activation rows padded to a multiple of 16*MT
     int Gp;      // groups padded to a multiple of 4
+    int Np;      // weight rows padded to a multiple of BN = 16*W*NT
+    size_t off_xs, off_st, off_tn, off_tf, bytes;  // workspace layout
 };
 
-PromptPlan prompt_plan(int K, int M) {
+// Eight waves of 4 activation tiles (two waves per SIMD, so one's weight
+// unpack overlaps the other's MFMAs) from 64 rows on; fewer rows, four waves
+// with one tile per 16 rows.
+PromptPlan prompt_plan(int N, int K, int M) {
     PromptPlan p;
-    p.MT = M > 64 ? 8 : M > 32 ? 4 : M > 16 ? 2 : 1;
-    const int bm = 16 * p.MT;
+    if (M > 32) {
+        p.MT = 4;
+        p.W = 8;
+    } else {
+        p.MT = M > 16 ? 2 : 1;
+        p.W = 4;
+    }
+    // W4_PROMPT_TILE="MT,W" overrides the tiling (schedule sweeps; every
+    // output's sum runs in the same order whatever the tiling)
+    if (const char *e = getenv("W4_PROMPT_TILE")) {
+        int mt = 0, w = 0;
+        if (sscanf(e, "%d,%d", &mt, &w) == 2 && (mt == 1 || mt == 2 || mt == 4 || mt == 8) &&
+            (w == 4 || w == 8) && (4 * mt) % w == 0) {
+            p.MT = mt;
+            p.W = w;
+        }
+    }
+    const int bm = 16 * p.MT, bn = 16 * p.W * kPromptNT;
     p.Mp = (M + bm - 1) / bm * bm;
     p.Gp = ((K / 32) + 3) / 4 * 4;
+    p.Np = (N + bn - 1) / bn * bn;
+    p.off_xs = (size_t)p.Gp * 4 * p.Mp * 16;          // after Xt
+    p.off_st = p.off_xs + (size_t)p.Mp * 8;           // after xs, xbad (16-byte multiple)
+    p.off_tn = p.off_st + (size_t)(p.Gp / 4) * p.Np * 8;
+    p.off_tf = p.off_tn + (size_t)p.Np * 4;
+    p.bytes = p.off_tf + (size_t)(p.Np / 16) * 4;
     return p;
 }
 
-PromptFn pick_prompt(int MT) {
+template <int D, int W>
+PromptFn pick_prompt_dw(int MT) {
     switch (MT) {
-        case 1: return prompt_kernel<1>;
-        case 2: return prompt_kernel<2>;
-        case 4: return prompt_kernel<4>;
-        case 8: return prompt_kernel<8>;
+        case 1: return W == 4 ? prompt_kernel<1, D, 4> : nullptr;
+        case 2: return prompt_kernel<2, D, W>;
+        case 4: return prompt_kernel<4, D, W>;
+        case 8: return prompt_kernel<8, D, W>;
     }
     return nullptr;
 }
 
+PromptFn pick_prompt(int MT, int D, int W) {
+    switch (D * 16 + W) {
+        case 2 * 16 + 4: return pick_prompt_dw<2, 4>(MT);
+        case 3 * 16 + 4: return pick_prompt_dw<3, 4>(MT);
+        case 2 * 16 + 8: return pick_prompt_dw<2, 8>(MT);
+        case 3 * 16 + 8: return pick_prompt_dw<3, 8>(MT);
+    }
+    return nullptr;
+}
+
+size_t prompt_lds_bytes(int MT, int D, int W) {
+    return (size_t)D * (16 * 16 * MT + 4 * 16 * W * kPromptNT + 64 * W) * 16;
+}
+
 }  // namespace
 
-size_t gemm_prompt_workspace(int N, int K, int M) {
-    (void)N;
-    const PromptPlan p = prompt_plan(K, M);
-    // staged chunks, then the row scales and the row flags
-    return (size_t)p.Gp * 4 * p.Mp * 16 + (size_t)p.Mp * 8;
-}
+size_t gemm_prompt_workspace(int N, int K, int M) { return prompt_plan(N, K, M).bytes; }
 
 hipError_t launch_gemm_prompt(const uint32_t *codes, const uint16_t *steps, int N, int K,
                               const uint16_t *X, long ldx, int dt, int M, float *Y, long ldy,
                               void *ws, hipStream_t stream) {
-    const PromptPlan p = prompt_plan(K, M);
-    PromptFn fn = pick_prompt(p.MT);
-    if (!fn || !ws || K < 32 || M < 1) return hipErrorInvalidConfiguration;
-    uint4 *Xt = static_cast<uint4 *>(ws);
-    int *xs = reinterpret_cast<int *>(Xt + (size_t)p.Gp * 4 * p.Mp);
+    const PromptPlan p = prompt_plan(N, K, M);
+    int D = kPromptD;
+    // W4_PROMPT_D overrides the ring depth (schedule sweeps; a depth whose
+    // ring does not fit the LDS is refused)
+    if (const char *e = getenv("W4_PROMPT_D")) D = atoi(e);
+    PromptFn fn = pick_prompt(p.MT, D, p.W);
+    if (prompt_lds_bytes(p.MT, D, p.W) > 150 * 1024) return hipErrorInvalidConfiguration;
+    if (!fn || !ws || K < 32 || M < 1 || N < 1 || (reinterpret_cast<uintptr_t>(ws) & 15))
+        return hipErrorInvalidConfiguration;
+    char *base = static_cast<char *>(ws);
+    uint4 *Xt = reinterpret_cast<uint4 *>(base);
+    int *xs = reinterpret_cast<int *>(base + p.off_xs);
     int *xbad = xs + p.Mp;
-    hipLaunchKernelGGL(prompt_stage_kernel, dim3((unsigned)p.Mp), dim3(256), 0, stream, X, ldx, dt, M,
-                       K, p.Gp, p.Mp, Xt, xs, xbad);
+    _Float16 *St = reinterpret_cast<_Float16 *>(base + p.off_st);
+    int *tn = reinterpret_cast<int *>(base + p.off_tn);
+    int *tf = reinterpret_cast<int *>(base + p.off_tf);
+    hipLaunchKernelGGL(prompt_stage_kernel, dim3((unsigned)(p.Mp + p.Np / 16)), dim3(256), 0, stream, X,
+                       ldx, dt, M, K, p.Gp, p.Mp, Xt, xs, xbad, steps, N, p.Np, St, tn, tf);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int bn = 64 * kPromptNT;
-    const size_t lds = (size_t)2 * 16 * 16 * p.MT * sizeof(uint4);
-    hipLaunchKernelGGL(fn, dim3((unsigned)((N + bn - 1) / bn), (unsigned)(p.Mp / (16 * p.MT))), dim3(256),
-                       lds, stream, reinterpret_cast<const uint4 *>(codes), steps, N, K, Xt, xs, xbad, X,
-                       ldx, dt, M, p.Mp, p.Gp, Y, ldy);
+    const int bn = 16 * p.W * kPromptNT, bm = 16 * p.MT;
+    const size_t lds = prompt_lds_bytes(p.MT, D, p.W);
+    hipLaunchKernelGGL(fn, dim3((unsigned)(p.Np / bn), (unsigned)(p.Mp / bm)), dim3(64 * p.W), lds, stream,
+                       reinterpret_cast<const uint4 *>(codes), steps, N, K, Xt, xs, xbad,
+                       reinterpret_cast<const uint4 *>(St), tn, tf, X, ldx, dt, M, p.Mp, p.Gp, p.Np, Y,
+                       ldy);
     return hipGetLastError();
 }
 

@@ -133,7 +133,7 @@ int w4_gemm_smallM(const uint32_t *codes, const uint16_t *steps, int32_t N, int3
  * Each weight (c - 8) * step, scaled by a power of two per weight row, and
  * each activation, scaled by a power of two per activation row, is an exact
  * fp16 operand; the products sum in fp32.  Rows outside those exponent ranges
- * (weight steps spanning more than 2^25, or a bf16 subnormal/inf/NaN step;
+ * (weight steps spanning more than 2^21, or a bf16 subnormal/inf/NaN step;
  * bf16 activation rows spanning more than 2^31, or holding inf/NaN or a
  * subnormal) take slower exact paths, so the bound above holds for all inputs.
  * Two kernels run: the activations are first staged as fp16 into the device

@@ -351,6 +351,37 @@ def extra_moe(w4, torch, np, synth, timer, reps: int = 5):
     return out
 
 
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 matrix peak
+
+
+def extra_prompt(w4, torch, np, synth, timer, reps: int = 64):
+    """Prompt-chunk product [256, 1536] x [1536, 24576] on the matrix cores
+    (the product the dev.to page quotes in TFLOP/s for 256-token prompt
+    chunks): 16 weight copies rotated (340 MB, beyond the 256 MB MALL), bf16
+    and fp16 activations; two launches per call (activation and step staging,
+    then the product)."""
+    M, K, N, copies = 256, 1536, 24576, 16
+    g = torch.Generator(device="cuda")
+    g.manual_seed(0)
+    mats = []
+    for _ in range(copies):
+        c, s = synth.w4_matrix_torch(g, N, K, "cuda")
+        mats.append((c.view(N, K // 8), s.view(N, K // 32).view(torch.bfloat16)))
+    flops = 2.0 * M * N * K
+    out = {"flop_per_call": flops, "weight_copies_rotated": copies}
+    for name, dt in (("bf16", torch.bfloat16), ("f16", torch.float16)):
+        X = torch.randn((M, K), generator=g, device="cuda").to(dt)
+        Y = torch.empty((M, N), device="cuda")
+        t = timer.per_call(lambda i: w4.w4_gemm_prompt(mats[i % copies][0], mats[i % copies][1], X, Y),
+                           reps, warmup=copies)
+        tf = flops / t / 1e12
+        out[name] = {"us_per_call": round(t * 1e6, 2), "TFLOPs": round(tf, 1),
+                     "frac_of_mfma_peak": round(tf / MFMA_F16_PEAK_TFLOPS, 4)}
+    del mats
+    torch.cuda.empty_cache()
+    return out
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -358,7 +389,7 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extra", action="store_true", help="only the vocabulary-head step")
-    ap.add_argument("--only", choices=["single", "sweep", "small_m", "moe"],
+    ap.add_argument("--only", choices=["single", "sweep", "small_m", "moe", "prompt"],
                     help="run one secondary workload alone (kernel traces) and print its JSON")
     args = ap.parse_args(argv)
     if args.gpus != 1:
@@ -376,7 +407,7 @@ def main(argv=None):
     timer = Timer(torch)
     if args.only:
         run = {"single": extra_single_gemv, "sweep": extra_sweep, "small_m": extra_small_m,
-               "moe": extra_moe}[args.only]
+               "moe": extra_moe, "prompt": extra_prompt}[args.only]
         print(json.dumps({"workload": args.only, "result": run(w4, torch, np, synth, timer)}), flush=True)
         return 0
     rng = np.random.default_rng(0)
@@ -465,6 +496,7 @@ def main(argv=None):
         ex["decode_sweep_35_layers"] = extra_sweep(w4, torch, np, synth, timer)
         ex["small_m_sweep_shapes_bf16"] = extra_small_m(w4, torch, np, synth, timer)
         ex["moe_30_layers_top8_of_128"] = extra_moe(w4, torch, np, synth, timer)
+        ex["prompt_chunk_256x1536x24576"] = extra_prompt(w4, torch, np, synth, timer)
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(codes, steps, x, ids)
     print(json.dumps(result), flush=True)

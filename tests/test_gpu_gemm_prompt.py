@@ -102,6 +102,32 @@ def test_prompt_rows_with_wide_steps_take_the_exact_path(w4):
     assert np.all(Y[:, 100] == 0.0)
 
 
+@pytest.mark.parametrize("span", [20, 21, 22])
+def test_prompt_step_span_at_the_scaling_limit(w4, span):
+    """A weight row whose nonzero steps span 2^span: up to 2^21 it is scaled
+    into fp16 with its steps inside the operand, beyond that its tile applies
+    the steps to fp32 sums.  Both sides of the limit stay within the bound."""
+    rng = np.random.default_rng(40 + span)
+    N, K, M = 100, 1024, 40
+    codes, steps = synth.w4_matrix(rng, N, K)
+    steps = steps.copy()
+    steps[17, :] = oracle.f64_to_bf16(1.0)
+    steps[17, 3] = oracle.f64_to_bf16(2.0 ** -span)
+    X = synth.activations(rng, (M, K), BF16)
+    Y = run_prompt(w4, codes, steps, X, BF16, M, K)
+    check(Y, codes, steps, K, X, BF16, M)
+
+
+def test_prompt_largest_chunk(w4):
+    """M = 4096 activation rows (the largest chunk), a narrow matrix."""
+    rng = np.random.default_rng(77)
+    N, K, M = 70, 64, 4096
+    codes, steps = synth.w4_matrix(rng, N, K)
+    X = synth.activations(rng, (M, K), BF16)
+    Y = run_prompt(w4, codes, steps, X, BF16, M, K)
+    check(Y, codes, steps, K, X, BF16, M)
+
+
 def test_prompt_bf16_rows_beyond_fp16_range(w4):
     """A bf16 activation row spanning more than 2^31 cannot be staged as fp16
     with one power of two; its block of rows is computed with plain fp32

@@ -405,19 +405,59 @@ __global__ __launch_bounds__(64 * W) void prompt_kernel(
     else
         main_loop(std::false_type{});
 
-    // lane (n_l, q) holds rows 4q..4q+3 of column n_l of each 16 x 16 tile
+    // Lane (n_l, q) holds rows 4q..4q+3 of column n_l of each 16 x 16 tile.
+    // Each value is scaled back first (its column's t_n, its row's s_m); then
+    // a 4 x 4 transpose inside each quad of lanes (two exchange stages, lanes
+    // 1 and 2 apart) leaves lane (4k + c, q) with row 4q + c, columns 4k..4k+3,
+    // stored as one 16-byte non-temporal write when the four columns exist and
+    // Y allows it.
+    const bool yvec = (reinterpret_cast<uintptr_t>(Y) & 15) == 0 && (ldy & 3) == 0;
+    const int c = n_l & 3, k4 = n_l >> 2;
+    auto xch = [](float v, auto ctrl) __attribute__((always_inline)) {
+        return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), decltype(ctrl)::value, 0xF, 0xF, false));
+    };
+    using X1 = std::integral_constant<int, 0xB1>;  // quad_perm [1,0,3,2]
+    using X2 = std::integral_constant<int, 0x4E>;  // quad_perm [2,3,0,1]
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-        const int n = nb0 + (wave * NT + t) * 16 + n_l;
-        if (n >= N) continue;
-        const int e_n = fast ? tn[n] : 0;
+        const int nt0 = nb0 + (wave * NT + t) * 16;
+        const int n = nt0 + n_l;
+        const int e_n = fast && n < N ? tn[n] : 0;
 #pragma unroll
         for (int i = 0; i < MT; ++i) {
+            float v[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int ml = 16 * i + 4 * q + j;
-                if (m0 + ml < M)
-                    Y[(long)(m0 + ml) * ldy + n] = __builtin_ldexpf(acc[i][t][j], -e_n - sh_xs[ml]);
+            for (int j = 0; j < 4; ++j) v[j] = __builtin_ldexpf(acc[i][t][j], -e_n - sh_xs[16 * i + 4 * q + j]);
+            {
+                const float p0 = xch(v[0], X1{}), p1 = xch(v[1], X1{}), p2 = xch(v[2], X1{}), p3 = xch(v[3], X1{});
+                if (c & 1) {
+                    v[0] = p1;
+                    v[2] = p3;
+                } else {
+                    v[1] = p0;
+                    v[3] = p2;
+                }
+            }
+            {
+                const float p0 = xch(v[0], X2{}), p1 = xch(v[1], X2{}), p2 = xch(v[2], X2{}), p3 = xch(v[3], X2{});
+                if (c & 2) {
+                    v[0] = p2;
+                    v[1] = p3;
+                } else {
+                    v[2] = p0;
+                    v[3] = p1;
+                }
+            }
+            const int ml = 16 * i + 4 * q + c, nc = nt0 + 4 * k4;
+            if (m0 + ml >= M) continue;
+            float *dst = Y + (long)(m0 + ml) * ldy + nc;
+            if (yvec && nc + 3 < N) {
+                typedef float f4v __attribute__((ext_vector_type(4)));
+                __builtin_nontemporal_store(f4v{v[0], v[1], v[2], v[3]}, reinterpret_cast<f4v *>(dst));
+            } else {
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj)
+                    if (nc + jj < N) dst[jj] = v[jj];
             }
         }
     }

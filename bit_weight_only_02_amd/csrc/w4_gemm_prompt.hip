@@ -355,47 +355,55 @@ __global__ __launch_bounds__(64 * W) void prompt_kernel(
                     }
                 }
             }
-            // A fragments of group j + 1 are requested before the weight
-            // unpack and the MFMAs of group j
+            // Software pipeline over the round's 4 groups: the A fragments of
+            // group j + 1 are requested before the MFMAs of group j, and its
+            // weight tiles are unpacked between them (one after each
+            // activation tile), so the VALU work sits among the MFMAs
             h8 a[2][MT];
 #pragma unroll
             for (int i = 0; i < MT; ++i) a[0][i] = Ah[q * BM + 16 * i + n_l];
 #pragma unroll
             for (int t = 0; t < NT; ++t) transpose_lane_groups(w[t]);
+            auto unpack = [&](int t, int j) __attribute__((always_inline)) {
+                const uint32_t wj = w[t][j];
+                const uint32_t u = wj >> 8;
+                const h2 s16 = sc[t][j] * k16th;
+                const h2 p0 = (as_h2(and_or(wj, m_lo, k_or)) - k1032) * sc[t][j];
+                const h2 p1 = (as_h2(and_or(wj, m_hi, k_or)) - k1152) * s16;
+                const h2 p2 = (as_h2(and_or(u, m_lo, k_or)) - k1032) * sc[t][j];
+                const h2 p3 = (as_h2(and_or(u, m_hi, k_or)) - k1152) * s16;
+                return h8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+            };
+            h8 bf[2][NT];
+#pragma unroll
+            for (int t = 0; t < NT; ++t) bf[0][t] = unpack(t, 0);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 if (j + 1 < 4) {
 #pragma unroll
                     for (int i = 0; i < MT; ++i) a[(j + 1) & 1][i] = Ah[(4 * (j + 1) + q) * BM + 16 * i + n_l];
                 }
-                h8 bf[NT];
-#pragma unroll
-                for (int t = 0; t < NT; ++t) {
-                    // (c - 8) [* step * 2^t_n] for the pairs (c0,c4) (c1,c5) (c2,c6) (c3,c7)
-                    const uint32_t wj = w[t][j];
-                    const uint32_t u = wj >> 8;
-                    const h2 s16 = sc[t][j] * k16th;
-                    const h2 p0 = (as_h2(and_or(wj, m_lo, k_or)) - k1032) * sc[t][j];
-                    const h2 p1 = (as_h2(and_or(wj, m_hi, k_or)) - k1152) * s16;
-                    const h2 p2 = (as_h2(and_or(u, m_lo, k_or)) - k1032) * sc[t][j];
-                    const h2 p3 = (as_h2(and_or(u, m_hi, k_or)) - k1152) * s16;
-                    bf[t] = h8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
-                }
 #pragma unroll
                 for (int i = 0; i < MT; ++i) {
 #pragma unroll
                     for (int t = 0; t < NT; ++t) {
                         if constexpr (FAST) {
-                            acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[j & 1][i], bf[t], acc[i][t], 0, 0, 0);
+                            acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[j & 1][i], bf[j & 1][t], acc[i][t], 0, 0, 0);
                         } else {
                             const f4 d = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                                a[j & 1][i], bf[t], f4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+                                a[j & 1][i], bf[j & 1][t], f4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
                             acc[i][t][0] = __builtin_fmaf(d[0], sf[t][j], acc[i][t][0]);
                             acc[i][t][1] = __builtin_fmaf(d[1], sf[t][j], acc[i][t][1]);
                             acc[i][t][2] = __builtin_fmaf(d[2], sf[t][j], acc[i][t][2]);
                             acc[i][t][3] = __builtin_fmaf(d[3], sf[t][j], acc[i][t][3]);
                         }
                     }
+                    // the next group's weight tiles, one after each activation tile
+                    if (j + 1 < 4 && i < NT) bf[(j + 1) & 1][i] = unpack(i, j + 1);
+                }
+                if (j + 1 < 4) {
+#pragma unroll
+                    for (int t = MT; t < NT; ++t) bf[(j + 1) & 1][t] = unpack(t, j + 1);
                 }
             }
         }
@@ -480,12 +488,15 @@ struct PromptPlan {
     size_t off_xs, off_st, off_tn, off_tf, bytes;  // workspace layout
 };
 
-// Eight waves of 4 activation tiles (two waves per SIMD, so one's weight
-// unpack overlaps the other's MFMAs) from 64 rows on; fewer rows, four waves
+// Above 64 rows, four waves of 8 activation tiles (each unpacked weight tile
+// feeds 8 MFMAs); from 33 to 64 rows eight waves of 4; fewer rows, four waves
 // with one tile per 16 rows.
 PromptPlan prompt_plan(int N, int K, int M) {
     PromptPlan p;
-    if (M > 32) {
+    if (M > 64) {
+        p.MT = 8;
+        p.W = 4;
+    } else if (M > 32) {
         p.MT = 4;
         p.W = 8;
     } else {

@@ -396,13 +396,6 @@ __device__ __forceinline__ void lds_dma16(const void *g, void *lds) {
     asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off nt" ::"v"(g), "s"(m) : "memory");
 }
 
-// The same without the non-temporal hint, for data that other workgroups read
-// again soon (it stays in the caches).
-__device__ __forceinline__ void lds_dma16_keep(const void *g, void *lds) {
-    const uint32_t m = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) void *)lds);
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(m) : "memory");
-}
-
 // The 4-byte form (lane i writes 4 bytes at lds + 4*i).
 __device__ __forceinline__ void lds_dma4(const void *g, void *lds) {
     const uint32_t m = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) void *)lds);

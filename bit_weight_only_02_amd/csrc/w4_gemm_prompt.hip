@@ -29,7 +29,7 @@
 // columns 32g + 8q .. +7 of every row), so that the product streams each
 // round of 4 groups of a row block into LDS with contiguous direct-to-LDS
 // loads; the product then gives each workgroup BM = 16*MT activation rows and
-// BN = 64*NT weight rows, each of its four waves 16*NT weight rows.
+// BN = 16*W*NT weight rows, each of its W waves 16*NT weight rows.
 #include <cstdio>
 #include <cstdlib>
 #include <type_traits>

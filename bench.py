@@ -351,6 +351,25 @@ def extra_moe(w4, torch, np, synth, timer, reps: int = 5):
     return out
 
 
+def extra_gather_per_layer(w4, torch, np, synth, timer, reps: int = 200):
+    """Row gather from the per-layer 4-bit table at its own width, 262144 x 8960
+    (1.32 GB packed): 64 ids per call, fresh ids each call, in one HIP graph."""
+    Vp, Kp, n = 262144, 8960, 64
+    g = torch.Generator(device="cuda")
+    g.manual_seed(5)
+    dc, ds = synth.w4_matrix_torch(g, Vp, Kp, "cuda")
+    dc, ds = dc.view(Vp, Kp // 8), ds.view(Vp, Kp // 32).view(torch.bfloat16)
+    ids = [torch.from_numpy(synth.token_ids(np.random.default_rng(10 + i), n, Vp)).cuda() for i in range(reps)]
+    out = torch.empty((n, Kp), dtype=torch.bfloat16, device="cuda")
+    t = timer.graph_per_call(lambda i: w4.w4_embed_gather(dc, ds, ids[i % reps], out), reps)
+    nbytes = gather_bytes(n, Kp)
+    res = {"us_per_call_graph": round(t * 1e6, 3), "bytes_per_call": nbytes,
+           "GBps_graph": round(gbps(nbytes, t), 1), "frac_of_peak_graph": round(gbps(nbytes, t) / HBM_PEAK_GBPS, 4)}
+    del dc, ds
+    torch.cuda.empty_cache()
+    return res
+
+
 MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 matrix peak
 
 
@@ -389,7 +408,7 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extra", action="store_true", help="only the vocabulary-head step")
-    ap.add_argument("--only", choices=["single", "sweep", "small_m", "moe", "prompt"],
+    ap.add_argument("--only", choices=["single", "sweep", "small_m", "moe", "prompt", "gather8960"],
                     help="run one secondary workload alone (kernel traces) and print its JSON")
     args = ap.parse_args(argv)
     if args.gpus != 1:
@@ -407,7 +426,7 @@ def main(argv=None):
     timer = Timer(torch)
     if args.only:
         run = {"single": extra_single_gemv, "sweep": extra_sweep, "small_m": extra_small_m,
-               "moe": extra_moe, "prompt": extra_prompt}[args.only]
+               "moe": extra_moe, "prompt": extra_prompt, "gather8960": extra_gather_per_layer}[args.only]
         print(json.dumps({"workload": args.only, "result": run(w4, torch, np, synth, timer)}), flush=True)
         return 0
     rng = np.random.default_rng(0)
@@ -497,6 +516,7 @@ def main(argv=None):
         ex["small_m_sweep_shapes_bf16"] = extra_small_m(w4, torch, np, synth, timer)
         ex["moe_30_layers_top8_of_128"] = extra_moe(w4, torch, np, synth, timer)
         ex["prompt_chunk_256x1536x24576"] = extra_prompt(w4, torch, np, synth, timer)
+        ex["gather_per_layer_table_262144x8960"] = extra_gather_per_layer(w4, torch, np, synth, timer)
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(codes, steps, x, ids)
     print(json.dumps(result), flush=True)

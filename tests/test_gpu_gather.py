@@ -31,6 +31,27 @@ def test_gather_vocab_table_64_ids_bit_exact(w4):
     assert np.array_equal(host_bits(out), ref)
 
 
+def test_gather_per_layer_table_width_8960(w4):
+    """The per-layer 4-bit table at its own width: 262144 rows x 8960 columns
+    (1.32 GB packed, generated on the device), 64 ids, bit-exact against the
+    oracle on the gathered rows."""
+    V, K = 262144, 8960
+    g = torch.Generator(device="cuda")
+    g.manual_seed(3)
+    dc, ds = synth.w4_matrix_torch(g, V, K, "cuda")
+    dc, ds = dc.view(V, K // 8), ds.view(V, K // 32).view(torch.bfloat16)
+    ids = synth.token_ids(np.random.default_rng(4), 64, V)
+    ids[:2] = [0, V - 1]
+    dids = torch.from_numpy(ids).cuda()
+    out = w4.w4_embed_gather(dc, ds, dids)
+    torch.cuda.synchronize()
+    sub_c = dc.index_select(0, dids.long()).cpu().numpy().view(np.uint32)
+    sub_s = ds.view(torch.int16).index_select(0, dids.long()).cpu().numpy().view(np.uint16)
+    ref, bad = oracle.gather(sub_c, sub_s, 64, K, np.arange(64, dtype=np.int32))
+    assert bad == 0
+    assert np.array_equal(host_bits(out), ref)
+
+
 def test_gather_golden_ties(w4):
     rows = []
     path = os.path.join(os.path.dirname(__file__), "golden", "gather_ties.txt")

@@ -186,7 +186,7 @@ __global__ __launch_bounds__(256) void prompt_stage_kernel(
 }
 
 // ---- the product -------------------------------------------------------------
-// Grid: x = blocks of BN = 64*NT weight rows, y = blocks of BM = 16*MT
+// Grid: x = blocks of BN = 16*W*NT weight rows, y = blocks of BM = 16*MT
 // activation rows.  Every operand goes through a ring of D stages in LDS, each
 // holding one round (4 groups) and filled by direct-to-LDS loads D-1 rounds
 // ahead of the round computed:

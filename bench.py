@@ -370,6 +370,24 @@ def extra_gather_per_layer(w4, torch, np, synth, timer, reps: int = 200):
     return res
 
 
+def extra_grid_pack(w4, torch, np, synth, timer, reps: int = 20):
+    """Grid packing of a 262144 x 1536 bf16 table into codes and steps (805 MB
+    read, 226 MB written per call), two table copies rotated."""
+    Vt, Kt, copies = 262144, 1536, 2
+    g = torch.Generator(device="cuda")
+    g.manual_seed(9)
+    tabs = [(torch.randn((Vt, Kt), generator=g, device="cuda") * 0.03).to(torch.bfloat16) for _ in range(copies)]
+    codes = torch.empty((Vt, Kt // 8), dtype=torch.int32, device="cuda")
+    steps = torch.empty((Vt, Kt // 32), dtype=torch.bfloat16, device="cuda")
+    t = timer.per_call(lambda i: w4.w4_grid_to_codes(tabs[i % copies], codes, steps), reps, warmup=2)
+    nbytes = 2 * Vt * Kt + w4_bytes(Vt, Kt)
+    res = {"us_per_call": round(t * 1e6, 2), "bytes_per_call": nbytes, "GBps": round(gbps(nbytes, t), 1),
+           "frac_of_peak": round(gbps(nbytes, t) / HBM_PEAK_GBPS, 4)}
+    del tabs
+    torch.cuda.empty_cache()
+    return res
+
+
 MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 matrix peak
 
 
@@ -408,7 +426,7 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extra", action="store_true", help="only the vocabulary-head step")
-    ap.add_argument("--only", choices=["single", "sweep", "small_m", "moe", "prompt", "gather8960"],
+    ap.add_argument("--only", choices=["single", "sweep", "small_m", "moe", "prompt", "gather8960", "grid"],
                     help="run one secondary workload alone (kernel traces) and print its JSON")
     args = ap.parse_args(argv)
     if args.gpus != 1:
@@ -426,7 +444,7 @@ def main(argv=None):
     timer = Timer(torch)
     if args.only:
         run = {"single": extra_single_gemv, "sweep": extra_sweep, "small_m": extra_small_m,
-               "moe": extra_moe, "prompt": extra_prompt, "gather8960": extra_gather_per_layer}[args.only]
+               "moe": extra_moe, "prompt": extra_prompt, "gather8960": extra_gather_per_layer, "grid": extra_grid_pack}[args.only]
         print(json.dumps({"workload": args.only, "result": run(w4, torch, np, synth, timer)}), flush=True)
         return 0
     rng = np.random.default_rng(0)
@@ -517,6 +535,7 @@ def main(argv=None):
         ex["moe_30_layers_top8_of_128"] = extra_moe(w4, torch, np, synth, timer)
         ex["prompt_chunk_256x1536x24576"] = extra_prompt(w4, torch, np, synth, timer)
         ex["gather_per_layer_table_262144x8960"] = extra_gather_per_layer(w4, torch, np, synth, timer)
+        ex["grid_pack_262144x1536"] = extra_grid_pack(w4, torch, np, synth, timer)
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(codes, steps, x, ids)
     print(json.dumps(result), flush=True)

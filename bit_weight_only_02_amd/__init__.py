@@ -55,6 +55,7 @@ _SIGNATURES = {
     "w4_gemv": [_P, _P, _I32, _I32, _P, _I32, _P, _P],
     "w4_gemm_smallM": [_P, _P, _I32, _I32, _P, _I32, _I32, _I64, _P, _I64, _P],
     "w4_gemm_prompt": [_P, _P, _I32, _I32, _P, _I32, _I32, _I64, _P, _I64, _P],
+    "w4_grid_to_codes": [_P, _I32, _I32, _P, _P, _P],
     "w4_moe_gemv_ids": [_P, _P, _I64, _I64, _I32, _I32, _P, _I32, _I32, _I64, _P, _I32, _I32,
                         _P, _I32, _I32, _P, _P, _P, _P, _P],
     "w4_embed_gather": [_P, _P, _I32, _I32, _P, _I32, _P, _P, _P],
@@ -157,6 +158,21 @@ def w4_gemm_prompt(codes, steps, X, Y=None, stream=None):
                               X.stride(0), _ptr(Y), Y.stride(0), _stream(stream)),
            "w4_gemm_prompt")
     return Y
+
+
+def w4_grid_to_codes(table, codes=None, steps=None, stream=None):
+    """Packs a bf16 table [N, K] whose groups of 32 lie on a 4-bit grid into
+    codes (int32 [N, K/8], uint32 words) and bf16 steps [N, K/32]."""
+    if table.dim() != 2 or not table.is_contiguous() or table.dtype != torch.bfloat16:
+        raise ValueError("table must be a contiguous bf16 [N, K] tensor")
+    N, K = table.shape
+    if codes is None:
+        codes = torch.empty((N, K // 8), dtype=torch.int32, device=table.device)
+    if steps is None:
+        steps = torch.empty((N, K // 32), dtype=torch.bfloat16, device=table.device)
+    _check(lib.w4_grid_to_codes(_ptr(table), N, K, _ptr(codes), _ptr(steps), _stream(stream)),
+           "w4_grid_to_codes")
+    return codes, steps
 
 
 def w4_moe_gemv_ids(codes_base, steps_base, expert_stride_codes, expert_stride_steps, N, K,

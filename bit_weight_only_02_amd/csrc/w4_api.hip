@@ -202,6 +202,24 @@ int w4_gemm_prompt(const uint32_t *codes, const uint16_t *steps, int32_t N, int3
                     "w4_gemm_prompt");
 }
 
+int w4_grid_to_codes(const uint16_t *table, int32_t N, int32_t K, uint32_t *codes,
+                     uint16_t *steps, void *stream) {
+    if (N < 0 || K < 0) return fail(W4_ERR_INVALID_ARG, "negative N or K");
+    if (K % 32) return fail(W4_ERR_INVALID_ARG, "K=%d is not a multiple of 32", K);
+    if (K > W4_MAX_K) return fail(W4_ERR_UNSUPPORTED, "K=%d exceeds %d", K, W4_MAX_K);
+    if ((long)N * K == 0) return W4_OK;
+    if (!table || !codes || !steps) return fail(W4_ERR_INVALID_ARG, "null table/codes/steps");
+    if (!aligned(table, 16)) return fail(W4_ERR_ALIGNMENT, "table not 16-byte aligned");
+    if (!aligned(codes, 16)) return fail(W4_ERR_ALIGNMENT, "codes not 16-byte aligned");
+    if (!aligned(steps, 2)) return fail(W4_ERR_ALIGNMENT, "steps not 2-byte aligned");
+    int st;
+    if ((st = device_ready())) return st;
+    if (forced_launch_error()) return fail(W4_ERR_HIP, "forced launch error (test hook)");
+    return launched(w4::launch_grid_pack(table, (long)N * (K / 32), codes, steps,
+                                         static_cast<hipStream_t>(stream)),
+                    "w4_grid_to_codes");
+}
+
 int w4_embed_gather(const uint32_t *codes, const uint16_t *steps, int32_t V, int32_t K,
                     const int32_t *ids, int32_t n, uint16_t *out_bf16, int32_t *dev_err,
                     void *stream) {

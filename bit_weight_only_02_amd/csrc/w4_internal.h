@@ -33,6 +33,9 @@ constexpr int kMaxGridColumns = 2048;
 constexpr size_t kWsCounterBytes = 16384;
 static_assert(kMaxGridColumns * 4 <= (int)kWsCounterBytes, "counter area");
 size_t gemm_smallm_workspace(int N, int K, int M);
+// grid packing of a bf16 table (w4_grid.hip): groups = N*K/32
+hipError_t launch_grid_pack(const uint16_t *table, long groups, uint32_t *codes, uint16_t *steps,
+                            hipStream_t stream);
 // prompt-chunk product (w4_gemm_prompt.hip): staged activations, row scales and flags
 size_t gemm_prompt_workspace(int N, int K, int M);
 hipError_t launch_gemm_prompt(const uint32_t *codes, const uint16_t *steps, int N, int K,

@@ -145,6 +145,23 @@ int w4_gemm_prompt(const uint32_t *codes, const uint16_t *steps, int32_t N, int3
                    float *Y, int64_t ldy, void *stream);
 
 /*
+ * Grid packing of a 16-bit table [P1-S2] (the conversion behind the 4-bit
+ * tables): table is bf16 [N][K] (raw uint16 bits, finite values, 16-byte
+ * aligned) whose groups of 32 are meant to lie on a 4-bit grid; writes
+ * codes [N][K/8] (16-byte aligned) and bf16 steps [N][K/32] in the storage
+ * format above.  Per group, in fp32: an = largest magnitude among negative
+ * values, ap = largest positive value (0 if none); step = bf16_RNE(an > ap ?
+ * an / 8 : ap / 7); code = clamp(rint(q) + 8, 0, 15) with q = v / step formed
+ * as r = 1 / step (correctly rounded), q0 = v * r, q = fma(fma(-q0, step, v),
+ * r, q0) (ties to even), or 8 everywhere when step is 0.  A group of exact
+ * grid values (c - 8) * step that uses code 0 or 15 packs back into those codes
+ * and that step; other values land within half a step (within about one step
+ * for a positive extreme clamped to code 15).  K % 32 == 0, K <= W4_MAX_K.
+ */
+int w4_grid_to_codes(const uint16_t *table, int32_t N, int32_t K, uint32_t *codes,
+                     uint16_t *steps, void *stream);
+
+/*
  * Expert-indexed product [P3].  T tokens each select topk experts:
  * ids[t*topk + j] is a REAL expert id in [0, n_experts).  The weights used for
  * that choice are the packed matrix [N][K] at

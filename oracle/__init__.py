@@ -80,6 +80,8 @@ def lib():
         L.w4o_moe.restype = i32
         L.w4o_rms_renorm.argtypes = [P, i64, i32, P]
         L.w4o_rms_renorm.restype = None
+        L.w4o_grid_to_codes.argtypes = [P, i64, i64, P, P]
+        L.w4o_grid_to_codes.restype = None
         L.w4o_num_threads.argtypes = []
         L.w4o_num_threads.restype = i32
         _lib = L
@@ -193,6 +195,16 @@ def rms_renorm(v, K, out_dtype):
     out = np.empty(K, dtype=np.uint16)
     lib().w4o_rms_renorm(_p(v), K, out_dtype, _p(out))
     return out
+
+
+def grid_to_codes(table, N, K):
+    """Codes uint32[N][K/8] and bf16 steps uint16[N][K/32] of a bf16 table
+    (bits) whose groups lie on a 4-bit grid (see w4o_grid_to_codes)."""
+    table = _c(table, np.uint16)
+    codes = np.empty((N, K // 8), dtype=np.uint32)
+    steps = np.empty((N, K // 32), dtype=np.uint16)
+    lib().w4o_grid_to_codes(_p(table), N, K, _p(codes), _p(steps))
+    return codes, steps
 
 
 def num_threads() -> int:

@@ -305,3 +305,61 @@ void w4o_rms_renorm(const float *v, int64_t K, int out_dtype, uint16_t *out) {
     for (int64_t k = 0; k < K; ++k)
         out[k] = w4o_f64_to_act_rne(r > 0.0 ? (double)v[k] / r : 0.0, out_dtype);
 }
+
+/*
+ * Grid packing of a 16-bit table [P1-S2]: the page's 4-bit tables were trained
+ * onto a grid of at most 16 levels per group of 32 and are stored as codes with
+ * each group's step recovered from the grid; how the step is found is not on
+ * the page.  Reading taken: per group, in fp32 arithmetic,
+ *   an  = the largest magnitude among negative values (0 if none),
+ *   ap  = the largest positive value (0 if none);
+ *   s   = an > ap ? an / 8 : ap / 7, so that the extreme value gets code 0
+ *         (an extreme -8 steps) or 15 (+7 steps; a tie means a grid without
+ *         code 0, whose positive extreme is 7 steps);
+ *   step = s rounded to bf16 (nearest, ties to even); sf = step as a float;
+ *   code = 8 for every value when sf == 0, else clamp(rint(q) + 8, 0, 15),
+ *          where q is the quotient v / sf formed as r = 1 / sf (correctly
+ *          rounded, once per group), q0 = v * r, e = fma(-q0, sf, v),
+ *          q = fma(e, r, q0) -- a reciprocal with one exact-residual
+ *          correction, within an ulp of v / sf and the same in any IEEE fp32
+ *          implementation -- and rint rounding ties to even.
+ * On a table whose groups hold exact grid values (c - 8) * step that use code 0
+ * or 15, this gives back those codes and steps.  Values must be finite.
+ */
+void w4o_grid_to_codes(const uint16_t *table, int64_t N, int64_t K, uint32_t *codes,
+                       uint16_t *steps) {
+    const int64_t G = K / 32;
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t g = 0; g < G; ++g) {
+            const uint16_t *v = table + n * K + g * 32;
+            float an = 0.0f, ap = 0.0f;
+            for (int k = 0; k < 32; ++k) {
+                const float x = (float)w4o_bf16_to_f64(v[k]);
+                if (-x > an) an = -x;
+                if (x > ap) ap = x;
+            }
+            const float s = an > ap ? an / 8.0f : ap / 7.0f;
+            const uint16_t sb = w4o_f64_to_bf16_rne((double)s);
+            const float sf = (float)w4o_bf16_to_f64(sb);
+            steps[n * G + g] = sb;
+            const float r = sf != 0.0f ? 1.0f / sf : 0.0f;
+            for (int w = 0; w < 4; ++w) {
+                uint32_t word = 0;
+                for (int j = 0; j < 8; ++j) {
+                    int c = 8;
+                    if (sf != 0.0f) {
+                        const float x = (float)w4o_bf16_to_f64(v[8 * w + j]);
+                        float q = x * r;
+                        const float e = fmaf(-q, sf, x);
+                        q = fmaf(e, r, q);
+                        q = rintf(q) + 8.0f;
+                        q = q < 0.0f ? 0.0f : (q > 15.0f ? 15.0f : q);
+                        c = (int)q;
+                    }
+                    word |= (uint32_t)c << (4 * j);
+                }
+                codes[n * (K / 8) + g * 4 + w] = word;
+            }
+        }
+    }
+}

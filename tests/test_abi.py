@@ -20,6 +20,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("w4_gemv", "w4_gemm_smallM", "w4_gemm_prompt", "w4_moe_gemv_ids", "w4_embed_gather",
+              "w4_grid_to_codes",
               "w4_rms_renorm", "w4_gemv_chain", "w4_probe_stream", "w4_strerror"):
         assert n in names
 
@@ -93,6 +94,18 @@ def test_gemm_argument_errors():
         assert fn(FAKE, FAKE, 64, 64, FAKE, 0, 2, 64, FAKE + 2, 64, None) == -2      # Y alignment
         assert fn(FAKE, FAKE, 64, 32768, FAKE, 0, 2, 32768, FAKE, 64, None) == -4    # K too large
         assert fn(FAKE, FAKE, 0, 64, FAKE, 0, 2, 64, FAKE, 64, None) == 0            # N = 0
+
+
+def test_grid_packing_argument_errors():
+    import bit_weight_only_02_amd as w4
+    L = w4.lib
+    assert L.w4_grid_to_codes(FAKE, 4, 48, FAKE, FAKE, None) == -1        # K % 32
+    assert L.w4_grid_to_codes(FAKE, -1, 32, FAKE, FAKE, None) == -1       # negative N
+    assert L.w4_grid_to_codes(FAKE, 4, 32768, FAKE, FAKE, None) == -4     # K too large
+    assert L.w4_grid_to_codes(None, 4, 32, FAKE, FAKE, None) == -1        # null table
+    assert L.w4_grid_to_codes(FAKE + 2, 4, 32, FAKE, FAKE, None) == -2    # table alignment
+    assert L.w4_grid_to_codes(FAKE, 4, 32, FAKE + 4, FAKE, None) == -2    # codes alignment
+    assert L.w4_grid_to_codes(FAKE, 0, 32, None, None, None) == 0         # empty
 
 
 def test_moe_argument_errors():

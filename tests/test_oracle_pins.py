@@ -441,3 +441,81 @@ def test_gbps_formula_reproduces_the_pages_figures():
     assert round(gbps(g["bytes_per_token_MiB"] * 1e6, 9.12e-3), 1) != g["v5"]["GBps_effective"]
     frac = g["v5"]["GBps_effective"] / g["plain_sum_read_GBps"]
     assert round(100 * frac) == g["v5_fraction_of_plain_read_percent"]
+
+
+# --- grid packing of a 16-bit table ----------------------------------------------
+
+def _grid_table(rng, N, K):
+    """Codes and 5-bit-significand positive bf16 steps (so every (c - 8) * step
+    is exact in bf16), with each group holding code 0 or 15 at a random place
+    (and, for the second kind, no code 0); the table is the oracle's exact
+    dequantisation rounded (exactly) to bf16."""
+    G = K // 32
+    c = rng.integers(0, 16, size=(N, K), dtype=np.int64)
+    use15 = rng.random((N, G)) < 0.5
+    for n in range(N):
+        for g in range(G):
+            grp = c[n, 32 * g:32 * g + 32]
+            if use15[n, g]:
+                grp[grp == 0] = 1
+                grp[rng.integers(0, 32)] = 15
+            else:
+                grp[rng.integers(0, 32)] = 0
+    codes = np.zeros((N, K // 8), dtype=np.uint32)
+    for j in range(8):
+        codes |= (c[:, j::8].astype(np.uint32) << np.uint32(4 * j))
+    exp = rng.integers(100, 140, size=(N, G), dtype=np.uint16)
+    mant = (rng.integers(0, 16, size=(N, G), dtype=np.uint16) << 3)
+    steps = ((exp << 7) | mant).astype(np.uint16)         # positive, low 3 mantissa bits zero
+    W = oracle.dequant(codes, steps, N, K)
+    table = np.array([oracle.f64_to_bf16(v) for v in W.ravel()], dtype=np.uint16).reshape(N, K)
+    assert np.array_equal(oracle.act_to_f64(table.ravel(), BF16).reshape(N, K), W)  # exact grid
+    return codes, steps, table
+
+
+def test_grid_packing_round_trips_exact_grids():
+    """A table whose groups are exact grid values using code 0 or 15 packs back
+    into exactly the codes and steps it came from."""
+    rng = np.random.default_rng(31)
+    N, K = 9, 96
+    codes, steps, table = _grid_table(rng, N, K)
+    c2, s2 = oracle.grid_to_codes(table, N, K)
+    assert np.array_equal(s2, steps)
+    assert np.array_equal(c2, codes)
+
+
+def test_grid_packing_closed_forms():
+    # all zeros: step 0 and code 8 everywhere
+    c, s = oracle.grid_to_codes(np.zeros((1, 32), dtype=np.uint16), 1, 32)
+    assert s[0, 0] == 0 and np.all(c == 0x88888888)
+    # +a and -a both present: a grid without code 0, whose step is a / 7
+    a = 7 * 0.125
+    t = np.zeros((1, 32), dtype=np.uint16)
+    t[0, 3] = oracle.f64_to_bf16(a)
+    t[0, 9] = oracle.f64_to_bf16(-a)
+    c, s = oracle.grid_to_codes(t, 1, 32)
+    assert oracle.bf16_to_f64(int(s[0, 0])) == 0.125
+    assert oracle.code(c, 32, 0, 3) == 15 and oracle.code(c, 32, 0, 9) == 1
+    # a strictly larger negative extreme: step = |min| / 8, the extreme gets code 0
+    t[0, 9] = oracle.f64_to_bf16(-1.0)
+    c, s = oracle.grid_to_codes(t, 1, 32)
+    assert oracle.bf16_to_f64(int(s[0, 0])) == 0.125 and oracle.code(c, 32, 0, 9) == 0
+    assert oracle.code(c, 32, 0, 3) == 15   # 0.875 / 0.125 = 7
+
+
+def test_grid_packing_error_bound_on_arbitrary_tables():
+    """On values that are not on a grid, each packed value is within half a
+    step of the input when it lies inside the grid's range, and within about
+    one step when it is the clamped positive extreme of a group whose negative
+    extreme sets the step."""
+    rng = np.random.default_rng(32)
+    N, K = 16, 256
+    table = synth.act_bits(rng.standard_normal((N, K)) * 0.05, BF16)
+    codes, steps = oracle.grid_to_codes(table, N, K)
+    v = oracle.act_to_f64(table.ravel(), BF16).reshape(N, K)
+    W = oracle.dequant(codes, steps, N, K)
+    sf = np.repeat(oracle.act_to_f64(steps.ravel(), BF16).reshape(N, K // 32), 32, axis=1)
+    err = np.abs(W - v)
+    inside = (v / sf >= -8.5) & (v / sf <= 7.5)
+    assert np.all(err[inside] <= 0.5 * sf[inside] * (1 + 2 ** -20))
+    assert np.all(err <= 1.05 * sf)

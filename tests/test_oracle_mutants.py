@@ -26,6 +26,10 @@ MUTANTS = {
     "route_weight_dropped": ("Y[t * N + n] += r * v;", "Y[t * N + n] += v;"),
     "rms_over_k_minus_1": ("sqrt(ss / (double)K)", "sqrt(ss / (double)(K - 1))"),
     "x_index_per_pair_ignored": ("(x_per_pair ? (t * topk + j) : t)", "(t)"),
+    "grid_step_always_eighth": ("an > ap ? an / 8.0f : ap / 7.0f", "an > ap ? an / 8.0f : ap / 8.0f"),
+    "grid_tie_to_negative": ("an > ap ? an / 8.0f", "an >= ap ? an / 8.0f"),
+    "grid_clamp_upper_14": ("(q > 15.0f ? 15.0f : q)", "(q > 14.0f ? 14.0f : q)"),
+    "grid_truncates": ("q = rintf(q) + 8.0f;", "q = truncf(q) + 8.0f;"),
 }
 
 

@@ -8,9 +8,8 @@
 // sets the step -- a negative extreme larger in magnitude than every positive
 // value is 8 steps below zero (code 0), otherwise the largest positive value is
 // 7 steps above (code 15) -- the step is rounded to bf16, and every value gets
-// code clamp(rint(q) + 8, 0, 15) in fp32, q the quotient v / step formed as a
-// correctly rounded reciprocal times v with one exact-residual correction
-// (ties to even).  Exact grid values that use code 0 or 15 come back as the
+// code clamp(rint(q) + 8, 0, 15) in fp32, q = v times the correctly rounded
+// reciprocal of the step (ties to even).  Exact grid values that use code 0 or 15 come back as the
 // codes and step they were made from.
 //
 // Four adjacent lanes per group, each with 8 values (one 16-byte load) and one
@@ -53,8 +52,8 @@ __global__ __launch_bounds__(256) void grid_pack_kernel(const uint4 *__restrict_
         const float s = an > ap ? an / 8.0f : ap / 7.0f;
         const uint16_t sb = __builtin_bit_cast(uint16_t, (__bf16)s);
         const float sf = bf16_to_f32(sb);
-        // quotient v / sf as a reciprocal (correctly rounded, once per group)
-        // with one exact-residual correction
+        // quotient v / sf as v times the reciprocal (correctly rounded, once
+        // per group)
         const float r = sf != 0.0f ? 1.0f / sf : 0.0f;
         // clamp(rint(q) + 8, 0, 15) as clamp(q, -8, 7) + (2^23 + 8): the add
         // rounds to an integer (ties to even) and leaves the code in the low
@@ -63,10 +62,7 @@ __global__ __launch_bounds__(256) void grid_pack_kernel(const uint4 *__restrict_
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const float x = v[j];
-            float q = x * r;
-            const float e = __builtin_fmaf(-q, sf, x);
-            q = __builtin_fmaf(e, r, q);
-            q = __builtin_amdgcn_fmed3f(q, -8.0f, 7.0f) + 8388616.0f;
+            const float q = __builtin_amdgcn_fmed3f(x * r, -8.0f, 7.0f) + 8388616.0f;
             wd |= (__float_as_uint(q) & 0xFu) << (4 * j);
         }
         if (sf == 0.0f) wd = 0x88888888u;

@@ -151,9 +151,8 @@ int w4_gemm_prompt(const uint32_t *codes, const uint16_t *steps, int32_t N, int3
  * codes [N][K/8] (16-byte aligned) and bf16 steps [N][K/32] in the storage
  * format above.  Per group, in fp32: an = largest magnitude among negative
  * values, ap = largest positive value (0 if none); step = bf16_RNE(an > ap ?
- * an / 8 : ap / 7); code = clamp(rint(q) + 8, 0, 15) with q = v / step formed
- * as r = 1 / step (correctly rounded), q0 = v * r, q = fma(fma(-q0, step, v),
- * r, q0) (ties to even), or 8 everywhere when step is 0.  A group of exact
+ * an / 8 : ap / 7); code = clamp(rint(v * r) + 8, 0, 15) with r = 1 / step
+ * (correctly rounded; all fp32, ties to even), or 8 everywhere when step is 0.  A group of exact
  * grid values (c - 8) * step that uses code 0 or 15 packs back into those codes
  * and that step; other values land within half a step (within about one step
  * for a positive extreme clamped to code 15).  K % 32 == 0, K <= W4_MAX_K.

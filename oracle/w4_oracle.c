@@ -318,11 +318,9 @@ void w4o_rms_renorm(const float *v, int64_t K, int out_dtype, uint16_t *out) {
  *         code 0, whose positive extreme is 7 steps);
  *   step = s rounded to bf16 (nearest, ties to even); sf = step as a float;
  *   code = 8 for every value when sf == 0, else clamp(rint(q) + 8, 0, 15),
- *          where q is the quotient v / sf formed as r = 1 / sf (correctly
- *          rounded, once per group), q0 = v * r, e = fma(-q0, sf, v),
- *          q = fma(e, r, q0) -- a reciprocal with one exact-residual
- *          correction, within an ulp of v / sf and the same in any IEEE fp32
- *          implementation -- and rint rounding ties to even.
+ *          where q = v * r with r = 1 / sf (correctly rounded, once per
+ *          group): the quotient within about an ulp, the same in any IEEE
+ *          fp32 implementation, and rint rounding ties to even.
  * On a table whose groups hold exact grid values (c - 8) * step that use code 0
  * or 15, this gives back those codes and steps.  Values must be finite.
  */
@@ -350,8 +348,6 @@ void w4o_grid_to_codes(const uint16_t *table, int64_t N, int64_t K, uint32_t *co
                     if (sf != 0.0f) {
                         const float x = (float)w4o_bf16_to_f64(v[8 * w + j]);
                         float q = x * r;
-                        const float e = fmaf(-q, sf, x);
-                        q = fmaf(e, r, q);
                         q = rintf(q) + 8.0f;
                         q = q < 0.0f ? 0.0f : (q > 15.0f ? 15.0f : q);
                         c = (int)q;

@@ -73,7 +73,7 @@ typedef enum {
     W4_ERR_INVALID_ARG = -1, /* null pointer, bad size, K % 32 != 0, ... */
     W4_ERR_ALIGNMENT = -2,   /* a pointer is not aligned as documented */
     W4_ERR_DTYPE = -3,       /* unknown activation dtype */
-    W4_ERR_UNSUPPORTED = -4, /* valid but beyond this build's limits */
+    W4_ERR_UNSUPPORTED = -4, /* valid but beyond the library's limits */
     W4_ERR_NODEV = -5,       /* no usable HIP device */
     W4_ERR_HIP = -6          /* a HIP call or kernel launch failed */
 } w4_status;

@@ -388,6 +388,29 @@ def extra_grid_pack(w4, torch, np, synth, timer, reps: int = 20):
     return res
 
 
+def extra_attention(w4, torch, np, synth, timer, reps: int = 20):
+    """Decode attention of one token, 8 query heads over one key/value head of
+    width 512: the full 131072-position cache (268 MB of keys and values, two
+    copies rotated) and a 512-slot ring."""
+    H, D = 8, 512
+    g = torch.Generator(device="cuda")
+    g.manual_seed(11)
+    q = torch.randn((H, D), generator=g, device="cuda").to(torch.bfloat16)
+    out = {}
+    for name, L, copies in (("full_131072", 131072, 2), ("ring_512", 512, 64)):
+        ks = [torch.randn((L, D), generator=g, device="cuda").to(torch.bfloat16) for _ in range(copies)]
+        vs = [torch.randn((L, D), generator=g, device="cuda").to(torch.bfloat16) for _ in range(copies)]
+        o = torch.empty((H, D), device="cuda")
+        t = timer.per_call(lambda i: w4.w4_decode_attention(q, ks[i % copies], vs[i % copies], 0.0442, o),
+                           reps, warmup=2)
+        nbytes = 2 * L * D * 2
+        out[name] = {"us_per_call": round(t * 1e6, 2), "kv_bytes": nbytes, "GBps": round(gbps(nbytes, t), 1),
+                     "frac_of_peak": round(gbps(nbytes, t) / HBM_PEAK_GBPS, 4)}
+        del ks, vs
+    torch.cuda.empty_cache()
+    return out
+
+
 MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 matrix peak
 
 
@@ -426,7 +449,7 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extra", action="store_true", help="only the vocabulary-head step")
-    ap.add_argument("--only", choices=["single", "sweep", "small_m", "moe", "prompt", "gather8960", "grid"],
+    ap.add_argument("--only", choices=["single", "sweep", "small_m", "moe", "prompt", "gather8960", "grid", "attention"],
                     help="run one secondary workload alone (kernel traces) and print its JSON")
     args = ap.parse_args(argv)
     if args.gpus != 1:
@@ -444,7 +467,7 @@ def main(argv=None):
     timer = Timer(torch)
     if args.only:
         run = {"single": extra_single_gemv, "sweep": extra_sweep, "small_m": extra_small_m,
-               "moe": extra_moe, "prompt": extra_prompt, "gather8960": extra_gather_per_layer, "grid": extra_grid_pack}[args.only]
+               "moe": extra_moe, "prompt": extra_prompt, "gather8960": extra_gather_per_layer, "grid": extra_grid_pack, "attention": extra_attention}[args.only]
         print(json.dumps({"workload": args.only, "result": run(w4, torch, np, synth, timer)}), flush=True)
         return 0
     rng = np.random.default_rng(0)
@@ -536,6 +559,7 @@ def main(argv=None):
         ex["prompt_chunk_256x1536x24576"] = extra_prompt(w4, torch, np, synth, timer)
         ex["gather_per_layer_table_262144x8960"] = extra_gather_per_layer(w4, torch, np, synth, timer)
         ex["grid_pack_262144x1536"] = extra_grid_pack(w4, torch, np, synth, timer)
+        ex["decode_attention_8x512"] = extra_attention(w4, torch, np, synth, timer)
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(codes, steps, x, ids)
     print(json.dumps(result), flush=True)

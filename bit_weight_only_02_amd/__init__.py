@@ -56,6 +56,7 @@ _SIGNATURES = {
     "w4_gemm_smallM": [_P, _P, _I32, _I32, _P, _I32, _I32, _I64, _P, _I64, _P],
     "w4_gemm_prompt": [_P, _P, _I32, _I32, _P, _I32, _I32, _I64, _P, _I64, _P],
     "w4_grid_to_codes": [_P, _I32, _I32, _P, _P, _P],
+    "w4_decode_attention": [_P, _I32, _I32, _P, _I64, _P, _I64, _I32, ctypes.c_float, _P, _P],
     "w4_moe_gemv_ids": [_P, _P, _I64, _I64, _I32, _I32, _P, _I32, _I32, _I64, _P, _I32, _I32,
                         _P, _I32, _I32, _P, _P, _P, _P, _P],
     "w4_embed_gather": [_P, _P, _I32, _I32, _P, _I32, _P, _P, _P],
@@ -173,6 +174,21 @@ def w4_grid_to_codes(table, codes=None, steps=None, stream=None):
     _check(lib.w4_grid_to_codes(_ptr(table), N, K, _ptr(codes), _ptr(steps), _stream(stream)),
            "w4_grid_to_codes")
     return codes, steps
+
+
+def w4_decode_attention(q, k, v, scale, o=None, stream=None):
+    """One query token's attention: q bf16 [H, D] (H <= 8 heads sharing one
+    key/value head), k, v bf16 [L, >=D] rows; returns o fp32 [H, D]."""
+    if q.dim() != 2 or not q.is_contiguous() or k.dim() != 2 or v.dim() != 2 or k.shape[0] != v.shape[0]:
+        raise ValueError("q [H, D] contiguous; k, v [L, >=D] with the same L")
+    if k.stride(1) != 1 or v.stride(1) != 1:
+        raise ValueError("k, v need unit column stride")
+    H, D = q.shape
+    if o is None:
+        o = torch.empty((H, D), dtype=torch.float32, device=q.device)
+    _check(lib.w4_decode_attention(_ptr(q), H, D, _ptr(k), k.stride(0), _ptr(v), v.stride(0), k.shape[0],
+                                   float(scale), _ptr(o), _stream(stream)), "w4_decode_attention")
+    return o
 
 
 def w4_moe_gemv_ids(codes_base, steps_base, expert_stride_codes, expert_stride_steps, N, K,

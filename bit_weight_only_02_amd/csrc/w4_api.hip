@@ -220,6 +220,31 @@ int w4_grid_to_codes(const uint16_t *table, int32_t N, int32_t K, uint32_t *code
                     "w4_grid_to_codes");
 }
 
+int w4_decode_attention(const uint16_t *q, int32_t H, int32_t D, const uint16_t *k, int64_t ldk,
+                        const uint16_t *v, int64_t ldv, int32_t L, float scale, float *o,
+                        void *stream) {
+    if (H < 1 || H > 8) return fail(W4_ERR_INVALID_ARG, "H=%d outside 1..8", H);
+    if (D != 256 && D != 512) return fail(W4_ERR_UNSUPPORTED, "D=%d (256 or 512)", D);
+    if (L < 1) return fail(W4_ERR_INVALID_ARG, "L=%d", L);
+    if (ldk < D || ldv < D) return fail(W4_ERR_INVALID_ARG, "ldk or ldv < D");
+    if (!q || !k || !v || !o) return fail(W4_ERR_INVALID_ARG, "null q/k/v/o");
+    const int va = D == 512 ? 16 : 8, vl = D == 512 ? 8 : 4;
+    if (!aligned(k, va) || !aligned(v, va) || ldk % vl || ldv % vl)
+        return fail(W4_ERR_ALIGNMENT, "k/v rows not %d-byte aligned", va);
+    if (!aligned(q, 2) || !aligned(o, 4)) return fail(W4_ERR_ALIGNMENT, "q or o misaligned");
+    int st;
+    if ((st = device_ready())) return st;
+    if (forced_launch_error()) return fail(W4_ERR_HIP, "forced launch error (test hook)");
+    void *ws = nullptr;
+    if ((st = staging_buffer(w4::kWsCounterBytes + w4::attn_workspace(H, D, L), static_cast<hipStream_t>(stream),
+                             &ws)))
+        return st;
+    return launched(w4::launch_attn(q, H, D, k, ldk, v, ldv, L, scale, o,
+                                    static_cast<char *>(ws) + w4::kWsCounterBytes,
+                                    static_cast<hipStream_t>(stream)),
+                    "w4_decode_attention");
+}
+
 int w4_embed_gather(const uint32_t *codes, const uint16_t *steps, int32_t V, int32_t K,
                     const int32_t *ids, int32_t n, uint16_t *out_bf16, int32_t *dev_err,
                     void *stream) {

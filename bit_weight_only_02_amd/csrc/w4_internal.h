@@ -33,6 +33,10 @@ constexpr int kMaxGridColumns = 2048;
 constexpr size_t kWsCounterBytes = 16384;
 static_assert(kMaxGridColumns * 4 <= (int)kWsCounterBytes, "counter area");
 size_t gemm_smallm_workspace(int N, int K, int M);
+// decode attention (w4_attn.hip): split partials in the workspace
+size_t attn_workspace(int H, int D, int L);
+hipError_t launch_attn(const uint16_t *q, int H, int D, const uint16_t *K, long ldk, const uint16_t *V,
+                       long ldv, int L, float scale, float *o, void *ws, hipStream_t stream);
 // grid packing of a bf16 table (w4_grid.hip): groups = N*K/32
 hipError_t launch_grid_pack(const uint16_t *table, long groups, uint32_t *codes, uint16_t *steps,
                             hipStream_t stream);

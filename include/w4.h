@@ -22,6 +22,11 @@
  *   [P1-S6] same page, "Step 6 - Read Prompts in 32-Bit on a Card Without Tensor
  *           Cores": a prompt is read in chunks of 256 tokens, each chunk a
  *           product of many activation rows with every weight matrix.
+ *   [P1-S5] same page, "Step 5 - Attention for One Token at a Time": one key/
+ *           value head shared by eight query heads, read once, split over the
+ *           cache, slices combined with an online softmax.
+ *   [P1-S7] same page, "Step 7 - Fit the Full 131,072-Token Context": the
+ *           cache is one head of width 512 per layer.
  *   [P3]    anyesh.me, "Running a 26B MoE on an 8 GB Jetson by streaming experts
  *           from SSD", section "Streaming without touching a single GPU kernel":
  *           the expert matmul addresses expert id as base + id * stride; a pool
@@ -159,6 +164,25 @@ int w4_gemm_prompt(const uint32_t *codes, const uint16_t *steps, int32_t N, int3
  */
 int w4_grid_to_codes(const uint16_t *table, int32_t N, int32_t K, uint32_t *codes,
                      uint16_t *steps, void *stream);
+
+/*
+ * Decode attention for one query token [P1-S5, P1-S7]: the H <= 8 query heads
+ * share one key/value head (P1-S5: each cached key and value is read once for
+ * all of them, split across the cache, slices combined with an online
+ * softmax; P1-S7: head width 512, a full cache of one slot per position or a
+ * 512-slot ring).
+ *   o[h][d] = sum_j p[h][j] * V[j][d],  p[h][.] = softmax_j(scale * q[h] . K[j])
+ * over the L cached positions j given (a ring passes its valid slots: the
+ * result does not depend on their order).
+ *   q: bf16 [H][D] contiguous.  K, V: bf16 rows ldk / ldv elements apart.
+ *   D is 256 or 512; K, V 16-byte aligned (8-byte for D = 256) and ldk, ldv
+ *   multiples of 8 (of 4).  o: fp32 [H][D], written.  1 <= L.
+ * The split partials live in the library's per-device buffer (see
+ * w4_gemm_smallM).  Accumulation in fp32 with base-2 exponentials.
+ */
+int w4_decode_attention(const uint16_t *q, int32_t H, int32_t D, const uint16_t *k, int64_t ldk,
+                        const uint16_t *v, int64_t ldv, int32_t L, float scale, float *o,
+                        void *stream);
 
 /*
  * Expert-indexed product [P3].  T tokens each select topk experts:

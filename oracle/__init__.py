@@ -207,6 +207,20 @@ def grid_to_codes(table, N, K):
     return codes, steps
 
 
+def decode_attention(q_bits, k_bits, v_bits, scale):
+    """One query token's attention in fp64 [P1-S5]: heads of q (bf16 bits
+    [H, D]) over the cached keys and values (bf16 bits [L, D]):
+    o[h] = sum_j softmax_j(scale * q[h] . k[j]) v[j]."""
+    q = act_to_f64(np.asarray(q_bits).ravel(), 1).reshape(np.shape(q_bits))
+    k = act_to_f64(np.asarray(k_bits).ravel(), 1).reshape(np.shape(k_bits))
+    v = act_to_f64(np.asarray(v_bits).ravel(), 1).reshape(np.shape(v_bits))
+    s = (q @ k.T) * float(scale)
+    s = s - s.max(axis=1, keepdims=True)
+    p = np.exp(s)
+    p = p / p.sum(axis=1, keepdims=True)
+    return p @ v
+
+
 def num_threads() -> int:
     return lib().w4o_num_threads()
 

@@ -519,3 +519,41 @@ def test_grid_packing_error_bound_on_arbitrary_tables():
     inside = (v / sf >= -8.5) & (v / sf <= 7.5)
     assert np.all(err[inside] <= 0.5 * sf[inside] * (1 + 2 ** -20))
     assert np.all(err <= 1.05 * sf)
+
+
+# --- decode attention ---------------------------------------------------------
+
+def _bits(rng, shape, scale=1.0):
+    return synth.act_bits(rng.standard_normal(shape) * scale, BF16)
+
+
+def test_attention_closed_forms():
+    rng = np.random.default_rng(71)
+    q, k, v = _bits(rng, (8, 64)), _bits(rng, (1, 64)), _bits(rng, (1, 64))
+    vv = oracle.act_to_f64(v.ravel(), BF16).reshape(1, 64)
+    # one cached position: every head returns its value row exactly
+    assert np.array_equal(oracle.decode_attention(q, k, v, 0.125), np.repeat(vv, 8, axis=0))
+    # equal keys, or a zero scale: uniform weights, the mean of the values
+    k5 = np.repeat(_bits(rng, (1, 64)), 5, axis=0)
+    v5 = _bits(rng, (5, 64))
+    mean = oracle.act_to_f64(v5.ravel(), BF16).reshape(5, 64).mean(axis=0)
+    assert np.allclose(oracle.decode_attention(q, k5, v5, 0.3), mean[None, :], rtol=0, atol=1e-15)
+    assert np.allclose(oracle.decode_attention(q, _bits(rng, (5, 64)), v5, 0.0), mean[None, :], rtol=0, atol=1e-15)
+
+
+def test_attention_dominant_key_and_order():
+    rng = np.random.default_rng(72)
+    H, D, L = 8, 64, 40
+    q = _bits(rng, (H, D))
+    k, v = _bits(rng, (L, D)), _bits(rng, (L, D))
+    # a key aligned with every head's query, scaled up, takes all the weight
+    qq = oracle.act_to_f64(q.ravel(), BF16).reshape(H, D)
+    k2 = k.copy()
+    k2[7] = synth.act_bits(qq.sum(axis=0) * 64.0, BF16)
+    o = oracle.decode_attention(q, k2, v, 1.0)
+    v7 = oracle.act_to_f64(v[7], BF16)
+    assert np.abs(o - v7[None, :]).max() < 1e-12
+    # the order of the cached positions does not matter (a ring's slots)
+    perm = rng.permutation(L)
+    assert np.allclose(oracle.decode_attention(q, k[perm], v[perm], 0.2),
+                       oracle.decode_attention(q, k, v, 0.2), rtol=0, atol=1e-14)

@@ -19,7 +19,8 @@
 // 2^(s - m) and the accumulated values, rescaled when m grows.  The waves of a
 // workgroup are merged in wave order into one partial {m, l, acc} per head.
 // attn_merge_kernel: output (h, d) = sum_w 2^(m_w - M) acc_w / sum_w 2^(m_w - M)
-// l_w over the partials in ascending order, M the largest m_w.
+// l_w over the partials (a running merge over each quarter of them, then the
+// quarters in order), M the largest m_w.
 #include <cmath>
 
 #include "w4_device.h"
@@ -131,27 +132,47 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_split_kernel(
     }
 }
 
+// Merge: workgroup (h, 64-dim block) with 256 threads, thread (quarter qt,
+// dim d): a running merge over slices qt, qt+4, ... (rescaled when the
+// maximum grows), then the four quarters combined in order in LDS.
 __global__ __launch_bounds__(256) void attn_merge_kernel(const float *__restrict__ ws, int S, int H, int D,
                                                          float *__restrict__ o) {
-    const int i = blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= H * D) return;
-    const int h = i / D, d = i % D;
+    __shared__ float pm[4][64], pa[4][64], pz[4][64];
+    const int h = blockIdx.y, d = blockIdx.x * 64 + (threadIdx.x & 63), qt = threadIdx.x >> 6;
     const long stride = 2 * kAttnH + (long)kAttnH * D;
-    float M = -INFINITY;
-    for (int s = 0; s < S; ++s) M = fmaxf(M, ws[s * stride + h]);
-    float a = 0.0f, z = 0.0f;
-    for (int s = 0; s < S; ++s) {
-        const float ms = ws[s * stride + h];
-        const float c = ms == -INFINITY ? 0.0f : exp2f(ms - M);
-        a += c * ws[s * stride + 2 * kAttnH + h * D + d];
-        z += c * ws[s * stride + kAttnH + h];
+    float M = -INFINITY, a = 0.0f, z = 0.0f;
+#pragma unroll 4
+    for (int sidx = qt; sidx < S; sidx += 4) {
+        const float *p = ws + sidx * stride;
+        const float ms = p[h];
+        if (ms == -INFINITY) continue;  // an empty slice
+        const float mn = fmaxf(M, ms);
+        const float c0 = exp2f(M - mn), c1 = exp2f(ms - mn);  // exp2(-inf) = 0 at the start
+        a = a * c0 + c1 * p[2 * kAttnH + h * D + d];
+        z = z * c0 + c1 * p[kAttnH + h];
+        M = mn;
     }
-    o[i] = a / z;
+    pm[qt][threadIdx.x & 63] = M;
+    pa[qt][threadIdx.x & 63] = a;
+    pz[qt][threadIdx.x & 63] = z;
+    __syncthreads();
+    if (qt == 0 && h < H) {
+        const int t = threadIdx.x & 63;
+        float MM = -INFINITY;
+        for (int k = 0; k < 4; ++k) MM = fmaxf(MM, pm[k][t]);
+        float A = 0.0f, Z = 0.0f;
+        for (int k = 0; k < 4; ++k) {
+            const float c = pm[k][t] == -INFINITY ? 0.0f : exp2f(pm[k][t] - MM);
+            A += c * pa[k][t];
+            Z += c * pz[k][t];
+        }
+        o[h * D + d] = A / Z;
+    }
 }
 
-// Splits: about 32 keys each (8 per wave), at most 256 (one per CU; more made
-// the merge the longer part: 131072 positions took 265 us with 256 splits,
-// 421 us with 512; a 512-slot ring 28 us with 16 splits, 38 us with 4).
+// Splits: about 32 keys each (8 per wave), at most 256 (one per CU): 131072
+// positions took 155 us with 256 splits, 203 us with 512, 300 us with 1024; a
+// 512-slot ring 21.5 us with 16 splits, 25 us with 64.
 // W4_ATTN_SPLITS overrides the count (schedule sweeps; the merge order is
 // fixed).
 static int attn_splits(int L) {
@@ -187,7 +208,7 @@ hipError_t launch_attn(const uint16_t *q, int H, int D, const uint16_t *K, long 
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(attn_merge_kernel, dim3((H * D + 255) / 256), dim3(256), 0, stream, w, S, H, D, o);
+    hipLaunchKernelGGL(attn_merge_kernel, dim3(D / 64, H), dim3(256), 0, stream, w, S, H, D, o);
     return hipGetLastError();
 }
 

@@ -251,18 +251,21 @@ def extra_small_m(w4, torch, np, synth, timer, reps: int = 20):
             mats.append((c[0], s[0].view(torch.bfloat16)))
         sets.append(mats)
     set_bytes = sum(w4_bytes(N, Kc) for N, Kc in SWEEP_SHAPES)
+    ws = w4.new_workspace(max(w4.w4_gemm_smallM_workspace_bytes(N, Kc, M)
+                              for N, Kc in SWEEP_SHAPES for M in (2, 4, 8, 16)))
     out = {}
     for M in (2, 4, 8, 16):
         X = [torch.randn((M, Kc), generator=g, device="cuda").to(torch.bfloat16) for _, Kc in SWEEP_SHAPES]
         Y = [torch.empty((M, N), device="cuda") for N, _ in SWEEP_SHAPES]
         per_shape = {}
         for si, (N, Kc) in enumerate(SWEEP_SHAPES):
-            t = timer.per_call(lambda i: w4.w4_gemm_smallM(*sets[i % copies][si], X[si], Y[si]), reps)
+            t = timer.per_call(lambda i: w4.w4_gemm_smallM(*sets[i % copies][si], X[si], Y[si], workspace=ws),
+                               reps)
             per_shape[f"{N}x{Kc}"] = round(t * 1e6, 2)
 
         def one_set(i):
             for si in range(4):
-                w4.w4_gemm_smallM(*sets[i % copies][si], X[si], Y[si])
+                w4.w4_gemm_smallM(*sets[i % copies][si], X[si], Y[si], workspace=ws)
         tset = timer.graph_per_call(one_set, copies)
         bytes_set = set_bytes + sum(2 * M * Kc + 4 * M * N for N, Kc in SWEEP_SHAPES)
         out[f"M{M}"] = {"us_per_shape_eager": per_shape, "us_per_set_graph": round(tset * 1e6, 2),
@@ -296,6 +299,8 @@ def extra_moe(w4, torch, np, synth, timer, reps: int = 5):
         route = [torch.from_numpy(p[1]).cuda() for p in picks]
         x0 = torch.randn((T, 2816), generator=g, device="cuda").to(torch.bfloat16)
         G = torch.empty((T * topk, 1408), device="cuda")
+        ws = w4.new_workspace(max(w4.w4_moe_gemv_ids_workspace_bytes(1408, 2816, T, topk, w4.W4_F32_RMS, False, False),
+                                  w4.w4_moe_gemv_ids_workspace_bytes(2816, 704, T, topk, w4.W4_F32_RMS, True, True)))
         Dn = [torch.empty((T, 2816), device="cuda") for _ in range(2)]
 
         # Each product renormalises its fp32 input rows on load (the gate half
@@ -308,9 +313,10 @@ def extra_moe(w4, torch, np, synth, timer, reps: int = 5):
                     gc, gs, dc, ds = pools[li]
                     kw = dict(slot_of=slot[li], n_slots=S)
                 w4.w4_moe_gemv_ids(gc, gs, 1408 * 2816 // 8, 1408 * 2816 // 32, 1408, 2816, x, ids[li],
-                                   n_experts=E, Y=G, **kw)
+                                   n_experts=E, Y=G, workspace=ws, **kw)
                 w4.w4_moe_gemv_ids(dc, ds, 2816 * 704 // 8, 2816 * 704 // 32, 2816, 704, G, ids[li],
-                                   x_per_pair=True, n_experts=E, route_w=route[li], Y=Dn[li & 1], **kw)
+                                   x_per_pair=True, n_experts=E, route_w=route[li], Y=Dn[li & 1],
+                                   workspace=ws, **kw)
                 x = Dn[li & 1]
         eager = timer.per_call(token, reps, warmup=1)
         graph = timer.graph_per_call(token, 1, replays=reps)
@@ -401,8 +407,9 @@ def extra_attention(w4, torch, np, synth, timer, reps: int = 20):
         ks = [torch.randn((L, D), generator=g, device="cuda").to(torch.bfloat16) for _ in range(copies)]
         vs = [torch.randn((L, D), generator=g, device="cuda").to(torch.bfloat16) for _ in range(copies)]
         o = torch.empty((H, D), device="cuda")
-        t = timer.per_call(lambda i: w4.w4_decode_attention(q, ks[i % copies], vs[i % copies], 0.0442, o),
-                           reps, warmup=2)
+        ws = w4.new_workspace(w4.w4_decode_attention_workspace_bytes(H, D, L))
+        t = timer.per_call(lambda i: w4.w4_decode_attention(q, ks[i % copies], vs[i % copies], 0.0442, o,
+                                                            workspace=ws), reps, warmup=2)
         nbytes = 2 * L * D * 2
         out[name] = {"us_per_call": round(t * 1e6, 2), "kv_bytes": nbytes, "GBps": round(gbps(nbytes, t), 1),
                      "frac_of_peak": round(gbps(nbytes, t) / HBM_PEAK_GBPS, 4)}
@@ -429,11 +436,12 @@ def extra_prompt(w4, torch, np, synth, timer, reps: int = 64):
         mats.append((c.view(N, K // 8), s.view(N, K // 32).view(torch.bfloat16)))
     flops = 2.0 * M * N * K
     out = {"flop_per_call": flops, "weight_copies_rotated": copies}
+    ws = w4.new_workspace(w4.w4_gemm_prompt_workspace_bytes(N, K, M))
     for name, dt in (("bf16", torch.bfloat16), ("f16", torch.float16)):
         X = torch.randn((M, K), generator=g, device="cuda").to(dt)
         Y = torch.empty((M, N), device="cuda")
-        t = timer.per_call(lambda i: w4.w4_gemm_prompt(mats[i % copies][0], mats[i % copies][1], X, Y),
-                           reps, warmup=copies)
+        t = timer.per_call(lambda i: w4.w4_gemm_prompt(mats[i % copies][0], mats[i % copies][1], X, Y,
+                                                       workspace=ws), reps, warmup=copies)
         tf = flops / t / 1e12
         out[name] = {"us_per_call": round(t * 1e6, 2), "TFLOPs": round(tf, 1),
                      "frac_of_mfma_peak": round(tf / MFMA_F16_PEAK_TFLOPS, 4)}
@@ -530,7 +538,7 @@ def main(argv=None):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16",
+        "dtype": "bf16",
         "data": "synthetic (seeded; codes uniform 0..15, steps bf16(|N(0,0.02)|+1e-4), x ~ N(0,1))",
         "config": {"workload": "vocabulary-head W4A16 GEMV 262144x1536 (bf16 x, batch 1) + "
                                "4-bit row gather of 64 ids from the same table",

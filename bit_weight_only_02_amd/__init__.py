@@ -12,6 +12,13 @@ Tensor conventions:
   steps  bfloat16 tensor (or int16/uint16 holding bf16 bits) [N, K/32];
   activations float16 or bfloat16 tensors (their dtype selects W4_F16/W4_BF16);
   outputs float32 (products) or bfloat16 (row gather).
+
+Workspaces: w4_gemm_smallM, w4_gemm_prompt, w4_decode_attention and
+w4_moe_gemv_ids take a caller-owned device workspace (``workspace=``, a
+zero-initialised byte tensor of at least the matching ``*_workspace_bytes``
+size).  When none is given, a zeroed one is taken from a cache kept per
+(device, stream), grown when a call needs more; calls issued on different
+streams therefore never share one.
 """
 
 from __future__ import annotations
@@ -53,12 +60,13 @@ lib = ctypes.CDLL(LIB_PATH)
 
 _SIGNATURES = {
     "w4_gemv": [_P, _P, _I32, _I32, _P, _I32, _P, _P],
-    "w4_gemm_smallM": [_P, _P, _I32, _I32, _P, _I32, _I32, _I64, _P, _I64, _P],
-    "w4_gemm_prompt": [_P, _P, _I32, _I32, _P, _I32, _I32, _I64, _P, _I64, _P],
+    "w4_gemm_smallM": [_P, _P, _I32, _I32, _P, _I32, _I32, _I64, _P, _I64, _P, _I64, _P],
+    "w4_gemm_prompt": [_P, _P, _I32, _I32, _P, _I32, _I32, _I64, _P, _I64, _P, _I64, _P],
     "w4_grid_to_codes": [_P, _I32, _I32, _P, _P, _P],
-    "w4_decode_attention": [_P, _I32, _I32, _P, _I64, _P, _I64, _I32, ctypes.c_float, _P, _P],
+    "w4_decode_attention": [_P, _I32, _I32, _P, _I64, _P, _I64, _I32, ctypes.c_float, _P, _P, _I64,
+                            _P],
     "w4_moe_gemv_ids": [_P, _P, _I64, _I64, _I32, _I32, _P, _I32, _I32, _I64, _P, _I32, _I32,
-                        _P, _I32, _I32, _P, _P, _P, _P, _P],
+                        _P, _I32, _I32, _P, _P, _P, _P, _P, _I64, _P],
     "w4_embed_gather": [_P, _P, _I32, _I32, _P, _I32, _P, _P, _P],
     "w4_rms_renorm": [_P, _I64, _I32, _I32, _P, _I64, _I32, _P],
     "w4_gemv_chain": [_P, _I32, _P, _P, _I64, _P],
@@ -68,6 +76,18 @@ for _name, _args in _SIGNATURES.items():
     _fn = getattr(lib, _name)
     _fn.argtypes = _args
     _fn.restype = ctypes.c_int
+_WS_SIGNATURES = {
+    "w4_gemm_smallM_workspace_bytes": [_I32, _I32, _I32],
+    "w4_gemm_prompt_workspace_bytes": [_I32, _I32, _I32],
+    "w4_decode_attention_workspace_bytes": [_I32, _I32, _I32],
+    "w4_moe_gemv_ids_workspace_bytes": [_I32, _I32, _I32, _I32, _I32, _I32, _I32],
+}
+for _name, _args in _WS_SIGNATURES.items():
+    _fn = getattr(lib, _name)
+    _fn.argtypes = _args
+    _fn.restype = ctypes.c_int64
+lib.w4_reload_settings.argtypes = []
+lib.w4_reload_settings.restype = None
 lib.w4_strerror.argtypes = [ctypes.c_int]
 lib.w4_strerror.restype = ctypes.c_char_p
 lib.w4_last_error_detail.argtypes = []
@@ -93,6 +113,63 @@ def _ptr(t) -> int | None:
 def _stream(stream=None) -> int:
     s = torch.cuda.current_stream() if stream is None else stream
     return s.cuda_stream
+
+
+def _ws_size(n: int, fn: str) -> int:
+    if n < 0:
+        raise W4Error(int(n), fn)
+    return int(n)
+
+
+_WS_CACHE: dict = {}
+
+
+def _workspace(nbytes: int, device, stream, given):
+    """(pointer, bytes) of the workspace for one call: the caller's tensor, or
+    a zeroed one cached per (device, stream) and grown on demand."""
+    if nbytes == 0:
+        return None, 0
+    if given is not None:
+        return given.data_ptr(), given.numel() * given.element_size()
+    s = torch.cuda.current_stream(device) if stream is None else stream
+    key = (torch.device(device).index, s.cuda_stream)
+    buf = _WS_CACHE.get(key)
+    if buf is None or buf.numel() < nbytes:
+        with torch.cuda.stream(s):
+            buf = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+        _WS_CACHE[key] = buf
+    return buf.data_ptr(), buf.numel()
+
+
+def new_workspace(nbytes: int, device="cuda") -> torch.Tensor:
+    """A zeroed workspace of nbytes (torch's allocations are 256-byte aligned)."""
+    return torch.zeros(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+def w4_reload_settings() -> None:
+    """Re-read the library's W4_* settings variables (tests)."""
+    lib.w4_reload_settings()
+
+
+reload_settings = w4_reload_settings
+
+
+def w4_gemm_smallM_workspace_bytes(N: int, K: int, M: int) -> int:
+    return _ws_size(lib.w4_gemm_smallM_workspace_bytes(N, K, M), "w4_gemm_smallM_workspace_bytes")
+
+
+def w4_gemm_prompt_workspace_bytes(N: int, K: int, M: int) -> int:
+    return _ws_size(lib.w4_gemm_prompt_workspace_bytes(N, K, M), "w4_gemm_prompt_workspace_bytes")
+
+
+def w4_decode_attention_workspace_bytes(H: int, D: int, L: int) -> int:
+    return _ws_size(lib.w4_decode_attention_workspace_bytes(H, D, L), "w4_decode_attention_workspace_bytes")
+
+
+def w4_moe_gemv_ids_workspace_bytes(N: int, K: int, T: int, topk: int, xdt: int, x_per_pair: bool,
+                                    combined: bool) -> int:
+    return _ws_size(lib.w4_moe_gemv_ids_workspace_bytes(N, K, T, topk, xdt, int(x_per_pair), int(combined)),
+                    "w4_moe_gemv_ids_workspace_bytes")
 
 
 def _act_dtype(t: torch.Tensor) -> int:
@@ -128,7 +205,7 @@ def w4_gemv(codes, steps, x, y=None, stream=None):
     return y
 
 
-def w4_gemm_smallM(codes, steps, X, Y=None, stream=None):
+def w4_gemm_smallM(codes, steps, X, Y=None, stream=None, workspace=None):
     """Y[m, n] for the M rows of X ([M, ldx] with row stride >= K); Y fp32 [M, N]."""
     N, K = _matrix(codes, steps)
     if X.dim() != 2 or X.stride(1) != 1 or X.shape[1] < K:
@@ -138,13 +215,15 @@ def w4_gemm_smallM(codes, steps, X, Y=None, stream=None):
         Y = torch.empty((M, N), dtype=torch.float32, device=codes.device)
     if Y.dim() != 2 or Y.stride(1) != 1 or Y.shape[0] != M or Y.shape[1] < N:
         raise ValueError("Y must be [M, >=N] with unit column stride")
+    ws, wsb = _workspace(max(int(lib.w4_gemm_smallM_workspace_bytes(N, K, M)), 0), codes.device, stream,
+                         workspace)
     _check(lib.w4_gemm_smallM(_ptr(codes), _ptr(steps), N, K, _ptr(X), _act_dtype(X), M,
-                              X.stride(0), _ptr(Y), Y.stride(0), _stream(stream)),
+                              X.stride(0), _ptr(Y), Y.stride(0), ws, wsb, _stream(stream)),
            "w4_gemm_smallM")
     return Y
 
 
-def w4_gemm_prompt(codes, steps, X, Y=None, stream=None):
+def w4_gemm_prompt(codes, steps, X, Y=None, stream=None, workspace=None):
     """Prompt-chunk product: Y[m, n] for the M rows of X ([M, ldx], ldx >= K,
     M up to W4_MAX_M_PROMPT) on the matrix cores; Y fp32 [M, N]."""
     N, K = _matrix(codes, steps)
@@ -155,8 +234,10 @@ def w4_gemm_prompt(codes, steps, X, Y=None, stream=None):
         Y = torch.empty((M, N), dtype=torch.float32, device=codes.device)
     if Y.dim() != 2 or Y.stride(1) != 1 or Y.shape[0] != M or Y.shape[1] < N:
         raise ValueError("Y must be [M, >=N] with unit column stride")
+    ws, wsb = _workspace(max(int(lib.w4_gemm_prompt_workspace_bytes(N, K, M)), 0), codes.device, stream,
+                         workspace)
     _check(lib.w4_gemm_prompt(_ptr(codes), _ptr(steps), N, K, _ptr(X), _act_dtype(X), M,
-                              X.stride(0), _ptr(Y), Y.stride(0), _stream(stream)),
+                              X.stride(0), _ptr(Y), Y.stride(0), ws, wsb, _stream(stream)),
            "w4_gemm_prompt")
     return Y
 
@@ -176,7 +257,7 @@ def w4_grid_to_codes(table, codes=None, steps=None, stream=None):
     return codes, steps
 
 
-def w4_decode_attention(q, k, v, scale, o=None, stream=None):
+def w4_decode_attention(q, k, v, scale, o=None, stream=None, workspace=None):
     """One query token's attention: q bf16 [H, D] (H <= 8 heads sharing one
     key/value head), k, v bf16 [L, >=D] rows; returns o fp32 [H, D]."""
     if q.dim() != 2 or not q.is_contiguous() or k.dim() != 2 or v.dim() != 2 or k.shape[0] != v.shape[0]:
@@ -186,14 +267,16 @@ def w4_decode_attention(q, k, v, scale, o=None, stream=None):
     H, D = q.shape
     if o is None:
         o = torch.empty((H, D), dtype=torch.float32, device=q.device)
+    ws, wsb = _workspace(max(int(lib.w4_decode_attention_workspace_bytes(H, D, k.shape[0])), 0), q.device,
+                         stream, workspace)
     _check(lib.w4_decode_attention(_ptr(q), H, D, _ptr(k), k.stride(0), _ptr(v), v.stride(0), k.shape[0],
-                                   float(scale), _ptr(o), _stream(stream)), "w4_decode_attention")
+                                   float(scale), _ptr(o), ws, wsb, _stream(stream)), "w4_decode_attention")
     return o
 
 
 def w4_moe_gemv_ids(codes_base, steps_base, expert_stride_codes, expert_stride_steps, N, K,
                     X, ids, x_per_pair=False, slot_of=None, n_experts=None, n_slots=0,
-                    row_scale=None, route_w=None, Y=None, dev_err=None, stream=None):
+                    row_scale=None, route_w=None, Y=None, dev_err=None, stream=None, workspace=None):
     """Expert-indexed product (see w4.h).  ``ids`` int32 [T, topk] of real ids;
     strides in uint32 words / uint16 elements; ``slot_of`` int32 [n_experts]
     selects pool addressing.  A float32 ``X`` is renormalised on load (each
@@ -207,12 +290,15 @@ def w4_moe_gemv_ids(codes_base, steps_base, expert_stride_codes, expert_stride_s
     rows = T * topk if route_w is None else T
     if Y is None:
         Y = torch.empty((rows, N), dtype=torch.float32, device=X.device)
+    xdt = W4_F32_RMS if X.dtype == torch.float32 else _act_dtype(X)
+    need = lib.w4_moe_gemv_ids_workspace_bytes(N, K, T, topk, xdt, 1 if x_per_pair else 0,
+                                               0 if route_w is None else 1)
+    ws, wsb = _workspace(max(int(need), 0), X.device, stream, workspace)
     _check(lib.w4_moe_gemv_ids(_ptr(codes_base), _ptr(steps_base), expert_stride_codes,
-                               expert_stride_steps, N, K, _ptr(X),
-                               W4_F32_RMS if X.dtype == torch.float32 else _act_dtype(X),
+                               expert_stride_steps, N, K, _ptr(X), xdt,
                                1 if x_per_pair else 0, X.stride(0), _ptr(ids), T, topk,
                                _ptr(slot_of), n_experts, n_slots, _ptr(row_scale),
-                               _ptr(route_w), _ptr(Y), _ptr(dev_err), _stream(stream)),
+                               _ptr(route_w), _ptr(Y), _ptr(dev_err), ws, wsb, _stream(stream)),
            "w4_moe_gemv_ids")
     return Y
 

@@ -9,6 +9,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <atomic>
 #include <mutex>
 
 #include "w4.h"
@@ -29,13 +30,7 @@ int fail(int status, const char *fmt, ...) {
 
 bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-// Test hook: W4_FORCE_LAUNCH_ERROR=1 makes every entry point return W4_ERR_HIP
-// after validation without enqueuing anything, so that tests can check that
-// outputs stay untouched on a failed call.
-bool forced_launch_error() {
-    const char *e = getenv("W4_FORCE_LAUNCH_ERROR");
-    return e && e[0] == '1';
-}
+bool forced_launch_error() { return w4::settings().force_launch_error; }
 
 int device_ready() {
     int dev = -1;
@@ -65,57 +60,102 @@ int check_dtype(int32_t dt) {
     return W4_OK;
 }
 
-// Per-device staging buffer of the combined expert product: allocated on first
-// use, grown (never shrunk) when a call needs more, and kept until the process
-// ends.  Growing is refused during graph capture.
-constexpr int kMaxDevices = 64;
-std::mutex g_ws_mu;
-void *g_ws_ptr[kMaxDevices] = {};
-size_t g_ws_bytes[kMaxDevices] = {};
-
-int staging_buffer(size_t bytes, hipStream_t stream, void **out) {
-    int dev = -1;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return fail(W4_ERR_NODEV, "hipGetDevice: %s", hipGetErrorString(e));
-    if (dev < 0 || dev >= kMaxDevices) return fail(W4_ERR_UNSUPPORTED, "device index %d", dev);
-    std::lock_guard<std::mutex> lock(g_ws_mu);
-    if (g_ws_bytes[dev] >= bytes) {
-        *out = g_ws_ptr[dev];
-        return W4_OK;
-    }
-    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-    e = hipStreamIsCapturing(stream, &cs);
-    if (e != hipSuccess) return fail(W4_ERR_HIP, "hipStreamIsCapturing: %s", hipGetErrorString(e));
-    if (cs != hipStreamCaptureStatusNone)
-        return fail(W4_ERR_UNSUPPORTED, "staging buffer must grow to %zu bytes outside graph capture",
-                    bytes);
-    if (g_ws_ptr[dev]) {
-        // the old buffer may still be read by queued work
-        e = hipDeviceSynchronize();
-        if (e != hipSuccess) return fail(W4_ERR_HIP, "hipDeviceSynchronize: %s", hipGetErrorString(e));
-        e = hipFree(g_ws_ptr[dev]);
-        g_ws_ptr[dev] = nullptr;
-        g_ws_bytes[dev] = 0;
-        if (e != hipSuccess) return fail(W4_ERR_HIP, "hipFree: %s", hipGetErrorString(e));
-    }
-    void *p = nullptr;
-    e = hipMalloc(&p, bytes);
-    if (e != hipSuccess) return fail(W4_ERR_HIP, "hipMalloc(%zu): %s", bytes, hipGetErrorString(e));
-    // the counter area at its start must read zero before first use
-    e = hipMemsetAsync(p, 0, w4::kWsCounterBytes, stream);
-    if (e != hipSuccess) {
-        (void)hipFree(p);
-        return fail(W4_ERR_HIP, "hipMemsetAsync: %s", hipGetErrorString(e));
-    }
-    g_ws_ptr[dev] = p;
-    g_ws_bytes[dev] = bytes;
-    *out = p;
+// A caller-owned workspace: at least `need` bytes, 256-byte aligned (NULL is
+// allowed when nothing is needed).
+int check_workspace(const void *ws, int64_t ws_bytes, size_t need) {
+    if (ws_bytes < 0) return fail(W4_ERR_INVALID_ARG, "negative workspace_bytes");
+    if (need == 0) return W4_OK;
+    if (!ws) return fail(W4_ERR_INVALID_ARG, "a workspace of %zu bytes is needed", need);
+    if ((uint64_t)ws_bytes < need)
+        return fail(W4_ERR_INVALID_ARG, "workspace of %lld bytes, %zu needed", (long long)ws_bytes, need);
+    if (!aligned(ws, 256)) return fail(W4_ERR_ALIGNMENT, "workspace not 256-byte aligned");
     return W4_OK;
+}
+
+// Bytes of the expert product's workspace: the counter area and the engine's
+// partial sums or per-choice rows, then (fp32 rows on the matrix engine) the
+// renormalised fp16 rows, 16-byte aligned.  *xoff gets the offset of those
+// rows after the counter area.
+size_t moe_ws_bytes(int32_t N, int32_t K, int32_t T, int32_t topk, int32_t xdt, int32_t x_per_pair,
+                    bool combined, size_t *xoff) {
+    size_t b = w4::moe_workspace(N, K, T, topk, combined);
+    const size_t off = (b + 15) / 16 * 16;
+    if (xoff) *xoff = off;
+    if (xdt == W4_F32_RMS && !w4::moe_by_pairs(T)) b = off + (size_t)(x_per_pair ? T * topk : T) * K * 2;
+    return b ? w4::kWsCounterBytes + b : 0;
+}
+
+// Settings: two copies, the current one published through an atomic pointer.
+std::mutex g_settings_mu;
+w4::Settings g_settings_buf[2];
+std::atomic<const w4::Settings *> g_settings{nullptr};
+int g_settings_next = 0;
+
+const w4::Settings *read_settings() {
+    std::lock_guard<std::mutex> lock(g_settings_mu);
+    w4::Settings &s = g_settings_buf[g_settings_next];
+    g_settings_next ^= 1;
+    s = w4::Settings{};
+    const char *e = getenv("W4_FORCE_LAUNCH_ERROR");
+    s.force_launch_error = e && e[0] == '1';
+    s.chain_spin_limit = 1u << 22;
+    s.smallm_rows_max = 4;
+    s.moe_pairs_max_t = 4;
+    if ((e = getenv("W4_SMALLM_ROWS_MAX"))) s.smallm_rows_max = atoi(e);
+    if ((e = getenv("W4_MOE_PAIRS_MAX_T"))) s.moe_pairs_max_t = atoi(e);
+    if ((e = getenv("W4_CHAIN_SPIN_LIMIT"))) s.chain_spin_limit = (unsigned)strtoul(e, nullptr, 10);
+    if ((e = getenv("W4_GEMV_TILE"))) {
+        w4::GemvTile &o = s.gemv_tile;
+        o.ring = 0;
+        o.pf = 0;
+        s.gemv_tile_set = sscanf(e, "%d,%d,%d,%d,%d,%d,%d", &o.L, &o.NG, &o.R, &o.waves, &o.blocks, &o.ring,
+                                 &o.pf) >= 5;
+    }
+    g_settings.store(&s, std::memory_order_release);
+    return &s;
 }
 
 }  // namespace
 
+namespace w4 {
+const Settings &settings() {
+    const Settings *s = g_settings.load(std::memory_order_acquire);
+    return s ? *s : *read_settings();
+}
+}  // namespace w4
+
 extern "C" {
+
+void w4_reload_settings(void) { (void)read_settings(); }
+
+int64_t w4_gemm_smallM_workspace_bytes(int32_t N, int32_t K, int32_t M) {
+    if (N < 0 || K < 0 || (K % 32) || M < 1 || M > W4_MAX_M || K > W4_MAX_K_SMALLM) return W4_ERR_INVALID_ARG;
+    if (N == 0 || K == 0) return 0;
+    const size_t b = w4::gemm_smallm_workspace(N, K, M);
+    return b ? (int64_t)(w4::kWsCounterBytes + b) : 0;
+}
+
+int64_t w4_gemm_prompt_workspace_bytes(int32_t N, int32_t K, int32_t M) {
+    if (N < 0 || K < 0 || (K % 32) || M < 1 || M > W4_MAX_M_PROMPT || K > W4_MAX_K_SMALLM)
+        return W4_ERR_INVALID_ARG;
+    if (N == 0 || K == 0) return 0;
+    return (int64_t)(w4::kWsCounterBytes + w4::gemm_prompt_workspace(N, K, M));
+}
+
+int64_t w4_decode_attention_workspace_bytes(int32_t H, int32_t D, int32_t L) {
+    if (H < 1 || H > 8 || (D != 256 && D != 512) || L < 1) return W4_ERR_INVALID_ARG;
+    return (int64_t)(w4::kWsCounterBytes + w4::attn_workspace(H, D, L));
+}
+
+int64_t w4_moe_gemv_ids_workspace_bytes(int32_t N, int32_t K, int32_t T, int32_t topk, int32_t xdt,
+                                        int32_t x_per_pair, int32_t combined) {
+    if (N < 0 || K < 0 || (K % 32) || K > W4_MAX_K_SMALLM || T < 0 || topk < 1 || topk > W4_MAX_TOPK ||
+        (int64_t)T * topk > 1024 || (xdt != W4_F16 && xdt != W4_BF16 && xdt != W4_F32_RMS) ||
+        (x_per_pair != 0 && x_per_pair != 1))
+        return W4_ERR_INVALID_ARG;
+    if (N == 0 || K == 0 || T == 0) return 0;
+    return (int64_t)moe_ws_bytes(N, K, T, topk, xdt, x_per_pair, combined != 0, nullptr);
+}
 
 int w4_gemv(const uint32_t *codes, const uint16_t *steps, int32_t N, int32_t K,
             const void *x, int32_t xdt, float *y, void *stream) {
@@ -135,7 +175,7 @@ int w4_gemv(const uint32_t *codes, const uint16_t *steps, int32_t N, int32_t K,
 
 int w4_gemm_smallM(const uint32_t *codes, const uint16_t *steps, int32_t N, int32_t K,
                    const void *X, int32_t xdt, int32_t M, int64_t ldx,
-                   float *Y, int64_t ldy, void *stream) {
+                   float *Y, int64_t ldy, void *workspace, int64_t workspace_bytes, void *stream) {
     int st;
     if ((st = check_matrix(codes, steps, N, K))) return st;
     if ((st = check_dtype(xdt))) return st;
@@ -145,6 +185,8 @@ int w4_gemm_smallM(const uint32_t *codes, const uint16_t *steps, int32_t N, int3
     if (N > 0 && (!Y || (K > 0 && !X))) return fail(W4_ERR_INVALID_ARG, "null X/Y");
     if (X && !aligned(X, 2)) return fail(W4_ERR_ALIGNMENT, "X not 2-byte aligned");
     if (Y && !aligned(Y, 4)) return fail(W4_ERR_ALIGNMENT, "Y not 4-byte aligned");
+    const size_t ws_need = (N > 0 && K > 0) ? (size_t)w4_gemm_smallM_workspace_bytes(N, K, M) : 0;
+    if ((st = check_workspace(workspace, workspace_bytes, ws_need))) return st;
     if (N == 0) return W4_OK;
     if ((st = device_ready())) return st;
     if (forced_launch_error()) return fail(W4_ERR_HIP, "forced launch error (test hook)");
@@ -157,19 +199,15 @@ int w4_gemm_smallM(const uint32_t *codes, const uint16_t *steps, int32_t N, int3
         }
         return launched(hipSuccess, "w4_gemm_smallM");
     }
-    void *ws = nullptr;
-    const size_t ws_bytes = w4::gemm_smallm_workspace(N, K, M);
-    if (ws_bytes && (st = staging_buffer(w4::kWsCounterBytes + ws_bytes, static_cast<hipStream_t>(stream), &ws)))
-        return st;
     return launched(w4::launch_gemm_smallm(codes, steps, N, K, static_cast<const uint16_t *>(X), ldx,
-                                           xdt, M, Y, ldy, ws,
+                                           xdt, M, Y, ldy, ws_need ? workspace : nullptr,
                                            static_cast<hipStream_t>(stream)),
                     "w4_gemm_smallM");
 }
 
 int w4_gemm_prompt(const uint32_t *codes, const uint16_t *steps, int32_t N, int32_t K,
                    const void *X, int32_t xdt, int32_t M, int64_t ldx,
-                   float *Y, int64_t ldy, void *stream) {
+                   float *Y, int64_t ldy, void *workspace, int64_t workspace_bytes, void *stream) {
     int st;
     if ((st = check_matrix(codes, steps, N, K))) return st;
     if ((st = check_dtype(xdt))) return st;
@@ -179,6 +217,8 @@ int w4_gemm_prompt(const uint32_t *codes, const uint16_t *steps, int32_t N, int3
     if (N > 0 && (!Y || (K > 0 && !X))) return fail(W4_ERR_INVALID_ARG, "null X/Y");
     if (X && !aligned(X, 2)) return fail(W4_ERR_ALIGNMENT, "X not 2-byte aligned");
     if (Y && !aligned(Y, 4)) return fail(W4_ERR_ALIGNMENT, "Y not 4-byte aligned");
+    const size_t ws_need = (N > 0 && K > 0) ? (size_t)w4_gemm_prompt_workspace_bytes(N, K, M) : 0;
+    if ((st = check_workspace(workspace, workspace_bytes, ws_need))) return st;
     if (N == 0) return W4_OK;
     if ((st = device_ready())) return st;
     if (forced_launch_error()) return fail(W4_ERR_HIP, "forced launch error (test hook)");
@@ -191,13 +231,9 @@ int w4_gemm_prompt(const uint32_t *codes, const uint16_t *steps, int32_t N, int3
         }
         return launched(hipSuccess, "w4_gemm_prompt");
     }
-    void *ws = nullptr;
-    if ((st = staging_buffer(w4::kWsCounterBytes + w4::gemm_prompt_workspace(N, K, M),
-                             static_cast<hipStream_t>(stream), &ws)))
-        return st;
-    // the staged rows go after the counter area, which other calls keep at zero
+    // the staged rows go after the counter area, which must stay zero
     return launched(w4::launch_gemm_prompt(codes, steps, N, K, static_cast<const uint16_t *>(X), ldx, xdt, M,
-                                           Y, ldy, static_cast<char *>(ws) + w4::kWsCounterBytes,
+                                           Y, ldy, static_cast<char *>(workspace) + w4::kWsCounterBytes,
                                            static_cast<hipStream_t>(stream)),
                     "w4_gemm_prompt");
 }
@@ -222,7 +258,7 @@ int w4_grid_to_codes(const uint16_t *table, int32_t N, int32_t K, uint32_t *code
 
 int w4_decode_attention(const uint16_t *q, int32_t H, int32_t D, const uint16_t *k, int64_t ldk,
                         const uint16_t *v, int64_t ldv, int32_t L, float scale, float *o,
-                        void *stream) {
+                        void *workspace, int64_t workspace_bytes, void *stream) {
     if (H < 1 || H > 8) return fail(W4_ERR_INVALID_ARG, "H=%d outside 1..8", H);
     if (D != 256 && D != 512) return fail(W4_ERR_UNSUPPORTED, "D=%d (256 or 512)", D);
     if (L < 1) return fail(W4_ERR_INVALID_ARG, "L=%d", L);
@@ -233,14 +269,12 @@ int w4_decode_attention(const uint16_t *q, int32_t H, int32_t D, const uint16_t 
         return fail(W4_ERR_ALIGNMENT, "k/v rows not %d-byte aligned", va);
     if (!aligned(q, 2) || !aligned(o, 4)) return fail(W4_ERR_ALIGNMENT, "q or o misaligned");
     int st;
+    if ((st = check_workspace(workspace, workspace_bytes, w4::kWsCounterBytes + w4::attn_workspace(H, D, L))))
+        return st;
     if ((st = device_ready())) return st;
     if (forced_launch_error()) return fail(W4_ERR_HIP, "forced launch error (test hook)");
-    void *ws = nullptr;
-    if ((st = staging_buffer(w4::kWsCounterBytes + w4::attn_workspace(H, D, L), static_cast<hipStream_t>(stream),
-                             &ws)))
-        return st;
     return launched(w4::launch_attn(q, H, D, k, ldk, v, ldv, L, scale, o,
-                                    static_cast<char *>(ws) + w4::kWsCounterBytes,
+                                    static_cast<char *>(workspace) + w4::kWsCounterBytes,
                                     static_cast<hipStream_t>(stream)),
                     "w4_decode_attention");
 }
@@ -290,7 +324,7 @@ int w4_moe_gemv_ids(const uint32_t *codes_base, const uint16_t *steps_base,
                     const int32_t *ids, int32_t T, int32_t topk,
                     const int32_t *slot_of, int32_t n_experts, int32_t n_slots,
                     const float *row_scale, const float *route_w,
-                    float *Y, int32_t *dev_err, void *stream) {
+                    float *Y, int32_t *dev_err, void *workspace, int64_t workspace_bytes, void *stream) {
     int st;
     if ((st = check_matrix(codes_base, steps_base, N, K))) return st;
     if (xdt != W4_F32_RMS && (st = check_dtype(xdt))) return st;
@@ -313,18 +347,17 @@ int w4_moe_gemv_ids(const uint32_t *codes_base, const uint16_t *steps_base,
     if (ids && !aligned(ids, 4)) return fail(W4_ERR_ALIGNMENT, "ids not 4-byte aligned");
     if (T == 0 || N == 0) return W4_OK;
     if (K == 0) return fail(W4_ERR_UNSUPPORTED, "K == 0");
+    // fp32 rows on the matrix engine: renormalised into the workspace, after
+    // the engine's part, as fp16 rows of K (16-byte aligned)
+    size_t xoff = 0;
+    const size_t ws_need = moe_ws_bytes(N, K, T, topk, xdt, x_per_pair, route_w != nullptr, &xoff);
+    if ((st = check_workspace(workspace, workspace_bytes, ws_need))) return st;
     if ((st = device_ready())) return st;
+    if (forced_launch_error()) return fail(W4_ERR_HIP, "forced launch error (test hook)");
     hipStream_t s = static_cast<hipStream_t>(stream);
-    void *ws = nullptr;
-    size_t ws_bytes = w4::moe_workspace(N, K, T, topk, route_w != nullptr);
-    // fp32 rows on the matrix engine: renormalised into the buffer, after the
-    // engine's part, as fp16 rows of K (16-byte aligned)
+    void *ws = ws_need ? workspace : nullptr;
     const int xrows = x_per_pair ? T * topk : T;
     const bool pre_rms = xdt == W4_F32_RMS && !w4::moe_by_pairs(T);
-    const size_t xoff = (ws_bytes + 15) / 16 * 16;
-    if (pre_rms) ws_bytes = xoff + (size_t)xrows * K * 2;
-    if (ws_bytes && (st = staging_buffer(w4::kWsCounterBytes + ws_bytes, s, &ws))) return st;
-    if (forced_launch_error()) return fail(W4_ERR_HIP, "forced launch error (test hook)");
     const void *Xk = X;
     int64_t ldk = ldx;
     int dtk = xdt;
@@ -355,11 +388,10 @@ int w4_gemv_chain(const w4_chain_mat *desc, int32_t n_mats, const uint16_t *x0, 
         return fail(W4_ERR_ALIGNMENT, "desc, x0 or sync misaligned");
     if ((st = device_ready())) return st;
     if (forced_launch_error()) return fail(W4_ERR_HIP, "forced launch error (test hook)");
-    // W4_CHAIN_SPIN_LIMIT bounds each wait for exchange cells (read rounds); tests set it tiny to
-    // exercise the timeout path without a hang.
-    unsigned spin = 1u << 22;
-    if (const char *e = getenv("W4_CHAIN_SPIN_LIMIT")) spin = (unsigned)strtoul(e, nullptr, 10);
-    return launched(w4::launch_chain(desc, n_mats, x0, sync, spin, static_cast<hipStream_t>(stream)),
+    // the settings' spin limit bounds each wait for exchange cells (read
+    // rounds); tests set it tiny to exercise the timeout path without a hang
+    return launched(w4::launch_chain(desc, n_mats, x0, sync, w4::settings().chain_spin_limit,
+                                     static_cast<hipStream_t>(stream)),
                     "w4_gemv_chain");
 }
 

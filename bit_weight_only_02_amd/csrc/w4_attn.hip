@@ -173,12 +173,9 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const float *__restrict
 // Splits: about 32 keys each (8 per wave), at most 256 (one per CU): 131072
 // positions took 155 us with 256 splits, 203 us with 512, 300 us with 1024; a
 // 512-slot ring 21.5 us with 16 splits, 25 us with 64.
-// W4_ATTN_SPLITS overrides the count (schedule sweeps; the merge order is
-// fixed).
 static int attn_splits(int L) {
     int S = (L + 31) / 32;
     if (S > 256) S = 256;
-    if (const char *e = getenv("W4_ATTN_SPLITS")) S = atoi(e);
     if (S > L) S = L;
     return S < 1 ? 1 : S;
 }

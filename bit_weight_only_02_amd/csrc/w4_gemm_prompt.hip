@@ -503,16 +503,6 @@ PromptPlan prompt_plan(int N, int K, int M) {
         p.MT = M > 16 ? 2 : 1;
         p.W = 4;
     }
-    // W4_PROMPT_TILE="MT,W" overrides the tiling (schedule sweeps; every
-    // output's sum runs in the same order whatever the tiling)
-    if (const char *e = getenv("W4_PROMPT_TILE")) {
-        int mt = 0, w = 0;
-        if (sscanf(e, "%d,%d", &mt, &w) == 2 && (mt == 1 || mt == 2 || mt == 4 || mt == 8) &&
-            (w == 4 || w == 8) && (4 * mt) % w == 0) {
-            p.MT = mt;
-            p.W = w;
-        }
-    }
     const int bm = 16 * p.MT, bn = 16 * p.W * kPromptNT;
     p.Mp = (M + bm - 1) / bm * bm;
     p.Gp = ((K / 32) + 3) / 4 * 4;
@@ -558,10 +548,7 @@ hipError_t launch_gemm_prompt(const uint32_t *codes, const uint16_t *steps, int 
                               const uint16_t *X, long ldx, int dt, int M, float *Y, long ldy,
                               void *ws, hipStream_t stream) {
     const PromptPlan p = prompt_plan(N, K, M);
-    int D = kPromptD;
-    // W4_PROMPT_D overrides the ring depth (schedule sweeps; a depth whose
-    // ring does not fit the LDS is refused)
-    if (const char *e = getenv("W4_PROMPT_D")) D = atoi(e);
+    const int D = kPromptD;
     PromptFn fn = pick_prompt(p.MT, D, p.W);
     if (prompt_lds_bytes(p.MT, D, p.W) > 150 * 1024) return hipErrorInvalidConfiguration;
     if (!fn || !ws || K < 32 || M < 1 || N < 1 || (reinterpret_cast<uintptr_t>(ws) & 15))

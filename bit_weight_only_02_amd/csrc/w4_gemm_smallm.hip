@@ -96,48 +96,17 @@ GemmFn pick_gemm_s(int R) {
 
 SmallMPlan gemm_plan(int N, int K, int M) { return smallm_plan(N, K, M, 1, kSmallMLdsFast, true); }
 
-// W4_SMALLM_PLAN="KW,S,workgroups" overrides the plan's waves per tile, K-slices
-// and workgroup cap (schedule sweeps; what is computed does not change).
-// Returns the cap (0: the default).
-int plan_override(int N, int K, int M, SmallMPlan &p) {
-    const char *e = getenv("W4_SMALLM_PLAN");
-    int kw = 0, S = 0, cap = 0;
-    if (!e || sscanf(e, "%d,%d,%d", &kw, &S, &cap) != 3) return 0;
-    if ((kw != 1 && kw != 2 && kw != 4) || S < 1 || cap < 0) return 0;
-    const int G = K / 32;
-    int mp = 1, lg = 0;
-    while (mp < M) { mp <<= 1; ++lg; }
-    int gs = ((G + S - 1) / S + 3) / 4 * 4;
-    if (gs < 4) gs = 4;
-    const int nr = gs / 4;
-    if (nr * 4 * 4 * mp * 16 > kSmallMLdsA) return 0;  // does not fit: keep the plan
-    p.Gs = gs;
-    p.S = (G + gs - 1) / gs;
-    p.KW = kw;
-    while (p.KW > 1 && nr < p.KW) p.KW /= 2;
-    const int rpw = (nr + p.KW - 1) / p.KW;
-    p.R = rpw <= 4 ? 4 : rpw <= 8 ? 8 : rpw <= 16 ? 16 : 24;
-    p.lds_a = (nr * 4 * 4 * mp + 63) / 64 * 64 * 16;
-    p.mp_log2 = lg;
-    return cap;
-}
-
 }  // namespace
 
 // Up to four rows: M batch-1 products side by side, their weights read from
 // HBM about once (the workgroups of a row block run together); on a set of
 // the four sweep shapes 28.1 against 32.3 us at M = 2, 34.3 against 37.9 us at
 // M = 4.  From 8 rows the matrix cores win (45.9 against 48.9 us at M = 8).
-// W4_SMALLM_ROWS_MAX overrides the bound (0: always the matrix cores).
-static bool smallm_by_rows(int M) {
-    const char *e = getenv("W4_SMALLM_ROWS_MAX");
-    return M <= (e ? atoi(e) : 4);
-}
+static bool smallm_by_rows(int M) { return M <= settings().smallm_rows_max; }
 
 size_t gemm_smallm_workspace(int N, int K, int M) {
     if (M == 1 || smallm_by_rows(M)) return 0;  // batch-1 products
-    SmallMPlan p = gemm_plan(N, K, M);
-    plan_override(N, K, M, p);
+    const SmallMPlan p = gemm_plan(N, K, M);
     return p.S > 1 ? (size_t)p.S * M * N * sizeof(float) : 0;
 }
 
@@ -163,14 +132,13 @@ hipError_t launch_gemm_smallm(const uint32_t *codes, const uint16_t *steps, int 
     // one activation row: the batch-1 kernel (no matrix-core padding)
     if (M == 1) return launch_gemv(codes, steps, N, K, X, dt, Y, stream);
     if (smallm_by_rows(M)) return launch_gemv_rows(codes, steps, N, K, X, ldx, dt, M, Y, ldy, stream);
-    SmallMPlan p = gemm_plan(N, K, M);
-    const int cap = plan_override(N, K, M, p);
+    const SmallMPlan p = gemm_plan(N, K, M);
     const bool steps8 = (K / 32) % 4 == 0 && (reinterpret_cast<uintptr_t>(steps) & 7) == 0;
     GemmFn fn = steps8 ? pick_gemm_s<true>(p.R) : pick_gemm_s<false>(p.R);
     if (!fn || (p.S > 1 && !ws)) return hipErrorInvalidConfiguration;
     unsigned *cnt = static_cast<unsigned *>(ws);
     float *part = ws ? reinterpret_cast<float *>(static_cast<char *>(ws) + kWsCounterBytes) : nullptr;
-    const int groups = cap > 0 ? cap : (int)(p.KW == 1 && M >= 8 ? kSmallMWideGroups : kSmallMTargetGroups);
+    const int groups = (int)(p.KW == 1 && M >= 8 ? kSmallMWideGroups : kSmallMTargetGroups);
     hipLaunchKernelGGL(fn, dim3(gemm_grid_x(N, p, groups), p.S),
                        dim3(64 * kSmallMWaves), p.lds_a,
                        stream, reinterpret_cast<const uint4 *>(codes), steps, N, K, X, ldx, dt, M, Y,

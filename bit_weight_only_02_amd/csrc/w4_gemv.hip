@@ -533,25 +533,9 @@ GemvTile gemv_tile(int N, int K) {
     const long rows_per_iter = (long)(64 / best.L) * best.R * best.waves;
     const long blocks = (N + rows_per_iter - 1) / rows_per_iter;
     best.blocks = (int)(blocks < 1 ? 1 : (blocks > 1024 ? 1024 : blocks));
+    // (the streaming ring variant measured no faster than this kernel; it is
+    // chosen only by the tile override)
     best.ring = 0;
-    // The streaming variant: eight waves per CU-sized workgroup, each with a
-    // ring as deep as the LDS allows (up to kRingMaxD tiles), when the shape
-    // meets its preconditions and there are enough tiles to keep every wave of
-    // the chip busy.
-    if (G > 0 && G % 8 == 0 && best.NG == (G + best.L - 1) / best.L &&
-        pick_ring(best.L, best.NG, 2) != nullptr) {
-        const int waves = 8;
-        const int per_wave = (kLdsBytes - stage_raw_halves(K) * 4) / waves;
-        int D = per_wave / ring_tile_bytes(best.L, K);
-        if (D > kRingMaxD) D = kRingMaxD;
-        const long tiles = (N + (64 / best.L) - 1) / (64 / best.L);
-        if (D >= 2 && tiles >= 256L * waves && getenv("W4_GEMV_RING_DEFAULT")) {
-            best.ring = D;
-            best.waves = waves;
-            best.R = 1;
-            best.blocks = 256;
-        }
-    }
     return best;
 }
 
@@ -571,15 +555,12 @@ hipError_t launch_gemv(const uint32_t *codes, const uint16_t *steps, int N, int 
             t = GemvTile{64, ng64, 1, 4, (int)(b64 > 1024 ? 1024 : b64), 0, 0};
         }
     }
-    // W4_GEMV_TILE="L,NG,R,waves,blocks[,ring depth[,prefetch]]" overrides the table (tile sweeps);
-    // it changes only the schedule, never what is computed.
-    if (const char *e = getenv("W4_GEMV_TILE")) {
-        GemvTile o;
-        o.ring = 0;
-        o.pf = 0;
-        const int nf = sscanf(e, "%d,%d,%d,%d,%d,%d,%d", &o.L, &o.NG, &o.R, &o.waves, &o.blocks, &o.ring,
-                              &o.pf);
-        if (nf >= 5 && o.L * o.NG * 32 >= K && o.waves >= 1 && o.waves <= (o.ring ? 8 : 4) &&
+    // The tile override of the settings (W4_GEMV_TILE, read once per process)
+    // changes only the schedule, never what is computed.
+    {
+        const Settings &cfg = settings();
+        const GemvTile &o = cfg.gemv_tile;
+        if (cfg.gemv_tile_set && o.L * o.NG * 32 >= K && o.waves >= 1 && o.waves <= (o.ring ? 8 : 4) &&
             o.blocks >= 1 && o.ring >= 0 && o.ring <= kRingMaxD)
             t = o;
     }
@@ -616,7 +597,6 @@ hipError_t launch_gemv_rows(const uint32_t *codes, const uint16_t *steps, int N,
     const long rows_per_iter = (long)(64 / t.L) * t.waves;
     const long need = (N + rows_per_iter - 1) / rows_per_iter;
     long bx = (512 + M - 1) / M;  // 512 in all: measured best at M = 2 and 4
-    if (const char *e = getenv("W4_ROWS_GEMV_BLOCKS")) bx = atol(e);
     if (bx > need) bx = need;
     if (bx < 1) bx = 1;
     GemvPairs bp{};
@@ -635,16 +615,13 @@ hipError_t launch_gemv_rows(const uint32_t *codes, const uint16_t *steps, int N,
 // workgroup).  Measured over an expert token: at 8 pairs (one token) 64 per
 // pair gave 566-579 us against 625 us with 72 and 629 us with 128; at 32
 // pairs 24 per pair gave 976-982 us against 999 with 32 and 1013 with 16.
-// W4_MOE_GEMV_BLOCKS overrides the workgroups per pair (schedule sweeps).
 hipError_t launch_gemv_pairs(const uint32_t *codes_base, const uint16_t *steps_base, int64_t stride_codes,
                              int64_t stride_steps, int N, int K, const uint16_t *X, long ldx, int dt,
                              int x_per_pair, const int32_t *ids, int P, int topk, const int32_t *slot_of,
                              int n_experts, int n_slots, const float *row_scale, float *out,
                              int32_t *dev_err, hipStream_t stream) {
     const GemvTile t = gemv_tile(N, K);
-    int R = 1, pf = 0;
-    // W4_MOE_GEMV_RPF="R,pf": rows per slot in flight and prefetch (sweeps)
-    if (const char *e = getenv("W4_MOE_GEMV_RPF")) sscanf(e, "%d,%d", &R, &pf);
+    const int R = 1, pf = 0;
     // dt 2: fp32 rows renormalised on load
     GemvFn fn = dt == 2 ? (R == 1 && pf == 0 && t.waves == 4 ? pick_rn(t.L, t.NG) : nullptr)
                         : pick(t.L, t.NG, R, pf);
@@ -652,7 +629,6 @@ hipError_t launch_gemv_pairs(const uint32_t *codes_base, const uint16_t *steps_b
     const long rows_per_iter = (long)(64 / t.L) * t.waves * R;
     const long need = (N + rows_per_iter - 1) / rows_per_iter;
     long bx = ((P <= 8 ? 512 : 768) + P - 1) / P;
-    if (const char *e = getenv("W4_MOE_GEMV_BLOCKS")) bx = atol(e);
     if (bx > need) bx = need;
     if (bx < 1) bx = 1;
     GemvPairs bp;

@@ -19,6 +19,21 @@ struct GemvTile {
 
 GemvTile gemv_tile(int N, int K);
 
+// Settings read from the environment once per process (again on
+// w4_reload_settings): the batch-1 tile override (W4_GEMV_TILE =
+// "L,NG,R,waves,blocks[,ring depth[,prefetch]]"), the bounds below which the
+// small-M and expert products run as side-by-side batch-1 products, and two
+// test hooks.  Each changes only the schedule, never what is computed.
+struct Settings {
+    bool force_launch_error;    // W4_FORCE_LAUNCH_ERROR=1
+    unsigned chain_spin_limit;  // W4_CHAIN_SPIN_LIMIT (read rounds of a chain wait)
+    bool gemv_tile_set;
+    GemvTile gemv_tile;
+    int smallm_rows_max;        // W4_SMALLM_ROWS_MAX (default 4; 0: always the matrix cores)
+    int moe_pairs_max_t;        // W4_MOE_PAIRS_MAX_T (default 4; 0: always the matrix engine)
+};
+const Settings &settings();
+
 hipError_t launch_gemv(const uint32_t *codes, const uint16_t *steps, int N, int K,
                        const uint16_t *x, int dt, float *y, hipStream_t stream);
 
@@ -26,9 +41,9 @@ hipError_t launch_gemv(const uint32_t *codes, const uint16_t *steps, int N, int 
 // splits K (and, for the expert product, when route weights are given);
 // *_workspace() returns the bytes of partial sums it needs (0: none).  The
 // workspace handed to the launchers starts with kWsCounterBytes of counters
-// (one per grid column, at most kMaxGridColumns; zero between calls: zeroed
-// when the buffer is allocated and left at zero by every kernel that uses
-// them); the partial sums follow.
+// (one per grid column, at most kMaxGridColumns; zero between calls: the
+// caller zeroes a new workspace, and every kernel that uses them leaves them
+// at zero); the partial sums follow.
 constexpr int kMaxGridColumns = 2048;
 constexpr size_t kWsCounterBytes = 16384;
 static_assert(kMaxGridColumns * 4 <= (int)kWsCounterBytes, "counter area");

@@ -248,31 +248,17 @@ MoeFn pick_moe_s(int R) {
 static SmallMPlan moe_plan(int N, int K, int T, int topk) {
     const int P = T * topk;
     SmallMPlan p = smallm_plan(N, K, P < 16 ? P : 16, P);
-    // W4_MOE_PLAN="KW,R" overrides the waves per tile and the rounds of loads
-    // a wave keeps in flight (schedule sweeps; what is computed does not change)
-    if (const char *e = getenv("W4_MOE_PLAN")) {
-        int kw = 0, r = 0;
-        if (sscanf(e, "%d,%d", &kw, &r) == 2 && (kw == 1 || kw == 2 || kw == 4) &&
-            (r == 4 || r == 8 || r == 16 || r == 24)) {
-            p.KW = kw;
-            p.R = r;
-        }
-    }
     return p;
 }
 
-// Up to kPairsMaxT tokens: every choice runs as its own matrix-vector
+// Up to a few tokens (a setting, 4 by default): every choice runs as its own matrix-vector
 // product, side by side in one launch of the batch-1 kernel (gridDim.y =
 // pairs).  With few tokens almost every chosen expert serves a single pair,
 // and the matrix engine would give it a 16-row MFMA tile with one live row:
 // one expert layer at 4 tokens measured 2.6x faster this way although the
 // few experts shared by two tokens are read twice.
-// W4_MOE_PAIRS_MAX_T overrides the token bound (0: always the engine).
-constexpr int kPairsMaxT = 4;
-bool moe_by_pairs(int T) {
-    const char *e = getenv("W4_MOE_PAIRS_MAX_T");
-    return T <= (e ? atoi(e) : kPairsMaxT);
-}
+// (the bound is a setting, 4 by default)
+bool moe_by_pairs(int T) { return T <= settings().moe_pairs_max_t; }
 
 size_t moe_workspace(int N, int K, int T, int topk, bool route) {
     if (moe_by_pairs(T)) return route ? (size_t)T * topk * N * sizeof(float) : 0;

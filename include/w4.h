@@ -47,9 +47,21 @@
  *   fp32; the row gather writes bf16.
  *
  * Conventions:
- *   - All array pointers are DEVICE pointers owned by the caller.  Besides the
- *     per-device staging buffer documented at w4_moe_gemv_ids, the library
- *     allocates nothing and frees nothing.
+ *   - All array pointers are DEVICE pointers owned by the caller.  The library
+ *     allocates, frees and synchronises nothing.
+ *   - Workspaces.  w4_gemm_smallM, w4_gemm_prompt, w4_decode_attention and
+ *     w4_moe_gemv_ids need device memory beyond their inputs and outputs
+ *     (partial sums, staged activations, per-split partials).  The caller owns
+ *     it: the matching *_workspace_bytes call gives the size for a shape (0:
+ *     none needed, NULL may be passed); the caller allocates at least that
+ *     many bytes, 256-byte aligned, sets them all to zero once before the
+ *     workspace's first use, and passes it with every call.  Every workspace
+ *     starts with a 16 KiB area of counters; every call that completes leaves
+ *     them at zero again, so one workspace serves any number of later calls
+ *     (of any of the four entry points, with the largest size they need)
+ *     without clearing.  Two calls that may run at the same time (different
+ *     streams or host threads) need different workspaces; the rest of their
+ *     contents is scratch.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Calls
  *     enqueue and return; the caller synchronises.
  *   - Return value: W4_OK (0) or a negative w4_status.  Argument errors are
@@ -62,7 +74,16 @@
  *   - Numerics: each product c-8 times an activation is exact; sums run in fp32.
  *     Every product output satisfies |y - y_exact| <= 1e-3 * sum_k |w(n,k) x_k|.
  *   - Thread safety: entry points may be called from several host threads and
- *     streams at once.
+ *     streams at once, each call with its own workspace (see above); a chain's
+ *     sync buffer is shared by the calls that use it, which must not overlap.
+ *   - Settings: five environment variables are read once per process (and
+ *     again by w4_reload_settings): W4_GEMV_TILE (a tile override of the
+ *     batch-1 product), W4_SMALLM_ROWS_MAX and W4_MOE_PAIRS_MAX_T (up to how
+ *     many rows / tokens the small-M and expert products run as side-by-side
+ *     batch-1 products; 4 by default), all three schedule only;
+ *     W4_CHAIN_SPIN_LIMIT (the bound of the chain's waits) and
+ *     W4_FORCE_LAUNCH_ERROR=1 (every entry point returns W4_ERR_HIP after
+ *     validation without enqueuing anything), two test hooks.
  */
 #ifndef W4_H
 #define W4_H
@@ -116,14 +137,14 @@ int w4_gemv(const uint32_t *codes, const uint16_t *steps, int32_t N, int32_t K,
  * about once).  M >= 5 runs on the matrix cores, each weight read from memory
  * once for all M rows; when the plan splits K into slices (to give the chip
  * enough independent work, or to fit the staged activations), the slices are
- * summed in a fixed order inside the same launch, through a device buffer that
- * the library allocates once per device and reuses (grown on demand while no
- * graph capture is active; such calls on one device from different streams
- * must not overlap).
+ * summed in a fixed order inside the same launch, through the workspace
+ * (w4_gemm_smallM_workspace_bytes; 0 bytes for the plans that do not split).
  */
+int64_t w4_gemm_smallM_workspace_bytes(int32_t N, int32_t K, int32_t M);
 int w4_gemm_smallM(const uint32_t *codes, const uint16_t *steps, int32_t N, int32_t K,
                    const void *X, int32_t xdt, int32_t M, int64_t ldx,
-                   float *Y, int64_t ldy, void *stream);
+                   float *Y, int64_t ldy, void *workspace, int64_t workspace_bytes,
+                   void *stream);
 
 /*
  * Prompt-chunk product [P1-S6] with M activation rows, 1 <= M <= W4_MAX_M_PROMPT
@@ -141,13 +162,15 @@ int w4_gemm_smallM(const uint32_t *codes, const uint16_t *steps, int32_t N, int3
  * (weight steps spanning more than 2^21, or a bf16 subnormal/inf/NaN step;
  * bf16 activation rows spanning more than 2^31, or holding inf/NaN or a
  * subnormal) take slower exact paths, so the bound above holds for all inputs.
- * Two kernels run: the activations are first staged as fp16 into the device
- * buffer that the library allocates once per device and reuses (see
- * w4_gemm_smallM; 2*K*M bytes, rounded up), then the product.
+ * Two kernels run: the activations are first staged as fp16 into the
+ * workspace (w4_gemm_prompt_workspace_bytes: about 2*K*M + N*K/16 bytes, with
+ * the scaled steps and per-row flags), then the product.
  */
+int64_t w4_gemm_prompt_workspace_bytes(int32_t N, int32_t K, int32_t M);
 int w4_gemm_prompt(const uint32_t *codes, const uint16_t *steps, int32_t N, int32_t K,
                    const void *X, int32_t xdt, int32_t M, int64_t ldx,
-                   float *Y, int64_t ldy, void *stream);
+                   float *Y, int64_t ldy, void *workspace, int64_t workspace_bytes,
+                   void *stream);
 
 /*
  * Grid packing of a 16-bit table [P1-S2] (the conversion behind the 4-bit
@@ -177,12 +200,14 @@ int w4_grid_to_codes(const uint16_t *table, int32_t N, int32_t K, uint32_t *code
  *   q: bf16 [H][D] contiguous.  K, V: bf16 rows ldk / ldv elements apart.
  *   D is 256 or 512; K, V 16-byte aligned (8-byte for D = 256) and ldk, ldv
  *   multiples of 8 (of 4).  o: fp32 [H][D], written.  1 <= L.
- * The split partials live in the library's per-device buffer (see
- * w4_gemm_smallM).  Accumulation in fp32 with base-2 exponentials.
+ * The split partials live in the workspace
+ * (w4_decode_attention_workspace_bytes).  Accumulation in fp32 with base-2
+ * exponentials.
  */
+int64_t w4_decode_attention_workspace_bytes(int32_t H, int32_t D, int32_t L);
 int w4_decode_attention(const uint16_t *q, int32_t H, int32_t D, const uint16_t *k, int64_t ldk,
                         const uint16_t *v, int64_t ldv, int32_t L, float scale, float *o,
-                        void *stream);
+                        void *workspace, int64_t workspace_bytes, void *stream);
 
 /*
  * Expert-indexed product [P3].  T tokens each select topk experts:
@@ -199,7 +224,7 @@ int w4_decode_attention(const uint16_t *q, int32_t H, int32_t D, const uint16_t 
  *      all choices of a token) or row t*topk + j (x_per_pair == 1).  xdt
  *      W4_F16 or W4_BF16 (2-byte aligned), or W4_F32_RMS (fp32 rows, 4-byte
  *      aligned, ldx in floats, renormalised on load; from 5 tokens the rows
- *      are renormalised into the library's device buffer first).
+ *      are renormalised into the workspace first).
  *   row_scale: optional float[n_experts][N] per-expert output scale, ALWAYS
  *      indexed by the real id (only the weight read goes through slot_of).
  *   route_w: optional float[T][topk].  NULL: Y is float[T*topk][N], one row per
@@ -211,12 +236,13 @@ int w4_decode_attention(const uint16_t *q, int32_t H, int32_t D, const uint16_t 
  *   dev_err: optional device int32; an id or slot out of range sets it to 1 and
  *      fills the affected output rows with NaN (never leaves them untouched).
  *   The combined form (route_w != NULL), and from 5 tokens any K > 3072
- *   (summed over K-slices in a fixed order), stage per-choice rows in a device buffer the
- *   library allocates once per device and reuses (grown on demand while no
- *   graph capture is active; such calls on one device from different streams
- *   must not overlap).
+ *   (summed over K-slices in a fixed order), stage per-choice rows in the
+ *   workspace (w4_moe_gemv_ids_workspace_bytes, with combined = route_w !=
+ *   NULL; 0 bytes when nothing is staged).
  * Limits: T*topk <= 1024, topk <= W4_MAX_TOPK, K <= W4_MAX_K_SMALLM.
  */
+int64_t w4_moe_gemv_ids_workspace_bytes(int32_t N, int32_t K, int32_t T, int32_t topk, int32_t xdt,
+                                        int32_t x_per_pair, int32_t combined);
 int w4_moe_gemv_ids(const uint32_t *codes_base, const uint16_t *steps_base,
                     int64_t expert_stride_codes, int64_t expert_stride_steps,
                     int32_t N, int32_t K,
@@ -224,7 +250,8 @@ int w4_moe_gemv_ids(const uint32_t *codes_base, const uint16_t *steps_base,
                     const int32_t *ids, int32_t T, int32_t topk,
                     const int32_t *slot_of, int32_t n_experts, int32_t n_slots,
                     const float *row_scale, const float *route_w,
-                    float *Y, int32_t *dev_err, void *stream);
+                    float *Y, int32_t *dev_err, void *workspace, int64_t workspace_bytes,
+                    void *stream);
 
 /*
  * Row gather from a 4-bit table [P1-S2] (the input-embedding use of the same
@@ -294,6 +321,10 @@ int w4_gemv_chain(const w4_chain_mat *desc, int32_t n_mats, const uint16_t *x0, 
  * quoted against ([P1-S3] compares its kernel with a plain sum over memory).
  */
 int w4_probe_stream(const void *buf, int64_t bytes, uint32_t *out, void *stream);
+
+/* Re-reads the settings variables (see Conventions); not to be called while
+ * another host thread is inside an entry point. */
+void w4_reload_settings(void);
 
 /* Static description of a status code. */
 const char *w4_strerror(int status);

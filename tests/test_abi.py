@@ -82,18 +82,19 @@ def test_gather_and_renorm_argument_errors():
 def test_gemm_argument_errors():
     import bit_weight_only_02_amd as w4
     L = w4.lib
+    WS, WSB = FAKE, 1 << 30  # a large enough (never touched) workspace
     for fn, mmax in ((L.w4_gemm_smallM, 16), (L.w4_gemm_prompt, 4096)):
-        # codes, steps, N, K, X, xdt, M, ldx, Y, ldy, stream
-        assert fn(FAKE, FAKE, 64, 64, FAKE, 0, 0, 64, FAKE, 64, None) == -1          # M = 0
-        assert fn(FAKE, FAKE, 64, 64, FAKE, 0, mmax + 1, 64, FAKE, 64, None) == -1   # M too large
-        assert fn(FAKE, FAKE, 64, 48, FAKE, 0, 2, 64, FAKE, 64, None) == -1          # K % 32
-        assert fn(FAKE, FAKE, 64, 64, FAKE, 0, 2, 32, FAKE, 64, None) == -1          # ldx < K
-        assert fn(FAKE, FAKE, 64, 64, FAKE, 0, 2, 64, FAKE, 32, None) == -1          # ldy < N
-        assert fn(FAKE, FAKE, 64, 64, FAKE, 9, 2, 64, FAKE, 64, None) == -3          # dtype
-        assert fn(FAKE, FAKE, 64, 64, FAKE + 1, 0, 2, 64, FAKE, 64, None) == -2      # X alignment
-        assert fn(FAKE, FAKE, 64, 64, FAKE, 0, 2, 64, FAKE + 2, 64, None) == -2      # Y alignment
-        assert fn(FAKE, FAKE, 64, 32768, FAKE, 0, 2, 32768, FAKE, 64, None) == -4    # K too large
-        assert fn(FAKE, FAKE, 0, 64, FAKE, 0, 2, 64, FAKE, 64, None) == 0            # N = 0
+        # codes, steps, N, K, X, xdt, M, ldx, Y, ldy, workspace, workspace_bytes, stream
+        assert fn(FAKE, FAKE, 64, 64, FAKE, 0, 0, 64, FAKE, 64, WS, WSB, None) == -1          # M = 0
+        assert fn(FAKE, FAKE, 64, 64, FAKE, 0, mmax + 1, 64, FAKE, 64, WS, WSB, None) == -1   # M too large
+        assert fn(FAKE, FAKE, 64, 48, FAKE, 0, 2, 64, FAKE, 64, WS, WSB, None) == -1          # K % 32
+        assert fn(FAKE, FAKE, 64, 64, FAKE, 0, 2, 32, FAKE, 64, WS, WSB, None) == -1          # ldx < K
+        assert fn(FAKE, FAKE, 64, 64, FAKE, 0, 2, 64, FAKE, 32, WS, WSB, None) == -1          # ldy < N
+        assert fn(FAKE, FAKE, 64, 64, FAKE, 9, 2, 64, FAKE, 64, WS, WSB, None) == -3          # dtype
+        assert fn(FAKE, FAKE, 64, 64, FAKE + 1, 0, 2, 64, FAKE, 64, WS, WSB, None) == -2      # X alignment
+        assert fn(FAKE, FAKE, 64, 64, FAKE, 0, 2, 64, FAKE + 2, 64, WS, WSB, None) == -2      # Y alignment
+        assert fn(FAKE, FAKE, 64, 32768, FAKE, 0, 2, 32768, FAKE, 64, WS, WSB, None) == -4    # K too large
+        assert fn(FAKE, FAKE, 0, 64, FAKE, 0, 2, 64, FAKE, 64, None, 0, None) == 0            # N = 0
 
 
 def test_grid_packing_argument_errors():
@@ -119,7 +120,8 @@ def test_moe_argument_errors():
         a = dict(ok, **kw)
         return L.w4_moe_gemv_ids(a["cb"], a["sb"], a["sc"], a["ss"], a["N"], a["K"], a["X"], a["dt"],
                                  a["xpp"], a["ldx"], a["ids"], a["T"], a["topk"], a["slot"], a["ne"],
-                                 a["ns"], a["rs"], a["rw"], a["Y"], a["err"], None)
+                                 a["ns"], a["rs"], a["rw"], a["Y"], a["err"], a.get("ws", FAKE),
+                                 a.get("wsb", 1 << 30), None)
     assert call(topk=0) == -1
     assert call(topk=33) == -1
     assert call(T=200) == -4                      # T*topk > 1024
@@ -129,6 +131,45 @@ def test_moe_argument_errors():
     assert call(xpp=2) == -1
     assert call(K=16416, sc=1408 * 16416 // 8, ss=1408 * 16416 // 32, ldx=16416) == -4
     assert call(T=0) == 0
+
+
+def test_workspace_sizes_and_checks():
+    """Workspace queries are host arithmetic; a call whose shape needs a
+    workspace refuses a missing, short or misaligned one before any launch."""
+    import bit_weight_only_02_amd as w4
+    L = w4.lib
+    # the prompt chunk always stages its activations: at least 2*K*M bytes
+    need = L.w4_gemm_prompt_workspace_bytes(24576, 1536, 256)
+    assert need >= 2 * 1536 * 256
+    assert L.w4_gemm_prompt_workspace_bytes(64, 48, 2) == -1        # K % 32
+    assert L.w4_gemm_prompt_workspace_bytes(64, 64, 0) == -1        # M = 0
+    assert L.w4_gemm_smallM_workspace_bytes(64, 64, 17) == -1       # M too large
+    assert L.w4_gemm_smallM_workspace_bytes(0, 64, 8) == 0          # nothing to do
+    assert L.w4_gemm_smallM_workspace_bytes(2048, 1536, 1) == 0     # batch 1: no split
+    assert L.w4_decode_attention_workspace_bytes(8, 512, 131072) >= 256 * 8 * 512 * 4
+    assert L.w4_decode_attention_workspace_bytes(9, 512, 16) == -1
+    # the combined expert product stages T*topk rows of N floats after the counters
+    comb = L.w4_moe_gemv_ids_workspace_bytes(2816, 704, 4, 8, 0, 1, 1)
+    assert comb >= 16384 + 4 * 8 * 2816 * 4
+    assert L.w4_moe_gemv_ids_workspace_bytes(2816, 704, 4, 8, 0, 1, 0) == 0
+    assert L.w4_moe_gemv_ids_workspace_bytes(2816, 704, 4, 8, 7, 1, 0) == -1   # dtype
+    fn = L.w4_gemm_prompt
+    args = (FAKE, FAKE, 24576, 1536, FAKE, 0, 256, 1536, FAKE, 24576)
+    assert fn(*args, None, 0, None) == -1                   # missing
+    assert fn(*args, FAKE, need - 1, None) == -1            # too small
+    assert fn(*args, FAKE + 16, need, None) == -2           # not 256-byte aligned
+
+
+def test_moe_workspace_checks():
+    import bit_weight_only_02_amd as w4
+    L = w4.lib
+    need = L.w4_moe_gemv_ids_workspace_bytes(2816, 704, 1, 8, 1, 1, 1)
+    assert need > 0
+    args = (FAKE, FAKE, 2816 * 704 // 8, 2816 * 704 // 32, 2816, 704, FAKE, 1, 1, 704, FAKE, 1, 8,
+            None, 128, 0, None, FAKE, FAKE, None)
+    assert L.w4_moe_gemv_ids(*args, None, 0, None) == -1
+    assert L.w4_moe_gemv_ids(*args, FAKE, need - 4, None) == -1
+    assert L.w4_moe_gemv_ids(*args, FAKE + 128, need, None) == -2
 
 
 @pytest.mark.skipif(os.path.exists("/dev/kfd"), reason="a GPU is present")

@@ -126,19 +126,19 @@ def test_chain_invalid_descriptor_sets_error_word(w4):
     assert torch.all(torch.isnan(ys[0]))
 
 
-def test_chain_barrier_timeout_is_reported_and_recovers(w4, monkeypatch):
+def test_chain_barrier_timeout_is_reported_and_recovers(w4, w4_settings):
     shapes = [(512, 64), (512, 512), (512, 512)]
     mats = make_mats(shapes, 3)
     ys = [torch.zeros(N, device="cuda") for N, _ in shapes]
     x0 = dev_act(synth.activations(np.random.default_rng(3), 64, F16), F16)
     desc = w4.w4_chain_desc(mats, ys)
     sync = w4.w4_chain_sync(len(shapes))
-    monkeypatch.setenv("W4_CHAIN_SPIN_LIMIT", "0")   # host-forced: every barrier wait gives up
+    w4_settings("W4_CHAIN_SPIN_LIMIT", "0")   # host-forced: every barrier wait gives up
     w4.w4_gemv_chain(desc, x0, sync)
     torch.cuda.synchronize()
     assert sync[2].item() == 1                        # reported, no hang
     assert sync[0].item() == 0
-    monkeypatch.delenv("W4_CHAIN_SPIN_LIMIT")
+    w4_settings("W4_CHAIN_SPIN_LIMIT")
     sync.zero_()
     w4.w4_gemv_chain(desc, x0, sync)
     torch.cuda.synchronize()

@@ -69,11 +69,11 @@ def test_gemm_decode_sweep_shapes(w4, M):
         assert ok, (N, K, M, worst)
 
 
-def test_gemm_split_k_is_deterministic_and_survives_other_calls(w4, monkeypatch):
+def test_gemm_split_k_is_deterministic_and_survives_other_calls(w4, w4_settings):
     """A product split into K-slices and summed by the last slice to arrive:
     bitwise the same on every call, also when expert products (which share the
     library's device buffer) run in between.  (Four rows on the matrix cores.)"""
-    monkeypatch.setenv("W4_SMALLM_ROWS_MAX", "0")
+    w4_settings("W4_SMALLM_ROWS_MAX", "0")
     rng = np.random.default_rng(11)
     N, K, M = 1536, 8192, 4
     codes, steps = synth.w4_matrix(rng, N, K)
@@ -178,9 +178,9 @@ def test_gemm_few_rows_match_batch1_bitwise(w4, M):
         assert y.cpu().numpy().tobytes() == Y[m].tobytes(), m
 
 
-def test_gemm_few_rows_on_the_matrix_cores(w4, monkeypatch):
+def test_gemm_few_rows_on_the_matrix_cores(w4, w4_settings):
     """Two to four rows forced onto the MFMA engine (the path from 5 rows)."""
-    monkeypatch.setenv("W4_SMALLM_ROWS_MAX", "0")
+    w4_settings("W4_SMALLM_ROWS_MAX", "0")
     rng = np.random.default_rng(30)
     for N, K, M in [(2560, 1536, 2), (1536, 2048, 4), (97, 704, 3), (1536, 8192, 4)]:
         codes, steps = synth.w4_matrix(rng, N, K)

@@ -53,9 +53,9 @@ RING_CASES = [(1000, 1536, "16,3,1,8,3,4"), (257, 2048, "16,4,1,8,2,3"),
 
 @pytest.mark.parametrize("dt", [F16, BF16])
 @pytest.mark.parametrize("N,K,tile", RING_CASES)
-def test_gemv_streaming_variant_vs_oracle(w4, monkeypatch, N, K, tile, dt):
+def test_gemv_streaming_variant_vs_oracle(w4, w4_settings, N, K, tile, dt):
     print(f"gemv ring N={N} K={K} tile={tile} dt={dt}", flush=True)
-    monkeypatch.setenv("W4_GEMV_TILE", tile)
+    w4_settings("W4_GEMV_TILE", tile)
     rng = np.random.default_rng(N * 11 + K + dt)
     codes, steps = synth.w4_matrix(rng, N, K)
     x = synth.activations(rng, K, dt)
@@ -65,10 +65,10 @@ def test_gemv_streaming_variant_vs_oracle(w4, monkeypatch, N, K, tile, dt):
     assert ok, f"worst |err|/sum|wx| = {worst}"
 
 
-def test_gemv_streaming_variant_exact_cases(w4, monkeypatch):
+def test_gemv_streaming_variant_exact_cases(w4, w4_settings):
     """Integer inputs (bit-exact), a one-hot subnormal x (bit-exact) and a
     vector too wide for fp16 staging (the exact fp32 path) through the ring."""
-    monkeypatch.setenv("W4_GEMV_TILE", "16,4,1,8,2,4")
+    w4_settings("W4_GEMV_TILE", "16,4,1,8,2,4")
     rng = np.random.default_rng(14)
     N, K = 300, 2048
     codes, _ = synth.w4_matrix(rng, N, K)
@@ -82,7 +82,7 @@ def test_gemv_streaming_variant_exact_cases(w4, monkeypatch):
     y = run_gemv(w4, codes, steps, x, F16)
     yo, _ = oracle.gemv(codes, steps, N, K, x, F16)
     assert np.array_equal(y.astype(np.float64), yo)
-    monkeypatch.setenv("W4_GEMV_TILE", "16,3,1,8,2,5")
+    w4_settings("W4_GEMV_TILE", "16,3,1,8,2,5")
     N, K = 129, 1536
     codes, steps = synth.w4_matrix(rng, N, K)
     v = rng.normal(0, 1, K)
@@ -199,12 +199,12 @@ def test_gemv_k_zero_writes_zeros(w4):
     assert torch.all(y == 0)
 
 
-def test_gemv_failed_launch_leaves_poisoned_output(w4, monkeypatch):
+def test_gemv_failed_launch_leaves_poisoned_output(w4, w4_settings):
     rng = np.random.default_rng(8)
     codes, steps = synth.w4_matrix(rng, 16, 64)
     x = synth.activations(rng, 64, F16)
     y = torch.full((16,), float("nan"), device="cuda")
-    monkeypatch.setenv("W4_FORCE_LAUNCH_ERROR", "1")
+    w4_settings("W4_FORCE_LAUNCH_ERROR", "1")
     with pytest.raises(w4.W4Error) as e:
         w4.w4_gemv(dev_codes(codes), dev_steps(steps), dev_act(x, F16), y)
     assert e.value.status == w4.W4_ERR_HIP

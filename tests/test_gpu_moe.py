@@ -74,10 +74,10 @@ def test_moe_small_vs_oracle_and_pool_identity(w4, T, topk, xpp, dt):
         assert ok, worst
 
 
-def test_moe_few_tokens_on_the_matrix_engine(w4, monkeypatch):
+def test_moe_few_tokens_on_the_matrix_engine(w4, w4_settings):
     """Four tokens forced onto the matrix engine (the path of larger batches):
     the same parity and pool identity as the default matrix-vector path."""
-    monkeypatch.setenv("W4_MOE_PAIRS_MAX_T", "0")
+    w4_settings("W4_MOE_PAIRS_MAX_T", "0")
     test_moe_small_vs_oracle_and_pool_identity(w4, 4, 8, 1, F16)
     test_moe_small_vs_oracle_and_pool_identity(w4, 1, 8, 0, BF16)
 

@@ -67,6 +67,8 @@ _SIGNATURES = {
                             _P],
     "w4_moe_gemv_ids": [_P, _P, _I64, _I64, _I32, _I32, _P, _I32, _I32, _I64, _P, _I32, _I32,
                         _P, _I32, _I32, _P, _P, _P, _P, _P, _I64, _P],
+    "w4_moe_gemv_ids_noalloc": [_P, _P, _I64, _I64, _I32, _I32, _P, _I32, _I32, _I64, _P, _I32, _I32,
+                                _P, _I32, _I32, _P, _P, _P, _P, _P],
     "w4_embed_gather": [_P, _P, _I32, _I32, _P, _I32, _P, _P, _P],
     "w4_rms_renorm": [_P, _I64, _I32, _I32, _P, _I64, _I32, _P],
     "w4_gemv_chain": [_P, _I32, _P, _P, _I64, _P],
@@ -301,6 +303,31 @@ def w4_moe_gemv_ids(codes_base, steps_base, expert_stride_codes, expert_stride_s
                                _ptr(route_w), _ptr(Y), _ptr(dev_err), ws, wsb, _stream(stream)),
            "w4_moe_gemv_ids")
     return Y
+
+
+def w4_moe_gemv_ids_noalloc(codes_base, steps_base, expert_stride_codes, expert_stride_steps, N, K,
+                            X, ids, x_per_pair=False, slot_of=None, n_experts=None, n_slots=0,
+                            row_scale=None, route_w=None, Y=None, dev_err=None, stream=None):
+    """w4_moe_gemv_ids whose scratch is the library's fixed per-GPU array
+    (nothing is allocated; overlapping calls on one GPU race)."""
+    T, topk = ids.shape
+    if n_experts is None:
+        raise ValueError("n_experts is required")
+    if X.dim() != 2 or X.stride(1) != 1:
+        raise ValueError("X must be 2-D with unit column stride")
+    if Y is None:
+        raise ValueError("Y is required (this entry point is for callers that allocate nothing)")
+    xdt = W4_F32_RMS if X.dtype == torch.float32 else _act_dtype(X)
+    _check(lib.w4_moe_gemv_ids_noalloc(_ptr(codes_base), _ptr(steps_base), expert_stride_codes,
+                                       expert_stride_steps, N, K, _ptr(X), xdt,
+                                       1 if x_per_pair else 0, X.stride(0), _ptr(ids), T, topk,
+                                       _ptr(slot_of), n_experts, n_slots, _ptr(row_scale),
+                                       _ptr(route_w), _ptr(Y), _ptr(dev_err), _stream(stream)),
+           "w4_moe_gemv_ids_noalloc")
+    return Y
+
+
+W4_NOALLOC_SCRATCH_BYTES = 8 << 20
 
 
 def w4_embed_gather(codes, steps, ids, out=None, dev_err=None, stream=None):

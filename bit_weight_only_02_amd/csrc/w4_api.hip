@@ -85,6 +85,35 @@ size_t moe_ws_bytes(int32_t N, int32_t K, int32_t T, int32_t topk, int32_t xdt, 
     return b ? w4::kWsCounterBytes + b : 0;
 }
 
+// Scratch of w4_moe_gemv_ids_noalloc: a fixed array in the library's device
+// image.  Each GPU the library runs on holds its own copy, at its own address,
+// until the process ends.  In host code `scratch` names a host-side stand-in,
+// not device memory: its device address is looked up once per device, with
+// that device current, and only that address is ever handed to a kernel.
+// Calls that share the array on one GPU must not overlap.
+static __device__ __align__(256) unsigned char scratch[W4_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_address(void **out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(W4_ERR_NODEV, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(W4_ERR_UNSUPPORTED, "device index %d", dev);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(W4_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return W4_OK;
+}
+
 // Settings: two copies, the current one published through an atomic pointer.
 std::mutex g_settings_mu;
 w4::Settings g_settings_buf[2];
@@ -317,14 +346,18 @@ int w4_rms_renorm(const float *v, int64_t ldv, int32_t K, int32_t rows, void *ou
                     "w4_rms_renorm");
 }
 
-int w4_moe_gemv_ids(const uint32_t *codes_base, const uint16_t *steps_base,
-                    int64_t expert_stride_codes, int64_t expert_stride_steps,
-                    int32_t N, int32_t K,
-                    const void *X, int32_t xdt, int32_t x_per_pair, int64_t ldx,
-                    const int32_t *ids, int32_t T, int32_t topk,
-                    const int32_t *slot_of, int32_t n_experts, int32_t n_slots,
-                    const float *row_scale, const float *route_w,
-                    float *Y, int32_t *dev_err, void *workspace, int64_t workspace_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// The expert product behind both of its entry points.  `noalloc`: the scratch
+// is the library's fixed per-device array (`workspace` is ignored).
+int moe_call(const uint32_t *codes_base, const uint16_t *steps_base, int64_t expert_stride_codes,
+             int64_t expert_stride_steps, int32_t N, int32_t K, const void *X, int32_t xdt, int32_t x_per_pair,
+             int64_t ldx, const int32_t *ids, int32_t T, int32_t topk, const int32_t *slot_of,
+             int32_t n_experts, int32_t n_slots, const float *row_scale, const float *route_w, float *Y,
+             int32_t *dev_err, void *workspace, int64_t workspace_bytes, bool noalloc, void *stream) {
+    const char *name = noalloc ? "w4_moe_gemv_ids_noalloc" : "w4_moe_gemv_ids";
     int st;
     if ((st = check_matrix(codes_base, steps_base, N, K))) return st;
     if (xdt != W4_F32_RMS && (st = check_dtype(xdt))) return st;
@@ -351,11 +384,23 @@ int w4_moe_gemv_ids(const uint32_t *codes_base, const uint16_t *steps_base,
     // the engine's part, as fp16 rows of K (16-byte aligned)
     size_t xoff = 0;
     const size_t ws_need = moe_ws_bytes(N, K, T, topk, xdt, x_per_pair, route_w != nullptr, &xoff);
-    if ((st = check_workspace(workspace, workspace_bytes, ws_need))) return st;
+    if (noalloc) {
+        if (ws_need > (size_t)W4_NOALLOC_SCRATCH_BYTES)
+            return fail(W4_ERR_UNSUPPORTED, "this call needs %zu bytes of scratch, beyond the fixed %d of %s",
+                        ws_need, (int)W4_NOALLOC_SCRATCH_BYTES, name);
+    } else if ((st = check_workspace(workspace, workspace_bytes, ws_need))) {
+        return st;
+    }
     if ((st = device_ready())) return st;
     if (forced_launch_error()) return fail(W4_ERR_HIP, "forced launch error (test hook)");
+    void *ws = nullptr;
+    if (ws_need) {
+        if (!noalloc)
+            ws = workspace;
+        else if ((st = scratch_address(&ws)))
+            return st;
+    }
     hipStream_t s = static_cast<hipStream_t>(stream);
-    void *ws = ws_need ? workspace : nullptr;
     const int xrows = x_per_pair ? T * topk : T;
     const bool pre_rms = xdt == W4_F32_RMS && !w4::moe_by_pairs(T);
     const void *Xk = X;
@@ -364,7 +409,7 @@ int w4_moe_gemv_ids(const uint32_t *codes_base, const uint16_t *steps_base,
     if (pre_rms) {
         uint16_t *xr = reinterpret_cast<uint16_t *>(static_cast<char *>(ws) + w4::kWsCounterBytes + xoff);
         hipError_t e = w4::launch_rms_renorm(static_cast<const float *>(X), ldx, K, xrows, xr, K, W4_F16, s);
-        if (e != hipSuccess) return launched(e, "w4_moe_gemv_ids");
+        if (e != hipSuccess) return launched(e, name);
         Xk = xr;
         ldk = K;
         dtk = W4_F16;
@@ -373,7 +418,37 @@ int w4_moe_gemv_ids(const uint32_t *codes_base, const uint16_t *steps_base,
                                    N, K, static_cast<const uint16_t *>(Xk), ldk, dtk, x_per_pair, ids,
                                    T, topk, slot_of, n_experts, n_slots, row_scale, route_w, Y,
                                    ws, dev_err, s),
-                    "w4_moe_gemv_ids");
+                    name);
+}
+
+}  // namespace
+
+extern "C" {
+
+int w4_moe_gemv_ids(const uint32_t *codes_base, const uint16_t *steps_base,
+                    int64_t expert_stride_codes, int64_t expert_stride_steps,
+                    int32_t N, int32_t K,
+                    const void *X, int32_t xdt, int32_t x_per_pair, int64_t ldx,
+                    const int32_t *ids, int32_t T, int32_t topk,
+                    const int32_t *slot_of, int32_t n_experts, int32_t n_slots,
+                    const float *row_scale, const float *route_w,
+                    float *Y, int32_t *dev_err, void *workspace, int64_t workspace_bytes, void *stream) {
+    return moe_call(codes_base, steps_base, expert_stride_codes, expert_stride_steps, N, K, X, xdt, x_per_pair,
+                    ldx, ids, T, topk, slot_of, n_experts, n_slots, row_scale, route_w, Y, dev_err, workspace,
+                    workspace_bytes, false, stream);
+}
+
+int w4_moe_gemv_ids_noalloc(const uint32_t *codes_base, const uint16_t *steps_base,
+                            int64_t expert_stride_codes, int64_t expert_stride_steps,
+                            int32_t N, int32_t K,
+                            const void *X, int32_t xdt, int32_t x_per_pair, int64_t ldx,
+                            const int32_t *ids, int32_t T, int32_t topk,
+                            const int32_t *slot_of, int32_t n_experts, int32_t n_slots,
+                            const float *row_scale, const float *route_w,
+                            float *Y, int32_t *dev_err, void *stream) {
+    return moe_call(codes_base, steps_base, expert_stride_codes, expert_stride_steps, N, K, X, xdt, x_per_pair,
+                    ldx, ids, T, topk, slot_of, n_experts, n_slots, row_scale, route_w, Y, dev_err, nullptr, 0,
+                    true, stream);
 }
 
 int w4_gemv_chain(const w4_chain_mat *desc, int32_t n_mats, const uint16_t *x0, void *sync,

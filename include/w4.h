@@ -48,7 +48,8 @@
  *
  * Conventions:
  *   - All array pointers are DEVICE pointers owned by the caller.  The library
- *     allocates, frees and synchronises nothing.
+ *     allocates, frees and synchronises nothing (w4_moe_gemv_ids_noalloc keeps
+ *     its scratch in a fixed array of the library's device image).
  *   - Workspaces.  w4_gemm_smallM, w4_gemm_prompt, w4_decode_attention and
  *     w4_moe_gemv_ids need device memory beyond their inputs and outputs
  *     (partial sums, staged activations, per-split partials).  The caller owns
@@ -75,7 +76,8 @@
  *     Every product output satisfies |y - y_exact| <= 1e-3 * sum_k |w(n,k) x_k|.
  *   - Thread safety: entry points may be called from several host threads and
  *     streams at once, each call with its own workspace (see above); a chain's
- *     sync buffer is shared by the calls that use it, which must not overlap.
+ *     sync buffer and w4_moe_gemv_ids_noalloc's scratch are shared by the
+ *     calls that use them, which must not overlap.
  *   - Settings: five environment variables are read once per process (and
  *     again by w4_reload_settings): W4_GEMV_TILE (a tile override of the
  *     batch-1 product), W4_SMALLM_ROWS_MAX and W4_MOE_PAIRS_MAX_T (up to how
@@ -252,6 +254,30 @@ int w4_moe_gemv_ids(const uint32_t *codes_base, const uint16_t *steps_base,
                     const float *row_scale, const float *route_w,
                     float *Y, int32_t *dev_err, void *workspace, int64_t workspace_bytes,
                     void *stream);
+
+/*
+ * The expert-indexed product for callers that cannot allocate device memory
+ * (code under graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): w4_moe_gemv_ids with the same arguments and results (the same
+ * kernels, bit for bit), but its scratch is a fixed array of
+ * W4_NOALLOC_SCRATCH_BYTES in the library's device image, one per GPU, held
+ * until the process ends; no call allocates, frees or synchronises.  A call
+ * whose shape needs more scratch than that (w4_moe_gemv_ids_workspace_bytes)
+ * returns W4_ERR_UNSUPPORTED before enqueuing anything.  Every call on a GPU
+ * shares that GPU's array, so calls on one GPU that may overlap (several
+ * streams or host threads) race and must be serialised by the caller.  No
+ * part of the array needs to start at zero: the kernels write every value
+ * they later read within the same call.
+ */
+#define W4_NOALLOC_SCRATCH_BYTES (8 << 20)
+int w4_moe_gemv_ids_noalloc(const uint32_t *codes_base, const uint16_t *steps_base,
+                            int64_t expert_stride_codes, int64_t expert_stride_steps,
+                            int32_t N, int32_t K,
+                            const void *X, int32_t xdt, int32_t x_per_pair, int64_t ldx,
+                            const int32_t *ids, int32_t T, int32_t topk,
+                            const int32_t *slot_of, int32_t n_experts, int32_t n_slots,
+                            const float *row_scale, const float *route_w,
+                            float *Y, int32_t *dev_err, void *stream);
 
 /*
  * Row gather from a 4-bit table [P1-S2] (the input-embedding use of the same

@@ -307,49 +307,79 @@ void w4o_rms_renorm(const float *v, int64_t K, int out_dtype, uint16_t *out) {
 }
 
 /*
- * Grid packing of a 16-bit table [P1-S2]: the page's 4-bit tables were trained
- * onto a grid of at most 16 levels per group of 32 and are stored as codes with
- * each group's step recovered from the grid; how the step is found is not on
- * the page.  Reading taken: per group, in fp32 arithmetic,
- *   an  = the largest magnitude among negative values (0 if none),
- *   ap  = the largest positive value (0 if none);
- *   s   = an > ap ? an / 8 : ap / 7, so that the extreme value gets code 0
- *         (an extreme -8 steps) or 15 (+7 steps; a tie means a grid without
- *         code 0, whose positive extreme is 7 steps);
- *   step = s rounded to bf16 (nearest, ties to even); sf = step as a float;
- *   code = 8 for every value when sf == 0, else clamp(rint(q) + 8, 0, 15),
- *          where q = v * r with r = 1 / sf (correctly rounded, once per
- *          group): the quotient within about an ulp, the same in any IEEE
- *          fp32 implementation, and rint rounding ties to even.
- * On a table whose groups hold exact grid values (c - 8) * step that use code 0
- * or 15, this gives back those codes and steps.  Values must be finite.
+ * Grid packing of a 16-bit table [P1-S2] (the conversion behind the 4-bit
+ * tables).  The page reports that the 16-bit tables were trained onto a 4-bit
+ * grid -- every group of 32 holds at most 16 distinct values -- and that the
+ * 4-bit tables hold codes with each group's step recovered from that grid;
+ * nearly every stored value then equals its 16-bit source, and the rest are
+ * off by a small fraction of a step.  How the step is recovered is not on the
+ * page.  Reading taken, per group of 32 values v (bf16, finite):
+ *   an = the largest magnitude among negative values (0 if none),
+ *   ap = the largest positive value (0 if none);
+ *   all zero: step 0 and code 8 everywhere.
+ *   Otherwise the step is the grid's own: the largest bf16 value s > 0 for
+ *   which every v is m * s with m an integer in [-8, 7].  Such an s puts the
+ *   negative extreme -an at some level -j, j = 1..8 (or, with no negative
+ *   value, ap at a level i = 1..7), so the candidates are an / j (ap / i) in
+ *   that order, largest first, and each counts only if it is a bf16 value.
+ *   When no candidate fits (values not on any such grid), the step comes from
+ *   the extreme: s = an / 8 if an > ap (the negative extreme at code 0), else
+ *   ap / 7 (the positive extreme at code 15), rounded to bf16 (ties to even).
+ *   code = clamp(rint(v / s) + 8, 0, 15), with the exact quotient v / s and
+ *   rint rounding halves to even.
+ * The quotient is taken in fp64: v and s carry 8 significant bits each, so a
+ * quotient that is not a half-integer lies at least 2^-12 of its size away
+ * from one, far beyond fp64's rounding, and rint decides as on the exact
+ * value.  On exact grid values this returns every value exactly (the codes of
+ * the coarsest such grid); elsewhere each value in the grid's range is within
+ * half a step.
  */
+static double w4o_bf16_round(double x) { return w4o_bf16_to_f64(w4o_f64_to_bf16_rne(x)); }
+
+/* every v[k] equal to m * s with m an integer in [-8, 7] */
+static int w4o_on_grid(const double *v, double s) {
+    for (int k = 0; k < 32; ++k) {
+        const double m = v[k] / s;
+        if (m != floor(m) || m < -8.0 || m > 7.0) return 0;
+    }
+    return 1;
+}
+
 void w4o_grid_to_codes(const uint16_t *table, int64_t N, int64_t K, uint32_t *codes,
                        uint16_t *steps) {
     const int64_t G = K / 32;
     for (int64_t n = 0; n < N; ++n) {
         for (int64_t g = 0; g < G; ++g) {
-            const uint16_t *v = table + n * K + g * 32;
-            float an = 0.0f, ap = 0.0f;
+            double v[32];
+            double an = 0.0, ap = 0.0;
             for (int k = 0; k < 32; ++k) {
-                const float x = (float)w4o_bf16_to_f64(v[k]);
-                if (-x > an) an = -x;
-                if (x > ap) ap = x;
+                v[k] = w4o_bf16_to_f64(table[n * K + g * 32 + k]);
+                if (-v[k] > an) an = -v[k];
+                if (v[k] > ap) ap = v[k];
             }
-            const float s = an > ap ? an / 8.0f : ap / 7.0f;
-            const uint16_t sb = w4o_f64_to_bf16_rne((double)s);
-            const float sf = (float)w4o_bf16_to_f64(sb);
-            steps[n * G + g] = sb;
-            const float r = sf != 0.0f ? 1.0f / sf : 0.0f;
+            double step = 0.0;
+            if (an > 0.0 || ap > 0.0) {
+                const double e = an > 0.0 ? an : ap;
+                const int jmax = an > 0.0 ? 8 : 7;
+                int found = 0;
+                for (int j = 1; j <= jmax && !found; ++j) {
+                    const double s = e / j;
+                    if (w4o_bf16_round(s) != s || s * j != e) continue;
+                    if (w4o_on_grid(v, s)) {
+                        step = s;
+                        found = 1;
+                    }
+                }
+                if (!found) step = w4o_bf16_round(an > ap ? an / 8.0 : ap / 7.0);
+            }
+            steps[n * G + g] = w4o_f64_to_bf16_rne(step);
             for (int w = 0; w < 4; ++w) {
                 uint32_t word = 0;
                 for (int j = 0; j < 8; ++j) {
                     int c = 8;
-                    if (sf != 0.0f) {
-                        const float x = (float)w4o_bf16_to_f64(v[8 * w + j]);
-                        float q = x * r;
-                        q = rintf(q) + 8.0f;
-                        q = q < 0.0f ? 0.0f : (q > 15.0f ? 15.0f : q);
+                    if (step != 0.0) {
+                        double q = nearbyint(v[8 * w + j] / step) + 8.0;
+                        q = q < 0.0 ? 0.0 : (q > 15.0 ? 15.0 : q);
                         c = (int)q;
                     }
                     word |= (uint32_t)c << (4 * j);

@@ -26,10 +26,18 @@ MUTANTS = {
     "route_weight_dropped": ("Y[t * N + n] += r * v;", "Y[t * N + n] += v;"),
     "rms_over_k_minus_1": ("sqrt(ss / (double)K)", "sqrt(ss / (double)(K - 1))"),
     "x_index_per_pair_ignored": ("(x_per_pair ? (t * topk + j) : t)", "(t)"),
-    "grid_step_always_eighth": ("an > ap ? an / 8.0f : ap / 7.0f", "an > ap ? an / 8.0f : ap / 8.0f"),
-    "grid_tie_to_negative": ("an > ap ? an / 8.0f", "an >= ap ? an / 8.0f"),
-    "grid_clamp_upper_14": ("(q > 15.0f ? 15.0f : q)", "(q > 14.0f ? 14.0f : q)"),
-    "grid_truncates": ("q = rintf(q) + 8.0f;", "q = truncf(q) + 8.0f;"),
+    "grid_step_always_eighth": ("an > ap ? an / 8.0 : ap / 7.0", "an > ap ? an / 8.0 : ap / 8.0"),
+    "grid_tie_to_negative": ("an > ap ? an / 8.0", "an >= ap ? an / 8.0"),
+    "grid_clamp_upper_14": ("(q > 15.0 ? 15.0 : q)", "(q > 14.0 ? 14.0 : q)"),
+    "grid_truncates": ("nearbyint(v[8 * w + j] / step)", "trunc(v[8 * w + j] / step)"),
+    # the quotient as the fp32 product with the step's reciprocal
+    "grid_reciprocal_fp32": ("nearbyint(v[8 * w + j] / step)",
+                             "nearbyint((double)((float)v[8 * w + j] * (1.0f / (float)step)))"),
+    # no search for the group's own grid: always the extreme rule
+    "grid_extreme_rule_only": ("j <= jmax && !found", "j <= 0 && !found"),
+    # the finest grid that holds the group instead of the coarsest
+    "grid_finest_not_coarsest": ("for (int j = 1; j <= jmax && !found; ++j)",
+                                 "for (int j = jmax; j >= 1 && !found; --j)"),
 }
 
 

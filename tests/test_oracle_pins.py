@@ -445,11 +445,22 @@ def test_gbps_formula_reproduces_the_pages_figures():
 
 # --- grid packing of a 16-bit table ----------------------------------------------
 
+def _pack_words(c):
+    """codes [N, K] in 0..15 -> packed uint32 words [N, K/8] (nibble j = column 8w+j)."""
+    N, K = c.shape
+    codes = np.zeros((N, K // 8), dtype=np.uint32)
+    for j in range(8):
+        codes |= (c[:, j::8].astype(np.uint32) << np.uint32(4 * j))
+    return codes
+
+
 def _grid_table(rng, N, K):
     """Codes and 5-bit-significand positive bf16 steps (so every (c - 8) * step
     is exact in bf16), with each group holding code 0 or 15 at a random place
-    (and, for the second kind, no code 0); the table is the oracle's exact
-    dequantisation rounded (exactly) to bf16."""
+    (and, for the second kind, no code 0) and codes 7 and 8 next to each other
+    (so the group's levels share no common factor: its own grid is the
+    coarsest one); the table is the oracle's exact dequantisation rounded
+    (exactly) to bf16."""
     G = K // 32
     c = rng.integers(0, 16, size=(N, K), dtype=np.int64)
     use15 = rng.random((N, G)) < 0.5
@@ -458,12 +469,12 @@ def _grid_table(rng, N, K):
             grp = c[n, 32 * g:32 * g + 32]
             if use15[n, g]:
                 grp[grp == 0] = 1
-                grp[rng.integers(0, 32)] = 15
+                p = rng.permutation(32)[:3]
+                grp[p] = (15, 7, 8)
             else:
-                grp[rng.integers(0, 32)] = 0
-    codes = np.zeros((N, K // 8), dtype=np.uint32)
-    for j in range(8):
-        codes |= (c[:, j::8].astype(np.uint32) << np.uint32(4 * j))
+                p = rng.permutation(32)[:3]
+                grp[p] = (0, 7, 8)
+    codes = _pack_words(c)
     exp = rng.integers(100, 140, size=(N, G), dtype=np.uint16)
     mant = (rng.integers(0, 16, size=(N, G), dtype=np.uint16) << 3)
     steps = ((exp << 7) | mant).astype(np.uint16)         # positive, low 3 mantissa bits zero
@@ -473,9 +484,62 @@ def _grid_table(rng, N, K):
     return codes, steps, table
 
 
+def _sparse_grid_table(rng, N, K):
+    """Exact grid groups that use a random subset of levels -- often without
+    code 0 or 15, sometimes only even levels or only a few -- plus a few
+    all-positive and all-negative groups.  Returns the table bits."""
+    G = K // 32
+    c = np.zeros((N, K), dtype=np.int64)
+    for n in range(N):
+        for g in range(G):
+            kind = rng.integers(0, 5)
+            if kind == 0:
+                levels = rng.choice(np.arange(-5, 6), size=rng.integers(2, 6), replace=False)
+            elif kind == 1:
+                levels = 2 * rng.choice(np.arange(-4, 4), size=rng.integers(2, 5), replace=False)
+            elif kind == 2:
+                levels = np.array([0, 2, 5]) * rng.choice([-1, 1])
+            elif kind == 3:
+                levels = rng.choice(np.arange(1, 8), size=rng.integers(1, 4), replace=False)
+            else:
+                levels = -rng.choice(np.arange(1, 9), size=rng.integers(1, 4), replace=False)
+            c[n, 32 * g:32 * g + 32] = rng.choice(levels, size=32) + 8
+    codes = _pack_words(c)
+    exp = rng.integers(100, 140, size=(N, G), dtype=np.uint16)
+    steps = ((exp << 7) | (rng.integers(0, 16, size=(N, G), dtype=np.uint16) << 3)).astype(np.uint16)
+    W = oracle.dequant(codes, steps, N, K)
+    table = np.array([oracle.f64_to_bf16(v) for v in W.ravel()], dtype=np.uint16).reshape(N, K)
+    assert np.array_equal(oracle.act_to_f64(table.ravel(), BF16).reshape(N, K), W)
+    return table
+
+
+def _coarsest_grid_step(vals):
+    """The largest s = a bf16 value > 0 with every value m * s, m an integer in
+    [-8, 7], by exact rational arithmetic over every candidate the group's
+    extremes allow (None if there is none)."""
+    from fractions import Fraction
+    fv = [Fraction(float(v)) for v in vals]
+    neg = [-v for v in fv if v < 0]
+    pos = [v for v in fv if v > 0]
+    cands = set()
+    if neg:
+        cands |= {max(neg) / j for j in range(1, 9)}
+    if pos:
+        cands |= {max(pos) / i for i in range(1, 8)}
+    best = None
+    for s in cands:
+        if float(s) == 0.0 or Fraction(oracle.bf16_to_f64(oracle.f64_to_bf16(float(s)))) != s:
+            continue
+        ms = [v / s for v in fv]
+        if all(m.denominator == 1 and -8 <= m <= 7 for m in ms):
+            best = s if best is None or s > best else best
+    return best
+
+
 def test_grid_packing_round_trips_exact_grids():
-    """A table whose groups are exact grid values using code 0 or 15 packs back
-    into exactly the codes and steps it came from."""
+    """A table whose groups are exact grid values using code 0 or 15, with two
+    neighbouring levels, packs back into exactly the codes and steps it came
+    from."""
     rng = np.random.default_rng(31)
     N, K = 9, 96
     codes, steps, table = _grid_table(rng, N, K)
@@ -484,23 +548,93 @@ def test_grid_packing_round_trips_exact_grids():
     assert np.array_equal(c2, codes)
 
 
+def test_grid_packing_recovers_grids_without_extreme_codes():
+    """Groups whose levels stop short of code 0 or 15 (or use every other level,
+    or lie on one side of zero) come back value for value, on the coarsest
+    grid that holds them: the step is the largest one an exact rational search
+    over the group's candidates finds."""
+    rng = np.random.default_rng(33)
+    N, K = 12, 256
+    table = _sparse_grid_table(rng, N, K)
+    codes, steps = oracle.grid_to_codes(table, N, K)
+    v = oracle.act_to_f64(table.ravel(), BF16).reshape(N, K)
+    W = oracle.dequant(codes, steps, N, K)
+    assert np.array_equal(W, v)                                   # every value back exactly
+    sf = oracle.act_to_f64(steps.ravel(), BF16).reshape(N, K // 32)
+    for n in range(N):
+        for g in range(K // 32):
+            best = _coarsest_grid_step(v[n, 32 * g:32 * g + 32])
+            assert best is not None and float(best) == sf[n, g], (n, g)
+
+
+def test_grid_packing_golden_ties():
+    """Half-step values on an exact division (tests/golden/grid_ties.txt, each
+    case derived with exact rationals) take the even code, also where the
+    fp32 product with the step's reciprocal lands on the other side."""
+    rows = []
+    for line in open(os.path.join(os.path.dirname(__file__), "golden", "grid_ties.txt")):
+        if line.startswith("#") or not line.strip():
+            continue
+        vb, sb, _, code = line.split()
+        rows.append((int(vb, 16), int(sb, 16), int(code)))
+    assert len(rows) >= 10
+    # one group per case: -8 steps (the negative extreme sets the step; no
+    # coarser grid holds the half-step value), the value, zeros elsewhere
+    t = np.zeros((len(rows), 32), dtype=np.uint16)
+    for i, (vb, sb, _) in enumerate(rows):
+        t[i, 0] = oracle.f64_to_bf16(-8.0 * oracle.bf16_to_f64(sb))
+        t[i, 5] = vb
+    codes, steps = oracle.grid_to_codes(t, len(rows), 32)
+    for i, (vb, sb, code) in enumerate(rows):
+        assert int(steps[i, 0]) == sb
+        assert oracle.code(codes, 32, i, 5) == code, (hex(vb), hex(sb))
+        assert oracle.code(codes, 32, i, 0) == 0
+
+
 def test_grid_packing_closed_forms():
     # all zeros: step 0 and code 8 everywhere
     c, s = oracle.grid_to_codes(np.zeros((1, 32), dtype=np.uint16), 1, 32)
     assert s[0, 0] == 0 and np.all(c == 0x88888888)
-    # +a and -a both present: a grid without code 0, whose step is a / 7
+    # +a and -a alone: the coarsest grid is a itself, levels -1 and +1
     a = 7 * 0.125
     t = np.zeros((1, 32), dtype=np.uint16)
     t[0, 3] = oracle.f64_to_bf16(a)
     t[0, 9] = oracle.f64_to_bf16(-a)
     c, s = oracle.grid_to_codes(t, 1, 32)
-    assert oracle.bf16_to_f64(int(s[0, 0])) == 0.125
-    assert oracle.code(c, 32, 0, 3) == 15 and oracle.code(c, 32, 0, 9) == 1
-    # a strictly larger negative extreme: step = |min| / 8, the extreme gets code 0
+    assert oracle.bf16_to_f64(int(s[0, 0])) == a
+    assert oracle.code(c, 32, 0, 3) == 9 and oracle.code(c, 32, 0, 9) == 7
+    # 0.875 and -1.0: only the grid of 0.125 holds both (levels 7 and -8)
     t[0, 9] = oracle.f64_to_bf16(-1.0)
     c, s = oracle.grid_to_codes(t, 1, 32)
     assert oracle.bf16_to_f64(int(s[0, 0])) == 0.125 and oracle.code(c, 32, 0, 9) == 0
     assert oracle.code(c, 32, 0, 3) == 15   # 0.875 / 0.125 = 7
+    # values off every grid: the extreme rule (a larger negative extreme is
+    # 8 steps below zero, otherwise the positive extreme is 7 steps above)
+    t = np.zeros((1, 32), dtype=np.uint16)
+    t[0, 0] = oracle.f64_to_bf16(-1.0)
+    t[0, 1] = oracle.f64_to_bf16(0.3)
+    c, s = oracle.grid_to_codes(t, 1, 32)
+    assert oracle.bf16_to_f64(int(s[0, 0])) == 0.125
+    assert oracle.code(c, 32, 0, 1) == 10                   # 0.3 / 0.125 = 2.4
+    t[0, 0] = oracle.f64_to_bf16(-0.3)
+    t[0, 1] = oracle.f64_to_bf16(1.0)
+    c, s = oracle.grid_to_codes(t, 1, 32)
+    assert oracle.bf16_to_f64(int(s[0, 0])) == oracle.bf16_to_f64(oracle.f64_to_bf16(1.0 / 7.0))
+    assert oracle.code(c, 32, 0, 1) == 15
+    # equal extremes off every grid: the positive one is 7 steps up, so both
+    # extremes stay inside the range (codes 15 and 1)
+    t[0, 0] = oracle.f64_to_bf16(-1.0)
+    t[0, 2] = oracle.f64_to_bf16(0.3)
+    c, s = oracle.grid_to_codes(t, 1, 32)
+    assert oracle.bf16_to_f64(int(s[0, 0])) == oracle.bf16_to_f64(oracle.f64_to_bf16(1.0 / 7.0))
+    assert oracle.code(c, 32, 0, 1) == 15 and oracle.code(c, 32, 0, 0) == 1
+    # a grid of bf16 subnormals: step 2^-133 * 3, levels -8..7 exact
+    sub = 3 * 2.0 ** -133
+    t = np.array([[oracle.f64_to_bf16(((k % 16) - 8) * sub) for k in range(32)]], dtype=np.uint16)
+    assert all(oracle.bf16_to_f64(int(b)) == ((k % 16) - 8) * sub for k, b in enumerate(t[0]))
+    c, s = oracle.grid_to_codes(t, 1, 32)
+    assert oracle.bf16_to_f64(int(s[0, 0])) == sub
+    assert all(oracle.code(c, 32, 0, k) == k % 16 for k in range(32))
 
 
 def test_grid_packing_error_bound_on_arbitrary_tables():
@@ -517,7 +651,7 @@ def test_grid_packing_error_bound_on_arbitrary_tables():
     sf = np.repeat(oracle.act_to_f64(steps.ravel(), BF16).reshape(N, K // 32), 32, axis=1)
     err = np.abs(W - v)
     inside = (v / sf >= -8.5) & (v / sf <= 7.5)
-    assert np.all(err[inside] <= 0.5 * sf[inside] * (1 + 2 ** -20))
+    assert np.all(err[inside] <= 0.5 * sf[inside])
     assert np.all(err <= 1.05 * sf)
 
 

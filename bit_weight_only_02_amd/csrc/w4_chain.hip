@@ -21,12 +21,20 @@
 // only after that), so it clears its own cells of step s-2; the last
 // workgroup out clears the last region that was read.
 //
+// Renormalisation as an output scale.  Matrix i > 0 multiplies the leading K
+// entries u of the previous output divided by their RMS r; since
+// W (u / r) = (W u) / r, the products run on u itself and each finished
+// output is multiplied by 1/r, so no step waits for r before its dot
+// products.  u goes to fp16 one group of 32 at a time, each group scaled by
+// its own power of two (its largest magnitude lands in [2^14, 2^15)), and the
+// group's partial sums are scaled back by the inverse power of two with the
+// group's step; r comes from fp32 sums of squares taken in a fixed order.
+//
 // Per step i (one workgroup of eight waves per CU; workgroup b owns the
 // contiguous row block [b*ceil(N/nwg), ...) of every matrix):
 //   1. input: x0 for the first matrix; else waves 0..3 read the leading K
-//      cells of step i-1 (agent-coherent loads), the workgroup takes their sum
-//      of squares in fp64 in the fixed order of w4_rms_renorm and writes
-//      u / rms rounded to fp16 into LDS (bit for bit what w4_rms_renorm gives);
+//      cells of step i-1 (agent-coherent loads), write each group as fp16
+//      with its scale into LDS and their sums of squares (one per wave);
 //      meanwhile waves 6..7 wait for their copy of this step's weights;
 //   2. waves 6..7 request the next step's weight block into the other LDS
 //      buffer (direct-to-LDS loads that only they wait for, at the start of
@@ -58,11 +66,16 @@ struct ChainMat {
 };
 static_assert(sizeof(ChainMat) == sizeof(w4_chain_mat), "descriptor layout");
 
-constexpr int kChainThreads = 512;  // eight waves
-constexpr int kChainWaves = kChainThreads / 64;
-constexpr int kPollThreads = 256;   // waves 0..3 read the exchange cells and renormalise
-constexpr int kCopyWave0 = 6;       // waves 6..7 copy weight blocks and compute nothing
-constexpr int kComputeWaves = 4;    // waves 0..3 compute rows (one per SIMD); waves 4..5 only join barriers
+// Waves 0..7 read the exchange cells, stage the input and compute rows (two
+// per SIMD: wave w runs on SIMD w mod 4, so each SIMD interleaves two of them
+// and one's waits are filled by the other's work); waves 8..9 copy weight
+// blocks (both, each block: a block of 72 copy instructions would overrun one
+// wave's limit of outstanding loads) and keep the step's bookkeeping.
+constexpr int kComputeWaves = 8;
+constexpr int kPollThreads = kComputeWaves * 64;
+constexpr int kCopyWave0 = kComputeWaves;
+constexpr int kChainWaves = kComputeWaves + 2;
+constexpr int kChainThreads = kChainWaves * 64;
 constexpr int kDescCache = 128;     // descriptors kept in LDS
 constexpr int kChainMaxK = 8192;
 
@@ -73,7 +86,7 @@ constexpr int kChainMaxK = 8192;
 // on the other half of the banks from planes 0 and 2 when they are written.
 __device__ __forceinline__ int chain_plane(int G) { return ((G + 7) >> 4) * 16 + 8; }
 constexpr int kXinBytes = 4 * (((kChainMaxK / 32 + 7) >> 4) * 16 + 8) * 16;
-constexpr int kWeightBuf = 64 * 1024;  // bytes of each of the two LDS weight buffers
+constexpr int kWeightBuf = 56 * 1024;  // bytes of each of the two LDS weight buffers
 // sync buffer: bytes [0, 256) a header (word 0 exit counter, word 2 error);
 // from byte 256, one region of kChainMaxK 4-byte cells per matrix.
 constexpr int kSyncExit = 0, kSyncError = 2;
@@ -168,11 +181,21 @@ __device__ __forceinline__ RowBlock chain_plan(const ChainMat &m, int k_next, in
     int n = lds_steps ? min(p.na + p.nb, kWeightBuf / (G * 18)) : 0;
     while (n > 0 && bytes(n) > kWeightBuf) --n;
     p.nlds = n;
-    // lanes per row from the row length alone: 16 lanes up to 64 groups, 32
-    // up to 128, else 64.  (Choosing by the least work per lane -- 64 lanes
-    // for a block of six 64-group rows, say -- measured slower over the whole
-    // decode sweep: passes are latency-bound, not arithmetic-bound.)
-    const int L = G <= 64 ? 16 : (G <= 128 ? 32 : 64);
+    // lanes per row: the least work per lane, passes x groups per lane (every
+    // computing wave runs every pass, on clamped rows where the block has
+    // none), at most 4 groups per lane; ties go to fewer lanes per row.
+    // Blocks of a few long rows take 64 lanes per row, one row per wave.
+    const int nr = max(p.na + p.nb, 1);
+    int L = 64, best = 1 << 30;
+    for (int l = 16; l <= 64; l <<= 1) {
+        const int ng = (G + l - 1) / l;
+        if (ng > 4) continue;
+        const int passes = (nr + kComputeWaves * (64 / l) - 1) / (kComputeWaves * (64 / l));
+        if (passes * ng < best) {
+            best = passes * ng;
+            L = l;
+        }
+    }
     p.sel = L * 8 + (G + L - 1) / L;
     p.k_next = k_next;
     p.pad = 0;
@@ -232,7 +255,8 @@ struct RowSink {
 // rows read from memory.
 template <int L, int NG>
 __device__ __forceinline__ void chain_rows(const ChainMat &m, const RowBlock &b, const uint4 *buf,
-                                           const uint16_t *xin, const RowSink &sink) {
+                                           const uint16_t *xin, const float *xf, const float2 *xos,
+                                           float oscale, const RowSink &sink) {
     constexpr int SLOTS = kWave / L;
     const int G = m.K >> 5;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -258,19 +282,27 @@ __device__ __forceinline__ void chain_rows(const ChainMat &m, const RowBlock &b,
             xr[i][w * 4 + 3] = as_h2(v.w);
         }
     }
+    // the groups' offset sums (staged with the input, or computed here for
+    // the first matrix) and input scales 2^-s
     float2 xo[NG];
+    float fx[NG];
 #pragma unroll
-    for (int i = 0; i < NG; ++i) xo[i] = group_offset(xr[i]);
+    for (int i = 0; i < NG; ++i) {
+        const int g = l + i * L;
+        xo[i] = xos ? (g < G ? xos[g] : make_float2(0.0f, 0.0f)) : group_offset(xr[i]);
+        fx[i] = g < G ? xf[g] : 0.0f;
+    }
     auto finish = [&](int row, const uint4 (&q)[NG], const uint32_t (&sv)[NG]) __attribute__((always_inline)) {
         float acc = 0.0f;
 #pragma unroll
         for (int i = 0; i < NG; ++i) {
             const int g = l + i * L;
-            acc = (g < G) ? __builtin_fmaf(group_dot_off(q[i], xr[i], xo[i]), bf16_to_f32(sv[i]), acc) : acc;
+            acc = (g < G) ? __builtin_fmaf(group_dot_off(q[i], xr[i], xo[i]), bf16_to_f32(sv[i]) * fx[i], acc)
+                          : acc;
         }
         acc = lane_group_sum<L>(acc);
         if (l == L - 1 && row >= 0) {
-            const float v = __builtin_ldexpf(acc, kGroupDotExp);
+            const float v = __builtin_ldexpf(acc, kGroupDotExp) * oscale;
             // (a global store: through the generic pointer it would be a flat
             // store, which every later LDS read would have to wait for)
             ((__attribute__((address_space(1))) float *)m.y)[row] = v;
@@ -316,17 +348,22 @@ __device__ __forceinline__ void chain_rows(const ChainMat &m, const RowBlock &b,
 }
 
 __device__ __forceinline__ void chain_rows_any(const ChainMat &m, const RowBlock &b, const uint4 *buf,
-                                               const uint16_t *xin, const RowSink &sink) {
+                                               const uint16_t *xin, const float *xf, const float2 *xos,
+                                               float oscale, const RowSink &sink) {
     if (b.na + b.nb == 0) return;
     switch (__builtin_amdgcn_readfirstlane(b.sel)) {
-        case 16 * 8 + 1: chain_rows<16, 1>(m, b, buf, xin, sink); break;
-        case 16 * 8 + 2: chain_rows<16, 2>(m, b, buf, xin, sink); break;
-        case 16 * 8 + 3: chain_rows<16, 3>(m, b, buf, xin, sink); break;
-        case 16 * 8 + 4: chain_rows<16, 4>(m, b, buf, xin, sink); break;
-        case 32 * 8 + 3: chain_rows<32, 3>(m, b, buf, xin, sink); break;
-        case 32 * 8 + 4: chain_rows<32, 4>(m, b, buf, xin, sink); break;
-        case 64 * 8 + 3: chain_rows<64, 3>(m, b, buf, xin, sink); break;
-        default: chain_rows<64, 4>(m, b, buf, xin, sink); break;
+        case 16 * 8 + 1: chain_rows<16, 1>(m, b, buf, xin, xf, xos, oscale, sink); break;
+        case 16 * 8 + 2: chain_rows<16, 2>(m, b, buf, xin, xf, xos, oscale, sink); break;
+        case 16 * 8 + 3: chain_rows<16, 3>(m, b, buf, xin, xf, xos, oscale, sink); break;
+        case 16 * 8 + 4: chain_rows<16, 4>(m, b, buf, xin, xf, xos, oscale, sink); break;
+        case 32 * 8 + 1: chain_rows<32, 1>(m, b, buf, xin, xf, xos, oscale, sink); break;
+        case 32 * 8 + 2: chain_rows<32, 2>(m, b, buf, xin, xf, xos, oscale, sink); break;
+        case 32 * 8 + 3: chain_rows<32, 3>(m, b, buf, xin, xf, xos, oscale, sink); break;
+        case 32 * 8 + 4: chain_rows<32, 4>(m, b, buf, xin, xf, xos, oscale, sink); break;
+        case 64 * 8 + 1: chain_rows<64, 1>(m, b, buf, xin, xf, xos, oscale, sink); break;
+        case 64 * 8 + 2: chain_rows<64, 2>(m, b, buf, xin, xf, xos, oscale, sink); break;
+        case 64 * 8 + 3: chain_rows<64, 3>(m, b, buf, xin, xf, xos, oscale, sink); break;
+        default: chain_rows<64, 4>(m, b, buf, xin, xf, xos, oscale, sink); break;
     }
 }
 
@@ -370,46 +407,39 @@ __device__ __forceinline__ int chain_read_cells(const uint32_t *cells, int K, un
     }
 }
 
-// Sum of squares over the poll waves' values, in the fixed order of
-// sum_squares_256 (thread t: chunks t, t+256, ... ascending; wave_sum_f64;
-// wave sums added in wave order) -- bit for bit the w4_rms_renorm value --
-// with a single workgroup barrier: the wave sums go to one of two LDS slots,
-// alternating from step to step, so a slot is rewritten only two barriers
-// after it was read.
-__device__ __forceinline__ double chain_sum_squares(int K, const float4 (&v)[kPollJ], double *red,
-                                                    bool active, int parity) {
-    const int tid = threadIdx.x;
-    double ss = 0.0;
-    if (active) {
-        // chunks past the end hold zeros, and adding +0 leaves the sum's bits
-        // unchanged: the bound is the wave-uniform chunk count, no lane test
-        const int jn = ((K >> 2) + kPollThreads - 1) / kPollThreads;
-#pragma unroll
-        for (int j = 0; j < kPollJ; ++j) {
-            if (j < jn) {
-                ss += (double)v[j].x * (double)v[j].x;
-                ss += (double)v[j].y * (double)v[j].y;
-                ss += (double)v[j].z * (double)v[j].z;
-                ss += (double)v[j].w * (double)v[j].w;
-            }
-        }
-    }
-    ss = wave_sum_f64(ss);
-    double *r = red + parity * 4;
-    if ((tid & 63) == 0 && tid < kPollThreads) r[tid >> 6] = ss;
-    lds_barrier();
-    return ((r[0] + r[1]) + r[2]) + r[3];
+// The largest of v over the 8 lanes of a group (lanes 8k..8k+7): quad
+// exchanges, then the mirror within each half row.
+__device__ __forceinline__ float group8_max(float v) {
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false)));
+    return fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false)));
 }
+
+// The power of two that puts a group's largest magnitude m in [2^14, 2^15)
+// (0 for an all-zero group), kept within fp32's range of powers of two.
+__device__ __forceinline__ int group_scale_exp(float m) {
+    if (!(m > 0.0f)) return 0;
+    const int s = 14 - f32_exponent(m);
+    return s > 149 ? 149 : s;
+}
+
+// Sum over the 64 lanes of a wave in a fixed order (row shifts within rows of
+// 16, then row broadcasts), left in lane 63.
+__device__ __forceinline__ float wave_sum_f32(float v) { return lane_group_sum<64>(v); }
 
 __global__ __launch_bounds__(kChainThreads) void chain_kernel(const ChainMat *__restrict__ desc,
                                                               int n, const uint16_t *__restrict__ x0,
                                                               unsigned *sync, unsigned spin_limit) {
     extern __shared__ uint4 smem[];
-    uint16_t *xin = reinterpret_cast<uint16_t *>(smem);   // the staged input, four planes
-    uint4 *bufs = smem + kXinBytes / 16;                   // two weight buffers
+    // the staged input (four planes) of even and odd steps: a wave may stage
+    // step i+1's input while another still reads step i's
+    uint16_t *xins = reinterpret_cast<uint16_t *>(smem);
+    uint4 *bufs = smem + 2 * (kXinBytes / 16);             // two weight buffers
     ChainMat *dtab = reinterpret_cast<ChainMat *>(bufs + 2 * (kWeightBuf / 16));
     RowBlock *ptab = reinterpret_cast<RowBlock *>(dtab + kDescCache);  // this workgroup's plans
-    __shared__ double dred[8];
+    __shared__ float xfs[2][kChainMaxK / 32];  // per input group: 2^-(its fp16 scale), by parity
+    __shared__ float2 xoss[2][kChainMaxK / 32];  // per input group: its offset sums, by parity
+    __shared__ double ssp[2][kComputeWaves];  // sums of squares of the poll waves, by step parity
     __shared__ int stop_s, bad_s;
     const int nwg = gridDim.x;
     const int tid = threadIdx.x, wave = tid >> 6;
@@ -460,6 +490,9 @@ __global__ __launch_bounds__(kChainThreads) void chain_kernel(const ChainMat *__
         for (int i = 0; i < n; ++i) {
             const ChainMat m = get(i);
             const int K = m.K;
+            uint16_t *xin = xins + (i & 1) * (kXinBytes / 2);
+            float *xf = xfs[i & 1];
+            float2 *xos = xoss[i & 1];
             // 1. input into LDS, in the pair order (x0,x4)(x1,x5)(x2,x6)(x3,x7)
             // of each 8-value block that the unpack of a packed word uses
             if (i == 0) {
@@ -473,6 +506,7 @@ __global__ __launch_bounds__(kChainThreads) void chain_kernel(const ChainMat *__
                                         __builtin_amdgcn_perm(v.w, v.y, 0x05040100u),
                                         __builtin_amdgcn_perm(v.w, v.y, 0x07060302u));
                 }
+                for (int g = tid; g < (K >> 5); g += kChainThreads) xf[g] = 1.0f;
                 if (copier) wait_vmcnt_mem<0>();  // block 0 landed
             } else {
                 float4 v[kPollJ];
@@ -486,61 +520,123 @@ __global__ __launch_bounds__(kChainThreads) void chain_kernel(const ChainMat *__
                     for (int j = 0; j < kPollJ; ++j) v[j] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
                     if (copier) wait_vmcnt_mem<0>();  // this step's block landed
                 }
-                // (its barriers also publish stop_s)
-                const double inv = renorm_scale(chain_sum_squares(K, v, dred, rn, i & 1), K);
-                if (stop_s) break;
                 if (rn) {
-                    const int Gs = chain_plane(K >> 5);
                     const int jn = ((K >> 2) + kPollThreads - 1) / kPollThreads;
+                    // the sum of squares: each chunk's on its group-scaled
+                    // values in fp32 (no overflow: they are below 2^15), then
+                    // scaled back exactly into fp64, over this thread's chunks
+                    // in ascending order, then over the wave in a fixed order
+                    double ss = 0.0;
+                    // each group to fp16 with its own power of two, in the
+                    // pair order (x0,x4)(x1,x5)(x2,x6)(x3,x7) of each
+                    // 8-value block: chunk c holds values 4(c&1)..+3 of block
+                    // u = c>>1 (uint4 u & 3 of group u >> 2); the even lane of
+                    // a pair writes the first two words, the odd lane the
+                    // last two, each taking two halves from the other
+                    const int Gs = chain_plane(K >> 5);
                     uint2 *x8 = reinterpret_cast<uint2 *>(xin);
 #pragma unroll
                     for (int j = 0; j < kPollJ; ++j) {
                         if (j < jn) {
-                            // chunk c holds values 4(c&1)..+3 of block u = c>>1
-                            // (uint4 u & 3 of group u >> 2), whose pair order is
-                            // (x0,x4)(x1,x5)(x2,x6)(x3,x7): the even lane of a
-                            // pair writes the first two words, the odd lane the
-                            // last two, each taking two halves from the other
                             const int c = tid + kPollThreads * j;
-                            const uint32_t h0 = renorm_value(v[j].x, inv, 0), h1 = renorm_value(v[j].y, inv, 0);
-                            const uint32_t h2 = renorm_value(v[j].z, inv, 0), h3 = renorm_value(v[j].w, inv, 0);
+                            const float m = group8_max(fmaxf(fmaxf(fabsf(v[j].x), fabsf(v[j].y)),
+                                                             fmaxf(fabsf(v[j].z), fabsf(v[j].w))));
+                            const int se = group_scale_exp(m);
+                            const float s0 = __builtin_ldexpf(v[j].x, se), s1 = __builtin_ldexpf(v[j].y, se);
+                            const float s2 = __builtin_ldexpf(v[j].z, se), s3 = __builtin_ldexpf(v[j].w, se);
+                            float q = s0 * s0;
+                            q = __builtin_fmaf(s1, s1, q);
+                            q = __builtin_fmaf(s2, s2, q);
+                            q = __builtin_fmaf(s3, s3, q);
+                            ss += __builtin_ldexp((double)q, -2 * se);
+                            const uint32_t h0 = __builtin_bit_cast(uint16_t, (_Float16)s0);
+                            const uint32_t h1 = __builtin_bit_cast(uint16_t, (_Float16)s1);
+                            const uint32_t h2v = __builtin_bit_cast(uint16_t, (_Float16)s2);
+                            const uint32_t h3 = __builtin_bit_cast(uint16_t, (_Float16)s3);
                             const bool odd = c & 1;
-                            const uint32_t give = odd ? (h0 | (h1 << 16)) : (h2 | (h3 << 16));
+                            const uint32_t give = odd ? (h0 | (h1 << 16)) : (h2v | (h3 << 16));
                             const uint32_t got = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)give, 0xB1, 0xF, 0xF, false);
-                            const uint2 w = odd ? make_uint2((got & 0xFFFFu) | (h2 << 16), (got >> 16) | (h3 << 16))
+                            const uint2 w = odd ? make_uint2((got & 0xFFFFu) | (h2v << 16), (got >> 16) | (h3 << 16))
                                                 : make_uint2(h0 | (got << 16), h1 | (got & 0xFFFF0000u));
                             const int u = c >> 1;
-                            if (c < (K >> 2)) x8[((u & 3) * Gs + (u >> 2)) * 2 + (c & 1)] = w;
+                            if (c < (K >> 2)) {
+                                x8[((u & 3) * Gs + (u >> 2)) * 2 + (c & 1)] = w;
+                                if ((c & 7) == 0) xf[c >> 3] = __builtin_ldexpf(1.0f, -se);
+                            }
+                        }
+                    }
+                    ss = wave_sum_f64(ss);
+                    if ((tid & 63) == 0) ssp[i & 1][tid >> 6] = ss;
+                    // each group's offset sums, once, by the wave that staged
+                    // it (its 8 chunks sit on 8 neighbouring lanes of this
+                    // wave, and a wave's LDS accesses complete in order)
+                    asm volatile("" ::: "memory");
+                    const uint4 *x16 = reinterpret_cast<const uint4 *>(xin);
+                    for (int j = 0; j < jn; ++j) {
+                        const int c = tid + kPollThreads * j;
+                        if ((c & 7) == 0 && c < (K >> 2)) {
+                            const int g = c >> 3;
+                            h2 xg[16];
+#pragma unroll
+                            for (int w4 = 0; w4 < 4; ++w4) {
+                                const uint4 q = x16[w4 * Gs + g];
+                                xg[w4 * 4 + 0] = as_h2(q.x);
+                                xg[w4 * 4 + 1] = as_h2(q.y);
+                                xg[w4 * 4 + 2] = as_h2(q.z);
+                                xg[w4 * 4 + 3] = as_h2(q.w);
+                            }
+                            xos[g] = group_offset(xg);
                         }
                     }
                 }
             }
             // input staged, and this step's weights landed
             lds_barrier();
+            if (stop_s) break;
             if (copier) {
                 // 2. the copy waves request the next step's block
                 if (i + 1 < n)
                     chain_copy(get(i + 1), plan(i + 1), bufs + ((i + 1) & 1) * (kWeightBuf / 16));
+                // the step's bookkeeping, off the computing waves' path:
+                // step i-1's cells are all in, so every workgroup is done
+                // with step i-2's and this one clears its own; descriptor
+                // i + kDescCache/2 and its plan go into the slot of
+                // i - kDescCache/2
+                if (wave == kCopyWave0) {
+                    if (i >= 2) {
+                        const RowBlock q = plan(i - 2);
+                        uint32_t *cells = regions + (long)(i - 2) * kChainMaxK;
+                        for (int r = q.ra + (tid & 63); r < min(q.ra + q.na, q.k_next); r += 64) clear_cell(cells, r);
+                    }
+                    const int j = i + kDescCache / 2;
+                    if (j >= kDescCache && j < n) {
+                        if ((tid & 63) < kWords)
+                            dwords[(j % kDescCache) * kWords + (tid & 63)] = dsrc[(long)j * kWords + (tid & 63)];
+                        if ((tid & 63) == kWords) ptab[j % kDescCache] = load_plan(j);
+                    }
+                }
             } else if (wave < kComputeWaves) {
                 // 3. this step's rows
                 RowSink sink;
                 sink.cells = regions + (long)i * kChainMaxK;
-                chain_rows_any(m, plan(i), bufs + (i & 1) * (kWeightBuf / 16), xin, sink);
-                // step i-1's cells are all in: every workgroup is done with
-                // step i-2's, so this one clears its own
-                if (wave == kComputeWaves - 1 && i >= 2) {
-                    const RowBlock q = plan(i - 2);
-                    uint32_t *cells = regions + (long)(i - 2) * kChainMaxK;
-                    for (int r = q.ra + (tid & 63); r < min(q.ra + q.na, q.k_next); r += 64) clear_cell(cells, r);
+                // the output scale 1/r, from the poll waves' sums of squares
+                // (ss = m 2^e with e even and m in [1/4, 1): 1/r =
+                // rsq(m / K) 2^(-e/2), each factor within an ulp or two)
+                float oscale = 1.0f;
+                if (i > 0) {
+                    double ss = ssp[i & 1][0];
+#pragma unroll
+                    for (int w = 1; w < kComputeWaves; ++w) ss += ssp[i & 1][w];
+                    if (ss > 0.0) {
+                        const int e = __builtin_amdgcn_frexp_exp(ss) & ~1;
+                        const float mk = (float)__builtin_ldexp(ss, -e) * __builtin_amdgcn_rcpf((float)K);
+                        oscale = __builtin_ldexpf(__builtin_amdgcn_rsqf(mk), -(e >> 1));
+                    } else {
+                        oscale = 0.0f;
+                    }
                 }
-                // refill: descriptor i + kDescCache/2 (and its plan) into the
-                // slot of i - kDescCache/2
-                const int j = i + kDescCache / 2;
-                if (wave == kComputeWaves - 1 && j >= kDescCache && j < n) {
-                    if ((tid & 63) < kWords)
-                        dwords[(j % kDescCache) * kWords + (tid & 63)] = dsrc[(long)j * kWords + (tid & 63)];
-                    if ((tid & 63) == kWords) ptab[j % kDescCache] = load_plan(j);
-                }
+                chain_rows_any(m, plan(i), bufs + (i & 1) * (kWeightBuf / 16), xin, xf, i > 0 ? xos : nullptr,
+                               oscale, sink);
             }
         }
     } else if (blockIdx.x == 0 && tid == 0) {
@@ -566,10 +662,11 @@ __global__ __launch_bounds__(kChainThreads) void chain_kernel(const ChainMat *__
     }
 }
 
-static_assert(kXinBytes + 2 * kWeightBuf + kDescCache * 64 + 256 <= 160 * 1024, "LDS of one workgroup");
+static_assert(2 * kXinBytes + 2 * kWeightBuf + kDescCache * 64 + 2 * kChainMaxK / 32 * 12 + 512 <= 160 * 1024,
+              "LDS of one workgroup");
 
 size_t chain_lds_bytes() {
-    return (size_t)kXinBytes + 2 * (size_t)kWeightBuf + kDescCache * (sizeof(ChainMat) + sizeof(RowBlock));
+    return 2 * (size_t)kXinBytes + 2 * (size_t)kWeightBuf + kDescCache * (sizeof(ChainMat) + sizeof(RowBlock));
 }
 
 hipError_t launch_chain(const void *desc, int n, const uint16_t *x0, void *sync, unsigned spin_limit,

@@ -308,11 +308,14 @@ int w4_rms_renorm(const float *v, int64_t ldv, int32_t K, int32_t rows, void *ou
  * One decode-step chain as a single launch [P1-S4]: n_mats packed matrices
  * applied in sequence.  Matrix i (a w4_chain_mat record) has shape [N][K] at
  * codes/steps and writes fp32 y[0..N).  Its input is x0 (fp16, K of matrix 0
- * long, 16-byte aligned) for i == 0, else the leading K entries of the previous matrix's y,
- * renormalised to RMS 1 and rounded to fp16 bit for bit as w4_rms_renorm
- * does on that output.  Each product meets the bound of w4_gemv; its row
- * mapping (and so the order of its fp32 sums) is chosen per matrix for the
- * whole-chip launch and can differ from w4_gemv's.
+ * long, 16-byte aligned) for i == 0, else x = u / r: u the leading K entries
+ * of the previous matrix's y, r = sqrt(mean(u^2)) (x = 0 when r = 0).  Each
+ * output satisfies |y[n] - sum_k w(n,k) x[k]| <= 1e-3 * sum_k |w(n,k) x[k]| on
+ * that exact x: the products run on u, rounded to fp16 one group of 32 at a
+ * time with the group's own power-of-two scale, and each finished output is
+ * multiplied by 1/r (r from fp32 sums of squares in a fixed order), so no
+ * product waits for r before its dot products.  Results are bitwise
+ * reproducible from call to call.
  *   desc: DEVICE array of n_mats records (it is read by the kernel).
  *   sync: device buffer of sync_bytes >= W4_CHAIN_SYNC_BYTES(n_mats) bytes,
  *         16-byte aligned, all zero before the first call and then owned by

@@ -71,6 +71,8 @@ def lib():
         L.w4o_gemv.restype = None
         L.w4o_gemv_omp.argtypes = [P, P, i64, i64, P, i32, P, P]
         L.w4o_gemv_omp.restype = None
+        L.w4o_gemv_x64_rows.argtypes = [P, P, i64, P, i64, i64, P, P]
+        L.w4o_gemv_x64_rows.restype = None
         L.w4o_gemm.argtypes = [P, P, i64, i64, P, i32, i64, i64, P, P]
         L.w4o_gemm.restype = None
         L.w4o_gather.argtypes = [P, P, i64, i64, P, i64, P]
@@ -141,6 +143,18 @@ def gemv(codes, steps, N, K, x, xdtype, rows=None, threads=False):
     y = np.empty(n1 - n0, dtype=np.float64)
     a = np.empty(n1 - n0, dtype=np.float64)
     lib().w4o_gemv_rows(_p(codes), _p(steps), N, K, _p(x), xdtype, n0, n1, _p(y), _p(a))
+    return y, a
+
+
+def gemv_x64(codes, steps, N, K, x, rows=None):
+    """y, a (fp64) of the packed GEMV on an fp64 input vector x (exact values);
+    ``rows`` = (n0, n1) samples a row range."""
+    codes, steps = _c(codes, np.uint32), _c(steps, np.uint16)
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    n0, n1 = (0, N) if rows is None else rows
+    y = np.empty(n1 - n0, dtype=np.float64)
+    a = np.empty(n1 - n0, dtype=np.float64)
+    lib().w4o_gemv_x64_rows(_p(codes), _p(steps), K, _p(x), n0, n1, _p(y), _p(a))
     return y, a
 
 

@@ -199,6 +199,26 @@ void w4o_gemv_omp(const uint32_t *codes, const uint16_t *steps, int64_t N, int64
         w4o_gemv_rows(codes, steps, N, K, x, xdtype, n, n + 1, y + n, a ? a + n : 0);
 }
 
+/*
+ * The same product on an input given exactly as fp64 values (rows n0..n1-1),
+ * with the bound's sum of |w x|: the decode chain's input x = u / r, the
+ * previous output's leading entries divided by their RMS (the chaining step of
+ * the decode sweep), enters the product exactly, not as a 16-bit vector.
+ */
+void w4o_gemv_x64_rows(const uint32_t *codes, const uint16_t *steps, int64_t K, const double *x,
+                       int64_t n0, int64_t n1, double *y, double *a) {
+    for (int64_t n = n0; n < n1; ++n) {
+        double acc = 0.0, mag = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            double p = w4o_weight(codes, steps, K, n, k) * x[k];
+            acc += p;
+            mag += fabs(p);
+        }
+        y[n - n0] = acc;
+        a[n - n0] = mag;
+    }
+}
+
 int w4o_num_threads(void) {
 #ifdef _OPENMP
     return omp_get_max_threads();

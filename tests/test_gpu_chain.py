@@ -1,8 +1,10 @@
 """The decode-step chain (one persistent launch) on the GPU.
 
-Parity is teacher-forced: for each matrix, its input is recomputed from the
-chain's own previous output with w4_rms_renorm (bitwise the chain's internal
-input), and the matrix's output is checked against the oracle on that input.
+Parity is teacher-forced: for each matrix i > 0, its input is the exact value
+x = u / r, with u the leading K entries of the chain's own output of matrix
+i - 1 and r their RMS (both in fp64 on the host), and the matrix's output is
+checked against the oracle's product on that x, within the bound
+|y - y_exact| <= 1e-3 * sum_k |w x| per output.
 """
 
 import os
@@ -35,24 +37,31 @@ def make_mats(shapes, seed):
     return mats
 
 
+def chain_input(x0, ys, i, K):
+    """The exact input of matrix i: x0 (fp16 values) for the first, else the
+    previous output's leading K entries over their RMS, in fp64."""
+    if i == 0:
+        return oracle.act_to_f64(host_bits(x0), F16)
+    u = ys[i - 1][:K].cpu().numpy().astype(np.float64)
+    r = np.sqrt(np.mean(u * u))
+    return u / r if r > 0 else np.zeros(K)
+
+
 def check_teacher_forced(w4, mats, x0, ys, rows=None, full_upto=None):
-    x = x0
+    torch.cuda.synchronize()
     for i, ((c, s), y) in enumerate(zip(mats, ys)):
         N, K = c.shape[0], c.shape[1] * 8
-        if i > 0:
-            x = w4.w4_rms_renorm(ys[i - 1], K, out_dtype=torch.float16)
-        torch.cuda.synchronize()
         cn = c.cpu().numpy().view(np.uint32)
         sn = s.view(torch.int16).cpu().numpy().view(np.uint16)
-        xn = host_bits(x)
+        x = chain_input(x0, ys, i, K)
         yn = y.cpu().numpy()
         if full_upto is None or i < full_upto:
-            yo, ao = oracle.gemv(cn, sn, N, K, xn, F16, threads=True)
+            yo, ao = oracle.gemv_x64(cn, sn, N, K, x)
             ok, worst = within_bound(yn[:N], yo, ao)
         else:
             ok = True
             for n0, n1 in rows(N):
-                yo, ao = oracle.gemv(cn, sn, N, K, xn, F16, rows=(n0, n1))
+                yo, ao = oracle.gemv_x64(cn, sn, N, K, x, rows=(n0, n1))
                 ok_r, worst = within_bound(yn[n0:n1], yo, ao)
                 ok = ok and ok_r
         assert ok, (i, N, K, worst)
@@ -144,3 +153,37 @@ def test_chain_barrier_timeout_is_reported_and_recovers(w4, w4_settings):
     torch.cuda.synchronize()
     assert sync[0].item() == 0 and sync[2].item() == 0
     check_teacher_forced(w4, mats, x0, ys)
+
+
+def test_chain_wide_range_and_zero_vectors(w4):
+    """Steps spanning 2^-60 .. 2^70 between matrices (outputs far outside fp16's
+    range; each input group gets its own power of two), a group of huge values
+    next to tiny ones, and a matrix whose codes are all 8 (a zero output, so
+    the next input is the zero vector and gives zeros)."""
+    rng = np.random.default_rng(12)
+    shapes = [(512, 64), (640, 512), (256, 640), (256, 256), (384, 256)]
+    scales = [2.0 ** 70, 2.0 ** -60, 1.0, 1.0, 2.0 ** 20]   # squares of 2^72 overflow fp32
+    mats = []
+    for (N, K), sc in zip(shapes, scales):
+        codes, steps = synth.w4_matrix(rng, N, K)
+        sv = oracle.act_to_f64(steps.ravel(), synth.BF16).reshape(steps.shape) * sc
+        steps = synth.act_bits(sv, synth.BF16)
+        mats.append((codes, steps))
+    # rows 0..31 of matrix 1 get steps 2^40 larger: one input group of matrix
+    # 2 is huge next to the others
+    c1, s1 = mats[1]
+    s1 = s1.copy()
+    s1[:32] = synth.act_bits(oracle.act_to_f64(s1[:32].ravel(), synth.BF16).reshape(32, -1) * 2.0 ** 40,
+                             synth.BF16)
+    mats[1] = (c1, s1)
+    mats[3] = (np.full_like(mats[3][0], 0x88888888), mats[3][1])   # all codes 8
+    dm = [(torch.from_numpy(c.view(np.int32)).cuda(),
+           torch.from_numpy(s.view(np.int16)).cuda().view(torch.bfloat16)) for c, s in mats]
+    ys = [torch.full((N,), float("nan"), device="cuda") for N, _ in shapes]
+    x0 = dev_act(synth.activations(rng, 64, F16), F16)
+    sync = w4.w4_chain_sync(len(shapes))
+    w4.w4_gemv_chain(w4.w4_chain_desc(dm, ys), x0, sync)
+    torch.cuda.synchronize()
+    assert sync[0].item() == 0 and sync[2].item() == 0
+    assert torch.all(ys[3] == 0) and torch.all(ys[4] == 0)
+    check_teacher_forced(w4, dm, x0, ys)

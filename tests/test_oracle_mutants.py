@@ -18,7 +18,12 @@ MUTANTS = {
     "nibble_order_reversed": ("(word >> (4 * (k % 8)))", "(word >> (4 * (7 - k % 8)))"),
     "offset_7_not_8": ("w4o_code(codes, K, n, k) - 8)", "w4o_code(codes, K, n, k) - 7)"),
     "step_index_k_over_64": ("steps[n * (K / 32) + k / 32]", "steps[n * (K / 32) + k / 64]"),
-    "bound_without_abs": ("mag += fabs(p);", "mag += p;"),
+    "bound_without_abs": ("mag += fabs(p);\n        }\n        y[n - n0] = acc;\n        if (a)",
+                          "mag += p;\n        }\n        y[n - n0] = acc;\n        if (a)"),
+    "bound_without_abs_exact_input": ("mag += fabs(p);\n        }\n        y[n - n0] = acc;\n        a[n - n0]",
+                                      "mag += p;\n        }\n        y[n - n0] = acc;\n        a[n - n0]"),
+    "exact_input_ignores_x": ("double p = w4o_weight(codes, steps, K, n, k) * x[k];",
+                              "double p = w4o_weight(codes, steps, K, n, k) * x[0];"),
     "bf16_bias_off_by_one": ("e - 134", "e - 133"),
     "f16_subnormal_scale": ("ldexp((double)f, -24)", "ldexp((double)f, -25)"),
     "round_half_up": ("nearbyint(a / quantum)", "floor(a / quantum + 0.5)"),

@@ -169,6 +169,21 @@ def test_gemv_matches_brute_force(N, K, dt):
     assert np.all(np.abs(y - yb) <= 1e-13 * ab)
 
 
+@pytest.mark.parametrize("N,K", [(1, 32), (33, 96), (65, 704)])
+def test_gemv_on_exact_input_matches_brute_force(N, K):
+    """The product on an fp64 input vector (the decode chain's u / r): against
+    the dense dequantised matrix times that vector, and a sampled row range."""
+    rng = np.random.default_rng(N * 7 + K)
+    codes, steps = synth.w4_matrix(rng, N, K)
+    x = rng.standard_normal(K) * 3.7
+    y, a = oracle.gemv_x64(codes, steps, N, K, x)
+    W = brute.dense(codes, steps, K)
+    assert np.all(np.abs(y - W @ x) <= 1e-13 * (np.abs(W) @ np.abs(x)))
+    assert np.allclose(a, np.abs(W) @ np.abs(x), rtol=1e-13, atol=0)
+    y2, a2 = oracle.gemv_x64(codes, steps, N, K, x, rows=(N // 2, N))
+    assert np.array_equal(y2, y[N // 2:]) and np.array_equal(a2, a[N // 2:])
+
+
 def test_gemv_closed_forms():
     K, N = 256, 3
     ones = np.full(K, 0x3C00, dtype=np.uint16)           # fp16 1.0

@@ -352,9 +352,148 @@ def extra_moe(w4, torch, np, synth, timer, reps: int = 5):
                         "expert_bytes_per_token": nbytes,
                         "pool_bitwise_identical_to_direct": identical}
         del pools
+    out["streaming_T1"] = moe_streaming(w4, torch, np, synth, layers, E, topk, S)
     del layers
     torch.cuda.empty_cache()
     return out
+
+
+def moe_streaming(w4, torch, np, synth, layers, E, topk, S, steps: int = 3):
+    """Expert streaming through 32-slot pools (the anyesh.me page's design, on
+    this box's PCIe link): the 30 layers' experts sit in a pinned host store;
+    per layer and token the LFU pool takes the misses by asynchronous copies on
+    a second stream while a shared dense FFN (gate/up 2x2816x2816, down
+    2816x2816, W4) runs on the compute stream, then one join.  The host reads
+    each layer's routing only after the previous layer has finished, as a
+    router's choice would be.  Reported: us
+    per token with the overlap on and off (join before the dense FFN) and with
+    every expert resident (direct addressing), bytes streamed per token, the
+    copy stream's GB/s, the overlap fraction (time saved by the overlap over
+    the overlap possible, min(copy, dense FFN) per layer), and bitwise identity
+    of the last layer's output against direct addressing."""
+    L, T = len(layers), 1
+    KG, NG, KD, ND, DF = 2816, 1408, 704, 2816, 2816
+    g = torch.Generator(device="cuda")
+    g.manual_seed(3)
+    parts = [[gc.view(E, -1), gs.view(torch.int16).view(E, -1), dc.view(E, -1), ds.view(torch.int16).view(E, -1)]
+             for gc, gs, dc, ds in layers]
+    part_bytes = [p[0].numel() * p.element_size() for p in parts[0]]
+    host = [[p.view(torch.uint8).cpu().pin_memory() for p in lp] for lp in parts]
+    pools = [[torch.empty((S, p.shape[1]), dtype=p.dtype, device="cuda") for p in lp] for lp in parts]
+    slots = [torch.full((E,), -1, dtype=torch.int32, device="cuda") for _ in range(L)]
+    dense = []
+    for _ in range(L):
+        a = synth.w4_matrix_torch(g, 2 * DF, DF, "cuda")
+        b = synth.w4_matrix_torch(g, DF, 2 * DF // 2, "cuda")
+        dense.append((a[0], a[1][0].view(torch.bfloat16), b[0][0], b[1][0].view(torch.bfloat16)))
+    rng = np.random.default_rng(7)
+    tokens = [[synth.expert_choice(rng, T, E, topk) for _ in range(L)] for _ in range(steps + 1)]
+    dev = [[(torch.from_numpy(i).cuda(), torch.from_numpy(r).cuda()) for i, r in tk] for tk in tokens]
+    x0 = torch.randn((T, KG), generator=g, device="cuda").to(torch.bfloat16)
+    Gb = torch.empty((T * topk, NG), device="cuda")
+    Db = [torch.empty((T, ND), device="cuda") for _ in range(2)]
+    Hd = torch.empty(2 * DF, device="cuda")
+    Yd = torch.empty(DF, device="cuda")
+    ws = w4.new_workspace(w4.w4_moe_gemv_ids_workspace_bytes(ND, KD, T, topk, w4.W4_F32_RMS, True, True))
+    xd = torch.empty(DF, dtype=torch.float16, device="cuda")
+    copy_stream = torch.cuda.Stream()
+
+    def dense_ffn(li, x):
+        ga, gs_, da, ds_ = dense[li]
+        w4.w4_rms_renorm(x, DF, out=xd)
+        w4.w4_gemv(ga[0], gs_, xd, Hd)
+        w4.w4_rms_renorm(Hd, DF, out=xd)
+        w4.w4_gemv(da, ds_, xd, Yd)
+
+    def token(k, stream_on=True, overlap=True):
+        x = x0
+        for li in range(L):
+            (gc, gs, dc, ds) = layers[li]
+            ids_dev, route = dev[k][li]
+            kw = {}
+            if stream_on:
+                # the router's choice is read on the host once the previous
+                # layer's output exists (the page's callback on the top-k
+                # node): a host wait, then the copies are requested
+                torch.cuda.current_stream().synchronize()
+                w4.w4_pool_prepare(pool, li, tokens[k][li][0], host[li], pools[li], slots[li], copy_stream)
+                if not overlap:
+                    w4.w4_pool_join(pool, li)
+                dense_ffn(li, Db[(li + 1) & 1] if li else torch.zeros(DF, device="cuda"))
+                if overlap:
+                    w4.w4_pool_join(pool, li)
+                gc, gs, dc, ds = (pools[li][0].view(-1, KG // 8), pools[li][1].view(torch.bfloat16).view(-1, KG // 32),
+                                  pools[li][2].view(-1, KD // 8), pools[li][3].view(torch.bfloat16).view(-1, KD // 32))
+                kw = dict(slot_of=slots[li], n_slots=S)
+            else:
+                dense_ffn(li, Db[(li + 1) & 1] if li else torch.zeros(DF, device="cuda"))
+            w4.w4_moe_gemv_ids(gc, gs, NG * KG // 8, NG * KG // 32, NG, KG, x, ids_dev, n_experts=E, Y=Gb,
+                               workspace=ws, **kw)
+            w4.w4_moe_gemv_ids(dc, ds, ND * KD // 8, ND * KD // 32, ND, KD, Gb, ids_dev, x_per_pair=True,
+                               n_experts=E, route_w=route, Y=Db[li & 1], workspace=ws, **kw)
+            if stream_on:
+                w4.w4_pool_release(pool, li)
+            x = Db[li & 1]
+        return x
+
+    def timed(fn):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        fn()
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0
+
+    def run_mode(overlap):
+        """A fresh manager and empty pools, token 0 to warm up, then tokens
+        1..steps: the same requests (so the same copies) in every mode."""
+        nonlocal pool
+        if pool is not None:
+            torch.cuda.synchronize()
+            w4.w4_pool_destroy(pool)
+        pool = w4.w4_pool_create(L, E, S, part_bytes)
+        for sl in slots:
+            sl.fill_(-1)
+        token(0, overlap=overlap)
+        h0, m0, b0 = w4.w4_pool_stats(pool)
+        t = sum(timed(lambda k=k: token(k, overlap=overlap)) for k in range(1, steps + 1)) / steps
+        h1, m1, b1 = w4.w4_pool_stats(pool)
+        return t, (h1 - h0) / steps, (m1 - m0) / steps, (b1 - b0) / steps
+
+    pool = None
+    t_off, _, _, _ = run_mode(False)
+    t_on, hits, misses, per_tok = run_mode(True)
+    t_res = sum(timed(lambda k=k: token(k, stream_on=False)) for k in range(1, steps + 1)) / steps
+    # identity: the last token's output through the pools (as they stand)
+    # against direct addressing of the resident experts
+    y_on = token(steps).clone()
+    y_off = token(steps, stream_on=False).clone()
+    torch.cuda.synchronize()
+    identical = bool(torch.equal(y_on.view(torch.int32), y_off.view(torch.int32)))
+    w4.w4_pool_destroy(pool)
+    # the copy stream alone: pinned host to device, 64 MB copies into scratch
+    src = host[0][0].view(-1)[:64 << 20]
+    dst = torch.empty(src.numel(), dtype=torch.uint8, device="cuda")
+    n = max(1, int(per_tok // src.numel()))
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(copy_stream):
+        e0.record()
+        for _ in range(n):
+            dst.copy_(src, non_blocking=True)
+        e1.record()
+    torch.cuda.synchronize()
+    copy_gbps = n * src.numel() / (e0.elapsed_time(e1) / 1e3) / 1e9
+    t_dense = sum(timed(lambda li=li: dense_ffn(li, Db[0])) for li in range(L))
+    t_copy = per_tok / (copy_gbps * 1e9)
+    res = {"us_per_token_overlap_on": round(t_on * 1e6, 1), "us_per_token_overlap_off": round(t_off * 1e6, 1),
+           "us_per_token_all_resident": round(t_res * 1e6, 1),
+           "expert_bytes_streamed_per_token": int(per_tok),
+           "misses_per_token": round(misses, 2), "hits_per_token": round(hits, 2),
+           "copy_GBps": round(copy_gbps, 1),
+           "overlap_fraction": round(max(0.0, t_off - t_on) / max(1e-9, min(t_copy, t_dense)), 3),
+           "us_dense_ffn_per_token": round(t_dense * 1e6, 1),
+           "streamed_bitwise_identical_to_resident": identical}
+    del host, pools, dense
+    return res
 
 
 def extra_gather_per_layer(w4, torch, np, synth, timer, reps: int = 200):

@@ -88,6 +88,20 @@ for _name, _args in _WS_SIGNATURES.items():
     _fn = getattr(lib, _name)
     _fn.argtypes = _args
     _fn.restype = ctypes.c_int64
+_POOL_SIGNATURES = {
+    "w4_pool_create": [_I32, _I32, _I32, _I32, _P, _P],
+    "w4_pool_plan": [_P, _I32, _P, _I32, _P, _P, _P],
+    "w4_pool_prepare": [_P, _I32, _P, _I32, _P, _P, _P, _P],
+    "w4_pool_join": [_P, _I32, _P],
+    "w4_pool_release": [_P, _I32, _P],
+    "w4_pool_stats": [_P, _P, _P, _P],
+}
+for _name, _args in _POOL_SIGNATURES.items():
+    _fn = getattr(lib, _name)
+    _fn.argtypes = _args
+    _fn.restype = ctypes.c_int
+lib.w4_pool_destroy.argtypes = [_P]
+lib.w4_pool_destroy.restype = None
 lib.w4_reload_settings.argtypes = []
 lib.w4_reload_settings.restype = None
 lib.w4_strerror.argtypes = [ctypes.c_int]
@@ -328,6 +342,68 @@ def w4_moe_gemv_ids_noalloc(codes_base, steps_base, expert_stride_codes, expert_
 
 
 W4_NOALLOC_SCRATCH_BYTES = 8 << 20
+
+
+def _i32_host(a):
+    import numpy as np
+    return np.ascontiguousarray(a, dtype=np.int32)
+
+
+def w4_pool_create(n_layers, n_experts, n_slots, part_bytes):
+    """Host-side manager of per-layer expert slot pools (see w4.h); returns an
+    opaque handle.  part_bytes: the bytes of each part of one expert."""
+    import numpy as np
+    pb = np.ascontiguousarray(part_bytes, dtype=np.int64)
+    h = ctypes.c_void_p()
+    _check(lib.w4_pool_create(n_layers, n_experts, n_slots, pb.size, pb.ctypes.data, ctypes.byref(h)),
+           "w4_pool_create")
+    return h
+
+
+def w4_pool_destroy(pool):
+    lib.w4_pool_destroy(pool)
+
+
+def w4_pool_plan(pool, layer, ids, n_experts):
+    """The LFU decision alone: returns (slot_of int32[n_experts], [(expert, slot)
+    of each miss])."""
+    import numpy as np
+    ids = _i32_host(ids).ravel()
+    slot_of = np.empty(n_experts, dtype=np.int32)
+    me = np.empty(max(ids.size, 1), dtype=np.int32)
+    ms = np.empty(max(ids.size, 1), dtype=np.int32)
+    n = lib.w4_pool_plan(pool, layer, ids.ctypes.data, ids.size, slot_of.ctypes.data, me.ctypes.data,
+                         ms.ctypes.data)
+    if n < 0:
+        raise W4Error(n, "w4_pool_plan")
+    return slot_of, list(zip(me[:n].tolist(), ms[:n].tolist()))
+
+
+def w4_pool_prepare(pool, layer, ids, host_parts, dev_parts, dev_slot_of, copy_stream):
+    """LFU decision, then the misses' copies and the slot map's upload on
+    copy_stream.  host_parts: pinned host tensors (expert-major), dev_parts:
+    the layer's device pool tensors (slot-major), dev_slot_of: int32 device
+    tensor [n_experts]."""
+    ids = _i32_host(ids).ravel()
+    hp = (ctypes.c_void_p * len(host_parts))(*[t.data_ptr() for t in host_parts])
+    dp = (ctypes.c_void_p * len(dev_parts))(*[t.data_ptr() for t in dev_parts])
+    _check(lib.w4_pool_prepare(pool, layer, ids.ctypes.data, ids.size, hp, dp, dev_slot_of.data_ptr(),
+                               copy_stream.cuda_stream), "w4_pool_prepare")
+
+
+def w4_pool_join(pool, layer, stream=None):
+    _check(lib.w4_pool_join(pool, layer, _stream(stream)), "w4_pool_join")
+
+
+def w4_pool_release(pool, layer, stream=None):
+    _check(lib.w4_pool_release(pool, layer, _stream(stream)), "w4_pool_release")
+
+
+def w4_pool_stats(pool):
+    """(hits, misses, bytes copied) since creation."""
+    h, m, b = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+    _check(lib.w4_pool_stats(pool, ctypes.byref(h), ctypes.byref(m), ctypes.byref(b)), "w4_pool_stats")
+    return h.value, m.value, b.value
 
 
 def w4_embed_gather(codes, steps, ids, out=None, dev_err=None, stream=None):

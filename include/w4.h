@@ -280,6 +280,57 @@ int w4_moe_gemv_ids_noalloc(const uint32_t *codes_base, const uint16_t *steps_ba
                             float *Y, int32_t *dev_err, void *stream);
 
 /*
+ * Expert slot pools [P3, "Streaming without touching a single GPU kernel" and
+ * "Numbers from the actual machine"]: routed experts are kept in a host store
+ * and streamed into a small per-layer pool of device slots; the expert
+ * product reads the pool through slot ids (w4_moe_gemv_ids with slot_of).
+ * A w4_pool holds the host-side state of n_layers layers of n_experts experts
+ * and n_slots slots; an expert is n_parts contiguous parts (for example gate/
+ * up codes, gate/up steps, down codes, down steps) of part_bytes[p] bytes each
+ * (multiples of 16).  Per layer, the caller owns:
+ *   a host store: part p of expert e at host_parts[p] + e * part_bytes[p],
+ *     in pinned host memory allocated as such (hipHostMalloc or torch's
+ *     pin_memory), so that the copies are asynchronous;
+ *   a device pool: part p of slot s at dev_parts[p] + s * part_bytes[p] (the
+ *     stride w4_moe_gemv_ids takes), and the device slot map int32[n_experts].
+ * Per layer and decode step, in order:
+ *   w4_pool_prepare(layer, ids)  as soon as the router's choices are known (ids
+ *     are real expert ids, host int32, duplicates allowed): the per-layer LFU
+ *     -- hits stay; each miss takes the lowest empty slot, else the slot whose
+ *     expert this call does not request with the fewest uses (one use per call
+ *     that requests it), then the least recently used, then the lowest index
+ *     -- and, on copy_stream (a second stream of default priority): a wait for
+ *     the layer's last release, the copies of the misses, the upload of the
+ *     slot map (-1 for experts not resident) and the layer's event.  More
+ *     distinct ids than slots, or an id outside [0, n_experts): an error, no
+ *     state changed.  The host blocks only if the slot-map staging of two calls
+ *     earlier on this layer is still being read.
+ *   (the layer's dense work on the compute stream, overlapping the copies)
+ *   w4_pool_join(layer, stream)  the one join: stream waits for the copies.
+ *   (the expert products on stream, with slot_of = the device slot map)
+ *   w4_pool_release(layer, stream)  after the layer's last read of its pool.
+ * w4_pool_plan is the host-side LFU decision alone (no device work; the same
+ * state change as prepare): it writes the slot map to slot_of_out
+ * (int32[n_experts]) and the misses' experts and slots (in request order) to
+ * miss_expert / miss_slot (room for n_ids each), and returns the miss count.
+ * One host thread at a time per pool.  w4_pool_stats: hits, misses and bytes
+ * copied since creation.
+ */
+#define W4_POOL_MAX_PARTS 8
+typedef struct w4_pool w4_pool;
+int w4_pool_create(int32_t n_layers, int32_t n_experts, int32_t n_slots, int32_t n_parts,
+                   const int64_t *part_bytes, w4_pool **pool);
+void w4_pool_destroy(w4_pool *pool);
+int w4_pool_plan(w4_pool *pool, int32_t layer, const int32_t *ids, int32_t n_ids, int32_t *slot_of_out,
+                 int32_t *miss_expert, int32_t *miss_slot);
+int w4_pool_prepare(w4_pool *pool, int32_t layer, const int32_t *ids, int32_t n_ids,
+                    const void *const *host_parts, void *const *dev_parts, int32_t *dev_slot_of,
+                    void *copy_stream);
+int w4_pool_join(w4_pool *pool, int32_t layer, void *stream);
+int w4_pool_release(w4_pool *pool, int32_t layer, void *stream);
+int w4_pool_stats(const w4_pool *pool, int64_t *hits, int64_t *misses, int64_t *bytes);
+
+/*
  * Row gather from a 4-bit table [P1-S2] (the input-embedding use of the same
  * table that w4_gemv multiplies as the output layer):
  *   out[i*K + k] = bf16_round_nearest_even((code(ids[i], k) - 8) * step)

@@ -86,8 +86,11 @@ typedef void (*GemmFn)(const uint4 *, const uint16_t *, int, int, const uint16_t
 template <bool S8>
 GemmFn pick_gemm_s(int R) {
     switch (R) {
+        case 3: return gemm_smallm_kernel<3, S8>;
         case 4: return gemm_smallm_kernel<4, S8>;
+        case 6: return gemm_smallm_kernel<6, S8>;
         case 8: return gemm_smallm_kernel<8, S8>;
+        case 12: return gemm_smallm_kernel<12, S8>;
         case 16: return gemm_smallm_kernel<16, S8>;
         case 24: return gemm_smallm_kernel<24, S8>;
     }

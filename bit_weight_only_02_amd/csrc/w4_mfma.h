@@ -49,6 +49,22 @@ constexpr int kSmallMMaxRounds = 8;       // rounds per wave above which K is sp
 constexpr long kSmallMTargetGroups = 768; // workgroups: 3 per CU, each looping over its tiles
 constexpr long kSmallMWideGroups = 256;   // the same for 8 or more rows with one wave per tile
 
+// Wait until at most n (wave-uniform) vector-memory instructions of this wave
+// are outstanding; counts past 63 wait for none (a binary search down to an
+// immediate).
+template <int Lo = 0, int Hi = 63>
+__device__ __forceinline__ void wait_vmcnt_upto(int n) {
+    if constexpr (Lo == Hi) {
+        wait_vmcnt_mem<Lo>();
+    } else {
+        constexpr int Mid = (Lo + Hi) / 2;
+        if (n <= Mid)
+            wait_vmcnt_upto<Lo, Mid>(n);
+        else
+            wait_vmcnt_upto<Mid + 1, Hi>(n);
+    }
+}
+
 // 4x4 transpose of words across the four 16-lane groups: on entry lane group
 // Q holds words 0..3 of group Q in v[0..3]; on exit lane group q holds word q
 // of groups 0..3 in v[0..3].
@@ -133,7 +149,9 @@ inline SmallMPlan smallm_plan(int N, int K, int M, int units, int lds_budget = k
     const int nr = gs / 4;
     while (p.KW > 1 && nr < p.KW) p.KW /= 2;
     const int rpw = (nr + p.KW - 1) / p.KW;
-    p.R = rpw <= 4 ? 4 : rpw <= 8 ? 8 : rpw <= 16 ? 16 : 24;
+    // rounds per batch of loads: exactly a wave's rounds where an instance
+    // exists (straight-line code), else the next larger one
+    p.R = rpw <= 3 ? (rpw == 3 ? 3 : 4) : rpw <= 4 ? 4 : rpw <= 6 ? 6 : rpw <= 8 ? 8 : rpw <= 12 ? 12 : rpw <= 16 ? 16 : 24;
     const int chunks = nr * 4 * 4 * mp;
     p.lds_a = (chunks + 63) / 64 * 64 * 16;
     return p;
@@ -161,7 +179,7 @@ __device__ __forceinline__ void smallm_engine(const uint4 *__restrict__ codes,
     const int G = K >> 5;
     const int ng = g_hi - g_lo;
     const int nr = (ng + 3) >> 2;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n_l = lane & 15, q = lane >> 4;
     const int ntiles = (N + 15) >> 4;
     const int tpw = kSmallMWaves / KW;             // tiles per step of the workgroup
@@ -180,11 +198,13 @@ __device__ __forceinline__ void smallm_engine(const uint4 *__restrict__ codes,
         const int row = min(tile * 16 + n_l, N - 1);
         const uint4 *crow = codes + (long)row * G;
         const uint16_t *srow = steps + (long)row * G;
+        int n = 0;  // 16-byte code loads issued: one instruction each (wave-uniform)
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             if (r0 + r < re) {
                 const int g0 = g_lo + 4 * (r0 + r);
                 qr[r] = crow[min(g0 + q, g_hi - 1)];
+                ++n;
                 if (STEPS8 && g0 + 3 < g_hi) {
                     sr[r] = *reinterpret_cast<const uint2 *>(srow + g0);
                 } else {
@@ -196,16 +216,17 @@ __device__ __forceinline__ void smallm_engine(const uint4 *__restrict__ codes,
                 }
             }
         }
+        return n;
     };
-
-    int tg = tg_first;
-    if (tg * tpw + tsub < ntiles && rb < re) load_rounds(tg * tpw + tsub, rb);
 
     // ---- stage the slice of the activations into A ------------------------
     // Chunk c = (gl*4 + q)*Mp + m.  Every lane of a direct-to-LDS instruction
     // moves one chunk; chunks of rows >= M, of groups past the slice and past
     // the last chunk read clamped valid addresses (their LDS is either never
-    // used, overwritten with zeros below, or padding).
+    // used, overwritten with zeros below, or padding).  The activations go
+    // out first and the first tile's weights right behind them: a wave's
+    // loads come back in issue order, so the staging below waits only for
+    // its own chunks while the weights are still in flight.
     const int nchunks = nr << (mp_log2 + 4);
     if (xvec) {
         for (int c0 = wave * 64; c0 < nchunks; c0 += kSmallMWaves * 64) {
@@ -214,18 +235,35 @@ __device__ __forceinline__ void smallm_engine(const uint4 *__restrict__ codes,
             const int qq = (c >> mp_log2) & 3;
             const int gl = min(c >> (mp_log2 + 2), ng - 1);
             const uint16_t *src = xrow(m) + (g_lo + gl) * 32 + 8 * qq;
-            __builtin_amdgcn_global_load_lds(
-                (const __attribute__((address_space(1))) void *)src,
-                (__attribute__((address_space(3))) void *)(A + c0), 16, 0, 0);
+            // (the asm form: the compiler would make every later LDS read wait
+            // for all outstanding loads, weights included; the wait for these
+            // chunks is the explicit one below)
+            lds_dma16(src, A + c0);
         }
-        wait_vmcnt<0>();
     }
+    asm volatile("" ::: "memory");  // (the weight loads stay behind the activation loads)
+    int tg = tg_first;
+    // (a count of load instructions younger than the activation loads, never
+    // above the true one: the code loads, one instruction each; the step
+    // loads are not counted, so waiting for at most that many to be
+    // outstanding leaves the activation loads complete)
+    int wloads = 0;
+    if (tg * tpw + tsub < ntiles && rb < re) wloads = load_rounds(tg * tpw + tsub, rb);
+    if (xvec) wait_vmcnt_upto(wloads);
     lds_barrier();
 
     // Thread t visits chunks t, t + 256, ...: always activation row t & mmask.
+    // (A is read and written through an LDS-typed pointer: through the generic
+    // one these are flat accesses, which also wait for every outstanding
+    // global load, the weights included)
+    typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+    lds_u32x4 *AL = (lds_u32x4 *)A;
     const int m = tid & mmask;
     auto raw_chunk = [&](int c) __attribute__((always_inline)) {
-        if (xvec) return A[c];
+        if (xvec) {
+            const u32x4 v = AL[c];
+            return make_uint4(v.x, v.y, v.z, v.w);
+        }
         const uint16_t *src = xrow(m) + (g_lo + (c >> (mp_log2 + 2))) * 32 + 8 * ((c >> mp_log2) & 3);
         return make_uint4(src[0] | ((uint32_t)src[1] << 16), src[2] | ((uint32_t)src[3] << 16),
                           src[4] | ((uint32_t)src[5] << 16), src[6] | ((uint32_t)src[7] << 16));
@@ -238,15 +276,22 @@ __device__ __forceinline__ void smallm_engine(const uint4 *__restrict__ codes,
         u16x2 vmx = {0, 0}, vmn = {0xFFFF, 0xFFFF};
         const u16x2 one = {1, 1};
         if (m < M) {
-            for (int c = tid; c < nchunks; c += kSmallMWaves * 64) {
-                if ((c >> (mp_log2 + 2)) >= ng) continue;
-                const uint4 v = raw_chunk(c);
-                const uint32_t w4v[4] = {v.x, v.y, v.z, v.w};
+            // four chunks per step, their reads issued together
+            for (int c0 = tid; c0 < nchunks; c0 += 4 * kSmallMWaves * 64) {
+                uint4 v[4];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const u16x2 mag = __builtin_bit_cast(u16x2, w4v[i] & 0x7FFF7FFFu);
-                    vmx = __builtin_elementwise_max(vmx, mag);
-                    vmn = __builtin_elementwise_min(vmn, mag - one);
+                for (int u = 0; u < 4; ++u) v[u] = raw_chunk(min(c0 + u * kSmallMWaves * 64, nchunks - 1));
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int c = c0 + u * kSmallMWaves * 64;
+                    const bool ok = c < nchunks && (c >> (mp_log2 + 2)) < ng;
+                    const uint32_t w4v[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const u16x2 mag = __builtin_bit_cast(u16x2, w4v[i] & 0x7FFF7FFFu);
+                        vmx = ok ? __builtin_elementwise_max(vmx, mag) : vmx;
+                        vmn = ok ? __builtin_elementwise_min(vmn, mag - one) : vmn;
+                    }
                 }
             }
         }
@@ -285,10 +330,18 @@ __device__ __forceinline__ void smallm_engine(const uint4 *__restrict__ codes,
     // Conversion in place: fp16 chunks are only permuted to pair order; bf16
     // chunks become fp16 x * 2^s_m; chunks of groups past the slice become 0.
     if (m < M) {
-        for (int c = tid; c < nchunks; c += kSmallMWaves * 64) {
+        // four chunks per step: reads first, then the converted chunks
+        for (int c0 = tid; c0 < nchunks; c0 += 4 * kSmallMWaves * 64) {
+            uint4 vv[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) vv[u] = raw_chunk(min(c0 + u * kSmallMWaves * 64, nchunks - 1));
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+            const int c = c0 + u * kSmallMWaves * 64;
+            if (c >= nchunks) break;
             uint4 o = make_uint4(0, 0, 0, 0);
             if ((c >> (mp_log2 + 2)) < ng) {
-                const uint4 v = raw_chunk(c);
+                const uint4 v = vv[u];
                 if (dt != 0) {
                     // x_i is half (i & 1) of word i >> 1; output word p = (x_p, x_{p+4})
                     auto f = [&](uint32_t w, int hi) __attribute__((always_inline)) {
@@ -307,7 +360,8 @@ __device__ __forceinline__ void smallm_engine(const uint4 *__restrict__ codes,
                     o.w = __builtin_amdgcn_perm(v.w, v.y, 0x07060302u);
                 }
             }
-            A[c] = o;
+            AL[c] = u32x4{o.x, o.y, o.z, o.w};
+            }
         }
     }
     lds_barrier();
@@ -336,50 +390,57 @@ __device__ __forceinline__ void smallm_engine(const uint4 *__restrict__ codes,
     }
 
     const h2 k8 = __builtin_bit_cast(h2, 0x00080008u);  // 8 * 2^-24 in both halves
-    const h8 *Ah = reinterpret_cast<const h8 *>(A);
+    const __attribute__((address_space(3))) h8 *Ah = (const __attribute__((address_space(3))) h8 *)A;
     const int arow = (q << mp_log2) + (n_l & mmask);   // this lane's A chunk within a group
 
     for (; tg * tpw < ntiles; tg += tg_stride) {
         const int tile = tg * tpw + tsub;
         f4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
         if (tile < ntiles) {
-            for (int r0 = rb; r0 < re; r0 += R) {
-                if (r0 > rb) load_rounds(tile, r0);
+            // one round: its 4 groups on the matrix cores, the steps applied per group
+            auto round = [&](const uint4 &qw, const uint2 &sw, int rr) __attribute__((always_inline)) {
+                h8 a[4];
 #pragma unroll
-                for (int r = 0; r < R; ++r) {
-                    if (r0 + r < re) {
-                        const int rr = r0 + r;
-                        h8 a[4];
+                for (int j = 0; j < 4; ++j) a[j] = Ah[((4 * rr + j) << (mp_log2 + 2)) + arow];
+                uint32_t w[4] = {qw.x, qw.y, qw.z, qw.w};
+                transpose_lane_groups(w);
+                h8 b[4];
 #pragma unroll
-                        for (int j = 0; j < 4; ++j) a[j] = Ah[((4 * rr + j) << (mp_log2 + 2)) + arow];
-                        uint32_t w[4] = {qr[r].x, qr[r].y, qr[r].z, qr[r].w};
-                        transpose_lane_groups(w);
-                        h8 b[4];
+                for (int j = 0; j < 4; ++j) {
+                    // (c - 8) * 2^-24 for the pairs (c0,c4) (c1,c5) (c2,c6) (c3,c7)
+                    const h2 p0 = as_h2(w[j] & 0x000F000Fu) - k8;
+                    const h2 p1 = as_h2((w[j] >> 4) & 0x000F000Fu) - k8;
+                    const h2 p2 = as_h2((w[j] >> 8) & 0x000F000Fu) - k8;
+                    const h2 p3 = as_h2((w[j] >> 12) & 0x000F000Fu) - k8;
+                    b[j][0] = p0[0]; b[j][1] = p0[1]; b[j][2] = p1[0]; b[j][3] = p1[1];
+                    b[j][4] = p2[0]; b[j][5] = p2[1]; b[j][6] = p3[0]; b[j][7] = p3[1];
+                }
+                const f4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
+                f4 d[4];
 #pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            // (c - 8) * 2^-24 for the pairs (c0,c4) (c1,c5) (c2,c6) (c3,c7)
-                            const h2 p0 = as_h2(w[j] & 0x000F000Fu) - k8;
-                            const h2 p1 = as_h2((w[j] >> 4) & 0x000F000Fu) - k8;
-                            const h2 p2 = as_h2((w[j] >> 8) & 0x000F000Fu) - k8;
-                            const h2 p3 = as_h2((w[j] >> 12) & 0x000F000Fu) - k8;
-                            b[j][0] = p0[0]; b[j][1] = p0[1]; b[j][2] = p1[0]; b[j][3] = p1[1];
-                            b[j][4] = p2[0]; b[j][5] = p2[1]; b[j][6] = p3[0]; b[j][7] = p3[1];
-                        }
-                        const f4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
-                        f4 d[4];
+                for (int j = 0; j < 4; ++j)
+                    d[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[j], b[j], zero, 0, 0, 0);
+                const float st[4] = {bf16_to_f32(sw.x & 0xFFFFu), bf16_to_f32(sw.x >> 16),
+                                     bf16_to_f32(sw.y & 0xFFFFu), bf16_to_f32(sw.y >> 16)};
 #pragma unroll
-                        for (int j = 0; j < 4; ++j)
-                            d[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[j], b[j], zero, 0, 0, 0);
-                        const float st[4] = {bf16_to_f32(sr[r].x & 0xFFFFu), bf16_to_f32(sr[r].x >> 16),
-                                             bf16_to_f32(sr[r].y & 0xFFFFu), bf16_to_f32(sr[r].y >> 16)};
+                for (int j = 0; j < 4; ++j) {
+                    acc[0] = __builtin_fmaf(d[j][0], st[j], acc[0]);
+                    acc[1] = __builtin_fmaf(d[j][1], st[j], acc[1]);
+                    acc[2] = __builtin_fmaf(d[j][2], st[j], acc[2]);
+                    acc[3] = __builtin_fmaf(d[j][3], st[j], acc[3]);
+                }
+            };
+            if (rb + R == re) {
+                // exactly one batch of R rounds: straight-line code, so that the
+                // rounds can overlap (a guard per round would cut them apart)
 #pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            acc[0] = __builtin_fmaf(d[j][0], st[j], acc[0]);
-                            acc[1] = __builtin_fmaf(d[j][1], st[j], acc[1]);
-                            acc[2] = __builtin_fmaf(d[j][2], st[j], acc[2]);
-                            acc[3] = __builtin_fmaf(d[j][3], st[j], acc[3]);
-                        }
-                    }
+                for (int r = 0; r < R; ++r) round(qr[r], sr[r], rb + r);
+            } else {
+                for (int r0 = rb; r0 < re; r0 += R) {
+                    if (r0 > rb) load_rounds(tile, r0);
+#pragma unroll
+                    for (int r = 0; r < R; ++r)
+                        if (r0 + r < re) round(qr[r], sr[r], r0 + r);
                 }
             }
         }

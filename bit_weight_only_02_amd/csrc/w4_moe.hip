@@ -233,8 +233,11 @@ typedef void (*MoeFn)(const uint4 *, const uint16_t *, int64_t, int64_t, int, in
 template <bool S8>
 MoeFn pick_moe_s(int R) {
     switch (R) {
+        case 3: return moe_kernel<3, S8>;
         case 4: return moe_kernel<4, S8>;
+        case 6: return moe_kernel<6, S8>;
         case 8: return moe_kernel<8, S8>;
+        case 12: return moe_kernel<12, S8>;
         case 16: return moe_kernel<16, S8>;
         case 24: return moe_kernel<24, S8>;
     }

@@ -89,24 +89,116 @@ def measured_traffic():
     return rec.get("traffic_bytes_per_launch"), name.split("(")[0].replace("void ", "")
 
 
-def cpu_baseline(codes, steps, x, ids, min_seconds: float = 10.0):
-    """The oracle, as it stands, on the same workload: the full vocabulary-head
-    GEMV (OpenMP over rows) plus the gather, repeated for >= min_seconds."""
+def cpu_model() -> str:
+    """The host CPU's model name (from /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def _median_rate(nbytes: float, fn, groups: int = 3, min_seconds: float = 2.0) -> float:
+    """Median over `groups` timed groups (each repeating fn for >= min_seconds)
+    of nbytes / (seconds per call), in GB/s."""
+    rates = []
+    for _ in range(groups):
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            fn()
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= min_seconds:
+                break
+        rates.append(gbps(nbytes, el / reps))
+    return sorted(rates)[len(rates) // 2]
+
+
+def cpu_baseline(codes, steps, x, ids):
+    """The oracle, as it stands, on the headline workload: all cores (OpenMP
+    over rows) on full steps (the 262144x1536 GEMV plus the 64-row gather), and
+    one core on a 16384-row sample of the GEMV plus the gather; each the median
+    of 3 timed groups of >= 2 s."""
     import oracle
     import synth
-    reps, t0 = 0, time.perf_counter()
-    while True:
-        oracle.gemv(codes, steps, V, K, x, synth.BF16, threads=True)
-        oracle.gather(codes, steps, V, K, ids)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= min_seconds:
-            break
-    per_step = el / reps
-    return {"value": round(gbps(STEP_BYTES, per_step), 3), "unit": "GB/s",
-            "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"{reps} full steps (262144x1536 GEMV + 64-row gather), "
-                      f"{per_step:.3f} s per step"}
+    full = lambda: (oracle.gemv(codes, steps, V, K, x, synth.BF16, threads=True),  # noqa: E731
+                    oracle.gather(codes, steps, V, K, ids))
+    rows = 16384
+    one = lambda: (oracle.gemv(codes, steps, V, K, x, synth.BF16, rows=(0, rows)),  # noqa: E731
+                   oracle.gather(codes, steps, V, K, ids))
+    all_cores = _median_rate(STEP_BYTES, full)
+    single = _median_rate(gemv_bytes(rows, K) + gather_bytes(NIDS, K), one)
+    return {"value": round(all_cores, 3), "unit": "GB/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": "full steps (262144x1536 GEMV + 64-row gather), median of 3 groups of >= 2 s",
+            "single_thread": {"value": round(single, 3), "unit": "GB/s",
+                              "sample": f"{rows}-row GEMV sample + 64-row gather, median of 3 groups of >= 2 s"},
+            "cpu_model": cpu_model()}
+
+
+def cpu_baselines(np, synth):
+    """The oracle on a bounded sample of every configuration, one core and (where
+    the oracle has a threaded form) all cores, each the median of 3 timed
+    groups, in the configuration's own unit."""
+    import oracle
+    rng = np.random.default_rng(7)
+    out = {"cpu_model": cpu_model(), "threads_all_cores": oracle.num_threads()}
+
+    def gemv_rates(N, Kx, rows_one):
+        c, st = synth.w4_matrix(rng, N, Kx)
+        xv = synth.activations(rng, Kx, synth.F16)
+        allc = _median_rate(gemv_bytes(N, Kx), lambda: oracle.gemv(c, st, N, Kx, xv, synth.F16, threads=True))
+        one = _median_rate(gemv_bytes(rows_one, Kx),
+                           lambda: oracle.gemv(c, st, N, Kx, xv, synth.F16, rows=(0, rows_one)))
+        return one, allc
+    # single GEMV 2048x1536 (GB/s)
+    one, allc = gemv_rates(2048, 1536, 2048)
+    out["single_gemv_2048x1536"] = {"unit": "GB/s", "one_core": round(one, 3), "all_cores": round(allc, 3),
+                                    "sample": "whole product"}
+    # 35-layer decode sweep (us per sweep): one layer's four products, times 35
+    shapes = [(2560, 1536), (1536, 2048), (16384, 1536), (1536, 8192)]
+    t_one = t_all = 0.0
+    for N, Kx in shapes:
+        one, allc = gemv_rates(N, Kx, min(N, 2048))
+        t_one += gemv_bytes(N, Kx) / (one * 1e9)
+        t_all += gemv_bytes(N, Kx) / (allc * 1e9)
+    out["decode_sweep_35_layers"] = {"unit": "us per sweep", "one_core": round(35 * t_one * 1e6, 1),
+                                     "all_cores": round(35 * t_all * 1e6, 1),
+                                     "sample": "one layer's four products (one core: up to 2048 rows of each), x35"}
+    # small-M products at M = 16 (us per set of the four shapes; the oracle's
+    # product of M rows has no threaded form): 256 rows of each shape
+    t = 0.0
+    for N, Kx in shapes:
+        c, st = synth.w4_matrix(rng, 256, Kx)
+        X = synth.activations(rng, (16, Kx), synth.F16)
+        r = _median_rate(w4_bytes(256, Kx), lambda: oracle.gemm(c, st, 256, Kx, X, synth.F16, 16), min_seconds=1.0)
+        t += w4_bytes(N, Kx) / (r * 1e9)
+    out["small_m_M16_set"] = {"unit": "us per set", "one_core": round(t * 1e6, 1), "all_cores": None,
+                              "sample": "256 rows of each of the four shapes at M = 16, scaled by rows"}
+    # expert layer, one token (us per token): 8 experts' gate/up and down with
+    # the routed sum, one layer, times 30 (the oracle's expert product has no
+    # threaded form)
+    E = 8
+    ids = np.arange(E, dtype=np.int32).reshape(1, E)
+    route = np.full((1, E), 1.0 / E, dtype=np.float32)
+    gc, gs = synth.w4_matrix(rng, E * 1408, 2816)
+    dc, ds = synth.w4_matrix(rng, E * 2816, 704)
+    x0 = synth.activations(rng, (1, 2816), synth.BF16)
+    G = synth.activations(rng, (E, 1408), synth.BF16)
+
+    def layer():
+        oracle.moe(gc, gs, 1408 * 2816 // 8, 1408 * 2816 // 32, 1408, 2816, x0, synth.BF16, 0, ids, E,
+                   n_experts=E)
+        oracle.moe(dc, ds, 2816 * 704 // 8, 2816 * 704 // 32, 2816, 704, G, synth.BF16, 1, ids, E,
+                   n_experts=E, route_w=route, ldx=1408)
+    lb = E * (w4_bytes(1408, 2816) + w4_bytes(2816, 704))
+    r = _median_rate(lb, layer, min_seconds=1.0)
+    out["moe_30_layers_top8_T1"] = {"unit": "us per token", "one_core": round(30 * lb / (r * 1e9) * 1e6, 1),
+                                    "all_cores": None, "sample": "one layer of 8 experts, x30"}
+    return out
 
 
 class Timer:
@@ -191,6 +283,29 @@ def extra_single_gemv(w4, torch, np, synth, timer):
            "weight_GBps_graph": round(gbps(wb, graph), 1),
            "frac_of_peak_graph": round(gbps(wb, graph) / HBM_PEAK_GBPS, 4)}
     del cs, ss
+    torch.cuda.empty_cache()
+    # Steady state in one multi-matrix launch: 128 independent copies of the
+    # matrix stacked like an expert table and run by the expert-indexed entry
+    # point (ids 0..127, one activation row per matrix); two such tables of
+    # 227 MB each, alternated, so that no launch finds its weights in the
+    # Infinity Cache.
+    per_launch = 128
+    tabs = [(c0.repeat(per_launch, 1).contiguous(), s0.repeat(per_launch, 1).contiguous()) for _ in range(2)]
+    ids = torch.arange(per_launch, dtype=torch.int32, device="cuda").view(4, per_launch // 4)
+    X = dx.view(1, Kc).repeat(per_launch, 1).contiguous()
+    Y = torch.empty((per_launch, N), device="cuda")
+
+    def multi(i):
+        tc, ts = tabs[i % 2]
+        w4.w4_moe_gemv_ids(tc, ts, N * Kc // 8, N * Kc // 32, N, Kc, X, ids, x_per_pair=True,
+                           n_experts=per_launch, Y=Y)
+    mg = timer.graph_per_call(multi, 20)
+    per_gemv = mg / per_launch
+    out["multi_matrix_launch"] = {"matrices_per_launch": per_launch, "us_per_launch_graph": round(mg * 1e6, 2),
+                                  "us_per_gemv": round(per_gemv * 1e6, 3),
+                                  "weight_GBps": round(gbps(wb, per_gemv), 1),
+                                  "frac_of_peak": round(gbps(wb, per_gemv) / HBM_PEAK_GBPS, 4)}
+    del tabs
     torch.cuda.empty_cache()
     return out
 
@@ -595,6 +710,8 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-baselines", action="store_true",
+                    help="time the CPU oracle on a sample of every configuration and print its JSON")
     ap.add_argument("--no-extra", action="store_true", help="only the vocabulary-head step")
     ap.add_argument("--only", choices=["single", "sweep", "small_m", "moe", "prompt", "gather8960", "grid", "attention"],
                     help="run one secondary workload alone (kernel traces) and print its JSON")
@@ -605,6 +722,12 @@ def main(argv=None):
         return 2
 
     import numpy as np
+
+    if args.cpu_baselines:
+        import synth
+        print(json.dumps({"cpu_baselines": cpu_baselines(np, synth)}), flush=True)
+        return 0
+
     import torch
 
     import bit_weight_only_02_amd as w4

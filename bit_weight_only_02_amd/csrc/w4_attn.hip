@@ -1,13 +1,13 @@
 // Decode attention for one query token, split over the key/value cache, for
 // gfx950.
 //
-// The dev.to page "Gemma 4 on a 4 GB GPU in Plain PyTorch" (section "Step 5 -
-// Attention for One Token at a Time") reads each cached key and value once for
-// all eight query heads that share the one key/value head, split across the
-// cache in slices whose results are combined with an online softmax; its
-// section "Step 7 - Fit the Full 131,072-Token Context" gives the cache: one
-// head of width 512, one slot per position on the full layers and a 512-slot
-// ring on the sliding ones.
+// Source: the dev.to page "Gemma 4 on a 4 GB GPU in Plain PyTorch", sections
+// "Step 5 - Attention for One Token at a Time" (a grouped-query layout: eight
+// query heads over a single key/value head, the cache cut into slices whose
+// partial softmax results are merged) and "Step 7 - Fit the Full 131,072-Token
+// Context" (the cache shape: one head of width 512, a slot per position on the
+// full layers, a 512-slot ring on the sliding-window layers).  Here every
+// cached row is streamed from memory once and used for all query heads.
 //
 // attn_split_kernel: workgroup w takes keys [w*C, min(L, (w+1)*C)); its waves
 // take kU consecutive keys at a time, in turn.  Lane l holds dims

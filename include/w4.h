@@ -22,9 +22,9 @@
  *   [P1-S6] same page, "Step 6 - Read Prompts in 32-Bit on a Card Without Tensor
  *           Cores": a prompt is read in chunks of 256 tokens, each chunk a
  *           product of many activation rows with every weight matrix.
- *   [P1-S5] same page, "Step 5 - Attention for One Token at a Time": one key/
- *           value head shared by eight query heads, read once, split over the
- *           cache, slices combined with an online softmax.
+ *   [P1-S5] same page, "Step 5 - Attention for One Token at a Time": grouped
+ *           query heads over one key/value head; the cache in slices whose
+ *           partial softmax results are merged.
  *   [P1-S7] same page, "Step 7 - Fit the Full 131,072-Token Context": the
  *           cache is one head of width 512 per layer.
  *   [P3]    anyesh.me, "Running a 26B MoE on an 8 GB Jetson by streaming experts
@@ -191,11 +191,10 @@ int w4_grid_to_codes(const uint16_t *table, int32_t N, int32_t K, uint32_t *code
                      uint16_t *steps, void *stream);
 
 /*
- * Decode attention for one query token [P1-S5, P1-S7]: the H <= 8 query heads
- * share one key/value head (P1-S5: each cached key and value is read once for
- * all of them, split across the cache, slices combined with an online
- * softmax; P1-S7: head width 512, a full cache of one slot per position or a
- * 512-slot ring).
+ * Decode attention for one query token [P1-S5, P1-S7]: H <= 8 query heads over
+ * one key/value head of width 256 or 512; the cache is a slot per position or
+ * a ring of slots (the page's sliding layers use 512).  Every cached row is
+ * streamed once for all heads, in slices whose partial results are merged.
  *   o[h][d] = sum_j p[h][j] * V[j][d],  p[h][.] = softmax_j(scale * q[h] . K[j])
  * over the L cached positions j given (a ring passes its valid slots: the
  * result does not depend on their order).

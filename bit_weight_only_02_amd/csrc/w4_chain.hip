@@ -28,24 +28,27 @@
 // products.  u goes to fp16 one group of 32 at a time, each group scaled by
 // its own power of two (its largest magnitude lands in [2^14, 2^15)), and the
 // group's partial sums are scaled back by the inverse power of two with the
-// group's step; r comes from fp32 sums of squares taken in a fixed order.
+// group's step.  r comes from the sum of squares of u: per chunk of four in
+// fp32 on the group-scaled values (which are below 2^15, so no overflow), each
+// chunk's sum scaled back into fp64, then added in a fixed order (a thread's
+// chunks ascending, a butterfly over the wave, the waves in order).
 //
-// Per step i (one workgroup of eight waves per CU; workgroup b owns the
+// Per step i (one workgroup of ten waves per CU; workgroup b owns the
 // contiguous row block [b*ceil(N/nwg), ...) of every matrix):
-//   1. input: x0 for the first matrix; else waves 0..3 read the leading K
-//      cells of step i-1 (agent-coherent loads), write each group as fp16
-//      with its scale into LDS and their sums of squares (one per wave);
-//      meanwhile waves 6..7 wait for their copy of this step's weights;
-//   2. waves 6..7 request the next step's weight block into the other LDS
-//      buffer (direct-to-LDS loads that only they wait for, at the start of
-//      the next step: neither the exchange loads of waves 0..3 nor any row
-//      computation queue behind weight traffic);
-//   3. waves 0..3 compute the block's rows from LDS and store y, and the
-//      cells of the rows the next step needs.  Wave w runs on SIMD w mod 4,
-//      so these are one wave per SIMD; a second computing wave on a SIMD
-//      (waves 4 and 5 did so) measured slower over the decode sweep: its
-//      rows finish last and hold up the next exchange.  Waves 4..5 only
-//      join the workgroup barriers.
+//   1. input: x0 for the first matrix; else the eight computing waves read
+//      the leading K cells of step i-1 (agent-coherent loads), write each
+//      group as fp16 into LDS with its scale and its offset sums, and one sum
+//      of squares per wave; meanwhile the two copy waves wait for their copy
+//      of this step's weights;
+//   2. the copy waves request the next step's weight block into the other
+//      LDS buffer (direct-to-LDS loads that only they wait for, at the start
+//      of the next step: neither the exchange loads nor any row computation
+//      queue behind weight traffic), then clear this workgroup's cells of
+//      step i-2 and bring in a later descriptor and its plan;
+//   3. the eight computing waves (two per SIMD: wave w runs on SIMD w mod 4,
+//      so one wave's waits are filled by the other's work) compute the
+//      block's rows from LDS, scale them by 1/r, and store y and the cells of
+//      the rows the next step needs.
 // The descriptors are copied into LDS once (the first kDescCache of them).
 #include <cstdio>
 #include <cstdlib>

@@ -363,7 +363,8 @@ int w4_rms_renorm(const float *v, int64_t ldv, int32_t K, int32_t rows, void *ou
  * output satisfies |y[n] - sum_k w(n,k) x[k]| <= 1e-3 * sum_k |w(n,k) x[k]| on
  * that exact x: the products run on u, rounded to fp16 one group of 32 at a
  * time with the group's own power-of-two scale, and each finished output is
- * multiplied by 1/r (r from fp32 sums of squares in a fixed order), so no
+ * multiplied by 1/r (r from sums of squares taken four values at a time in
+ * fp32 and added in fp64 in a fixed order), so no
  * product waits for r before its dot products.  Results are bitwise
  * reproducible from call to call.
  *   desc: DEVICE array of n_mats records (it is read by the kernel).

@@ -147,12 +147,16 @@ def cpu_baselines(np, synth):
     rng = np.random.default_rng(7)
     out = {"cpu_model": cpu_model(), "threads_all_cores": oracle.num_threads()}
 
+    def done(name):
+        print(f"cpu baseline: {name} timed", file=sys.stderr, flush=True)
+
     def gemv_rates(N, Kx, rows_one):
         c, st = synth.w4_matrix(rng, N, Kx)
         xv = synth.activations(rng, Kx, synth.F16)
         allc = _median_rate(gemv_bytes(N, Kx), lambda: oracle.gemv(c, st, N, Kx, xv, synth.F16, threads=True))
         one = _median_rate(gemv_bytes(rows_one, Kx),
                            lambda: oracle.gemv(c, st, N, Kx, xv, synth.F16, rows=(0, rows_one)))
+        done(f"{N}x{Kx} product")
         return one, allc
     # single GEMV 2048x1536 (GB/s)
     one, allc = gemv_rates(2048, 1536, 2048)
@@ -176,6 +180,7 @@ def cpu_baselines(np, synth):
         X = synth.activations(rng, (16, Kx), synth.F16)
         r = _median_rate(w4_bytes(256, Kx), lambda: oracle.gemm(c, st, 256, Kx, X, synth.F16, 16), min_seconds=1.0)
         t += w4_bytes(N, Kx) / (r * 1e9)
+        done(f"small-M {N}x{Kx}")
     out["small_m_M16_set"] = {"unit": "us per set", "one_core": round(t * 1e6, 1), "all_cores": None,
                               "sample": "256 rows of each of the four shapes at M = 16, scaled by rows"}
     # expert layer, one token (us per token): 8 experts' gate/up and down with
@@ -196,6 +201,7 @@ def cpu_baselines(np, synth):
                    n_experts=E, route_w=route, ldx=1408)
     lb = E * (w4_bytes(1408, 2816) + w4_bytes(2816, 704))
     r = _median_rate(lb, layer, min_seconds=1.0)
+    done("expert layer")
     out["moe_30_layers_top8_T1"] = {"unit": "us per token", "one_core": round(30 * lb / (r * 1e9) * 1e6, 1),
                                     "all_cores": None, "sample": "one layer of 8 experts, x30"}
     return out

@@ -9,18 +9,31 @@
 // full layers, a 512-slot ring on the sliding-window layers).  Here every
 // cached row is streamed from memory once and used for all query heads.
 //
-// attn_split_kernel: workgroup w takes keys [w*C, min(L, (w+1)*C)); its waves
-// take kU consecutive keys at a time, in turn.  Lane l holds dims
-// [l*DPL, (l+1)*DPL) of q (pre-scaled by scale * log2 e), of the keys and values
-// and of the accumulators of all kH heads, so one 16-byte load per lane reads a
-// whole 1 KiB key row.  A score is the whole-wave sum of the lanes' partial
-// dots (row shifts and broadcasts, then read from the last lane: the same value
-// in every lane); each head keeps a running maximum m, a running sum l of
-// 2^(s - m) and the accumulated values, rescaled when m grows.  The waves of a
-// workgroup are merged in wave order into one partial {m, l, acc} per head.
-// attn_merge_kernel: output (h, d) = sum_w 2^(m_w - M) acc_w / sum_w 2^(m_w - M)
-// l_w over the partials (a running merge over each quarter of them, then the
-// quarters in order), M the largest m_w.
+// attn_split_kernel: workgroup b's wave w takes the keys
+// [(4b + w) * KPW, ...) (KPW a multiple of 16, at most L), 16 at a time.  The
+// scores of a tile come from the matrix cores: S^T = K_tile Q^T with
+// v_mfma_f32_16x16x32_bf16, the tile's 16 key rows as the A operand (one
+// 16-byte piece of a key row per lane, straight from memory) and the query
+// heads as the B operand (held in registers for the whole range; heads past H
+// are zero).  Lane i then holds the scores of keys 4(i/16)..+3 of the tile for
+// head i%16, so each head's running maximum is an in-lane maximum and two
+// exchanges across lane groups, and its running sum is kept per lane and added
+// over the four lane groups at the end.  The weighted sum of the values stays
+// on the VALU in fp32 (the matrix cores would need the tile's values
+// transposed, and bf16 weights would cost the output precision): lane i holds
+// dims [i*DPL, (i+1)*DPL) of all heads' accumulators, reads each key's weights
+// for the 8 heads from a small LDS buffer written by the score lanes, and
+// multiplies them into the value row it loaded (one 16-byte load per lane per
+// key).  The next tile's keys and values are requested while the current one is
+// used: each key block right after its matrix instruction, each value row right
+// after its multiply-adds (clamped to the last key of the range, which stays
+// in the caches, when there is no next tile).  The waves of a workgroup are then
+// merged in wave order into one partial {m, l, acc} per head.
+// attn_merge_kernel: output (h, d) = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s -
+// M) l_s over the partials, M the largest m_s: the weights first (one pass
+// over the partials' maxima), then sixteen interleaved sixteenths of the
+// partials summed with all their loads in flight, then the sixteenths in
+// order.
 #include <cmath>
 
 #include "w4_device.h"
@@ -30,88 +43,135 @@ namespace w4 {
 
 constexpr int kAttnH = 8;      // query heads per key/value head handled per pass
 constexpr int kAttnWaves = 4;  // waves per workgroup
-constexpr int kAttnU = 4;      // keys per wave step
+constexpr int kAttnT = 16;     // keys per tile (the matrix instruction's rows)
 
-template <int DPL>
+typedef __bf16 attn_bf8 __attribute__((ext_vector_type(8)));
+typedef float attn_f4 __attribute__((ext_vector_type(4)));
+typedef unsigned attn_u2 __attribute__((ext_vector_type(2)));
+
+// 16 bytes of a bf16 row (two 8-byte loads when rows may be only 8-byte
+// aligned)
+template <bool A16>
+__device__ __forceinline__ u32x4 attn_load16(const uint16_t *p) {
+    if constexpr (A16) {
+        return *reinterpret_cast<const u32x4 *>(p);
+    } else {
+        const attn_u2 a = *reinterpret_cast<const attn_u2 *>(p), b = *reinterpret_cast<const attn_u2 *>(p + 4);
+        return u32x4{a.x, a.y, b.x, b.y};
+    }
+}
+
+template <int DPL, bool A16>
 __global__ __launch_bounds__(64 * kAttnWaves) void attn_split_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ K, long ldk,
-    const uint16_t *__restrict__ V, long ldv, int H, int L, int C, float scale_log2,
+    const uint16_t *__restrict__ V, long ldv, int H, int L, int KPW, float scale_log2,
     float *__restrict__ ws) {
     constexpr int D = 64 * DPL;
+    constexpr int NB = D / 32;  // matrix instructions per score tile
+    typedef unsigned short vrow __attribute__((ext_vector_type(DPL)));
+    __shared__ float pl[kAttnWaves][kAttnT][kAttnH];  // a tile's weights, [key][head]
+    __shared__ float pc[kAttnWaves][kAttnH];           // the tile's rescale per head
     __shared__ float sm[kAttnWaves][kAttnH], sl[kAttnWaves][kAttnH];
     __shared__ float sacc[kAttnWaves][kAttnH][D];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int l0 = blockIdx.x * C, l1 = min(L, l0 + C);
-    typedef unsigned short us_v __attribute__((ext_vector_type(DPL)));
-    float qf[kAttnH][DPL];
+    const int n = lane & 15, g = lane >> 4;
+    const long k_lo = ((long)blockIdx.x * kAttnWaves + wave) * KPW;
+    const int k_hi = (int)min((long)L, k_lo + KPW);  // k_lo >= k_hi: an empty wave
+    // the heads as the B operand: lane i holds q[i%16][32t + 8(i/16) .. +7]
+    u32x4 qb[NB];
+    const uint16_t *qrow = q + (long)min(n, H - 1) * D + 8 * g;  // (rows past H read row H-1, then zeroed)
+#pragma unroll
+    for (int t = 0; t < NB; ++t)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t v = (uint32_t)qrow[32 * t + 2 * j] | ((uint32_t)qrow[32 * t + 2 * j + 1] << 16);
+            qb[t][j] = n < H ? v : 0u;
+        }
+    float acc[kAttnH][DPL];
 #pragma unroll
     for (int h = 0; h < kAttnH; ++h)
 #pragma unroll
-        for (int d = 0; d < DPL; ++d)
-            qf[h][d] = h < H ? bf16_to_f32(q[h * D + lane * DPL + d]) * scale_log2 : 0.0f;
-    float m[kAttnH], l[kAttnH], acc[kAttnH][DPL];
-#pragma unroll
-    for (int h = 0; h < kAttnH; ++h) {
-        m[h] = -INFINITY;
-        l[h] = 0.0f;
-#pragma unroll
         for (int d = 0; d < DPL; ++d) acc[h][d] = 0.0f;
+    float m = -INFINITY, lsum = 0.0f;  // head n's running maximum and this lane's part of its sum
+    u32x4 ka[NB];
+    vrow vr[kAttnT];
+    if (k_lo < k_hi) {
+        const int kl = (int)k_lo;
+        const uint16_t *kp = K + (long)min(kl + n, k_hi - 1) * ldk + 8 * g;
+#pragma unroll
+        for (int t = 0; t < NB; ++t) ka[t] = attn_load16<A16>(kp + 32 * t);
+#pragma unroll
+        for (int j = 0; j < kAttnT; ++j)
+            vr[j] = *reinterpret_cast<const vrow *>(V + (long)min(kl + j, k_hi - 1) * ldv + lane * DPL);
     }
-    for (int k0 = l0 + wave * kAttnU; k0 < l1; k0 += kAttnWaves * kAttnU) {
-        // the step's keys and values, all requested before any is used
-        // (keys past the range re-read the last one and get no weight)
-        us_v kr[kAttnU], vr[kAttnU];
+    for (int k0 = (int)k_lo; k0 < k_hi; k0 += kAttnT) {
+        const int nx = k0 + kAttnT;  // the next tile (or past the range)
+        // scores: S^T[key 4g + r][head n] in s[r]
+        attn_f4 s = {0.0f, 0.0f, 0.0f, 0.0f};
+        const uint16_t *kp = K + (long)min(nx + n, k_hi - 1) * ldk + 8 * g;
 #pragma unroll
-        for (int u = 0; u < kAttnU; ++u) {
-            const int key = min(k0 + u, l1 - 1);
-            kr[u] = *reinterpret_cast<const us_v *>(K + (long)key * ldk + lane * DPL);
-            vr[u] = *reinterpret_cast<const us_v *>(V + (long)key * ldv + lane * DPL);
+        for (int t = 0; t < NB; ++t) {
+            s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(attn_bf8, ka[t]),
+                                                        __builtin_bit_cast(attn_bf8, qb[t]), s, 0, 0, 0);
+            ka[t] = attn_load16<A16>(kp + 32 * t);
         }
-        float s[kAttnU][kAttnH];
+        // the tile's online-softmax step for head n (keys past the range get
+        // no weight; the tile holds at least one key of the range)
+        float sc[4];
 #pragma unroll
-        for (int u = 0; u < kAttnU; ++u)
+        for (int r = 0; r < 4; ++r) sc[r] = k0 + 4 * g + r < k_hi ? s[r] * scale_log2 : -INFINITY;
+        float tm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+        tm = fmaxf(tm, __shfl_xor(tm, 16, kWave));
+        tm = fmaxf(tm, __shfl_xor(tm, 32, kWave));
+        const float mn = fmaxf(m, tm);
+        const float corr = exp2f(m - mn);  // 0 on the first tile (m = -inf)
+        float pr[4];
 #pragma unroll
-            for (int h = 0; h < kAttnH; ++h) {
-                float t = 0.0f;
+        for (int r = 0; r < 4; ++r) pr[r] = exp2f(sc[r] - mn);
+        lsum = lsum * corr + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
+        m = mn;
+        if (n < kAttnH) {
 #pragma unroll
-                for (int d = 0; d < DPL; ++d) t = __builtin_fmaf(qf[h][d], bf16_to_f32(kr[u][d]), t);
-                t = lane_group_sum<64>(t);
-                s[u][h] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, t), 63));
-                if (k0 + u >= l1) s[u][h] = -INFINITY;
-            }
+            for (int r = 0; r < 4; ++r) pl[wave][4 * g + r][n] = pr[r];
+            if (g == 0) pc[wave][n] = corr;
+        }
+        // the values: acc[h][.] = acc[h][.] * corr[h] + sum_j p[j][h] V[j][.]
+        {
+            const float4 c0 = *reinterpret_cast<const float4 *>(&pc[wave][0]);
+            const float4 c1 = *reinterpret_cast<const float4 *>(&pc[wave][4]);
+            const float cr[kAttnH] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
 #pragma unroll
-        for (int h = 0; h < kAttnH; ++h) {
-            float mn = m[h];
+            for (int h = 0; h < kAttnH; ++h)
 #pragma unroll
-            for (int u = 0; u < kAttnU; ++u) mn = fmaxf(mn, s[u][h]);
-            const float corr = exp2f(m[h] - mn);  // 0 on the first step (m = -inf)
-            float p[kAttnU], ps = 0.0f;
+                for (int d = 0; d < DPL; ++d) acc[h][d] *= cr[h];
+        }
+        const uint16_t *vp = V + lane * DPL;
 #pragma unroll
-            for (int u = 0; u < kAttnU; ++u) {
-                p[u] = exp2f(s[u][h] - mn);  // 0 for keys past the range
-                ps += p[u];
-            }
-            l[h] = l[h] * corr + ps;
+        for (int j = 0; j < kAttnT; ++j) {
+            const float4 p0 = *reinterpret_cast<const float4 *>(&pl[wave][j][0]);
+            const float4 p1 = *reinterpret_cast<const float4 *>(&pl[wave][j][4]);
+            const float pj[kAttnH] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+            float vf[DPL];
 #pragma unroll
-            for (int d = 0; d < DPL; ++d) {
-                float a = acc[h][d] * corr;
+            for (int d = 0; d < DPL; ++d) vf[d] = bf16_to_f32(vr[j][d]);
 #pragma unroll
-                for (int u = 0; u < kAttnU; ++u) a = __builtin_fmaf(p[u], bf16_to_f32(vr[u][d]), a);
-                acc[h][d] = a;
-            }
-            m[h] = mn;
+            for (int h = 0; h < kAttnH; ++h)
+#pragma unroll
+                for (int d = 0; d < DPL; ++d) acc[h][d] = __builtin_fmaf(pj[h], vf[d], acc[h][d]);
+            vr[j] = *reinterpret_cast<const vrow *>(vp + (long)min(nx + j, k_hi - 1) * ldv);
         }
     }
-    // the waves of this workgroup merged in wave order
+    // head n's sum over the four lane groups; the waves merged in wave order
+    lsum += __shfl_xor(lsum, 16, kWave);
+    lsum += __shfl_xor(lsum, 32, kWave);
+    if (lane < kAttnH) {
+        sm[wave][lane] = m;
+        sl[wave][lane] = lsum;
+    }
 #pragma unroll
-    for (int h = 0; h < kAttnH; ++h) {
-        if (lane == 0) {
-            sm[wave][h] = m[h];
-            sl[wave][h] = l[h];
-        }
+    for (int h = 0; h < kAttnH; ++h)
 #pragma unroll
         for (int d = 0; d < DPL; ++d) sacc[wave][h][lane * DPL + d] = acc[h][d];
-    }
     __syncthreads();
     float *out = ws + (long)blockIdx.x * (2 * kAttnH + kAttnH * D);
     for (int i = threadIdx.x; i < kAttnH * D; i += 64 * kAttnWaves) {
@@ -132,80 +192,111 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_split_kernel(
     }
 }
 
-// Merge: workgroup (h, 64-dim block) with 256 threads, thread (quarter qt,
-// dim d): a running merge over slices qt, qt+4, ... (rescaled when the
-// maximum grows), then the four quarters combined in order in LDS.
-__global__ __launch_bounds__(256) void attn_merge_kernel(const float *__restrict__ ws, int S, int H, int D,
-                                                         float *__restrict__ o) {
-    __shared__ float pm[4][64], pa[4][64], pz[4][64];
-    const int h = blockIdx.y, d = blockIdx.x * 64 + (threadIdx.x & 63), qt = threadIdx.x >> 6;
+// Merge: workgroup (64-dim block, head h) of 1024 threads.  The weight of
+// partial s is c_s = 2^(m_s - M) (0 for an empty one), M the largest m_s; Z =
+// sum_s c_s l_s in ascending s; thread (w, d) sums c_s acc_s[h][d] over s = w,
+// w + 16, ... with all its loads issued first, and the sixteen sums are added
+// in order.
+constexpr int kMergeThreads = 1024;
+constexpr int kMergeParts = kMergeThreads / 64;
+constexpr int kMaxSplits = 256;
+
+__global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(const float *__restrict__ ws, int S, int H,
+                                                                   int D, float *__restrict__ o) {
+    __shared__ float cs[kMaxSplits];
+    __shared__ float pa[kMergeParts][64];
+    __shared__ float red[kMergeParts];
+    __shared__ float zs;
+    const int h = blockIdx.y, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int d = blockIdx.x * 64 + lane;
     const long stride = 2 * kAttnH + (long)kAttnH * D;
-    float M = -INFINITY, a = 0.0f, z = 0.0f;
-#pragma unroll 4
-    for (int sidx = qt; sidx < S; sidx += 4) {
-        const float *p = ws + sidx * stride;
-        const float ms = p[h];
-        if (ms == -INFINITY) continue;  // an empty slice
-        const float mn = fmaxf(M, ms);
-        const float c0 = exp2f(M - mn), c1 = exp2f(ms - mn);  // exp2(-inf) = 0 at the start
-        a = a * c0 + c1 * p[2 * kAttnH + h * D + d];
-        z = z * c0 + c1 * p[kAttnH + h];
-        M = mn;
-    }
-    pm[qt][threadIdx.x & 63] = M;
-    pa[qt][threadIdx.x & 63] = a;
-    pz[qt][threadIdx.x & 63] = z;
+    // M: the largest maximum over the partials
+    float ms = tid < S ? ws[tid * stride + h] : -INFINITY;
+    float mx = ms;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, kWave));
+    if (lane == 0) red[w] = mx;
     __syncthreads();
-    if (qt == 0 && h < H) {
-        const int t = threadIdx.x & 63;
-        float MM = -INFINITY;
-        for (int k = 0; k < 4; ++k) MM = fmaxf(MM, pm[k][t]);
-        float A = 0.0f, Z = 0.0f;
-        for (int k = 0; k < 4; ++k) {
-            const float c = pm[k][t] == -INFINITY ? 0.0f : exp2f(pm[k][t] - MM);
-            A += c * pa[k][t];
-            Z += c * pz[k][t];
-        }
-        o[h * D + d] = A / Z;
+    float M = red[0];
+#pragma unroll
+    for (int k = 1; k < kMergeParts; ++k) M = fmaxf(M, red[k]);
+    if (tid < S) cs[tid] = ms == -INFINITY ? 0.0f : exp2f(ms - M);
+    __syncthreads();
+    if (tid == 0) {
+        float z = 0.0f;
+        for (int sidx = 0; sidx < S; ++sidx) z = __builtin_fmaf(cs[sidx], ws[sidx * stride + kAttnH + h], z);
+        zs = z;
+    }
+    // this thread's sixteenth of the partials, every load in flight at once
+    constexpr int kPer = kMaxSplits / kMergeParts;
+    float v[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+        const int sidx = w + kMergeParts * k;
+        v[k] = sidx < S ? ws[sidx * stride + 2 * kAttnH + (long)h * D + d] : 0.0f;
+    }
+    float a = 0.0f;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+        const int sidx = w + kMergeParts * k;
+        if (sidx < S) a = __builtin_fmaf(cs[sidx], v[k], a);
+    }
+    pa[w][lane] = a;
+    __syncthreads();
+    if (w == 0 && h < H) {
+        float A = 0.0f;
+#pragma unroll
+        for (int k = 0; k < kMergeParts; ++k) A += pa[k][lane];
+        o[(long)h * D + d] = A / zs;
     }
 }
 
-// Splits: about 32 keys each (8 per wave), at most 256 (one per CU): 131072
-// positions took 155 us with 256 splits, 203 us with 512, 300 us with 1024; a
-// 512-slot ring 21.5 us with 16 splits, 25 us with 64.
-static int attn_splits(int L) {
-    int S = (L + 31) / 32;
-    if (S > 256) S = 256;
-    if (S > L) S = L;
-    return S < 1 ? 1 : S;
+// Work split: tiles of 16 keys, about L / 1024 keys per wave (so that
+// 256 workgroups of 4 waves cover the cache), at most 256 workgroups.
+static void attn_plan(int L, int *S, int *kpw) {
+    const int waves = kMaxSplits * kAttnWaves;
+    const int per = (L + waves - 1) / waves;
+    int k = (per + kAttnT - 1) / kAttnT * kAttnT;
+    if (k < kAttnT) k = kAttnT;
+    *kpw = k;
+    *S = (L + kAttnWaves * k - 1) / (kAttnWaves * k);
+    if (*S < 1) *S = 1;
 }
 
 size_t attn_workspace(int H, int D, int L) {
     (void)H;
-    return (size_t)attn_splits(L) * (2 * kAttnH + (size_t)kAttnH * D) * sizeof(float);
+    int S = 0, kpw = 0;
+    attn_plan(L, &S, &kpw);
+    return (size_t)S * (2 * kAttnH + (size_t)kAttnH * D) * sizeof(float);
 }
 
 hipError_t launch_attn(const uint16_t *q, int H, int D, const uint16_t *K, long ldk, const uint16_t *V,
                        long ldv, int L, float scale, float *o, void *ws, hipStream_t stream) {
-    const int S = attn_splits(L);
-    const int C = (L + S - 1) / S;
+    int S = 0, kpw = 0;
+    attn_plan(L, &S, &kpw);
+    if (S > kMaxSplits) return hipErrorInvalidConfiguration;
     const float sl2 = scale * 1.4426950408889634f;  // log2 e
     float *w = static_cast<float *>(ws);
+    const bool a16 = (reinterpret_cast<uintptr_t>(K) & 15) == 0 && (ldk & 7) == 0;
     switch (D) {
         case 512:
-            hipLaunchKernelGGL(attn_split_kernel<8>, dim3(S), dim3(64 * kAttnWaves), 0, stream, q, K, ldk, V,
-                               ldv, H, L, C, sl2, w);
+            hipLaunchKernelGGL((attn_split_kernel<8, true>), dim3(S), dim3(64 * kAttnWaves), 0, stream, q, K, ldk,
+                               V, ldv, H, L, kpw, sl2, w);
             break;
         case 256:
-            hipLaunchKernelGGL(attn_split_kernel<4>, dim3(S), dim3(64 * kAttnWaves), 0, stream, q, K, ldk, V,
-                               ldv, H, L, C, sl2, w);
+            if (a16)
+                hipLaunchKernelGGL((attn_split_kernel<4, true>), dim3(S), dim3(64 * kAttnWaves), 0, stream, q, K,
+                                   ldk, V, ldv, H, L, kpw, sl2, w);
+            else
+                hipLaunchKernelGGL((attn_split_kernel<4, false>), dim3(S), dim3(64 * kAttnWaves), 0, stream, q,
+                                   K, ldk, V, ldv, H, L, kpw, sl2, w);
             break;
         default:
             return hipErrorInvalidConfiguration;
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(attn_merge_kernel, dim3(D / 64, H), dim3(256), 0, stream, w, S, H, D, o);
+    hipLaunchKernelGGL(attn_merge_kernel, dim3(D / 64, H), dim3(kMergeThreads), 0, stream, w, S, H, D, o);
     return hipGetLastError();
 }
 

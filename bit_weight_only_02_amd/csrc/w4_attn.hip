@@ -73,7 +73,9 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_split_kernel(
     __shared__ float pc[kAttnWaves][kAttnH];           // the tile's rescale per head
     __shared__ float sm[kAttnWaves][kAttnH], sl[kAttnWaves][kAttnH];
     __shared__ float sacc[kAttnWaves][kAttnH][D];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    // (the wave index made uniform, so that the key range and every row
+    // address computed from it stay in scalar registers)
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int n = lane & 15, g = lane >> 4;
     const long k_lo = ((long)blockIdx.x * kAttnWaves + wave) * KPW;
     const int k_hi = (int)min((long)L, k_lo + KPW);  // k_lo >= k_hi: an empty wave
@@ -93,19 +95,24 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_split_kernel(
 #pragma unroll
         for (int d = 0; d < DPL; ++d) acc[h][d] = 0.0f;
     float m = -INFINITY, lsum = 0.0f;  // head n's running maximum and this lane's part of its sum
-    u32x4 ka[NB];
-    vrow vr[kAttnT];
-    if (k_lo < k_hi) {
-        const int kl = (int)k_lo;
-        const uint16_t *kp = K + (long)min(kl + n, k_hi - 1) * ldk + 8 * g;
+    // two tiles in flight: slot 0 holds the even tiles of the range, slot 1
+    // the odd ones; a slot's next tile is requested as soon as each piece of
+    // it is used
+    u32x4 ka0[NB], ka1[NB];
+    vrow vr0[kAttnT], vr1[kAttnT];
+    auto load_k = [&](u32x4 (&ka)[NB], int kt) __attribute__((always_inline)) {
+        const uint16_t *kp = K + (long)min(kt + n, k_hi - 1) * ldk + 8 * g;
 #pragma unroll
         for (int t = 0; t < NB; ++t) ka[t] = attn_load16<A16>(kp + 32 * t);
+    };
+    auto load_v = [&](vrow (&vr)[kAttnT], int kt) __attribute__((always_inline)) {
+        const uint16_t *vp = V + lane * DPL;
 #pragma unroll
-        for (int j = 0; j < kAttnT; ++j)
-            vr[j] = *reinterpret_cast<const vrow *>(V + (long)min(kl + j, k_hi - 1) * ldv + lane * DPL);
-    }
-    for (int k0 = (int)k_lo; k0 < k_hi; k0 += kAttnT) {
-        const int nx = k0 + kAttnT;  // the next tile (or past the range)
+        for (int j = 0; j < kAttnT; ++j) vr[j] = *reinterpret_cast<const vrow *>(vp + (long)min(kt + j, k_hi - 1) * ldv);
+    };
+    // one tile: keys [k0, k0 + 16) from slot (ka, vr), whose loads then move
+    // on to the tile at nx (clamped to the range's last key past its end)
+    auto tile = [&](u32x4 (&ka)[NB], vrow (&vr)[kAttnT], int k0, int nx) __attribute__((always_inline)) {
         // scores: S^T[key 4g + r][head n] in s[r]
         attn_f4 s = {0.0f, 0.0f, 0.0f, 0.0f};
         const uint16_t *kp = K + (long)min(nx + n, k_hi - 1) * ldk + 8 * g;
@@ -160,6 +167,18 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_split_kernel(
                 for (int d = 0; d < DPL; ++d) acc[h][d] = __builtin_fmaf(pj[h], vf[d], acc[h][d]);
             vr[j] = *reinterpret_cast<const vrow *>(vp + (long)min(nx + j, k_hi - 1) * ldv);
         }
+    };
+    if (k_lo < k_hi) {
+        const int kl = (int)k_lo;
+        load_k(ka0, kl);
+        load_v(vr0, kl);
+        load_k(ka1, kl + kAttnT);
+        load_v(vr1, kl + kAttnT);
+        for (int k0 = kl; k0 < k_hi; k0 += 2 * kAttnT) {
+            tile(ka0, vr0, k0, k0 + 2 * kAttnT);
+            if (k0 + kAttnT >= k_hi) break;
+            tile(ka1, vr1, k0 + kAttnT, k0 + 3 * kAttnT);
+        }
     }
     // head n's sum over the four lane groups; the waves merged in wave order
     lsum += __shfl_xor(lsum, 16, kWave);
@@ -192,11 +211,12 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_split_kernel(
     }
 }
 
-// Merge: workgroup (64-dim block, head h) of 1024 threads.  The weight of
-// partial s is c_s = 2^(m_s - M) (0 for an empty one), M the largest m_s; Z =
-// sum_s c_s l_s in ascending s; thread (w, d) sums c_s acc_s[h][d] over s = w,
-// w + 16, ... with all its loads issued first, and the sixteen sums are added
-// in order.
+// Merge: workgroup (64-dim block, head h) of 1024 threads.  Every load is
+// issued first: thread (w, d) its sixteenth of the partials' values for
+// (h, d) -- s = w, w + 16, ... -- and thread s < S partial s's maximum and sum.
+// Then M = the largest m_s, c_s = 2^(m_s - M) (0 for an empty partial), Z =
+// sum_s c_s l_s (a fixed-order sum within each wave, then the waves in order),
+// each thread's sum of c_s acc_s[h][d], and the sixteen sums in order.
 constexpr int kMergeThreads = 1024;
 constexpr int kMergeParts = kMergeThreads / 64;
 constexpr int kMaxSplits = 256;
@@ -205,13 +225,19 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(const float *
                                                                    int D, float *__restrict__ o) {
     __shared__ float cs[kMaxSplits];
     __shared__ float pa[kMergeParts][64];
-    __shared__ float red[kMergeParts];
-    __shared__ float zs;
+    __shared__ float red[kMergeParts], redz[kMergeParts];
     const int h = blockIdx.y, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int d = blockIdx.x * 64 + lane;
     const long stride = 2 * kAttnH + (long)kAttnH * D;
-    // M: the largest maximum over the partials
-    float ms = tid < S ? ws[tid * stride + h] : -INFINITY;
+    constexpr int kPer = kMaxSplits / kMergeParts;
+    float v[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+        const int sidx = w + kMergeParts * k;
+        v[k] = sidx < S ? ws[sidx * stride + 2 * kAttnH + (long)h * D + d] : 0.0f;
+    }
+    const float ms = tid < S ? ws[tid * stride + h] : -INFINITY;
+    const float ls = tid < S ? ws[tid * stride + kAttnH + h] : 0.0f;
     float mx = ms;
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, kWave));
@@ -220,21 +246,11 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(const float *
     float M = red[0];
 #pragma unroll
     for (int k = 1; k < kMergeParts; ++k) M = fmaxf(M, red[k]);
-    if (tid < S) cs[tid] = ms == -INFINITY ? 0.0f : exp2f(ms - M);
+    const float c = ms == -INFINITY ? 0.0f : exp2f(ms - M);
+    if (tid < S) cs[tid] = c;
+    const float zw = lane_group_sum<64>(c * ls);  // the wave's sum, complete in its last lane
+    if (lane == 63) redz[w] = zw;
     __syncthreads();
-    if (tid == 0) {
-        float z = 0.0f;
-        for (int sidx = 0; sidx < S; ++sidx) z = __builtin_fmaf(cs[sidx], ws[sidx * stride + kAttnH + h], z);
-        zs = z;
-    }
-    // this thread's sixteenth of the partials, every load in flight at once
-    constexpr int kPer = kMaxSplits / kMergeParts;
-    float v[kPer];
-#pragma unroll
-    for (int k = 0; k < kPer; ++k) {
-        const int sidx = w + kMergeParts * k;
-        v[k] = sidx < S ? ws[sidx * stride + 2 * kAttnH + (long)h * D + d] : 0.0f;
-    }
     float a = 0.0f;
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
@@ -244,10 +260,13 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(const float *
     pa[w][lane] = a;
     __syncthreads();
     if (w == 0 && h < H) {
-        float A = 0.0f;
+        float A = 0.0f, Z = 0.0f;
 #pragma unroll
-        for (int k = 0; k < kMergeParts; ++k) A += pa[k][lane];
-        o[(long)h * D + d] = A / zs;
+        for (int k = 0; k < kMergeParts; ++k) {
+            A += pa[k][lane];
+            Z += redz[k];
+        }
+        o[(long)h * D + d] = A / Z;
     }
 }
 

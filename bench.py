@@ -59,8 +59,9 @@ def gather_bytes(n_ids: int, k: int) -> int:
 STEP_BYTES = gemv_bytes(V, K) + gather_bytes(NIDS, K)
 
 
-GEMV_SOURCES = ["bit_weight_only_02_amd/csrc/w4_gemv.hip", "bit_weight_only_02_amd/csrc/w4_device.h"]
-TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "gemv_vocab_head_traffic.json")
+GEMV_SOURCES = ["bit_weight_only_02_amd/csrc/w4_gemv.hip", "bit_weight_only_02_amd/csrc/w4_device.h",
+                "bit_weight_only_02_amd/csrc/w4_gather.h"]
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "gemv_gather_vocab_head_step_traffic.json")
 
 
 def kernel_source_digest() -> str:
@@ -75,9 +76,10 @@ def kernel_source_digest() -> str:
 
 
 def measured_traffic():
-    """(HBM bytes per launch, kernel instance) of the vocabulary-head GEMV from
-    the stored rocprofv3 FETCH_SIZE/WRITE_SIZE runs; (None, None) if the
-    kernel's sources have changed since they were taken."""
+    """(HBM bytes per launch, kernel instance) of the decode step's launch (the
+    vocabulary-head product with the gather workgroups) from the stored
+    rocprofv3 FETCH_SIZE/WRITE_SIZE runs; (None, None) if the kernel's sources
+    have changed since they were taken."""
     try:
         with open(TRAFFIC_RECORD) as f:
             rec = json.load(f)
@@ -769,6 +771,11 @@ def main(argv=None):
     gout = torch.empty((NIDS, K), dtype=torch.bfloat16, device="cuda")
 
     def step(i):
+        # the product and the gather of the same table, one launch
+        c = i % COPIES
+        w4.w4_gemv_gather(dcodes[c], dsteps[c], dx, dids, y, gout)
+
+    def step_two_launches(i):
         c = i % COPIES
         w4.w4_gemv(dcodes[c], dsteps[c], dx, y)
         w4.w4_embed_gather(dcodes[c], dsteps[c], dids, gout)
@@ -776,33 +783,44 @@ def main(argv=None):
     # One decode step is replayed as one HIP graph (as the dev.to page does per
     # decode step); one graph per table copy, replayed in rotation.
     side = torch.cuda.Stream()
-    graphs = []
-    for c in range(COPIES):
-        step(c)
+
+    def step_graphs(fn):
+        gs = []
+        for c in range(COPIES):
+            fn(c)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.stream(side):
+                with torch.cuda.graph(g, stream=side):
+                    fn(c)
+            gs.append(g)
         torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.stream(side):
-            with torch.cuda.graph(g, stream=side):
-                step(c)
-        graphs.append(g)
-    torch.cuda.synchronize()
+        return gs
+    # The step is one launch: W untimed steps, then K steps launched back to
+    # back on the stream, bracketed by synchronisations (this is also the
+    # dominant kernel's duration: a rocprofv3 trace of this command agrees).
     for i in range(args.warmup):
-        graphs[i % COPIES].replay()
+        step(i)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    step_s = timer.per_call(lambda i: graphs[i % COPIES].replay(), args.steps, warmup=0)
+    step_s = timer.per_call(step, args.steps, warmup=0)
     wall = time.perf_counter() - t0
-    step_eager_s = timer.per_call(step, args.steps, warmup=0)
-    # dominant kernel: the GEMV alone, launched back to back on the stream
-    # (measured closest to the kernel's own duration in a rocprofv3 trace of
-    # this command; a graph of the same launches adds a gap per node)
+    # the same step replayed as one HIP graph per step (the page replays a graph
+    # per decode step; with one launch it only adds the replay's overhead)
+    graphs = step_graphs(step)
+    step_graph_s = timer.per_call(lambda i: graphs[i % COPIES].replay(), args.steps, warmup=2)
+    # for comparison: the product alone, the gather alone, and the step as two
+    # launches in one graph
     gemv_call = lambda i: w4.w4_gemv(dcodes[i % COPIES], dsteps[i % COPIES], dx, y)  # noqa: E731
     gemv_s = timer.per_call(gemv_call, args.steps, warmup=2)
     gemv_graph_s = timer.graph_per_call(gemv_call, args.steps)
     gather_s = timer.graph_per_call(lambda i: w4.w4_embed_gather(dcodes[i % COPIES], dsteps[i % COPIES],
                                                                   dids, gout), args.steps)
+    graphs2 = step_graphs(step_two_launches)
+    step2_s = timer.per_call(lambda i: graphs2[i % COPIES].replay(), args.steps, warmup=2)
+    del graphs2
     ceiling = probe_ceiling(w4, torch)
-    achieved = gbps(gemv_bytes(V, K), gemv_s)
+    achieved = gbps(STEP_BYTES, step_s)
     traffic, kname = measured_traffic()
     result = {
         "metric": "achieved HBM GB/s (% of peak) for W4A16 GEMV; us per 35-layer decode sweep",
@@ -822,15 +840,19 @@ def main(argv=None):
                    "table_copies_rotated": COPIES, "step_bytes": STEP_BYTES},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": traffic, "kernel": kname or "w4::gemv_kernel",
-                     "bytes_per_launch": gemv_bytes(V, K),
-                     "avg_launch_us": round(gemv_s * 1e6, 3)},
-        "extra": {"gemv_weight_GBps": round(gbps(w4_bytes(V, K), gemv_s), 2),
-                  "gemv_us_graph": round(gemv_graph_s * 1e6, 3),
-                  "ms_per_step_eager": round(step_eager_s * 1e3, 5),
-                  "gather_us": round(gather_s * 1e6, 3),
+                     "traffic": traffic,
+                     "kernel": (kname or "w4::gemv_kernel") + " (product and gather workgroups, one launch)",
+                     "bytes_per_launch": STEP_BYTES,
+                     "avg_launch_us": round(step_s * 1e6, 3)},
+        "extra": {"ms_per_step_graph": round(step_graph_s * 1e3, 5),
+                  "ms_per_step_two_launches_graph": round(step2_s * 1e3, 5),
+                  "gemv_alone_us": round(gemv_s * 1e6, 3),
+                  "gemv_alone_us_graph": round(gemv_graph_s * 1e6, 3),
+                  "gemv_alone_GBps": round(gbps(gemv_bytes(V, K), gemv_s), 2),
+                  "gemv_alone_weight_GBps": round(gbps(w4_bytes(V, K), gemv_s), 2),
+                  "gather_alone_us_graph": round(gather_s * 1e6, 3),
                   "probe_read_ceiling_GBps": {k: round(v, 1) for k, v in ceiling.items()},
-                  "gemv_frac_of_probe": round(achieved / max(ceiling.values()), 4),
+                  "step_frac_of_probe": round(achieved / max(ceiling.values()), 4),
                   "timed_wall_s": round(wall, 4)},
     }
     del dcodes, dsteps, graphs

@@ -70,6 +70,7 @@ _SIGNATURES = {
     "w4_moe_gemv_ids_noalloc": [_P, _P, _I64, _I64, _I32, _I32, _P, _I32, _I32, _I64, _P, _I32, _I32,
                                 _P, _I32, _I32, _P, _P, _P, _P, _P],
     "w4_embed_gather": [_P, _P, _I32, _I32, _P, _I32, _P, _P, _P],
+    "w4_gemv_gather": [_P, _P, _I32, _I32, _P, _I32, _P, _P, _I32, _P, _P, _P],
     "w4_rms_renorm": [_P, _I64, _I32, _I32, _P, _I64, _I32, _P],
     "w4_gemv_chain": [_P, _I32, _P, _P, _I64, _P],
     "w4_probe_stream": [_P, _I64, _P, _P],
@@ -415,6 +416,22 @@ def w4_embed_gather(codes, steps, ids, out=None, dev_err=None, stream=None):
     _check(lib.w4_embed_gather(_ptr(codes), _ptr(steps), V, K, _ptr(ids), n, _ptr(out),
                                _ptr(dev_err), _stream(stream)), "w4_embed_gather")
     return out
+
+
+def w4_gemv_gather(codes, steps, x, ids, y=None, out=None, dev_err=None, stream=None):
+    """w4_gemv and w4_embed_gather of the same table in one launch; returns
+    (y fp32 [V], out bf16 [n, K])."""
+    V, K = _matrix(codes, steps)
+    if x.numel() != K or not x.is_contiguous():
+        raise ValueError("x must be contiguous with K elements")
+    n = ids.numel()
+    if y is None:
+        y = torch.empty(V, dtype=torch.float32, device=codes.device)
+    if out is None:
+        out = torch.empty((n, K), dtype=torch.bfloat16, device=codes.device)
+    _check(lib.w4_gemv_gather(_ptr(codes), _ptr(steps), V, K, _ptr(x), _act_dtype(x), _ptr(y), _ptr(ids), n,
+                              _ptr(out), _ptr(dev_err), _stream(stream)), "w4_gemv_gather")
+    return y, out
 
 
 def w4_rms_renorm(v, K, out=None, out_dtype=torch.float16, stream=None):

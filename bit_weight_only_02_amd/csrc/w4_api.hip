@@ -327,6 +327,28 @@ int w4_embed_gather(const uint32_t *codes, const uint16_t *steps, int32_t V, int
                     "w4_embed_gather");
 }
 
+int w4_gemv_gather(const uint32_t *codes, const uint16_t *steps, int32_t V, int32_t K,
+                   const void *x, int32_t xdt, float *y, const int32_t *ids, int32_t n,
+                   uint16_t *out_bf16, int32_t *dev_err, void *stream) {
+    int st;
+    if ((st = check_matrix(codes, steps, V, K))) return st;
+    if ((st = check_dtype(xdt))) return st;
+    if (V > 0 && (!y || (K > 0 && !x))) return fail(W4_ERR_INVALID_ARG, "null x/y");
+    if (x && !aligned(x, 2)) return fail(W4_ERR_ALIGNMENT, "x not 2-byte aligned");
+    if (y && !aligned(y, 4)) return fail(W4_ERR_ALIGNMENT, "y not 4-byte aligned");
+    if (n < 0) return fail(W4_ERR_INVALID_ARG, "negative n");
+    if (n > 0 && (!ids || !out_bf16)) return fail(W4_ERR_INVALID_ARG, "null ids/out");
+    if (ids && !aligned(ids, 4)) return fail(W4_ERR_ALIGNMENT, "ids not 4-byte aligned");
+    if (out_bf16 && !aligned(out_bf16, 16)) return fail(W4_ERR_ALIGNMENT, "out not 16-byte aligned");
+    if (dev_err && !aligned(dev_err, 4)) return fail(W4_ERR_ALIGNMENT, "dev_err not aligned");
+    if (V == 0) return W4_OK;
+    if ((st = device_ready())) return st;
+    if (forced_launch_error()) return fail(W4_ERR_HIP, "forced launch error (test hook)");
+    return launched(w4::launch_gemv_gather(codes, steps, V, K, static_cast<const uint16_t *>(x), xdt, y, ids,
+                                           K > 0 ? n : 0, out_bf16, dev_err, static_cast<hipStream_t>(stream)),
+                    "w4_gemv_gather");
+}
+
 int w4_rms_renorm(const float *v, int64_t ldv, int32_t K, int32_t rows, void *out, int64_t ldo,
                   int32_t out_dt, void *stream) {
     int st;

@@ -18,6 +18,7 @@
 #include <type_traits>
 
 #include "w4_device.h"
+#include "w4_gather.h"
 #include "w4_internal.h"
 
 namespace w4 {
@@ -36,6 +37,13 @@ struct GemvPairs {
     long ldx;
     int n_experts, n_slots, x_per_pair, topk;
     long ldy;  // ids == nullptr and ldy != 0: gridDim.y activation rows (X ldx, Y ldy apart)
+    // The row gather from the same table, run by the last g_wgs workgroups of
+    // the grid (one wave per output row and slice of g_slices): rows g_ids[i]
+    // of the matrix, dequantised to bf16 into g_out (see gather_row_slice).
+    const int32_t *g_ids;
+    uint16_t *g_out;
+    int32_t *g_err;
+    int g_n, g_slices, g_wgs;
 };
 
 // RN: the activations are fp32 rows (x points at floats; the pair's row is
@@ -50,6 +58,15 @@ __global__ __launch_bounds__(256) void gemv_kernel(const uint4 *__restrict__ cod
                                                    float *__restrict__ y, const GemvPairs bp) {
     constexpr int SLOTS = kWave / L;
     extern __shared__ _Float16 xs[];  // the raw activations (stage_raw_halves(K))
+    // the gather workgroups (none unless asked for); the product uses the rest
+    const int gx = (int)gridDim.x - bp.g_wgs;
+    if ((int)blockIdx.x >= gx) {
+        const int idx = ((int)blockIdx.x - gx) * (int)(blockDim.x >> 6) + (int)(threadIdx.x >> 6);
+        if (idx < bp.g_n * bp.g_slices)
+            gather_row_slice(reinterpret_cast<const uint32_t *>(codes), steps, N, K, bp.g_ids, idx / bp.g_slices,
+                             idx % bp.g_slices, bp.g_out, bp.g_err);
+        return;
+    }
     // This workgroup's expert (uniform: scalar loads).  An id or slot out of
     // range leaves no row untouched: the pair's rows become NaN and the error
     // word is set.  The weight address is the only place the slot enters.
@@ -65,7 +82,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(const uint4 *__restrict__ cod
         }
         y += (long)p * N;
         if (bad) {
-            for (int n = blockIdx.x * blockDim.x + threadIdx.x; n < N; n += gridDim.x * blockDim.x)
+            for (int n = blockIdx.x * blockDim.x + threadIdx.x; n < N; n += gx * blockDim.x)
                 y[n] = __builtin_nanf("");
             if (blockIdx.x == 0 && threadIdx.x == 0 && bp.dev_err) *bp.dev_err = 1;
             return;
@@ -88,10 +105,10 @@ __global__ __launch_bounds__(256) void gemv_kernel(const uint4 *__restrict__ cod
     const int nwaves = blockDim.x >> 6;
     const int l = lane % L, slot = lane / L;
     const int rows_per_iter = nwaves * SLOTS * R;
-    const int gstride = gridDim.x * rows_per_iter;
+    const int gstride = gx * rows_per_iter;
 
     if (G == 0) {  // empty sums
-        for (int n = blockIdx.x * blockDim.x + threadIdx.x; n < N; n += gridDim.x * blockDim.x)
+        for (int n = blockIdx.x * blockDim.x + threadIdx.x; n < N; n += gx * blockDim.x)
             y[n] = 0.0f;
         return;
     }
@@ -539,8 +556,9 @@ GemvTile gemv_tile(int N, int K) {
     return best;
 }
 
-hipError_t launch_gemv(const uint32_t *codes, const uint16_t *steps, int N, int K,
-                       const uint16_t *x, int dt, float *y, hipStream_t stream) {
+// The schedule of a batch-1 product: the per-shape table, the wide-row form
+// for products too small to fill the chip, then the settings' override.
+static GemvTile choose_gemv_tile(int N, int K) {
     GemvTile t = gemv_tile(N, K);
     // A product too small to give every CU a workgroup is latency-bound: 64
     // lanes per row (four rows per workgroup) spread it over more workgroups
@@ -564,6 +582,12 @@ hipError_t launch_gemv(const uint32_t *codes, const uint16_t *steps, int N, int 
             o.blocks >= 1 && o.ring >= 0 && o.ring <= kRingMaxD)
             t = o;
     }
+    return t;
+}
+
+hipError_t launch_gemv(const uint32_t *codes, const uint16_t *steps, int N, int K,
+                       const uint16_t *x, int dt, float *y, hipStream_t stream) {
+    const GemvTile t = choose_gemv_tile(N, K);
     if (t.ring) {
         // the ring kernel's preconditions (a bad override is refused)
         const int G = K / 32;
@@ -583,6 +607,37 @@ hipError_t launch_gemv(const uint32_t *codes, const uint16_t *steps, int N, int 
     const size_t lds = (size_t)2 * stage_raw_halves(K) * sizeof(_Float16);
     hipLaunchKernelGGL(fn, dim3(t.blocks), dim3(64 * t.waves), lds, stream,
                        reinterpret_cast<const uint4 *>(codes), steps, N, K, x, dt, y, GemvPairs{});
+    return hipGetLastError();
+}
+
+// The product and the row gather from the same table in one launch: the
+// product's grid as launch_gemv would run it, plus one workgroup per
+// (waves per workgroup) gather rows and slices after it.  The two share no
+// memory but the table they read, so each output is bitwise what the separate
+// launches give.  (Under a ring-kernel override the two run as two launches.)
+hipError_t launch_gemv_gather(const uint32_t *codes, const uint16_t *steps, int N, int K, const uint16_t *x,
+                              int dt, float *y, const int32_t *ids, int n, uint16_t *out, int32_t *dev_err,
+                              hipStream_t stream) {
+    const GemvTile t = choose_gemv_tile(N, K);
+    const int slices = ((K >> 3) + kSliceWords - 1) / kSliceWords;
+    if (t.ring || n == 0 || K == 0) {
+        hipError_t e = launch_gemv(codes, steps, N, K, x, dt, y, stream);
+        if (e != hipSuccess || n == 0 || K == 0) return e;
+        return launch_gather(codes, steps, N, K, ids, n, out, dev_err, stream);
+    }
+    GemvFn fn = pick(t.L, t.NG, t.R, t.pf);
+    const long gwaves = (long)n * slices, gwgs = (gwaves + t.waves - 1) / t.waves;
+    if (!fn || gwgs > 65535 || (long)t.blocks + gwgs > 2147483647L) return hipErrorInvalidConfiguration;
+    GemvPairs bp{};
+    bp.g_ids = ids;
+    bp.g_out = out;
+    bp.g_err = dev_err;
+    bp.g_n = n;
+    bp.g_slices = slices;
+    bp.g_wgs = (int)gwgs;
+    const size_t lds = (size_t)2 * stage_raw_halves(K) * sizeof(_Float16);
+    hipLaunchKernelGGL(fn, dim3((unsigned)(t.blocks + gwgs)), dim3(64 * t.waves), lds, stream,
+                       reinterpret_cast<const uint4 *>(codes), steps, N, K, x, dt, y, bp);
     return hipGetLastError();
 }
 
@@ -631,7 +686,7 @@ hipError_t launch_gemv_pairs(const uint32_t *codes_base, const uint16_t *steps_b
     long bx = ((P <= 8 ? 512 : 768) + P - 1) / P;
     if (bx > need) bx = need;
     if (bx < 1) bx = 1;
-    GemvPairs bp;
+    GemvPairs bp{};
     bp.ids = ids;
     bp.slot_of = slot_of;
     bp.row_scale = row_scale;

@@ -36,6 +36,9 @@ const Settings &settings();
 
 hipError_t launch_gemv(const uint32_t *codes, const uint16_t *steps, int N, int K,
                        const uint16_t *x, int dt, float *y, hipStream_t stream);
+hipError_t launch_gemv_gather(const uint32_t *codes, const uint16_t *steps, int N, int K, const uint16_t *x,
+                              int dt, float *y, const int32_t *ids, int n, uint16_t *out, int32_t *dev_err,
+                              hipStream_t stream);
 
 // Small-M products (w4_mfma.h engine).  A workspace is needed when the plan
 // splits K (and, for the expert product, when route weights are given);

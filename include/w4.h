@@ -342,6 +342,20 @@ int w4_embed_gather(const uint32_t *codes, const uint16_t *steps, int32_t V, int
                     int32_t *dev_err, void *stream);
 
 /*
+ * The two uses of one 4-bit vocabulary table in a decode step [P1-S2, P1-S3],
+ * in a single launch: y = W x as w4_gemv computes it (W the [V][K] table) and
+ * the rows ids[0..n) of W dequantised to bf16 as w4_embed_gather computes it.
+ * The launch's last workgroups do the gather while the others run the
+ * product; both results are bitwise those of the two separate calls.
+ * Arguments, layouts, limits and errors are those of w4_gemv (codes, steps,
+ * V, K, x, xdt, y) and of w4_embed_gather (ids, n, out_bf16, dev_err); n may
+ * be 0 (the product alone).
+ */
+int w4_gemv_gather(const uint32_t *codes, const uint16_t *steps, int32_t V, int32_t K,
+                   const void *x, int32_t xdt, float *y, const int32_t *ids, int32_t n,
+                   uint16_t *out_bf16, int32_t *dev_err, void *stream);
+
+/*
  * Renormalisation between chained products [P1-S4], for `rows` vectors at
  * once (K a multiple of 4): for each row r, take the leading K entries u of
  * the fp32 vector

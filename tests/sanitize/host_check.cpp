@@ -116,6 +116,10 @@ int main() {
     // gather, renormalisation, chain, probe
     EXPECT(w4_embed_gather(c, s, N, K, ids.data(), -1, x.data(), nullptr, nullptr) != W4_OK);
     EXPECT(w4_embed_gather(c, s, N, K, ids.data(), 4, x.data(), nullptr, nullptr) == W4_ERR_NODEV);
+    EXPECT(w4_gemv_gather(c, s, N, K, x.data(), W4_BF16, y.data(), ids.data(), -1, x.data(), nullptr, nullptr) != W4_OK);
+    EXPECT(w4_gemv_gather(c, s, N, K, x.data(), 9, y.data(), ids.data(), 4, x.data(), nullptr, nullptr) != W4_OK);
+    EXPECT(w4_gemv_gather(c, s, N, K, x.data(), W4_BF16, y.data(), ids.data(), 4, x.data(), nullptr, nullptr) == W4_ERR_NODEV);
+    EXPECT(w4_gemv_gather(c, s, N, K, x.data(), W4_F16, y.data(), nullptr, 0, nullptr, nullptr, nullptr) == W4_ERR_NODEV);
     EXPECT(w4_rms_renorm(xf.data(), K, K, 2, x.data(), K, 7, nullptr) != W4_OK);
     EXPECT(w4_rms_renorm(xf.data(), K - 1, K, 2, x.data(), K, W4_F16, nullptr) != W4_OK);
     EXPECT(w4_rms_renorm(xf.data(), K, K, 2, x.data(), K, W4_F16, nullptr) == W4_ERR_NODEV);

@@ -20,7 +20,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("w4_gemv", "w4_gemm_smallM", "w4_gemm_prompt", "w4_moe_gemv_ids", "w4_embed_gather",
-              "w4_grid_to_codes",
+              "w4_gemv_gather", "w4_grid_to_codes",
               "w4_rms_renorm", "w4_gemv_chain", "w4_probe_stream", "w4_strerror"):
         assert n in names
 
@@ -73,6 +73,14 @@ def test_gather_and_renorm_argument_errors():
     assert L.w4_embed_gather(FAKE, FAKE, 10, 64, FAKE, 4, FAKE + 2, None, None) == -2
     assert L.w4_embed_gather(FAKE, FAKE, 10, 64, None, 4, FAKE, None, None) == -1
     assert L.w4_embed_gather(FAKE, FAKE, 10, 64, FAKE, 0, FAKE, None, None) == 0    # empty
+    # the product and the gather in one launch: the errors of either
+    assert L.w4_gemv_gather(FAKE, FAKE, 10, 48, FAKE, 0, FAKE, FAKE, 4, FAKE, None, None) == -1   # K % 32
+    assert L.w4_gemv_gather(FAKE, FAKE, 10, 64, FAKE, 5, FAKE, FAKE, 4, FAKE, None, None) == -3   # dtype
+    assert L.w4_gemv_gather(FAKE, FAKE, 10, 64, FAKE, 0, FAKE, FAKE, -1, FAKE, None, None) == -1  # n < 0
+    assert L.w4_gemv_gather(FAKE, FAKE, 10, 64, FAKE, 0, FAKE, None, 4, FAKE, None, None) == -1   # null ids
+    assert L.w4_gemv_gather(FAKE, FAKE, 10, 64, FAKE, 0, FAKE, FAKE, 4, FAKE + 2, None, None) == -2
+    assert L.w4_gemv_gather(FAKE, FAKE, 10, 64, None, 0, FAKE, FAKE, 4, FAKE, None, None) == -1   # null x
+    assert L.w4_gemv_gather(None, None, 0, 64, None, 0, None, None, 0, None, None, None) == 0     # empty
     assert L.w4_rms_renorm(FAKE, 64, 64, 1, FAKE, 64, 5, None) == -3
     assert L.w4_rms_renorm(None, 64, 64, 1, FAKE, 64, 0, None) == -1
     assert L.w4_rms_renorm(FAKE, 32, 64, 2, FAKE, 64, 0, None) == -1   # ldv < K

@@ -8,7 +8,7 @@ import torch
 
 import oracle
 import synth
-from tests.gpu_util import dev_codes, dev_steps, host_bits
+from tests.gpu_util import dev_act, dev_codes, dev_steps, host_bits, within_bound
 
 pytestmark = pytest.mark.gpu
 
@@ -98,3 +98,88 @@ def test_gather_bad_ids_give_nan_rows_and_error_flag(w4):
     assert np.all(np.isnan(o[1])) and np.all(np.isnan(o[2]))
     ref, bad = oracle.gather(codes, steps, V, K, ids[[0, 3]])
     assert np.array_equal(host_bits(out)[[0, 3]], ref)
+
+
+# ---- the product and the gather of one table in a single launch ----------------
+
+def run_fused(w4, dc, ds, x, ids, n_out=None):
+    V, K = dc.shape[0], dc.shape[1] * 8
+    y = torch.full((V,), float("nan"), dtype=torch.float32, device="cuda")
+    n = ids.numel()
+    out = torch.full((n, K), float("nan"), dtype=torch.bfloat16, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    w4.w4_gemv_gather(dc, ds, x, ids, y, out, err)
+    torch.cuda.synchronize()
+    return y, out, int(err.item())
+
+
+@pytest.mark.parametrize("dt", [synth.F16, synth.BF16])
+@pytest.mark.parametrize("V,K,n", [(1, 32, 1), (33, 96, 5), (4097, 1536, 64), (1000, 2816, 7),
+                                   (513, 8960, 3), (20000, 704, 1), (129, 16384, 2)])
+def test_gemv_gather_vs_oracle(w4, V, K, n, dt):
+    """Both outputs of the single launch against the oracle: every output of
+    the product within the bound, every gathered row bit-exact (rows 0 and
+    V - 1 included; 8960 and 16384 columns take several slices per row)."""
+    print(f"gemv_gather V={V} K={K} n={n} dt={dt}", flush=True)
+    rng = np.random.default_rng(V * 13 + K + n + dt)
+    codes, steps = synth.w4_matrix(rng, V, K)
+    x = synth.activations(rng, K, dt)
+    ids = synth.token_ids(rng, n, V)
+    ids[0] = V - 1
+    if n > 1:
+        ids[1] = 0
+    y, out, err = run_fused(w4, dev_codes(codes), dev_steps(steps), dev_act(x, dt), torch.from_numpy(ids).cuda())
+    assert err == 0
+    yo, ao = oracle.gemv(codes, steps, V, K, x, dt, threads=True)
+    ok, worst = within_bound(y.cpu().numpy(), yo, ao)
+    assert ok, f"worst |err|/sum|wx| = {worst}"
+    ref, bad = oracle.gather(codes, steps, V, K, ids)
+    assert bad == 0
+    assert np.array_equal(host_bits(out), ref)
+
+
+def test_gemv_gather_vocab_head_equals_separate_launches(w4):
+    """The decode step's shape, 262144 x 1536 with bf16 x and 64 ids: the
+    single launch gives bitwise the outputs of w4_gemv and w4_embed_gather,
+    and its gathered rows equal the oracle's."""
+    rng = np.random.default_rng(0)
+    V, K = 262144, 1536
+    codes, steps = synth.w4_matrix(rng, V, K)
+    x = synth.activations(rng, K, synth.BF16)
+    ids = synth.token_ids(np.random.default_rng(1), 64, V)
+    dc, ds, dx, dids = dev_codes(codes), dev_steps(steps), dev_act(x, synth.BF16), torch.from_numpy(ids).cuda()
+    y, out, err = run_fused(w4, dc, ds, dx, dids)
+    assert err == 0
+    y_sep = w4.w4_gemv(dc, ds, dx)
+    out_sep = w4.w4_embed_gather(dc, ds, dids)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int32), y_sep.view(torch.int32))
+    assert torch.equal(out.view(torch.int16), out_sep.view(torch.int16))
+    ref, bad = oracle.gather(codes, steps, V, K, ids)
+    assert bad == 0 and np.array_equal(host_bits(out), ref)
+    yo, ao = oracle.gemv(codes, steps, V, K, x, synth.BF16, rows=(V - 4096, V))
+    ok, worst = within_bound(y[V - 4096:].cpu().numpy(), yo, ao)
+    assert ok, f"worst |err|/sum|wx| = {worst}"
+
+
+def test_gemv_gather_bad_id_and_no_ids(w4):
+    """An id out of range: its row is NaN and the error word is set, the
+    other rows and the product are unaffected; n = 0 runs the product alone."""
+    rng = np.random.default_rng(21)
+    V, K = 3000, 1536
+    codes, steps = synth.w4_matrix(rng, V, K)
+    x = synth.activations(rng, K, synth.F16)
+    dc, ds, dx = dev_codes(codes), dev_steps(steps), dev_act(x, synth.F16)
+    ids = np.array([5, V, 7, -1], dtype=np.int32)
+    y, out, err = run_fused(w4, dc, ds, dx, torch.from_numpy(ids).cuda())
+    assert err == 1
+    bits = host_bits(out)
+    ref, _ = oracle.gather(codes, steps, V, K, np.array([5, 0, 7, 0], dtype=np.int32))
+    assert np.array_equal(bits[0], ref[0]) and np.array_equal(bits[2], ref[2])
+    assert np.all(bits[1] == 0x7FC0) and np.all(bits[3] == 0x7FC0)
+    y_sep = w4.w4_gemv(dc, ds, dx)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int32), y_sep.view(torch.int32))
+    y0, out0, err0 = run_fused(w4, dc, ds, dx, torch.empty(0, dtype=torch.int32, device="cuda"))
+    assert err0 == 0 and out0.numel() == 0
+    assert torch.equal(y0.view(torch.int32), y_sep.view(torch.int32))

@@ -656,7 +656,25 @@ def extra_grid_pack(w4, torch, np, synth, timer, reps: int = 20):
     t = timer.per_call(lambda i: w4.w4_grid_to_codes(tabs[i % copies], codes, steps), reps, warmup=2)
     nbytes = 2 * Vt * Kt + w4_bytes(Vt, Kt)
     res = {"us_per_call": round(t * 1e6, 2), "bytes_per_call": nbytes, "GBps": round(gbps(nbytes, t), 1),
-           "frac_of_peak": round(gbps(nbytes, t) / HBM_PEAK_GBPS, 4)}
+           "frac_of_peak": round(gbps(nbytes, t) / HBM_PEAK_GBPS, 4), "table": "arbitrary bf16 N(0, 0.03)"}
+    # a table on a 4-bit grid, as the page's trained tables are: codes uniform
+    # in 0..15, one positive step per group with a 5-bit significand (so every
+    # (c - 8) * step is a bf16 value), the values exact in bf16
+    del tabs
+    torch.cuda.empty_cache()
+    G = Kt // 32
+    tabs = []
+    for _ in range(copies):
+        c = torch.randint(0, 16, (Vt, Kt), generator=g, device="cuda", dtype=torch.int32)
+        e = torch.randint(100, 140, (Vt, G), generator=g, device="cuda", dtype=torch.int32)
+        mnt = torch.randint(0, 16, (Vt, G), generator=g, device="cuda", dtype=torch.int32) * 8
+        st = ((e * 128 + mnt).to(torch.int16)).view(torch.bfloat16).float()
+        tabs.append(((c - 8).float().view(Vt, G, 32) * st.view(Vt, G, 1)).view(Vt, Kt).to(torch.bfloat16))
+        del c, e, mnt, st
+    t = timer.per_call(lambda i: w4.w4_grid_to_codes(tabs[i % copies], codes, steps), reps, warmup=2)
+    res["grid_table"] = {"us_per_call": round(t * 1e6, 2), "GBps": round(gbps(nbytes, t), 1),
+                         "frac_of_peak": round(gbps(nbytes, t) / HBM_PEAK_GBPS, 4),
+                         "table": "on a 4-bit grid: codes uniform, 5-bit-significand steps"}
     del tabs
     torch.cuda.empty_cache()
     return res

@@ -104,37 +104,48 @@ __global__ __launch_bounds__(256) void grid_pack_kernel(const uint4 *__restrict_
             const float eu = an > 0.0f ? an : ap;  // the extreme the candidates divide
             const float e = eu * sc;
             const float re = 1.0f / e;
-            // the test every grid group passes (see above)
-            bool grid = true;
-#pragma unroll
-            for (int k = 0; k < 8; ++k) {
+            // The test every grid group passes (see above), on the lane's first
+            // value alone: groups of an arbitrary table nearly always fail it
+            // there, and a wave with no group left skips the search (a
+            // wave-uniform branch).  A candidate that no group of the wave has
+            // is skipped; the others are tested on two values per lane first
+            // and on the other six only in waves where some group passed; a
+            // candidate's full test is the definition itself, so passing the
+            // first test is needed, not trusted.
+            auto on840 = [&](int k) __attribute__((always_inline)) {
                 const float t = vs[k] * 840.0f;
                 const float m = __builtin_rintf(t * re);
-                grid = grid && m * e == t && fabsf(m) <= 6720.0f &&
-                       (v[k] == 0.0f || fabsf(v[k]) >= eu * 0.125f);
-            }
+                return m * e == t && fabsf(m) <= 6720.0f && (v[k] == 0.0f || fabsf(v[k]) >= eu * 0.125f);
+            };
+            const bool grid = quad_all(on840(0));
             bool found = false;
-            if (quad_all(grid)) {
+            if (__builtin_amdgcn_ballot_w64(grid) != 0) {
                 // the coarsest exact grid: candidates e / j, largest first
                 const int jmax = an > 0.0f ? 8 : 7;
 #pragma unroll
                 for (int j = 1; j <= 8; ++j) {
-                    if (found || j > jmax) continue;
                     const float fj = (float)j;
                     // e / j when that is a bf16 value: a candidate within two
                     // fp32 ulps of it rounds to it, and s * j == e is exact
                     const float s = bf16_round(e * (1.0f / fj));
-                    if (s * fj != e) continue;
                     const float u = s * (1.0f / sc);  // the step itself
-                    if (u * sc != s || (__float_as_uint(u) & 0xFFFFu) != 0u) continue;
-                    bool ok = true;
-#pragma unroll
-                    for (int k = 0; k < 8; ++k) {
+                    const bool cand = grid && !found && j <= jmax && s * fj == e && u * sc == s &&
+                                      (__float_as_uint(u) & 0xFFFFu) == 0u;
+                    auto on_grid = [&](int k) __attribute__((always_inline)) {
                         const float t = vs[k] * fj;
                         const float m = __builtin_rintf(t * re);
-                        ok = ok && m * e == t && m >= -8.0f && m <= 7.0f;
+                        return m * e == t && m >= -8.0f && m <= 7.0f;
+                    };
+                    bool ok = false;
+                    if (__builtin_amdgcn_ballot_w64(cand) != 0) {
+                        ok = quad_all(cand && on_grid(0) && on_grid(1));
+                        if (__builtin_amdgcn_ballot_w64(ok) != 0) {
+#pragma unroll
+                            for (int k = 2; k < 8; ++k) ok = ok && on_grid(k);
+                            ok = quad_all(ok);
+                        }
                     }
-                    if (quad_all(ok)) {
+                    if (ok) {
                         step = u;
                         ss = s;
                         found = true;

@@ -674,10 +674,13 @@ size_t chain_lds_bytes() {
 
 hipError_t launch_chain(const void *desc, int n, const uint16_t *x0, void *sync, unsigned spin_limit,
                         hipStream_t stream) {
-    // One workgroup per CU, all resident together on an otherwise idle device
-    // (the occupancy check makes sure one fits per CU).  A plain launch: if
-    // some workgroups could not start while others wait, the bounded waits for
-    // their cells end with the timeout error instead of a hang.
+    // One workgroup per CU, all of which must be resident together (each
+    // waits for the others' cells): a cooperative launch, which the runtime
+    // starts only when the whole grid can be resident and refuses when it
+    // never can (the occupancy check makes sure one fits per CU).  The bounded
+    // waits for cells stay, for a producer that does not finish.  (A plain
+    // launch measured about 10 us faster over the 35-layer sweep, without the
+    // guarantee.)
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
@@ -688,9 +691,12 @@ hipError_t launch_chain(const void *desc, int n, const uint16_t *x0, void *sync,
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, chain_kernel, kChainThreads, lds);
     if (e != hipSuccess) return e;
     if (per_cu < 1) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(chain_kernel, dim3(cus), dim3(kChainThreads), lds, stream,
-                       static_cast<const ChainMat *>(desc), n, x0, static_cast<unsigned *>(sync),
-                       spin_limit);
+    const ChainMat *d = static_cast<const ChainMat *>(desc);
+    unsigned *sy = static_cast<unsigned *>(sync);
+    void *args[] = {(void *)&d, (void *)&n, (void *)&x0, (void *)&sy, (void *)&spin_limit};
+    e = hipLaunchCooperativeKernel(reinterpret_cast<const void *>(chain_kernel), dim3(cus), dim3(kChainThreads),
+                                   args, (unsigned)lds, stream);
+    if (e != hipSuccess) return e;
     return hipGetLastError();
 }
 

@@ -393,9 +393,11 @@ int w4_rms_renorm(const float *v, int64_t ldv, int32_t K, int32_t rows, void *ou
  *         W4_MAX_K_CHAIN or than the previous N, a null or misaligned pointer;
  *         nothing computed).  After an error the caller zeroes the whole
  *         buffer before the next call.
- * One workgroup per CU, all resident at once on an otherwise idle device; if
- * they cannot all run together the bounded waits end with error 1 rather than
- * a hang.  Concurrent chains must use different sync buffers.
+ * One workgroup per CU, all resident at once: the kernel is launched
+ * cooperatively, so the runtime starts it only when the whole grid can be
+ * resident and the call fails with W4_ERR_HIP when it never can; a wait for a
+ * producer that does not finish still ends with error 1 rather than a hang.
+ * Concurrent chains must use different sync buffers.
  */
 #define W4_CHAIN_SYNC_BYTES(n_mats) (256 + (int64_t)(n_mats) * 32768)
 typedef struct {

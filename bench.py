@@ -8,8 +8,11 @@ dev.to page "Gemma 4 on a 4 GB GPU in Plain PyTorch", section "Step 2 - Keep
 the Vocabulary Tables in 4-Bit").  Three copies of the table are rotated so that
 the 256 MB Infinity Cache cannot hold the working set.
 
-`value` = algorithmic HBM bytes of one step / measured step time (GB/s, 1e9 B),
-each step replayed as one HIP graph.
+`value` = algorithmic HBM bytes of one step / measured step time (GB/s, 1e9 B).
+A step is one launch (w4_gemv_gather: the product and the gather together),
+the steps launched back to back; the same step replayed as one HIP graph per
+step, and as two launches (product, then gather) in one graph, are reported
+beside it.
 Printed as ONE JSON line, with the dominant kernel's roofline, the CPU oracle's
 time on a bounded sample of the same workload, and (under "extra") the other
 workloads of this path: the single 2048 x 1536 GEMV, the 35-layer decode-step

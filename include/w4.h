@@ -47,9 +47,11 @@
  *   fp32; the row gather writes bf16.
  *
  * Conventions:
- *   - All array pointers are DEVICE pointers owned by the caller.  The library
- *     allocates, frees and synchronises nothing (w4_moe_gemv_ids_noalloc keeps
- *     its scratch in a fixed array of the library's device image).
+ *   - All array pointers are DEVICE pointers owned by the caller (the slot
+ *     pools' host store excepted).  The compute entry points allocate, free
+ *     and synchronise nothing (w4_moe_gemv_ids_noalloc keeps its scratch in a
+ *     fixed array of the library's device image); the slot-pool object owns
+ *     host state, events and a small pinned staging area (see w4_pool_*).
  *   - Workspaces.  w4_gemm_smallM, w4_gemm_prompt, w4_decode_attention and
  *     w4_moe_gemv_ids need device memory beyond their inputs and outputs
  *     (partial sums, staged activations, per-split partials).  The caller owns

@@ -190,33 +190,38 @@ __device__ __forceinline__ void smallm_engine(const uint4 *__restrict__ codes,
 
     uint4 qr[R];
     uint2 sr[R];
-    // Loads of rounds r0 .. r0+R-1 (below re) of one tile.  Lane (n, Q) reads
+    // Loads of rounds r0 .. r0+R-1 of one tile (r0 < re).  Lane (n, Q) reads
     // the whole 16-byte group g0+Q of row n; rows past N and groups past the
     // slice are clamped to valid addresses (their A operands are zero, their
-    // steps 0).
+    // steps 0).  All R rounds are requested, those past re as copies of round
+    // re - 1 (never used), with no branch between the loads: the compiler then
+    // knows how many loads are in flight and waits for each round alone, not
+    // for all of them at the first use.  With STEPS8 every round of a slice is
+    // whole (K/32 and the slice length are multiples of 4), so its four steps
+    // are one 8-byte load.
     auto load_rounds = [&](int tile, int r0) __attribute__((always_inline)) {
         const int row = min(tile * 16 + n_l, N - 1);
         const uint4 *crow = codes + (long)row * G;
         const uint16_t *srow = steps + (long)row * G;
-        int n = 0;  // 16-byte code loads issued: one instruction each (wave-uniform)
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            if (r0 + r < re) {
-                const int g0 = g_lo + 4 * (r0 + r);
-                qr[r] = crow[min(g0 + q, g_hi - 1)];
-                ++n;
-                if (STEPS8 && g0 + 3 < g_hi) {
-                    sr[r] = *reinterpret_cast<const uint2 *>(srow + g0);
-                } else {
-                    const uint32_t s0 = srow[g0];
-                    const uint32_t s1 = g0 + 1 < g_hi ? srow[g0 + 1] : 0u;
-                    const uint32_t s2 = g0 + 2 < g_hi ? srow[g0 + 2] : 0u;
-                    const uint32_t s3 = g0 + 3 < g_hi ? srow[g0 + 3] : 0u;
-                    sr[r] = make_uint2(s0 | (s1 << 16), s2 | (s3 << 16));
-                }
+            const int g0 = g_lo + 4 * min(r0 + r, re - 1);
+            qr[r] = crow[min(g0 + q, g_hi - 1)];
+            if constexpr (STEPS8) {
+                sr[r] = *reinterpret_cast<const uint2 *>(srow + g0);
+            } else {
+                const uint32_t s0 = srow[g0];
+                const uint32_t t1 = srow[min(g0 + 1, g_hi - 1)];
+                const uint32_t t2 = srow[min(g0 + 2, g_hi - 1)];
+                const uint32_t t3 = srow[min(g0 + 3, g_hi - 1)];
+                const uint32_t s1 = g0 + 1 < g_hi ? t1 : 0u;
+                const uint32_t s2 = g0 + 2 < g_hi ? t2 : 0u;
+                const uint32_t s3 = g0 + 3 < g_hi ? t3 : 0u;
+                sr[r] = make_uint2(s0 | (s1 << 16), s2 | (s3 << 16));
             }
         }
-        return n;
+        // load instructions issued (wave-uniform)
+        return STEPS8 ? 2 * R : 5 * R;
     };
 
     // ---- stage the slice of the activations into A ------------------------
@@ -228,7 +233,23 @@ __device__ __forceinline__ void smallm_engine(const uint4 *__restrict__ codes,
     // loads come back in issue order, so the staging below waits only for
     // its own chunks while the weights are still in flight.
     const int nchunks = nr << (mp_log2 + 4);
-    if (xvec) {
+    // (A is read and written through an LDS-typed pointer: through the generic
+    // one these are flat accesses, which also wait for every outstanding
+    // global load, the weights included)
+    typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+    lds_u32x4 *AL = (lds_u32x4 *)A;
+    const int m = tid & mmask;
+    if (!xvec) {
+        // rows that are not 16-byte aligned: 16-bit loads, written to LDS as
+        // they are before any weight load is requested, so that nothing below
+        // waits for the weights (the chunk's row is m: 256 is a multiple of Mp)
+        for (int c = tid; c < nchunks; c += kSmallMWaves * 64) {
+            const int gl = min(c >> (mp_log2 + 2), ng - 1);
+            const uint16_t *src = xrow(min(m, M - 1)) + (g_lo + gl) * 32 + 8 * ((c >> mp_log2) & 3);
+            AL[c] = u32x4{src[0] | ((uint32_t)src[1] << 16), src[2] | ((uint32_t)src[3] << 16),
+                          src[4] | ((uint32_t)src[5] << 16), src[6] | ((uint32_t)src[7] << 16)};
+        }
+    } else {
         for (int c0 = wave * 64; c0 < nchunks; c0 += kSmallMWaves * 64) {
             const int c = c0 + lane;
             const int m = min(c & mmask, M - 1);
@@ -243,30 +264,18 @@ __device__ __forceinline__ void smallm_engine(const uint4 *__restrict__ codes,
     }
     asm volatile("" ::: "memory");  // (the weight loads stay behind the activation loads)
     int tg = tg_first;
-    // (a count of load instructions younger than the activation loads, never
-    // above the true one: the code loads, one instruction each; the step
-    // loads are not counted, so waiting for at most that many to be
-    // outstanding leaves the activation loads complete)
+    // (the load instructions younger than the activation loads: waiting for at
+    // most that many to be outstanding leaves the activation loads complete)
     int wloads = 0;
     if (tg * tpw + tsub < ntiles && rb < re) wloads = load_rounds(tg * tpw + tsub, rb);
     if (xvec) wait_vmcnt_upto(wloads);
     lds_barrier();
 
     // Thread t visits chunks t, t + 256, ...: always activation row t & mmask.
-    // (A is read and written through an LDS-typed pointer: through the generic
-    // one these are flat accesses, which also wait for every outstanding
-    // global load, the weights included)
-    typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
-    lds_u32x4 *AL = (lds_u32x4 *)A;
-    const int m = tid & mmask;
+    // Every chunk is in LDS by now, by either path.
     auto raw_chunk = [&](int c) __attribute__((always_inline)) {
-        if (xvec) {
-            const u32x4 v = AL[c];
-            return make_uint4(v.x, v.y, v.z, v.w);
-        }
-        const uint16_t *src = xrow(m) + (g_lo + (c >> (mp_log2 + 2))) * 32 + 8 * ((c >> mp_log2) & 3);
-        return make_uint4(src[0] | ((uint32_t)src[1] << 16), src[2] | ((uint32_t)src[3] << 16),
-                          src[4] | ((uint32_t)src[5] << 16), src[6] | ((uint32_t)src[7] << 16));
+        const u32x4 v = AL[c];
+        return make_uint4(v.x, v.y, v.z, v.w);
     };
 
     int s_m = 0, fallback = 0;

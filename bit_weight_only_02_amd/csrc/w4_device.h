@@ -210,17 +210,20 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
 // a wave are combined by wave_sum_f64; the four wave sums are added in wave
 // order.  load4(c) returns chunk c as a float4.  Every thread gets the total.
 // `red` is 4 doubles of shared scratch.
+// (one chunk's squares, in element order: every form of this sum uses it)
+__device__ __forceinline__ double add_squares4(double ss, float4 v) {
+    ss += (double)v.x * (double)v.x;
+    ss += (double)v.y * (double)v.y;
+    ss += (double)v.z * (double)v.z;
+    ss += (double)v.w * (double)v.w;
+    return ss;
+}
+
 template <class Load4>
 __device__ __forceinline__ double sum_squares_256(int K, Load4 load4, double *red) {
     const int tid = threadIdx.x;
     double ss = 0.0;
-    for (int c = tid; c < (K >> 2); c += 256) {
-        const float4 v = load4(c);
-        ss += (double)v.x * (double)v.x;
-        ss += (double)v.y * (double)v.y;
-        ss += (double)v.z * (double)v.z;
-        ss += (double)v.w * (double)v.w;
-    }
+    for (int c = tid; c < (K >> 2); c += 256) ss = add_squares4(ss, load4(c));
     ss = wave_sum_f64(ss);
     if ((tid & 63) == 0) red[tid >> 6] = ss;
     __syncthreads();
@@ -441,6 +444,39 @@ template <int pending>
 __device__ __forceinline__ void wait_vmcnt_mem() {
     static_assert(pending >= 0 && pending < 64, "vmcnt range");
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(pending) : "memory");
+}
+
+// stage_issue's requests written as inline assembly (with a memory clobber), so
+// that loads issued after them stay after them: a wait for at most n
+// outstanding loads, n the number of load instructions issued since, then
+// covers the activations alone.  Not marked non-temporal: every workgroup
+// reads x.
+__device__ __forceinline__ void stage_issue_ordered(const uint16_t *__restrict__ x, int K, uint16_t *raw) {
+    const int n16 = K >> 3;
+    if (n16 == 0) return;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    uint4 *r16 = reinterpret_cast<uint4 *>(raw);
+    for (int c0 = wave * 64; c0 < n16; c0 += (int)blockDim.x) {
+        const int c = min(c0 + lane, n16 - 1);
+        lds_dma16_so<false>(x, (uint32_t)c * 16u,
+                            (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void *)(r16 + c0));
+    }
+}
+
+// Wait until at most n (wave-uniform) vector-memory instructions of this wave
+// are outstanding; counts past 63 wait until at most 63 are (a binary search
+// down to an immediate).
+template <int Lo = 0, int Hi = 63>
+__device__ __forceinline__ void wait_vmcnt_upto(int n) {
+    if constexpr (Lo == Hi) {
+        wait_vmcnt_mem<Lo>();
+    } else {
+        constexpr int Mid = (Lo + Hi) / 2;
+        if (n <= Mid)
+            wait_vmcnt_upto<Lo, Mid>(n);
+        else
+            wait_vmcnt_upto<Mid + 1, Hi>(n);
+    }
 }
 
 // Wait until at most `pending` vector-memory loads are outstanding (gfx9

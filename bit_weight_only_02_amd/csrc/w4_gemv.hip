@@ -50,6 +50,10 @@ struct GemvPairs {
 // ldx floats apart), renormalised on load: the leading K entries divided by
 // their RMS, with the sum of squares in the order of w4_rms_renorm and the
 // same two roundings, so the staged fp16 values are bitwise that kernel's.
+// Rows renormalised on load of up to this many 4-value chunks per thread
+// (K <= 4096) are held in registers between the sum of squares and the staging.
+constexpr int kRnRegChunks = 4;
+
 template <int L, int NG, int R, int PF, bool RN = false>
 __global__ __launch_bounds__(256) void gemv_kernel(const uint4 *__restrict__ codes,
                                                    const uint16_t *__restrict__ steps,
@@ -136,45 +140,87 @@ __global__ __launch_bounds__(256) void gemv_kernel(const uint4 *__restrict__ cod
         }
     };
 
-    // The activations go to LDS by DMA with the first rows' weights requested
-    // right behind them; the workgroup then stages them once (exact fp16
-    // pairs, or the fp32 path for the whole workgroup when they cannot be
-    // staged exactly) and every lane copies its own groups into registers.
+    // The activations are requested first and the first rows' weights right
+    // behind them (every load issued without a branch, rows clamped), so that
+    // the staging waits for the activations alone while the weights are in
+    // flight; the workgroup stages them once (exact fp16 pairs, or the fp32
+    // path for the whole workgroup when they cannot be staged exactly) and
+    // every lane copies its own groups into registers.
     uint16_t *raw = reinterpret_cast<uint16_t *>(xs);
     uint4 *staged = reinterpret_cast<uint4 *>(raw + stage_raw_halves(K));
     int row0 = blockIdx.x * rows_per_iter;
     uint4 qa[R][NG];
     uint32_t sa[R][NG];
     Staging st;
+    st.scale = 0;  // (RN: fp16 values staged as they are)
+    st.fallback = 0;
     if constexpr (RN) {
-        // the fp32 row is read twice from memory (it is small and was just
-        // written): for the sum of squares, then for the staged fp16 pairs
         __shared__ double red_rn[4];
-        if (row0 < N) load_rows(qa, sa, row0);
         const float *xf = reinterpret_cast<const float *>(x);
         const bool vec = (reinterpret_cast<uintptr_t>(xf) & 15) == 0;
         auto load4 = [&](int c) __attribute__((always_inline)) {
             return vec ? reinterpret_cast<const float4 *>(xf)[c]
                        : make_float4(xf[4 * c], xf[4 * c + 1], xf[4 * c + 2], xf[4 * c + 3]);
         };
-        const double inv = renorm_scale(sum_squares_256(K, load4, red_rn), K);
-        for (int c = threadIdx.x; c < (K >> 3); c += blockDim.x) {
-            const float4 a = load4(2 * c), b = load4(2 * c + 1);
-            const uint32_t h0 = renorm_value(a.x, inv, 0), h1 = renorm_value(a.y, inv, 0);
-            const uint32_t h2v = renorm_value(a.z, inv, 0), h3 = renorm_value(a.w, inv, 0);
-            const uint32_t h4 = renorm_value(b.x, inv, 0), h5 = renorm_value(b.y, inv, 0);
-            const uint32_t h6 = renorm_value(b.z, inv, 0), h7 = renorm_value(b.w, inv, 0);
-            staged[c] = make_uint4(h0 | (h4 << 16), h1 | (h5 << 16), h2v | (h6 << 16), h3 | (h7 << 16));
+        const int nc = K >> 2;  // 4-value chunks of the row
+        if (nc <= kRnRegChunks * 256) {
+            // Thread t holds chunks t, t + 256, ... in registers: the row is
+            // read once, for the sum of squares (in sum_squares_256's order)
+            // and the staged fp16 pairs.
+            float4 xv[kRnRegChunks];
+#pragma unroll
+            for (int j = 0; j < kRnRegChunks; ++j) xv[j] = load4(min((int)threadIdx.x + 256 * j, nc - 1));
+            asm volatile("" ::: "memory");  // (the weight loads stay behind the row's)
+            load_rows(qa, sa, row0);
+            double ss = 0.0;
+#pragma unroll
+            for (int j = 0; j < kRnRegChunks; ++j)
+                if ((int)threadIdx.x + 256 * j < nc) ss = add_squares4(ss, xv[j]);
+            ss = wave_sum_f64(ss);
+            if ((threadIdx.x & 63) == 0) red_rn[threadIdx.x >> 6] = ss;
+            lds_barrier();
+            const double inv = renorm_scale(((red_rn[0] + red_rn[1]) + red_rn[2]) + red_rn[3], K);
+            // chunk c holds values 4c..4c+3: the low (c even) or high (c odd)
+            // halves of the four words of staged[c / 2]
+            uint16_t *sh = reinterpret_cast<uint16_t *>(staged);
+#pragma unroll
+            for (int j = 0; j < kRnRegChunks; ++j) {
+                const int c = (int)threadIdx.x + 256 * j;
+                if (c < nc) {
+                    uint16_t *o = sh + (c >> 1) * 8 + (c & 1);
+                    o[0] = renorm_value(xv[j].x, inv, 0);
+                    o[2] = renorm_value(xv[j].y, inv, 0);
+                    o[4] = renorm_value(xv[j].z, inv, 0);
+                    o[6] = renorm_value(xv[j].w, inv, 0);
+                }
+            }
+        } else {
+            // a long row: read twice (for the sum of squares, then for the
+            // staged pairs)
+            load_rows(qa, sa, row0);
+            const double inv = renorm_scale(sum_squares_256(K, load4, red_rn), K);
+            for (int c = threadIdx.x; c < (K >> 3); c += blockDim.x) {
+                const float4 a = load4(2 * c), b = load4(2 * c + 1);
+                const uint32_t h0 = renorm_value(a.x, inv, 0), h1 = renorm_value(a.y, inv, 0);
+                const uint32_t h2v = renorm_value(a.z, inv, 0), h3 = renorm_value(a.w, inv, 0);
+                const uint32_t h4 = renorm_value(b.x, inv, 0), h5 = renorm_value(b.y, inv, 0);
+                const uint32_t h6 = renorm_value(b.z, inv, 0), h7 = renorm_value(b.w, inv, 0);
+                staged[c] = make_uint4(h0 | (h4 << 16), h1 | (h5 << 16), h2v | (h6 << 16), h3 | (h7 << 16));
+            }
         }
         lds_barrier();
-        st.scale = 0;  // fp16 values staged as they are
-        st.fallback = 0;
     } else {
-        stage_issue(x, K, raw);
-        if (row0 < N) load_rows(qa, sa, row0);
-        if (!stage_vector_path(x))
+        // (rows that are not 16-byte aligned: 16-bit loads, written to LDS
+        // before any weight load is requested)
+        const bool xvec = stage_vector_path(x);
+        if (xvec)
+            stage_issue_ordered(x, K, raw);
+        else
             for (int i = threadIdx.x; i < K; i += blockDim.x) raw[i] = x[i];
-        wait_vmcnt<0>();
+        asm volatile("" ::: "memory");  // (the weight loads stay behind the activations)
+        load_rows(qa, sa, row0);
+        // each (row, group) takes one 16-byte and one 2-byte load instruction
+        if (xvec) wait_vmcnt_upto(2 * R * NG);
         lds_barrier();
         // x staged once per workgroup, then each lane takes its own groups
         st = stage_x_workgroup(raw, staged, K, dt);

@@ -49,22 +49,6 @@ constexpr int kSmallMMaxRounds = 8;       // rounds per wave above which K is sp
 constexpr long kSmallMTargetGroups = 768; // workgroups: 3 per CU, each looping over its tiles
 constexpr long kSmallMWideGroups = 256;   // the same for 8 or more rows with one wave per tile
 
-// Wait until at most n (wave-uniform) vector-memory instructions of this wave
-// are outstanding; counts past 63 wait for none (a binary search down to an
-// immediate).
-template <int Lo = 0, int Hi = 63>
-__device__ __forceinline__ void wait_vmcnt_upto(int n) {
-    if constexpr (Lo == Hi) {
-        wait_vmcnt_mem<Lo>();
-    } else {
-        constexpr int Mid = (Lo + Hi) / 2;
-        if (n <= Mid)
-            wait_vmcnt_upto<Lo, Mid>(n);
-        else
-            wait_vmcnt_upto<Mid + 1, Hi>(n);
-    }
-}
-
 // 4x4 transpose of words across the four 16-lane groups: on entry lane group
 // Q holds words 0..3 of group Q in v[0..3]; on exit lane group q holds word q
 // of groups 0..3 in v[0..3].

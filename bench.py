@@ -490,19 +490,22 @@ def extra_moe(w4, torch, np, synth, timer, reps: int = 5):
     return out
 
 
-def moe_streaming(w4, torch, np, synth, layers, E, topk, S, steps: int = 3):
+def moe_streaming(w4, torch, np, synth, layers, E, topk, S, steps: int = 6):
     """Expert streaming through 32-slot pools (the anyesh.me page's design, on
     this box's PCIe link): the 30 layers' experts sit in a pinned host store;
     per layer and token the LFU pool takes the misses by asynchronous copies on
     a second stream while a shared dense FFN (gate/up 2x2816x2816, down
     2816x2816, W4) runs on the compute stream, then one join.  The host reads
     each layer's routing only after the previous layer has finished, as a
-    router's choice would be.  Reported: us
-    per token with the overlap on and off (join before the dense FFN) and with
-    every expert resident (direct addressing), bytes streamed per token, the
-    copy stream's GB/s, the overlap fraction (time saved by the overlap over
-    the overlap possible, min(copy, dense FFN) per layer), and bitwise identity
-    of the last layer's output against direct addressing."""
+    router's choice would be.  Two managers with pools of their own run the
+    same tokens, one joining before the dense FFN (overlap off) and one after
+    it (overlap on), token by token in alternation so that drift of the link
+    falls on both.  Reported: the medians of us per token with the overlap on
+    and off and with every expert resident (direct addressing), bytes streamed
+    per token, the copy stream's GB/s, the overlap fraction (the median of the
+    per-token time saved over the overlap possible, min(copy, dense FFN) per
+    token), and bitwise identity of the last layer's output against direct
+    addressing."""
     L, T = len(layers), 1
     KG, NG, KD, ND, DF = 2816, 1408, 704, 2816, 2816
     g = torch.Generator(device="cuda")
@@ -511,8 +514,6 @@ def moe_streaming(w4, torch, np, synth, layers, E, topk, S, steps: int = 3):
              for gc, gs, dc, ds in layers]
     part_bytes = [p[0].numel() * p.element_size() for p in parts[0]]
     host = [[p.view(torch.uint8).cpu().pin_memory() for p in lp] for lp in parts]
-    pools = [[torch.empty((S, p.shape[1]), dtype=p.dtype, device="cuda") for p in lp] for lp in parts]
-    slots = [torch.full((E,), -1, dtype=torch.int32, device="cuda") for _ in range(L)]
     dense = []
     for _ in range(L):
         a = synth.w4_matrix_torch(g, 2 * DF, DF, "cuda")
@@ -537,16 +538,24 @@ def moe_streaming(w4, torch, np, synth, layers, E, topk, S, steps: int = 3):
         w4.w4_rms_renorm(Hd, DF, out=xd)
         w4.w4_gemv(da, ds_, xd, Yd)
 
-    def token(k, stream_on=True, overlap=True):
+    def new_state():
+        """A fresh manager with empty pools of its own."""
+        return {"pool": w4.w4_pool_create(L, E, S, part_bytes),
+                "pools": [[torch.empty((S, p.shape[1]), dtype=p.dtype, device="cuda") for p in lp] for lp in parts],
+                "slots": [torch.full((E,), -1, dtype=torch.int32, device="cuda") for _ in range(L)]}
+
+    def token(k, st=None, overlap=True):
+        """One token; st None: every expert resident (direct addressing)."""
         x = x0
         for li in range(L):
             (gc, gs, dc, ds) = layers[li]
             ids_dev, route = dev[k][li]
             kw = {}
-            if stream_on:
+            if st is not None:
                 # the router's choice is read on the host once the previous
                 # layer's output exists (the page's callback on the top-k
                 # node): a host wait, then the copies are requested
+                pool, pools, slots = st["pool"], st["pools"], st["slots"]
                 torch.cuda.current_stream().synchronize()
                 w4.w4_pool_prepare(pool, li, tokens[k][li][0], host[li], pools[li], slots[li], copy_stream)
                 if not overlap:
@@ -563,8 +572,8 @@ def moe_streaming(w4, torch, np, synth, layers, E, topk, S, steps: int = 3):
                                workspace=ws, **kw)
             w4.w4_moe_gemv_ids(dc, ds, ND * KD // 8, ND * KD // 32, ND, KD, Gb, ids_dev, x_per_pair=True,
                                n_experts=E, route_w=route, Y=Db[li & 1], workspace=ws, **kw)
-            if stream_on:
-                w4.w4_pool_release(pool, li)
+            if st is not None:
+                w4.w4_pool_release(st["pool"], li)
             x = Db[li & 1]
         return x
 
@@ -575,33 +584,27 @@ def moe_streaming(w4, torch, np, synth, layers, E, topk, S, steps: int = 3):
         torch.cuda.synchronize()
         return time.perf_counter() - t0
 
-    def run_mode(overlap):
-        """A fresh manager and empty pools, token 0 to warm up, then tokens
-        1..steps: the same requests (so the same copies) in every mode."""
-        nonlocal pool
-        if pool is not None:
-            torch.cuda.synchronize()
-            w4.w4_pool_destroy(pool)
-        pool = w4.w4_pool_create(L, E, S, part_bytes)
-        for sl in slots:
-            sl.fill_(-1)
-        token(0, overlap=overlap)
-        h0, m0, b0 = w4.w4_pool_stats(pool)
-        t = sum(timed(lambda k=k: token(k, overlap=overlap)) for k in range(1, steps + 1)) / steps
-        h1, m1, b1 = w4.w4_pool_stats(pool)
-        return t, (h1 - h0) / steps, (m1 - m0) / steps, (b1 - b0) / steps
-
-    pool = None
-    t_off, _, _, _ = run_mode(False)
-    t_on, hits, misses, per_tok = run_mode(True)
-    t_res = sum(timed(lambda k=k: token(k, stream_on=False)) for k in range(1, steps + 1)) / steps
+    # the two managers see the same requests (so the same copies), token by
+    # token in alternation; token 0 warms each up
+    st_off, st_on = new_state(), new_state()
+    token(0, st_off, overlap=False)
+    token(0, st_on, overlap=True)
+    h0, m0, b0 = w4.w4_pool_stats(st_on["pool"])
+    t_off, t_on = [], []
+    for k in range(1, steps + 1):
+        t_off.append(timed(lambda: token(k, st_off, overlap=False)))
+        t_on.append(timed(lambda: token(k, st_on, overlap=True)))
+    h1, m1, b1 = w4.w4_pool_stats(st_on["pool"])
+    hits, misses, per_tok = (h1 - h0) / steps, (m1 - m0) / steps, (b1 - b0) / steps
+    t_res = [timed(lambda k=k: token(k)) for k in range(1, steps + 1)]
     # identity: the last token's output through the pools (as they stand)
     # against direct addressing of the resident experts
-    y_on = token(steps).clone()
-    y_off = token(steps, stream_on=False).clone()
+    y_on = token(steps, st_on).clone()
+    y_off = token(steps).clone()
     torch.cuda.synchronize()
     identical = bool(torch.equal(y_on.view(torch.int32), y_off.view(torch.int32)))
-    w4.w4_pool_destroy(pool)
+    w4.w4_pool_destroy(st_off["pool"])
+    w4.w4_pool_destroy(st_on["pool"])
     # the copy stream alone: pinned host to device, 64 MB copies into scratch
     src = host[0][0].view(-1)[:64 << 20]
     dst = torch.empty(src.numel(), dtype=torch.uint8, device="cuda")
@@ -616,15 +619,18 @@ def moe_streaming(w4, torch, np, synth, layers, E, topk, S, steps: int = 3):
     copy_gbps = n * src.numel() / (e0.elapsed_time(e1) / 1e3) / 1e9
     t_dense = sum(timed(lambda li=li: dense_ffn(li, Db[0])) for li in range(L))
     t_copy = per_tok / (copy_gbps * 1e9)
-    res = {"us_per_token_overlap_on": round(t_on * 1e6, 1), "us_per_token_overlap_off": round(t_off * 1e6, 1),
-           "us_per_token_all_resident": round(t_res * 1e6, 1),
+    med = lambda v: float(np.median(v))
+    saved = med([a - b for a, b in zip(t_off, t_on)])
+    res = {"us_per_token_overlap_on": round(med(t_on) * 1e6, 1), "us_per_token_overlap_off": round(med(t_off) * 1e6, 1),
+           "us_per_token_all_resident": round(med(t_res) * 1e6, 1),
+           "tokens_timed_per_mode": steps,
            "expert_bytes_streamed_per_token": int(per_tok),
            "misses_per_token": round(misses, 2), "hits_per_token": round(hits, 2),
            "copy_GBps": round(copy_gbps, 1),
-           "overlap_fraction": round(max(0.0, t_off - t_on) / max(1e-9, min(t_copy, t_dense)), 3),
+           "overlap_fraction": round(saved / max(1e-9, min(t_copy, t_dense)), 3),
            "us_dense_ffn_per_token": round(t_dense * 1e6, 1),
            "streamed_bitwise_identical_to_resident": identical}
-    del host, pools, dense
+    del host, st_off, st_on, dense
     return res
 
 

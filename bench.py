@@ -345,7 +345,14 @@ def extra_sweep(w4, torch, np, synth, timer, reps: int = 20):
                           ).cuda().view(torch.float16)
     desc = w4.w4_chain_desc(mats, ys)
     sync = w4.w4_chain_sync(len(shapes))
-    chain = timer.per_call(lambda i: w4.w4_gemv_chain(desc, x0, sync), reps)
+    # The chain (a cooperative launch) runs on a stream of its own: on the
+    # default stream of a process that had used four other streams it measured
+    # 692 against 622 us per sweep (a plain launch of the same kernel: 603 us
+    # on either).
+    cs = torch.cuda.Stream()
+    with torch.cuda.stream(cs):
+        chain = timer.per_call(lambda i: w4.w4_gemv_chain(desc, x0, sync), reps)
+    torch.cuda.synchronize()
     err = int(sync[2].item())
 
     def separate(i):

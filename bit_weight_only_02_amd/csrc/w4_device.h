@@ -357,10 +357,12 @@ __device__ __forceinline__ void load_staged_group(const uint4 *staged, int g, h2
 
 // Staging of a raw activation vector: stage_issue() requests all of x straight
 // into LDS (global_load_lds_dwordx4: no registers; each wave moves 64 chunks of
-// 16 bytes per instruction); the kernel then issues its first weight loads and
-// waits for every outstanding load (wait_vmcnt<0>) before reading the staged
-// bytes.  (Waiting for a partial count would depend on the compiler keeping the
-// weight loads after the activation loads, which it does not promise.)
+// 16 bytes per instruction); a kernel using it issues its first weight loads
+// and waits for every outstanding load (wait_vmcnt<0>) before reading the
+// staged bytes, since with the builtin the compiler does not promise to keep
+// the weight loads after the activation loads.  stage_issue_ordered() (below)
+// makes the same requests as inline assembly, which later loads stay behind,
+// so that a wait for the activations alone suffices.
 // `raw` needs stage_raw_halves(K) halves.
 __device__ __forceinline__ bool stage_vector_path(const uint16_t *x) {
     return (reinterpret_cast<uintptr_t>(x) & 15) == 0;

@@ -109,6 +109,36 @@ def test_chain_decode_sweep_35_layers(w4):
     check_teacher_forced(w4, mats, x0, ys, rows=rows, full_upto=4)
 
 
+def test_chain_on_a_stream_of_its_own_matches_the_default_stream(w4):
+    """The cooperative chain launched on a non-default stream (as the sweep
+    benchmark runs it), with other streams in use, gives the bits of the same
+    chain on the default stream and leaves every exchange cell cleared."""
+    shapes = [(2560, 1536), (1536, 2048), (16384, 1536), (1536, 8192)] * 3
+    mats = make_mats(shapes, 5)
+    x0 = dev_act(synth.activations(np.random.default_rng(5), 1536, F16), F16)
+    ref = [torch.empty(N, device="cuda") for N, _ in shapes]
+    sync = w4.w4_chain_sync(len(shapes))
+    w4.w4_gemv_chain(w4.w4_chain_desc(mats, ref), x0, sync)
+    torch.cuda.synchronize()
+    busy = torch.zeros(1 << 16, device="cuda")
+    others = [torch.cuda.Stream() for _ in range(4)]
+    for s_ in others:
+        with torch.cuda.stream(s_):
+            busy.add_(1.0)
+    own = torch.cuda.Stream()
+    ys = [torch.full((N,), float("nan"), device="cuda") for N, _ in shapes]
+    desc = w4.w4_chain_desc(mats, ys)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(own):
+        w4.w4_gemv_chain(desc, x0, sync)
+        w4.w4_gemv_chain(desc, x0, sync, stream=own)
+    torch.cuda.synchronize()
+    assert sync[0].item() == 0 and sync[2].item() == 0
+    assert int(torch.count_nonzero(sync)) == 0
+    for a, b in zip(ref, ys):
+        assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+
+
 def test_chain_longer_than_descriptor_cache(w4):
     """300 small matrices: descriptors past the first 256 are brought into the
     kernel's table while the chain runs."""

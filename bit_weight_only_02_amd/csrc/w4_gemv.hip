@@ -473,26 +473,28 @@ namespace {
 
 typedef void (*GemvFn)(const uint4 *, const uint16_t *, int, int, const uint16_t *, int, float *,
                        const GemvPairs);
-template <int L>
+template <int L, int R>
 GemvFn pick_rn_ng(int NG) {
     switch (NG) {
-        case 1: return gemv_kernel<L, 1, 1, 0, true>;
-        case 2: return gemv_kernel<L, 2, 1, 0, true>;
-        case 3: return gemv_kernel<L, 3, 1, 0, true>;
-        case 4: return gemv_kernel<L, 4, 1, 0, true>;
-        case 6: return gemv_kernel<L, 6, 1, 0, true>;
-        case 8: return gemv_kernel<L, 8, 1, 0, true>;
+        case 1: return gemv_kernel<L, 1, R, 0, true>;
+        case 2: return gemv_kernel<L, 2, R, 0, true>;
+        case 3: return gemv_kernel<L, 3, R, 0, true>;
+        case 4: return gemv_kernel<L, 4, R, 0, true>;
+        case 6: return gemv_kernel<L, 6, R, 0, true>;
+        case 8: return gemv_kernel<L, 8, R, 0, true>;
     }
     return nullptr;
 }
 
-// the kernels that renormalise fp32 rows on load (one row per slot, no prefetch)
+// the kernels that renormalise fp32 rows on load (R = 1 or 3 rows per slot in
+// flight, no prefetch)
+template <int R>
 GemvFn pick_rn(int L, int NG) {
     switch (L) {
-        case 8: return pick_rn_ng<8>(NG);
-        case 16: return pick_rn_ng<16>(NG);
-        case 32: return pick_rn_ng<32>(NG);
-        case 64: return pick_rn_ng<64>(NG);
+        case 8: return pick_rn_ng<8, R>(NG);
+        case 16: return pick_rn_ng<16, R>(NG);
+        case 32: return pick_rn_ng<32, R>(NG);
+        case 64: return pick_rn_ng<64, R>(NG);
     }
     return nullptr;
 }
@@ -722,9 +724,13 @@ hipError_t launch_gemv_pairs(const uint32_t *codes_base, const uint16_t *steps_b
                              int n_experts, int n_slots, const float *row_scale, float *out,
                              int32_t *dev_err, hipStream_t stream) {
     const GemvTile t = gemv_tile(N, K);
-    const int R = 1, pf = 0;
-    // dt 2: fp32 rows renormalised on load
-    GemvFn fn = dt == 2 ? (R == 1 && pf == 0 && t.waves == 4 ? pick_rn(t.L, t.NG) : nullptr)
+    // dt 2: fp32 rows renormalised on load.  Up to 8 pairs (one token) those
+    // launches keep three rows per slot in flight, so that a workgroup's rows
+    // are requested at once (an expert token 441-445 against 455-458 us);
+    // with more pairs one row per slot stays (at 32 pairs three measured
+    // 932-938 against 851-884 us).
+    const int R = (dt == 2 && P <= 8) ? 3 : 1, pf = 0;
+    GemvFn fn = dt == 2 ? (t.waves == 4 ? (R == 3 ? pick_rn<3>(t.L, t.NG) : pick_rn<1>(t.L, t.NG)) : nullptr)
                         : pick(t.L, t.NG, R, pf);
     if (!fn || P < 1 || P > 65535) return hipErrorInvalidConfiguration;
     const long rows_per_iter = (long)(64 / t.L) * t.waves * R;

@@ -105,6 +105,32 @@ def test_gemm_leading_dimensions(w4):
     assert within_bound(Y, Yo, Ao)[0]
 
 
+@pytest.mark.parametrize("M,dt", [(8, BF16), (16, F16), (6, BF16)])
+def test_gemm_rows_not_16_byte_aligned(w4, M, dt):
+    """Activation rows that are not 16-byte aligned (an odd row stride, and a
+    view that starts one element in) are staged by 16-bit loads instead of
+    direct-to-LDS copies: the same staged values, so the same bits as the
+    aligned rows, and within the bound of the oracle."""
+    print(f"smallM unaligned rows M={M} dt={dt}", flush=True)
+    rng = np.random.default_rng(30 + M + dt)
+    N, K = 700, 1536
+    codes, steps = synth.w4_matrix(rng, N, K)
+    X = synth.activations(rng, (M, K), dt)
+    dc, ds = dev_codes(codes), dev_steps(steps)
+    ref = w4.w4_gemm_smallM(dc, ds, dev_act(X, dt))
+    ld = K + 3                                   # odd row stride (not a multiple of 8)
+    big = np.zeros((M, ld + 1), dtype=np.uint16)
+    big[:, 1:K + 1] = X                          # rows start one element in
+    dbig = dev_act(big, dt)
+    Xv = dbig[:, 1:K + 1]
+    assert Xv.stride(0) == ld + 1 and (Xv.data_ptr() % 16) != 0
+    got = w4.w4_gemm_smallM(dc, ds, Xv)
+    torch.cuda.synchronize()
+    assert torch.equal(ref.view(torch.int32), got.view(torch.int32))
+    Yo, Ao = oracle_rows(codes, steps, N, K, X, dt, M)
+    assert within_bound(got.cpu().numpy(), Yo, Ao)[0]
+
+
 def test_gemm_one_hot_rows_are_bit_exact(w4):
     rng = np.random.default_rng(2)
     N, K, M = 64, 2048, 16

@@ -127,6 +127,27 @@ def test_gemv_vocab_head_262144x1536_bf16_sampled(w4):
 
 
 @pytest.mark.parametrize("dt", [F16, BF16])
+@pytest.mark.parametrize("N,K", [(97, 1536), (1000, 2816), (20000, 704)])
+def test_gemv_x_not_16_byte_aligned(w4, N, K, dt):
+    """An activation vector that starts one element past a 16-byte boundary is
+    copied to LDS by 16-bit loads instead of direct-to-LDS copies: the same
+    staged values, so the bits of the aligned vector."""
+    print(f"gemv unaligned x N={N} K={K} dt={dt}", flush=True)
+    rng = np.random.default_rng(N + K + 5 * dt)
+    codes, steps = synth.w4_matrix(rng, N, K)
+    x = synth.activations(rng, K, dt)
+    dc, ds = dev_codes(codes), dev_steps(steps)
+    ref = w4.w4_gemv(dc, ds, dev_act(x, dt))
+    big = np.zeros(K + 8, dtype=np.uint16)
+    big[1:K + 1] = x
+    xv = dev_act(big, dt)[1:K + 1]
+    assert xv.data_ptr() % 16 != 0
+    got = w4.w4_gemv(dc, ds, xv)
+    torch.cuda.synchronize()
+    assert torch.equal(ref.view(torch.int32), got.view(torch.int32))
+
+
+@pytest.mark.parametrize("dt", [F16, BF16])
 def test_gemv_one_hot_is_bit_exact(w4, dt):
     rng = np.random.default_rng(3)
     N, K = 77, 1536

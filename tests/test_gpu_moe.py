@@ -219,6 +219,32 @@ def test_moe_fp32_rows_renormalised_on_load(w4, T, xpp, K):
     assert ok, worst
 
 
+@pytest.mark.parametrize("T,K", [(1, 2816), (4, 704), (6, 704)])
+def test_moe_rows_not_16_byte_aligned(w4, T, K):
+    """Activation rows at an odd row stride (fp32 rows renormalised on load,
+    and bf16 rows) are read without vector loads or direct-to-LDS copies: the
+    bits of the same rows at an aligned stride, on both paths."""
+    print(f"moe unaligned rows T={T} K={K}", flush=True)
+    rng = np.random.default_rng(90 + T + K)
+    E, N, topk = 12, 160, 4
+    codes, steps = experts(rng, E, N, K)
+    ids, route = synth.expert_choice(rng, T, E, topk)
+    dc, ds = dev_codes(codes.reshape(-1, K // 8)), dev_steps(steps.reshape(-1, K // 32))
+    dids = torch.from_numpy(ids.astype(np.int32)).cuda()
+    X32 = torch.from_numpy(rng.normal(0, 2, size=(T, K)).astype(np.float32)).cuda()
+    Xb = dev_act(synth.activations(rng, (T, K), BF16), BF16)
+    for X in (X32, Xb):
+        big = torch.zeros((T, K + 3), dtype=X.dtype, device="cuda")
+        big[:, 1:K + 1] = X
+        Xv = big[:, 1:K + 1]
+        ref = w4.w4_moe_gemv_ids(dc, ds, N * K // 8, N * K // 32, N, K, X.contiguous(), dids, n_experts=E,
+                                 route_w=torch.from_numpy(route).cuda())
+        got = w4.w4_moe_gemv_ids(dc, ds, N * K // 8, N * K // 32, N, K, Xv, dids, n_experts=E,
+                                 route_w=torch.from_numpy(route).cuda())
+        torch.cuda.synchronize()
+        assert torch.equal(ref.view(torch.int32), got.view(torch.int32)), (T, K, X.dtype)
+
+
 def test_moe_many_pairs_share_an_expert(w4):
     # 20 tokens all choose expert 3 first: more pairs than one MFMA tile of rows
     rng = np.random.default_rng(6)
